@@ -1,0 +1,213 @@
+/*
+ * nvfp4.h -- C ABI of the NVFP4 quantized linear for AMD Instinct MI355X (gfx950).
+ *
+ * Formats (FlashInfer PR #3597 "Add BF16_FP4 GEMM ... for W4A16 workloads",
+ * Description, API example and review thread; FreeToken PR #737, Changes):
+ *   - a weight or activation matrix [rows, K] in NVFP4 is two device buffers:
+ *       codes  uint8 [rows, K/2]  two e2m1 codes per byte, even k in the low
+ *                                 nibble; a code keeps its sign in bit 3 and
+ *                                 its magnitude index (0, .5, 1, 1.5, 2, 3, 4,
+ *                                 6) in bits 2..0;
+ *       scales uint8 [rows, K/16] one OCP FP8 E4M3 block scale per 16 k,
+ *                                 row-major (no swizzle);
+ *     plus an fp32 per-tensor global g = 448*6 / max|x| (static for
+ *     activations, from a calibration batch);
+ *   - the value of element k of a row is e2m1(code) * E4M3(scale[k/16]) and
+ *     the real value it stands for is that divided by g.
+ *
+ * Conventions shared by every call:
+ *   - all tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates, frees and synchronises nothing and launches only on the given
+ *     stream, so calls may be captured in a HIP graph;
+ *   - bf16 tensors hold raw bfloat16 bits; scalar inputs (globals, alphas) are
+ *     1-element fp32 DEVICE buffers, so no call reads device memory on the host;
+ *   - every argument is validated on the host before any launch; on error the
+ *     call returns a status and launches nothing; a failed launch returns
+ *     NVFP4_ERR_HIP (from hipGetLastError, without synchronising);
+ *   - M = 0 (or N = 0) is a successful no-op;
+ *   - nothing is printed and no C++ exception crosses the ABI.
+ *   - Shapes: K % 16 == 0 for the quantizer; K % 256 == 0 for the linears
+ *     (NVFP4_ERR_UNSUPPORTED otherwise).  Row strides (lda, ldo) count
+ *     elements; bf16 inputs need 16-byte aligned base pointers and lda % 8 == 0;
+ *     code / scale buffers need 16-byte aligned bases.  Outputs accept any
+ *     ldo >= N and any base alignment of 2 bytes.  Sizes must fit in int32
+ *     (M, N, K < 2^31 and M*K/16 < 2^31).
+ *
+ * Numerics (decisions every caller can rely on):
+ *   - quantization decides on the exact real values amax*g/6 and |x|*g/S:
+ *     nearest E4M3 scale (ties to even mantissa, saturating at 448) and
+ *     nearest e2m1 magnitude (ties to even, saturating at 6); a scale that
+ *     rounds to 0 gives magnitude 0 everywhere; the sign bit of x is kept;
+ *   - the linears dequantize exactly, accumulate in fp32 (order unspecified
+ *     for the W4A4 path; fixed for the W4A16 path), multiply by alpha, and
+ *     round once to bf16 (nearest even).
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARGUMENT = 1, /* null pointer where one is required, negative size */
+  NVFP4_ERR_INVALID_SHAPE = 2,    /* K % 16 != 0, lda < K, ldo < N, size overflow */
+  NVFP4_ERR_ALIGNMENT = 3,        /* misaligned base pointer or stride */
+  NVFP4_ERR_UNSUPPORTED = 4,      /* valid NVFP4 but outside this build's kernels (K % 256, M > 16 on W4A16) */
+  NVFP4_ERR_WORKSPACE = 5,        /* workspace missing or too small */
+  NVFP4_ERR_HIP = 6               /* a kernel launch failed */
+} nvfp4_status;
+
+/* Prepared weight descriptor: plain data, no heap state.  Produced by
+ * nvfp4_prepare_weight; "freeing" it is the caller freeing its buffers. */
+typedef struct nvfp4_weight {
+  const void* codes;  /* device, uint8 [N, K/2] */
+  const void* scales; /* device, uint8 [N, K/16] E4M3 */
+  int64_t N;
+  int64_t K;
+  int32_t layout;     /* 0 = canonical row-major (the only layout of this build) */
+  int32_t reserved;
+} nvfp4_weight;
+
+/* Routes of the M-threshold dispatch. */
+enum { NVFP4_ROUTE_W4A16 = 0, NVFP4_ROUTE_W4A4 = 1 };
+
+/* Human-readable name of a status (static storage). */
+const char* nvfp4_status_str(nvfp4_status s);
+
+/* Library version as an integer (major * 10000 + minor * 100 + patch). */
+int nvfp4_version(void);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_quantize_act -- NVFP4 quantization of bf16 rows under a static global.
+ * FreeToken PR #737, Changes (the activation quant kernel of the W4A4 route,
+ * split into row blocks); FlashInfer PR #3597, Description (per-16-element
+ * FP8-E4M3 block scales) and API example (global (448*6)/max|x|).
+ *   a      bf16 [M, K], row stride lda >= K (elements)
+ *   g      device fp32[1], the global scale g > 0 (finite)
+ *   codes  out, uint8 [M, K/2] contiguous
+ *   scales out, uint8 [M, K/16] contiguous
+ * Per 16-element block: scale = E4M3(amax*g/6), code_i = sign | e2m1(|x_i|*g/S).
+ * Works on weights as well (quantizing a bf16 weight with its own global).
+ * Errors: INVALID_ARGUMENT (null), INVALID_SHAPE (K % 16, lda < K),
+ * ALIGNMENT (a, codes not 16-byte aligned, lda % 8), HIP.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_quantize_act(const void* a, int64_t M, int64_t K, int64_t lda, const float* g,
+                                void* codes, void* scales, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_global_scale -- calibration helper: g = fp32(448*6 / max|x|) of a bf16
+ * matrix, with IEEE fp32 division (FlashInfer PR #3597, API example:
+ * g_w = (448 * 6) / w.float().abs().max()).  0 for an all-zero matrix.
+ *   x      bf16 [rows, cols], row stride ld; cols % 8 == 0
+ *   g_out  device fp32[1]; also used as the reduction's scratch word
+ * Three launches on the stream (clear, reduce, divide).
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_global_scale(const void* x, int64_t rows, int64_t cols, int64_t ld, float* g_out,
+                                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_alpha -- alpha = fp32(1 / (g_w * g_a)), the product and quotient in
+ * double as the pages' Python computes it (FlashInfer PR #3597, API example:
+ * alpha = 1.0 / g_w.item() stored as fp32).  g_a may be NULL (W4A16 alpha
+ * 1/g_w).  One single-thread launch.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_alpha(const float* g_w, const float* g_a, float* alpha_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_prepare_weight -- validate a canonical NVFP4 weight once and fill its
+ * descriptor (FlashInfer PR #3597, API: prepare_bf16_fp4_weights then
+ * mm_bf16_fp4, the prepare step run once per weight).  Both linears read the
+ * canonical row-major [N, K/2] codes and [N, K/16] scales directly (FreeToken
+ * PR #737: one weight copy, no repack), so this build's prepare step copies
+ * nothing: nvfp4_prepared_weight_bytes() returns 0 and dst may be NULL.
+ *   codes, scales  device buffers as above (16-byte aligned), kept alive by
+ *                  the caller for as long as the descriptor is used
+ *   out            host pointer to the descriptor to fill
+ * Errors: INVALID_ARGUMENT, INVALID_SHAPE (K % 16, N < 0), UNSUPPORTED
+ * (K % 256), ALIGNMENT.  Launches nothing.
+ * ------------------------------------------------------------------------- */
+size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
+nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t N, int64_t K, void* dst,
+                                  size_t dst_bytes, nvfp4_weight* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_linear_w4a16 -- out = bf16((a @ dequant(W).T) * alpha), fp32
+ * accumulation (FlashInfer PR #3597, Description), for decode-sized M <= 16
+ * (FreeToken PR #737, Changes: small-batch kernels on the same row-major
+ * weight).
+ *   a      bf16 [M, K], lda >= K
+ *   w      prepared weight descriptor (host pointer)
+ *   alpha  device fp32[1] (1/g_w)
+ *   out    bf16 [M, N], ldo >= N
+ * Deterministic: the fp32 sum order depends only on (M, N, K).
+ * Errors: as above; UNSUPPORTED for M > 16.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* alpha,
+                                void* out, int64_t ldo, hipStream_t stream);
+
+/* Same with an explicit kernel configuration (for tests and tuning):
+ * row_tiles (16-row MFMA tiles per wave) and steps_per_wave (256-k steps per
+ * wave; the waves of one workgroup split K) from (1,1) (1,2) (1,4) (2,1) (2,2)
+ * (2,4) (4,1), with ceil(K/256 / steps_per_wave) <= 16 waves (<= 8 when
+ * steps_per_wave = 4); other values return INVALID_ARGUMENT.
+ * row_tiles = 0 selects the default configuration. */
+nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w,
+                                   const float* alpha, void* out, int64_t ldo, int row_tiles, int steps_per_wave,
+                                   hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_linear_w4a4 -- out = bf16((dequant(A) @ dequant(W).T) * alpha) on
+ * NVFP4 activations, alpha = 1/(g_w * g_a) (FreeToken PR #737, Changes:
+ * prefill runs W4A4 GEMMs on NVFP4 activations; FreeToken PR #736, Changes:
+ * the same product inside the MoE experts).
+ *   a_codes, a_scales  uint8 [M, K/2], [M, K/16] contiguous (nvfp4_quantize_act output)
+ *   w                  prepared weight descriptor
+ *   alpha              device fp32[1]
+ *   out                bf16 [M, N], ldo >= N
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
+                               const float* alpha, void* out, int64_t ldo, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * M-threshold dispatch (FreeToken PR #737, Changes: W4A4 for prefill on
+ * checkpoints with static activation scales, W4A16 kernels for batches up to
+ * a threshold T, 8 or 16 there).
+ *   nvfp4_route: pure; W4A4 iff has_act_global && M > M*; else W4A16.
+ *   nvfp4_set_route_m_max / get: M* (default 16; values above 16 are clamped
+ *   to 16, the W4A16 kernel's limit, and a missing activation global with
+ *   M > 16 is UNSUPPORTED).
+ * ------------------------------------------------------------------------- */
+int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global);
+void nvfp4_set_route_m_max(int64_t m_max);
+int64_t nvfp4_get_route_m_max(void);
+
+/* Workspace nvfp4_linear needs: M*K/2 + M*K/16 bytes (plus alignment) for the
+ * quantized activations on the W4A4 route, 0 on the W4A16 route. */
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_linear -- the dispatched linear: W4A16 on bf16 a when M <= M* (or no
+ * activation global), else quantize a under g_act into the workspace and run
+ * W4A4.  The routes give different numerics, so the route taken is returned.
+ *   g_act         device fp32[1] or NULL (W4A16 only)
+ *   alpha_w4a16   device fp32[1], 1/g_w
+ *   alpha_w4a4    device fp32[1], 1/(g_w g_act) (may be NULL when g_act is)
+ *   ws, ws_bytes  device workspace, >= nvfp4_linear_workspace_bytes(M, N, K)
+ *   route_taken   host int out (NVFP4_ROUTE_*), may be NULL
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,
+                          const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo, void* ws,
+                          size_t ws_bytes, int* route_taken, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

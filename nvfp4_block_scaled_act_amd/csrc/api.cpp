@@ -1,0 +1,223 @@
+// C ABI of the NVFP4 library: host-side validation, the M-threshold dispatch
+// and the calls into the gfx950 kernels.  Every check runs before any launch.
+#include "../../include/nvfp4.h"
+
+#include <atomic>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kInt32Max = 2147483647LL;
+std::atomic<int64_t> g_route_m_max{16};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+// Checks shared by the linears: the weight descriptor and the output.
+nvfp4_status check_weight(const nvfp4_weight* w) {
+  if (!w || !w->codes || !w->scales) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (w->N < 0 || w->K <= 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (w->K % 16 != 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (w->N > kInt32Max || w->K > kInt32Max) return NVFP4_ERR_INVALID_SHAPE;
+  if (w->layout != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (w->K % 256 != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned16(w->codes) || !aligned16(w->scales)) return NVFP4_ERR_ALIGNMENT;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_out(const void* out, int64_t M, int64_t N, int64_t ldo) {
+  if (!out) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (ldo < N || ldo < 1) return NVFP4_ERR_INVALID_SHAPE;
+  if (M > kInt32Max || (M > 0 && ldo > (INT64_MAX / 2) / M)) return NVFP4_ERR_INVALID_SHAPE;
+  if (!aligned2(out)) return NVFP4_ERR_ALIGNMENT;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_bf16_input(const void* a, int64_t M, int64_t K, int64_t lda) {
+  if (!a) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (lda < K) return NVFP4_ERR_INVALID_SHAPE;
+  if (M > kInt32Max || K > kInt32Max) return NVFP4_ERR_INVALID_SHAPE;
+  if (!aligned16(a) || lda % 8 != 0) return NVFP4_ERR_ALIGNMENT;
+  return NVFP4_OK;
+}
+
+nvfp4_status w4a16_checked(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* alpha,
+                           void* out, int64_t ldo, const nvfp4::W4A16Config* cfg_in, hipStream_t stream) {
+  if (M < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!alpha) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_weight(w);
+  if (st != NVFP4_OK) return st;
+  if (M == 0) return NVFP4_OK;  // empty batch: a and out may be null
+  if ((st = check_bf16_input(a, M, w->K, lda)) != NVFP4_OK) return st;
+  if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
+  if (M > 16) return NVFP4_ERR_UNSUPPORTED;
+  nvfp4::W4A16Config cfg = cfg_in ? *cfg_in : nvfp4::w4a16_default_config(M, w->N, w->K);
+  if (!nvfp4::w4a16_config_valid(cfg, w->K)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (M == 0 || w->N == 0) return NVFP4_OK;
+  return hip_status(nvfp4::launch_w4a16(a, M, lda, w->codes, w->scales, w->N, w->K, alpha, out, ldo, cfg, stream));
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_str(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case NVFP4_ERR_INVALID_SHAPE: return "invalid shape";
+    case NVFP4_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported by this build's kernels";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int nvfp4_version(void) { return 100; }
+
+nvfp4_status nvfp4_quantize_act(const void* a, int64_t M, int64_t K, int64_t lda, const float* g, void* codes,
+                                void* scales, hipStream_t stream) {
+  if (M < 0 || K <= 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (K % 16 != 0 || lda < K) return NVFP4_ERR_INVALID_SHAPE;
+  if (M == 0) return NVFP4_OK;  // empty batch: buffers may be null
+  if (!g || !codes || !scales) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_bf16_input(a, M, K, lda);
+  if (st != NVFP4_OK) return st;
+  if (!aligned16(codes)) return NVFP4_ERR_ALIGNMENT;
+  if (M * (K / 16) > kInt32Max) return NVFP4_ERR_INVALID_SHAPE;
+  if ((M + 3) / 4 > 65535) return NVFP4_ERR_UNSUPPORTED;  // grid.y limit of the row mapping
+  if (M == 0) return NVFP4_OK;
+  return hip_status(nvfp4::launch_quantize(a, M, K, lda, g, codes, scales, stream));
+}
+
+nvfp4_status nvfp4_global_scale(const void* x, int64_t rows, int64_t cols, int64_t ld, float* g_out,
+                                hipStream_t stream) {
+  if (!x || !g_out) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (rows < 0 || cols <= 0 || ld < cols) return NVFP4_ERR_INVALID_SHAPE;
+  if (cols % 8 != 0 || ld % 8 != 0 || !aligned16(x) || (reinterpret_cast<uintptr_t>(g_out) & 3u))
+    return NVFP4_ERR_ALIGNMENT;
+  return hip_status(nvfp4::launch_global_scale(x, rows, cols, ld, g_out, stream));
+}
+
+nvfp4_status nvfp4_alpha(const float* g_w, const float* g_a, float* alpha_out, hipStream_t stream) {
+  if (!g_w || !alpha_out) return NVFP4_ERR_INVALID_ARGUMENT;
+  return hip_status(nvfp4::launch_alpha(g_w, g_a, alpha_out, stream));
+}
+
+size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t N, int64_t K, void* dst,
+                                  size_t dst_bytes, nvfp4_weight* out, hipStream_t stream) {
+  (void)dst;
+  (void)dst_bytes;
+  (void)stream;
+  if (!codes || !scales || !out) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_weight w;
+  w.codes = codes;
+  w.scales = scales;
+  w.N = N;
+  w.K = K;
+  w.layout = 0;
+  w.reserved = 0;
+  nvfp4_status st = check_weight(&w);
+  if (st != NVFP4_OK) return st;
+  *out = w;
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* alpha,
+                                void* out, int64_t ldo, hipStream_t stream) {
+  return w4a16_checked(a, M, lda, w, alpha, out, ldo, nullptr, stream);
+}
+
+nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w,
+                                   const float* alpha, void* out, int64_t ldo, int row_tiles, int steps_per_wave,
+                                   hipStream_t stream) {
+  if (row_tiles == 0) return w4a16_checked(a, M, lda, w, alpha, out, ldo, nullptr, stream);
+  nvfp4::W4A16Config cfg;
+  cfg.row_tiles = row_tiles;
+  cfg.steps_per_wave = steps_per_wave;
+  return w4a16_checked(a, M, lda, w, alpha, out, ldo, &cfg, stream);
+}
+
+nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
+                               const float* alpha, void* out, int64_t ldo, hipStream_t stream) {
+  if (M < 0 || !alpha) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_weight(w);
+  if (st != NVFP4_OK) return st;
+  if (M == 0) return NVFP4_OK;  // empty batch: buffers may be null
+  if (!a_codes || !a_scales) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
+  if (M > kInt32Max || M * (w->K / 16) > INT64_MAX / 16) return NVFP4_ERR_INVALID_SHAPE;
+  if (!aligned16(a_codes) || !aligned16(a_scales)) return NVFP4_ERR_ALIGNMENT;
+  if ((M + 127) / 128 > 65535) return NVFP4_ERR_UNSUPPORTED;
+  if (M == 0 || w->N == 0) return NVFP4_OK;
+  return hip_status(
+      nvfp4::launch_w4a4(a_codes, a_scales, M, w->codes, w->scales, w->N, w->K, alpha, out, ldo, stream));
+}
+
+int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global) {
+  (void)N;
+  (void)K;
+  return (has_act_global && M > g_route_m_max.load()) ? NVFP4_ROUTE_W4A4 : NVFP4_ROUTE_W4A16;
+}
+
+void nvfp4_set_route_m_max(int64_t m_max) {
+  if (m_max < 0) m_max = 0;
+  if (m_max > 16) m_max = 16;
+  g_route_m_max.store(m_max);
+}
+
+int64_t nvfp4_get_route_m_max(void) { return g_route_m_max.load(); }
+
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  if (M <= 0 || K <= 0) return 0;
+  return align_up(size_t(M) * size_t(K / 2), 256) + align_up(size_t(M) * size_t(K / 16), 256);
+}
+
+nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,
+                          const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo, void* ws,
+                          size_t ws_bytes, int* route_taken, hipStream_t stream) {
+  if (M < 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_weight(w);
+  if (st != NVFP4_OK) return st;
+  const int route = nvfp4_route(M, w->N, w->K, g_act != nullptr);
+  if (M == 0) {
+    if (route_taken) *route_taken = route;
+    return NVFP4_OK;
+  }
+  if (route == NVFP4_ROUTE_W4A16) {
+    if (M > 16) return NVFP4_ERR_UNSUPPORTED;
+    st = w4a16_checked(a, M, lda, w, alpha_w4a16, out, ldo, nullptr, stream);
+  } else {
+    if (!alpha_w4a4) return NVFP4_ERR_INVALID_ARGUMENT;
+    if ((st = check_bf16_input(a, M, w->K, lda)) != NVFP4_OK) return st;
+    if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
+    const size_t need = nvfp4_linear_workspace_bytes(M, w->N, w->K);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(ws)) return NVFP4_ERR_ALIGNMENT;
+    if (M * (w->K / 16) > kInt32Max || (M + 3) / 4 > 65535 || (M + 127) / 128 > 65535)
+      return NVFP4_ERR_UNSUPPORTED;
+    uint8_t* codes = static_cast<uint8_t*>(ws);
+    uint8_t* scales = codes + align_up(size_t(M) * size_t(w->K / 2), 256);
+    st = hip_status(nvfp4::launch_quantize(a, M, w->K, lda, g_act, codes, scales, stream));
+    if (st == NVFP4_OK)
+      st = hip_status(nvfp4::launch_w4a4(codes, scales, M, w->codes, w->scales, w->N, w->K, alpha_w4a4, out, ldo,
+                                         stream));
+  }
+  if (st == NVFP4_OK && route_taken) *route_taken = route;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+// NVFP4 quantization of bf16 rows on gfx950, plus the calibration helpers
+// (per-tensor global scale and alpha).
+//
+// What is computed (FlashInfer PR #3597, Description and API example; FreeToken
+// PR #737, Changes: "The activation quant kernel splits rows into blocks"):
+//   for every 16 consecutive elements of a row:
+//     amax   = max |x|
+//     scale  = the E4M3 byte nearest to amax*g/6 (ties to even, saturating 448)
+//     code_i = sign(x_i) | the e2m1 index nearest to |x_i|*g/S (ties to even,
+//              saturating 6), S = value of the scale byte
+//   two codes per byte, the even-k element in the low nibble; scales row-major.
+// Both roundings decide on the exact real values amax*g/6 and |x|*g/S.
+//
+// Mapping: one lane per 16-element block; a wave covers 64 consecutive blocks
+// of one row (2 KB of contiguous bf16 through dwordx4 loads), a workgroup four
+// rows.  The block max is an integer max over bf16 magnitude bits.
+//
+// Rounding of the codes: the fast path forms w = x * fl(g/S) and lets the
+// hardware f32 -> e2m1 convert round it (nearest, ties to even, saturating,
+// sign kept -- checked against the oracle).  w differs from the exact real
+// value by at most two fp32 ulps, so the result can only differ when w lies
+// within a few ulps of a rounding threshold (0.25, 0.75, 1.25, 1.75, 2.5, 3.5
+// or 5 -- all with their low 21 mantissa bits zero).  A lane that sees such a
+// w recomputes its block by exact comparisons: the sign of fma(|x|, g, -T*S)
+// is the sign of the exact |x|*g - T*S (T*S is exact in fp32).
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+// Value of a non-negative E4M3 byte 0x00..0x7E (exact in fp32).
+__device__ __forceinline__ float e4m3_pos_value(uint32_t b) {
+  const uint32_t e = b >> 3, m = b & 7u;
+  return e == 0 ? float(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// The E4M3 byte nearest to the exact amax*g/6.  An fp32 estimate picks a
+// candidate that is at most one byte off; the two neighbouring midpoints are
+// then compared exactly (6*midpoint has at most 7 significant bits).
+__device__ __forceinline__ uint32_t scale_byte(float amax, float g) {
+  const float t = amax * g * (1.0f / 6.0f);
+  uint32_t s;
+  if (!(t < 464.0f)) {
+    s = 126;
+  } else if (t < 0x1p-6f) {
+    s = uint32_t(__builtin_rintf(t * 512.0f));  // subnormal range, 0..8
+  } else {
+    uint32_t u = __float_as_uint(t);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the fp32 mantissa to 3 bits
+    s = min(((u >> 23) - 120u) * 8u + ((u >> 20) & 7u), 126u);
+  }
+  if (s > 0) {
+    const float d = __builtin_fmaf(amax, g, -3.0f * (e4m3_pos_value(s - 1) + e4m3_pos_value(s)));
+    if (d < 0.0f || (d == 0.0f && ((s - 1) & 1u) == 0)) s -= 1;
+  }
+  if (s < 126) {
+    const float d = __builtin_fmaf(amax, g, -3.0f * (e4m3_pos_value(s) + e4m3_pos_value(s + 1)));
+    if (d > 0.0f || (d == 0.0f && ((s + 1) & 1u) == 0)) s += 1;
+  }
+  return s;
+}
+
+// Exact e2m1 code of x under scale S (S > 0): a three-level search over the
+// thresholds 0.25..5 (x S).  Thresholds below odd indices round down on a tie
+// (>), the others up (>=), which is ties-to-even.
+__device__ __forceinline__ uint32_t exact_code(float x, float g, float S) {
+  const float ax = __builtin_fabsf(x);
+  const bool c2 = __builtin_fmaf(ax, g, -1.75f * S) >= 0.0f;
+  const bool c1 = __builtin_fmaf(ax, g, -(c2 ? 3.5f : 0.75f) * S) >= 0.0f;
+  const float t0 = c2 ? (c1 ? 5.0f : 2.5f) : (c1 ? 1.25f : 0.25f);
+  const bool c0 = __builtin_fmaf(ax, g, -t0 * S) > 0.0f;
+  const uint32_t mag = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
+  return ((__float_as_uint(x) >> 28) & 8u) | mag;
+}
+
+__device__ __forceinline__ bool near_threshold(float w) {
+  return ((__float_as_uint(w) + 4u) & 0x1FFFFFu) <= 8u;
+}
+
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t acc, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, SEL);
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ a, int64_t lda,
+                                                       int32_t rows, int32_t blocks_per_row,
+                                                       const float* __restrict__ g_ptr,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  const int32_t j = int32_t(blockIdx.x) * 64 + int32_t(threadIdx.x & 63);
+  const int32_t row = int32_t(blockIdx.y) * 4 + int32_t(threadIdx.x >> 6);
+  if (j >= blocks_per_row || row >= rows) return;
+  const uint16_t* src = a + int64_t(row) * lda + int64_t(j) * 16;
+  const uint4 v0 = ld16_nt(src);
+  const uint4 v1 = ld16_nt(src + 8);
+  const float g = *g_ptr;
+  const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+
+  uint32_t mbits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mbits = max(mbits, max(d[i] & 0x7FFFu, (d[i] >> 16) & 0x7FFFu));
+  const float amax = bf16_bits_to_f32(mbits);
+  const uint32_t s = scale_byte(amax, g);
+  const float S = e4m3_pos_value(s);
+  const float G = (s == 0) ? 0.0f : g / S;
+
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __uint_as_float(d[i] << 16);
+    x[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+  }
+  uint32_t c0 = 0, c1 = 0;
+  bool near = false;
+  float w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    w[i] = x[i] * G;
+    near |= near_threshold(w[i]);
+  }
+  c0 = cvt_pair<0>(c0, w[0], w[1]);
+  c0 = cvt_pair<1>(c0, w[2], w[3]);
+  c0 = cvt_pair<2>(c0, w[4], w[5]);
+  c0 = cvt_pair<3>(c0, w[6], w[7]);
+  c1 = cvt_pair<0>(c1, w[8], w[9]);
+  c1 = cvt_pair<1>(c1, w[10], w[11]);
+  c1 = cvt_pair<2>(c1, w[12], w[13]);
+  c1 = cvt_pair<3>(c1, w[14], w[15]);
+
+  if (near && s != 0) {
+    c0 = 0;
+    c1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c0 |= exact_code(x[i], g, S) << (4 * i);
+      c1 |= exact_code(x[8 + i], g, S) << (4 * i);
+    }
+  }
+  const int32_t half_k = blocks_per_row * 8;
+  uint2* dst = reinterpret_cast<uint2*>(codes + int64_t(row) * half_k + int64_t(j) * 8);
+  *dst = make_uint2(c0, c1);
+  scales[int64_t(row) * blocks_per_row + j] = uint8_t(s);
+}
+
+// ---------------------------------------------------------------- calibration
+
+__global__ void set_u32_kernel(uint32_t* p, uint32_t v) { *p = v; }
+
+// max |x| over a bf16 matrix, as bf16 magnitude bits, into *out (atomic max).
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                   int64_t ld, uint32_t* __restrict__ out) {
+  const int64_t chunks = cols / 8;
+  const int64_t total = rows * chunks;
+  uint32_t m = 0;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / chunks, c = i - r * chunks;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + r * ld + c * 8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(d[k] & 0x7FFFu, (d[k] >> 16) & 0x7FFFu));
+  }
+  for (int o = 32; o > 0; o >>= 1) m = max(m, uint32_t(__shfl_xor(int(m), o, 64)));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, m);
+}
+
+// g = fp32(448 * 6 / amax) with IEEE fp32 division (0 for an all-zero tensor).
+__global__ void global_from_amax_kernel(uint32_t* inout) {
+  const float amax = bf16_bits_to_f32(*inout);
+  const float g = amax > 0.0f ? 2688.0f / amax : 0.0f;
+  *reinterpret_cast<float*>(inout) = g;
+}
+
+// alpha = fp32(1 / (g_w * g_a)) with the product and quotient in double; g_a
+// may be null (W4A16 alpha = fp32(1 / g_w)).
+__global__ void alpha_kernel(const float* gw, const float* ga, float* alpha) {
+  const double den = ga ? double(*gw) * double(*ga) : double(*gw);
+  *alpha = float(1.0 / den);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* a, int64_t M, int64_t K, int64_t lda, const float* g, void* codes,
+                           void* scales, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int32_t bpr = int32_t(K / 16);
+  dim3 grid((bpr + 63) / 64, uint32_t((M + 3) / 4));
+  hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a), lda,
+                     int32_t(M), bpr, g, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales));
+  return hipGetLastError();
+}
+
+hipError_t launch_global_scale(const void* x, int64_t rows, int64_t cols, int64_t ld, float* g_out,
+                               hipStream_t stream) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(g_out);
+  hipLaunchKernelGGL(set_u32_kernel, dim3(1), dim3(1), 0, stream, bits, 0u);
+  const int64_t total = rows * (cols / 8);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(amax_kernel, dim3(uint32_t(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), rows, cols, ld, bits);
+  hipLaunchKernelGGL(global_from_amax_kernel, dim3(1), dim3(1), 0, stream, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_alpha(const float* g_w, const float* g_a, float* alpha, hipStream_t stream) {
+  hipLaunchKernelGGL(alpha_kernel, dim3(1), dim3(1), 0, stream, g_w, g_a, alpha);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

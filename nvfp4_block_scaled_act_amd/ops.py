@@ -1,0 +1,183 @@
+"""PyTorch-facing wrappers of the C ABI: argument marshalling only.
+
+Tensors live on the current HIP device; every call launches on torch's current
+stream.  All arithmetic happens in the gfx950 kernels of libnvfp4.so.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import lib as _L
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def _scalar(t: torch.Tensor, name: str) -> None:
+    _need(t, torch.float32, name)
+    if t.numel() < 1:
+        raise ValueError(f"{name} must hold one fp32 value")
+
+
+@dataclass
+class Weight:
+    """A prepared NVFP4 weight: the canonical codes/scales and their descriptor."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    desc: _L.Weight
+
+    @property
+    def N(self) -> int:
+        return int(self.desc.N)
+
+    @property
+    def K(self) -> int:
+        return int(self.desc.K)
+
+
+def global_scale(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    _need(x, torch.bfloat16, "x")
+    ld = _rows(x, "x")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _L.check("nvfp4_global_scale",
+             _L.load().nvfp4_global_scale(_ptr(x), x.shape[0], x.shape[1], ld, _ptr(out), _stream()))
+    return out
+
+
+def alpha(g_w: torch.Tensor, g_a: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    _scalar(g_w, "g_w")
+    if g_a is not None:
+        _scalar(g_a, "g_a")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=g_w.device)
+    _L.check("nvfp4_alpha", _L.load().nvfp4_alpha(_ptr(g_w), _ptr(g_a), _ptr(out), _stream()))
+    return out
+
+
+def quantize_act(a: torch.Tensor, g: torch.Tensor, codes: torch.Tensor | None = None,
+                 scales: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    _need(a, torch.bfloat16, "a")
+    _scalar(g, "g")
+    lda = _rows(a, "a")
+    M, K = a.shape
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=a.device)
+    _L.check("nvfp4_quantize_act",
+             _L.load().nvfp4_quantize_act(_ptr(a), M, K, lda, _ptr(g), _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def prepare_weight(codes: torch.Tensor, scales: torch.Tensor) -> Weight:
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if not codes.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("weight codes and scales must be contiguous")
+    N, half = codes.shape
+    K = 2 * half
+    if tuple(scales.shape) != (N, K // 16):
+        raise ValueError(f"scales must be [N, K/16] = [{N}, {K // 16}], got {tuple(scales.shape)}")
+    desc = _L.Weight()
+    _L.check("nvfp4_prepare_weight",
+             _L.load().nvfp4_prepare_weight(_ptr(codes), _ptr(scales), N, K, None, 0, C.byref(desc), _stream()))
+    return Weight(codes, scales, desc)
+
+
+def _out(out, M, N, device):
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    _need(out, torch.bfloat16, "out")
+    return out, _rows(out, "out")
+
+
+def linear_w4a16(a: torch.Tensor, w: Weight, alpha_: torch.Tensor, out: torch.Tensor | None = None,
+                 row_tiles: int = 0, steps_per_wave: int = 0) -> torch.Tensor:
+    _need(a, torch.bfloat16, "a")
+    _scalar(alpha_, "alpha")
+    lda = _rows(a, "a")
+    M = a.shape[0]
+    if a.shape[1] != w.K:
+        raise ValueError("a.shape[1] != K")
+    out, ldo = _out(out, M, w.N, a.device)
+    _L.check("nvfp4_linear_w4a16_ex",
+             _L.load().nvfp4_linear_w4a16_ex(_ptr(a), M, lda, C.byref(w.desc), _ptr(alpha_), _ptr(out), ldo,
+                                             row_tiles, steps_per_wave, _stream()))
+    return out
+
+
+def linear_w4a4(a_codes: torch.Tensor, a_scales: torch.Tensor, w: Weight, alpha_: torch.Tensor,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    _need(a_codes, torch.uint8, "a_codes")
+    _need(a_scales, torch.uint8, "a_scales")
+    _scalar(alpha_, "alpha")
+    M = a_codes.shape[0]
+    if a_codes.shape[1] * 2 != w.K or tuple(a_scales.shape) != (M, w.K // 16):
+        raise ValueError("activation codes/scales do not match the weight's K")
+    if not a_codes.is_contiguous() or not a_scales.is_contiguous():
+        raise ValueError("activation codes and scales must be contiguous")
+    out, ldo = _out(out, M, w.N, a_codes.device)
+    _L.check("nvfp4_linear_w4a4",
+             _L.load().nvfp4_linear_w4a4(_ptr(a_codes), _ptr(a_scales), M, C.byref(w.desc), _ptr(alpha_),
+                                         _ptr(out), ldo, _stream()))
+    return out
+
+
+def route(M: int, N: int, K: int, has_act_global: bool) -> int:
+    return int(_L.load().nvfp4_route(M, N, K, 1 if has_act_global else 0))
+
+
+def set_route_m_max(m: int) -> None:
+    _L.load().nvfp4_set_route_m_max(int(m))
+
+
+def get_route_m_max() -> int:
+    return int(_L.load().nvfp4_get_route_m_max())
+
+
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_L.load().nvfp4_linear_workspace_bytes(M, N, K))
+
+
+def linear(a: torch.Tensor, w: Weight, g_act: torch.Tensor | None, alpha_w4a16: torch.Tensor,
+           alpha_w4a4: torch.Tensor | None, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, int]:
+    """Dispatched linear; returns (out, route taken)."""
+    _need(a, torch.bfloat16, "a")
+    lda = _rows(a, "a")
+    M = a.shape[0]
+    out, ldo = _out(out, M, w.N, a.device)
+    need = linear_workspace_bytes(M, w.N, w.K)
+    if workspace is None and g_act is not None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    r = C.c_int(-1)
+    _L.check("nvfp4_linear",
+             _L.load().nvfp4_linear(_ptr(a), M, lda, C.byref(w.desc), _ptr(g_act), _ptr(alpha_w4a16),
+                                    _ptr(alpha_w4a4), _ptr(out), ldo, _ptr(workspace), ws_bytes, C.byref(r),
+                                    _stream()))
+    return out, int(r.value)

@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and its host-side validation returns the documented status
+before any launch (no call here reaches a kernel)."""
+import ctypes as C
+import subprocess
+
+import pytest
+
+from nvfp4_block_scaled_act_amd import lib as L
+
+OK, ARG, SHAPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5
+A16 = 0x10000  # a fake, 16-byte aligned device address: never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def nv():
+    return L.load()
+
+
+def test_exports_every_declared_function(nv):
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    declared = L.header_functions()
+    assert declared, "no declarations parsed"
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        assert hasattr(nv, f)
+
+
+def test_status_strings(nv):
+    for code in range(7):
+        assert nv.nvfp4_status_str(code)
+    assert nv.nvfp4_version() >= 100
+
+
+def _w(N=64, K=256, codes=A16, scales=A16):
+    w = L.Weight()
+    w.codes, w.scales, w.N, w.K, w.layout, w.reserved = codes, scales, N, K, 0, 0
+    return w
+
+
+def test_quantize_validation(nv):
+    q = nv.nvfp4_quantize_act
+    assert q(A16, 4, 24, 24, A16, A16, A16, None) == SHAPE          # K % 16
+    assert q(A16, 4, 32, 16, A16, A16, A16, None) == SHAPE          # lda < K
+    assert q(None, 4, 32, 32, A16, A16, A16, None) == ARG
+    assert q(A16, 4, 32, 32, None, A16, A16, None) == ARG
+    assert q(A16 + 2, 4, 32, 32, A16, A16, A16, None) == ALIGN      # a not 16-byte aligned
+    assert q(A16, 4, 32, 36, A16, A16, A16, None) == ALIGN          # lda % 8
+    assert q(A16, 4, 32, 32, A16, A16 + 8, A16, None) == ALIGN      # codes
+    assert q(A16, -1, 32, 32, A16, A16, A16, None) == SHAPE
+    assert q(A16, 0, 32, 32, A16, A16, A16, None) == OK             # empty: no launch
+    assert q(None, 0, 32, 32, None, None, None, None) == OK         # empty: null buffers allowed
+
+
+def test_prepare_weight_validation(nv):
+    d = L.Weight()
+    assert nv.nvfp4_prepared_weight_bytes(128, 256) == 0
+    assert nv.nvfp4_prepare_weight(A16, A16, 128, 256, None, 0, C.byref(d), None) == OK
+    assert (d.N, d.K, d.layout) == (128, 256, 0) and d.codes == A16
+    assert nv.nvfp4_prepare_weight(A16, A16, 128, 24, None, 0, C.byref(d), None) == SHAPE
+    assert nv.nvfp4_prepare_weight(A16, A16, 128, 128, None, 0, C.byref(d), None) == UNSUP  # K % 256
+    assert nv.nvfp4_prepare_weight(A16 + 4, A16, 128, 256, None, 0, C.byref(d), None) == ALIGN
+    assert nv.nvfp4_prepare_weight(None, A16, 128, 256, None, 0, C.byref(d), None) == ARG
+    assert nv.nvfp4_prepare_weight(A16, A16, -1, 256, None, 0, C.byref(d), None) == SHAPE
+
+
+def test_w4a16_validation(nv):
+    f = nv.nvfp4_linear_w4a16
+    w = _w()
+    assert f(A16, 17, 256, C.byref(w), A16, A16, 64, None) == UNSUP    # M > 16
+    assert f(A16, 4, 256, C.byref(w), None, A16, 64, None) == ARG      # alpha
+    assert f(A16, 4, 256, C.byref(w), A16, A16, 63, None) == SHAPE     # ldo < N
+    assert f(A16, 4, 255, C.byref(w), A16, A16, 64, None) == SHAPE     # lda < K
+    assert f(A16, 4, 260, C.byref(w), A16, A16, 64, None) == ALIGN     # lda % 8
+    assert f(A16, 4, 256, C.byref(w), A16, A16 + 1, 64, None) == ALIGN  # odd output address
+    assert f(A16, 4, 256, None, A16, A16, 64, None) == ARG
+    assert f(A16, -2, 256, C.byref(w), A16, A16, 64, None) == ARG
+    assert f(A16, 0, 256, C.byref(w), A16, A16, 64, None) == OK        # empty
+    assert f(None, 0, 256, C.byref(w), A16, None, 64, None) == OK      # empty, null buffers
+    wz = _w(N=0)
+    assert f(A16, 4, 256, C.byref(wz), A16, A16, 1, None) == OK         # N = 0
+    g = nv.nvfp4_linear_w4a16_ex
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 3, 1, None) == ARG  # row_tiles 3
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 0, None) == ARG  # steps_per_wave 0
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 3, None) == ARG  # steps_per_wave 3
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 4, 2, None) == ARG  # (4, 2) not compiled
+    wk = _w(K=256 * 20)
+    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 1, 1, None) == ARG  # 20 waves > 16
+
+
+def test_w4a4_validation(nv):
+    f = nv.nvfp4_linear_w4a4
+    w = _w()
+    assert f(None, A16, 8, C.byref(w), A16, A16, 64, None) == ARG
+    assert f(A16, A16 + 4, 8, C.byref(w), A16, A16, 64, None) == ALIGN
+    assert f(A16, A16, 8, C.byref(w), A16, A16, 10, None) == SHAPE
+    assert f(A16, A16, 0, C.byref(w), A16, A16, 64, None) == OK
+    assert f(None, None, 0, C.byref(w), A16, None, 64, None) == OK
+    wbad = _w(K=512 + 16)
+    assert f(A16, A16, 8, C.byref(wbad), A16, A16, 64, None) == UNSUP
+
+
+def test_route_is_a_pure_threshold(nv):
+    nv.nvfp4_set_route_m_max(16)
+    assert nv.nvfp4_get_route_m_max() == 16
+    for M in range(0, 40):
+        for has_g in (0, 1):
+            want = 1 if (has_g and M > 16) else 0
+            assert nv.nvfp4_route(M, 8704, 5120, has_g) == want
+    nv.nvfp4_set_route_m_max(4)
+    assert nv.nvfp4_route(5, 1, 256, 1) == 1 and nv.nvfp4_route(4, 1, 256, 1) == 0
+    nv.nvfp4_set_route_m_max(100)          # clamped to the W4A16 kernel's limit
+    assert nv.nvfp4_get_route_m_max() == 16
+    nv.nvfp4_set_route_m_max(-3)
+    assert nv.nvfp4_get_route_m_max() == 0
+    nv.nvfp4_set_route_m_max(16)
+
+
+def test_linear_dispatch_validation(nv):
+    f = nv.nvfp4_linear
+    w = _w()
+    r = C.c_int(-1)
+    nv.nvfp4_set_route_m_max(16)
+    # W4A4 route without workspace
+    assert f(A16, 32, 256, C.byref(w), A16, A16, A16, A16, 64, None, 0, C.byref(r), None) == WS
+    need = nv.nvfp4_linear_workspace_bytes(32, 64, 256)
+    assert need >= 32 * 128 + 32 * 16
+    assert f(A16, 32, 256, C.byref(w), A16, A16, A16, A16, 64, A16, need - 1, C.byref(r), None) == WS
+    # W4A16 route beyond its limit when no activation global is given
+    assert f(A16, 32, 256, C.byref(w), None, A16, None, A16, 64, None, 0, C.byref(r), None) == UNSUP
+    # W4A4 route needs alpha_w4a4
+    assert f(A16, 32, 256, C.byref(w), A16, A16, None, A16, 64, A16, need, C.byref(r), None) == ARG
+    # empty batch, either route
+    r.value = -1
+    assert f(A16, 0, 256, C.byref(w), None, A16, None, A16, 64, None, 0, C.byref(r), None) == OK
+    assert r.value == 0

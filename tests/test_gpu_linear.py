@@ -1,0 +1,229 @@
+"""GPU parity of the W4A16 and W4A4 linears and the dispatch against the
+oracle: max |err| <= 2 bf16 ulp (with the Sabs floor) and rel-L2 <= 1e-3."""
+import numpy as np
+import pytest
+
+from nvfp4_block_scaled_act_amd import synth
+
+from helpers import bf16_dev, bf16_host, f32_dev, gemm_check, u8_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from nvfp4_block_scaled_act_amd import ops as O
+
+    return O
+
+
+class Quantized:
+    """A bf16 weight quantized on the GPU (checked against the oracle's codes)
+    plus the oracle's own codes for the reference."""
+
+    def __init__(self, ops, orc, w_bits, check_rows=None):
+        self.bits = w_bits
+        self.g = orc.global_scale(w_bits)
+        wd = bf16_dev(w_bits)
+        gd = ops.global_scale(wd)
+        assert gd.item() == self.g
+        c, s = ops.quantize_act(wd, gd)
+        self.w = ops.prepare_weight(c, s)
+        self.alpha = ops.alpha(gd)
+        assert self.alpha.item() == orc.alpha(self.g)
+        self.g_dev = gd
+        rows = np.arange(w_bits.shape[0]) if check_rows is None else check_rows
+        oc, os_ = orc.quantize(w_bits[rows], self.g)
+        assert (u8_host(c)[rows] == oc).all() and (u8_host(s)[rows] == os_).all(), "weight quantization mismatch"
+        if check_rows is None:
+            self.codes, self.scales = oc, os_
+
+
+def test_w4a16_small_config(ops, orc):
+    # W4A16 linear, M=4, N=512, K=1024
+    W = synth.normal_bf16(synth.seed_for("w4a16_small", synth.ROLE_W), 512, 1024)
+    a = synth.normal_bf16(synth.seed_for("w4a16_small", synth.ROLE_A), 4, 1024)
+    q = Quantized(ops, orc, W)
+    out = ops.linear_w4a16(bf16_dev(a), q.w, q.alpha)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    gemm_check(bf16_host(out), ref, sabs)
+
+
+@pytest.mark.parametrize("shape_index", range(4))
+def test_w4a16_decode_sweep(ops, orc, shape_index):
+    N, K = synth.W4A16_DECODE_SHAPES[shape_index]
+    W = synth.normal_bf16(synth.seed_for("w4a16_decode", synth.ROLE_W, shape_index), N, K)
+    a = synth.normal_bf16(synth.seed_for("w4a16_decode", synth.ROLE_A, shape_index), 16, K)
+    q = Quantized(ops, orc, W)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    ad = bf16_dev(a)
+    for M in synth.W4A16_DECODE_M:
+        out = ops.linear_w4a16(ad[:M], q.w, q.alpha)
+        gemm_check(bf16_host(out), ref[:M], sabs[:M])
+
+
+def test_w4a16_every_kernel_config(ops, orc):
+    # ragged N, K with an odd number of 256-k steps, M between powers of two
+    N, K, M = 1000, 4352, 7
+    W = synth.normal_bf16(11, N, K)
+    a = synth.normal_bf16(12, M, K)
+    q = Quantized(ops, orc, W)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    ad = bf16_dev(a)
+    steps = K // 256
+    for rt, spw in [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1)]:
+        if -(-steps // spw) > (8 if spw == 4 else 16):
+            with pytest.raises(ValueError):
+                ops.linear_w4a16(ad, q.w, q.alpha, row_tiles=rt, steps_per_wave=spw)
+            continue
+        out = ops.linear_w4a16(ad, q.w, q.alpha, row_tiles=rt, steps_per_wave=spw)
+        gemm_check(bf16_host(out), ref, sabs)
+    # a K with fewer steps than one wave's share, on every variant
+    K2 = 512
+    W2 = synth.normal_bf16(13, 300, K2)
+    a2 = synth.normal_bf16(14, 16, K2)
+    q2 = Quantized(ops, orc, W2)
+    ref2, _, sabs2 = orc.linear_w4a16(a2, q2.codes, q2.scales, orc.alpha(q2.g))
+    for rt, spw in [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1)]:
+        for M in (1, 5, 16):
+            out = ops.linear_w4a16(bf16_dev(a2[:M]), q2.w, q2.alpha, row_tiles=rt, steps_per_wave=spw)
+            gemm_check(bf16_host(out), ref2[:M], sabs2[:M])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 12, 256), (16, 12, 512), (3, 17, 768), (9, 100, 1024), (13, 4000, 2048)])
+def test_w4a16_edges(ops, orc, M, N, K):
+    import torch
+
+    W = synth.normal_bf16(20 + N, N, K)
+    a = synth.normal_bf16(30 + M, M, K)
+    q = Quantized(ops, orc, W)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    # strided input (lda > K) and output (ldo > N), with guard values around the output
+    lda, ldo = K + 64, N + 5
+    abuf = torch.zeros((M, lda), dtype=torch.bfloat16, device="cuda")
+    abuf[:, :K] = bf16_dev(a)
+    obuf = torch.full((M + 1, ldo), 7.0, dtype=torch.bfloat16, device="cuda")
+    ops.linear_w4a16(abuf[:, :K], q.w, q.alpha, out=obuf[:M, :N])
+    o = bf16_host(obuf)
+    gemm_check(o[:M, :N], ref, sabs)
+    assert (o[:M, N:] == 0x40E0).all() and (o[M] == 0x40E0).all(), "write outside the output"
+
+
+def test_w4a16_empty_and_limits(ops, orc):
+    import torch
+
+    W = synth.normal_bf16(5, 64, 256)
+    q = Quantized(ops, orc, W)
+    out = ops.linear_w4a16(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), q.w, q.alpha)
+    assert out.shape == (0, 64)
+    with pytest.raises(ValueError):
+        ops.linear_w4a16(torch.zeros((17, 256), dtype=torch.bfloat16, device="cuda"), q.w, q.alpha)
+
+
+def test_w4a16_deterministic(ops, orc):
+    W = synth.normal_bf16(8, 3584, 5120)
+    q = Quantized(ops, orc, W, check_rows=np.arange(0, 3584, 97))
+    a = bf16_dev(synth.normal_bf16(9, 16, 5120))
+    o1 = bf16_host(ops.linear_w4a16(a, q.w, q.alpha))
+    for _ in range(3):
+        assert (bf16_host(ops.linear_w4a16(a, q.w, q.alpha)) == o1).all()
+
+
+# ------------------------------------------------------------------ W4A4
+
+def _w4a4_case(ops, orc, W, a, cal, rows=None, cols=None, check_rows=None):
+    q = Quantized(ops, orc, W, check_rows=check_rows)
+    ga = orc.global_scale(cal)
+    gad = ops.global_scale(bf16_dev(cal))
+    assert gad.item() == ga
+    ad = bf16_dev(a)
+    ac, as_ = ops.quantize_act(ad, gad)
+    al = ops.alpha(q.g_dev, gad)
+    assert al.item() == orc.alpha(q.g, ga)
+    out = bf16_host(ops.linear_w4a4(ac, as_, q.w, al))
+    oac, oas = orc.quantize(a if rows is None else a[rows], ga)
+    if rows is None:
+        assert (u8_host(ac) == oac).all() and (u8_host(as_) == oas).all()
+    else:
+        assert (u8_host(ac)[rows] == oac).all() and (u8_host(as_)[rows] == oas).all()
+    if cols is None:
+        wc, ws = q.codes, q.scales
+        sel_out = out if rows is None else out[rows]
+        ref, _, sabs = orc.linear_w4a4(oac, oas, wc, ws, orc.alpha(q.g, ga))
+    else:
+        wc, ws = orc.quantize(W[cols], q.g)
+        ref, _, sabs = orc.linear_w4a4(oac, oas, wc, ws, orc.alpha(q.g, ga))
+        sel_out = out[np.ix_(rows, cols)]
+    return gemm_check(sel_out, ref, sabs)
+
+
+def test_w4a4_prefill_m1024_full(ops, orc):
+    N, K = 8704, 5120
+    W = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_W), N, K)
+    a = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), 1024, K)
+    cal = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_CAL), 512, K)
+    _w4a4_case(ops, orc, W, a, cal)
+
+
+@pytest.mark.parametrize("M", [4096, 8192])
+def test_w4a4_prefill_sampled(ops, orc, M):
+    N, K = 8704, 5120
+    W = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_W), N, K)
+    a = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), 8192, K)[:M]
+    cal = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_CAL), 512, K)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([rng.integers(0, M, 96), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, N, 384), [0, N - 1]]))
+    _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols, check_rows=cols)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (130, 200, 512), (127, 129, 768), (300, 1000, 1024), (17, 8, 256)])
+def test_w4a4_ragged(ops, orc, M, N, K):
+    W = synth.normal_bf16(40 + N, N, K)
+    a = synth.normal_bf16(50 + M, M, K)
+    cal = synth.normal_bf16(60 + M, 64, K)
+    _w4a4_case(ops, orc, W, a, cal)
+
+
+def test_w4a4_deterministic(ops, orc):
+    W = synth.normal_bf16(70, 1024, 1024)
+    q = Quantized(ops, orc, W)
+    a = bf16_dev(synth.normal_bf16(71, 512, 1024))
+    g = f32_dev(400.0)
+    ac, as_ = ops.quantize_act(a, g)
+    al = ops.alpha(q.g_dev, g)
+    o1 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al))
+    for _ in range(3):
+        assert (bf16_host(ops.linear_w4a4(ac, as_, q.w, al)) == o1).all()
+
+
+# ------------------------------------------------------------------ dispatch
+
+def test_dispatch_routes_and_numerics(ops, orc):
+    # Large fused-weight shape scaled down in N (the routes do not depend on N).
+    N, K = 4096, 5120
+    W = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_W), N, K)
+    a = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_A), 256, K)
+    cal = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_CAL), 512, K)
+    q = Quantized(ops, orc, W)
+    ga = orc.global_scale(cal)
+    gad = ops.global_scale(bf16_dev(cal))
+    a16 = q.alpha
+    a4 = ops.alpha(q.g_dev, gad)
+    ad = bf16_dev(a)
+    ops.set_route_m_max(16)
+    for M in [1, 8, 16, 17, 64, 256]:
+        out, route = ops.linear(ad[:M], q.w, gad, a16, a4)
+        assert route == ops.route(M, N, K, True) == (1 if M > 16 else 0)
+        if route == 0:
+            ref, _, sabs = orc.linear_w4a16(a[:M], q.codes, q.scales, orc.alpha(q.g))
+        else:
+            oac, oas = orc.quantize(a[:M], ga)
+            ref, _, sabs = orc.linear_w4a4(oac, oas, q.codes, q.scales, orc.alpha(q.g, ga))
+        gemm_check(bf16_host(out), ref, sabs)
+    # no activation global: always W4A16
+    out, route = ops.linear(ad[:8], q.w, None, a16, None)
+    assert route == 0
