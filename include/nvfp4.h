@@ -26,8 +26,8 @@
  *     NVFP4_ERR_HIP (from hipGetLastError, without synchronising);
  *   - M = 0 (or N = 0) is a successful no-op;
  *   - nothing is printed and no C++ exception crosses the ABI.
- *   - Shapes: K % 16 == 0 for the quantizer; K % 256 == 0 for the linears
- *     (NVFP4_ERR_UNSUPPORTED otherwise).  Row strides (lda, ldo) count
+ *   - Shapes: K % 16 == 0 for the quantizer; K % 256 == 0 for the prepared
+ *     weight and the linears (NVFP4_ERR_UNSUPPORTED otherwise).  Row strides (lda, ldo) count
  *     elements; bf16 inputs need 16-byte aligned base pointers and lda % 8 == 0;
  *     code / scale buffers need 16-byte aligned bases.  Outputs accept any
  *     ldo >= N and any base alignment of 2 bytes.  Sizes must fit in int32
@@ -64,14 +64,17 @@ typedef enum nvfp4_status {
   NVFP4_ERR_HIP = 6               /* a kernel launch failed */
 } nvfp4_status;
 
+/* Layouts of a prepared weight. */
+enum { NVFP4_LAYOUT_TILED = 1 };
+
 /* Prepared weight descriptor: plain data, no heap state.  Produced by
- * nvfp4_prepare_weight; "freeing" it is the caller freeing its buffers. */
+ * nvfp4_prepare_weight; "freeing" it is the caller freeing the buffer it
+ * passed as dst.  The linears read nothing but data. */
 typedef struct nvfp4_weight {
-  const void* codes;  /* device, uint8 [N, K/2] */
-  const void* scales; /* device, uint8 [N, K/16] E4M3 */
+  const void* data;   /* device, the tiled weight (nvfp4_prepared_weight_bytes bytes) */
   int64_t N;
   int64_t K;
-  int32_t layout;     /* 0 = canonical row-major (the only layout of this build) */
+  int32_t layout;     /* NVFP4_LAYOUT_TILED */
   int32_t reserved;
 } nvfp4_weight;
 
@@ -121,17 +124,27 @@ nvfp4_status nvfp4_global_scale(const void* x, int64_t rows, int64_t cols, int64
 nvfp4_status nvfp4_alpha(const float* g_w, const float* g_a, float* alpha_out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
- * nvfp4_prepare_weight -- validate a canonical NVFP4 weight once and fill its
- * descriptor (FlashInfer PR #3597, API: prepare_bf16_fp4_weights then
- * mm_bf16_fp4, the prepare step run once per weight).  Both linears read the
- * canonical row-major [N, K/2] codes and [N, K/16] scales directly (FreeToken
- * PR #737: one weight copy, no repack), so this build's prepare step copies
- * nothing: nvfp4_prepared_weight_bytes() returns 0 and dst may be NULL.
- *   codes, scales  device buffers as above (16-byte aligned), kept alive by
- *                  the caller for as long as the descriptor is used
- *   out            host pointer to the descriptor to fill
- * Errors: INVALID_ARGUMENT, INVALID_SHAPE (K % 16, N < 0), UNSUPPORTED
- * (K % 256), ALIGNMENT.  Launches nothing.
+ * nvfp4_prepare_weight -- re-tile a canonical NVFP4 weight once into the
+ * layout both linears read (FlashInfer PR #3597, API: prepare_bf16_fp4_weights
+ * runs once per weight so the GEMM dequantizes fast; FreeToken PR #737,
+ * Changes: one weight copy serves the W4A16 and W4A4 linears).
+ *   codes   device uint8 [N, K/2], row-major, 8-byte aligned
+ *   scales  device uint8 [N, K/16], row-major
+ *   dst     device buffer of at least nvfp4_prepared_weight_bytes(N, K) bytes,
+ *           16-byte aligned, owned by the caller; after the call's work has
+ *           run on the stream the canonical codes/scales may be freed
+ *   out     host pointer to the descriptor to fill
+ * Tiled layout: ceil(N/16) * (K/256) units of 2304 bytes; unit (t, s) at byte
+ * (t * K/256 + s) * 2304 covers rows 16t..16t+15 (rows >= N are zero) and
+ * k in [256s, 256s + 256).  With lane l = r + 16q (r = row in the tile,
+ * q = 0..3) owning the 16-k groups 4p + q (p = 0..3) of its row:
+ *   unit bytes [16l, 16l+16)         canonical code bytes of groups q, 4+q
+ *   unit bytes [1024+16l, +16)       canonical code bytes of groups 8+q, 12+q
+ *   unit bytes [2048+4l, +4)         scale bytes of groups q, 4+q, 8+q, 12+q
+ * One launch on the stream.  nvfp4_prepared_weight_bytes returns 0 for an
+ * invalid shape.
+ * Errors: INVALID_ARGUMENT (null), INVALID_SHAPE (K % 16, N < 0),
+ * UNSUPPORTED (K % 256), WORKSPACE (dst_bytes too small), ALIGNMENT, HIP.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K);
 nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t N, int64_t K, void* dst,
@@ -140,27 +153,30 @@ nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t
 /* ---------------------------------------------------------------------------
  * nvfp4_linear_w4a16 -- out = bf16((a @ dequant(W).T) * alpha), fp32
  * accumulation (FlashInfer PR #3597, Description), for decode-sized M <= 16
- * (FreeToken PR #737, Changes: small-batch kernels on the same row-major
- * weight).
+ * (FreeToken PR #737, Changes: small-batch kernels on the same weight).
  *   a      bf16 [M, K], lda >= K
  *   w      prepared weight descriptor (host pointer)
  *   alpha  device fp32[1] (1/g_w)
  *   out    bf16 [M, N], ldo >= N
- * Deterministic: the fp32 sum order depends only on (M, N, K).
+ * One launch, no workspace.  Deterministic: the fp32 sum order depends only
+ * on (M, N, K).
  * Errors: as above; UNSUPPORTED for M > 16.
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* alpha,
                                 void* out, int64_t ldo, hipStream_t stream);
 
-/* Same with an explicit kernel configuration (for tests and tuning):
- * row_tiles (16-row MFMA tiles per wave) and steps_per_wave (256-k steps per
- * wave; the waves of one workgroup split K) from (1,1) (1,2) (1,4) (2,1) (2,2)
- * (2,4) (4,1), with ceil(K/256 / steps_per_wave) <= 16 waves (<= 8 when
- * steps_per_wave = 4); other values return INVALID_ARGUMENT.
- * row_tiles = 0 selects the default configuration. */
+/* Same with an explicit schedule (for tests and tuning):
+ *   schedule 0     the default for (M, N, K); the other arguments are ignored
+ *   schedule 1     split: one workgroup per 16-row tile whose ksplit (1..16)
+ *                  waves split K into contiguous runs of 256-k steps
+ *   schedule 2     shared: one workgroup per 8 tiles over all of K, the
+ *                  activations streamed through LDS in chunks of chunk_steps
+ *                  256-k steps; needs M * min(chunk_steps, K/256) <= 64
+ * Other values return INVALID_ARGUMENT.  The result bits depend on (M, N, K)
+ * and the schedule. */
 nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w,
-                                   const float* alpha, void* out, int64_t ldo, int row_tiles, int steps_per_wave,
-                                   hipStream_t stream);
+                                   const float* alpha, void* out, int64_t ldo, int schedule, int ksplit,
+                                   int chunk_steps, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * nvfp4_linear_w4a4 -- out = bf16((dequant(A) @ dequant(W).T) * alpha) on
@@ -188,8 +204,8 @@ int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global);
 void nvfp4_set_route_m_max(int64_t m_max);
 int64_t nvfp4_get_route_m_max(void);
 
-/* Workspace nvfp4_linear needs: M*K/2 + M*K/16 bytes (plus alignment) for the
- * quantized activations on the W4A4 route, 0 on the W4A16 route. */
+/* Workspace nvfp4_linear needs: M*K/2 + M*K/16 bytes (256-byte aligned parts)
+ * for the quantized activations of the W4A4 route; the W4A16 route uses none. */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------------
@@ -200,6 +216,7 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   alpha_w4a16   device fp32[1], 1/g_w
  *   alpha_w4a4    device fp32[1], 1/(g_w g_act) (may be NULL when g_act is)
  *   ws, ws_bytes  device workspace, >= nvfp4_linear_workspace_bytes(M, N, K)
+ *                 on the W4A4 route (may be NULL on the W4A16 route)
  *   route_taken   host int out (NVFP4_ROUTE_*), may be NULL
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,

@@ -16,15 +16,24 @@ bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0
 
 nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
-// Checks shared by the linears: the weight descriptor and the output.
+// Shape checks shared by prepare and the linears.
+nvfp4_status check_weight_shape(int64_t N, int64_t K) {
+  if (N < 0 || K <= 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (K % 16 != 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (N > kInt32Max - 15 || K > kInt32Max) return NVFP4_ERR_INVALID_SHAPE;
+  if (K % 256 != 0) return NVFP4_ERR_UNSUPPORTED;
+  return NVFP4_OK;
+}
+
+// Checks shared by the linears: the prepared weight descriptor.
 nvfp4_status check_weight(const nvfp4_weight* w) {
-  if (!w || !w->codes || !w->scales) return NVFP4_ERR_INVALID_ARGUMENT;
-  if (w->N < 0 || w->K <= 0) return NVFP4_ERR_INVALID_SHAPE;
-  if (w->K % 16 != 0) return NVFP4_ERR_INVALID_SHAPE;
-  if (w->N > kInt32Max || w->K > kInt32Max) return NVFP4_ERR_INVALID_SHAPE;
-  if (w->layout != 0) return NVFP4_ERR_UNSUPPORTED;
-  if (w->K % 256 != 0) return NVFP4_ERR_UNSUPPORTED;
-  if (!aligned16(w->codes) || !aligned16(w->scales)) return NVFP4_ERR_ALIGNMENT;
+  if (!w) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_weight_shape(w->N, w->K);
+  if (st != NVFP4_OK) return st;
+  if (w->layout != NVFP4_LAYOUT_TILED) return NVFP4_ERR_UNSUPPORTED;
+  if (w->N == 0) return NVFP4_OK;  // empty weight: data may be null
+  if (!w->data) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(w->data)) return NVFP4_ERR_ALIGNMENT;
   return NVFP4_OK;
 }
 
@@ -54,10 +63,10 @@ nvfp4_status w4a16_checked(const void* a, int64_t M, int64_t lda, const nvfp4_we
   if ((st = check_bf16_input(a, M, w->K, lda)) != NVFP4_OK) return st;
   if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
   if (M > 16) return NVFP4_ERR_UNSUPPORTED;
-  nvfp4::W4A16Config cfg = cfg_in ? *cfg_in : nvfp4::w4a16_default_config(M, w->N, w->K);
-  if (!nvfp4::w4a16_config_valid(cfg, w->K)) return NVFP4_ERR_INVALID_ARGUMENT;
-  if (M == 0 || w->N == 0) return NVFP4_OK;
-  return hip_status(nvfp4::launch_w4a16(a, M, lda, w->codes, w->scales, w->N, w->K, alpha, out, ldo, cfg, stream));
+  if (cfg_in && !nvfp4::w4a16_config_valid(*cfg_in, M, w->K)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (w->N == 0) return NVFP4_OK;
+  const nvfp4::W4A16Config cfg = cfg_in ? *cfg_in : nvfp4::w4a16_default_config(M, w->N, w->K);
+  return hip_status(nvfp4::launch_w4a16(a, M, lda, w->data, w->N, w->K, alpha, out, ldo, cfg, stream));
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -111,26 +120,29 @@ nvfp4_status nvfp4_alpha(const float* g_w, const float* g_a, float* alpha_out, h
 }
 
 size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K) {
-  (void)N;
-  (void)K;
-  return 0;
+  if (check_weight_shape(N, K) != NVFP4_OK) return 0;
+  return size_t(nvfp4::tiled_weight_bytes(N, K));
 }
 
 nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t N, int64_t K, void* dst,
                                   size_t dst_bytes, nvfp4_weight* out, hipStream_t stream) {
-  (void)dst;
-  (void)dst_bytes;
-  (void)stream;
-  if (!codes || !scales || !out) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (!out) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_weight_shape(N, K);
+  if (st != NVFP4_OK) return st;
+  const size_t need = size_t(nvfp4::tiled_weight_bytes(N, K));
+  if (need > 0 && (!codes || !scales || !dst)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (dst_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (need > 0 && (!aligned16(dst) || (reinterpret_cast<uintptr_t>(codes) & 7u))) return NVFP4_ERR_ALIGNMENT;
+  if (need > 0) {
+    st = hip_status(nvfp4::launch_retile(codes, scales, N, K, dst, stream));
+    if (st != NVFP4_OK) return st;
+  }
   nvfp4_weight w;
-  w.codes = codes;
-  w.scales = scales;
+  w.data = dst;
   w.N = N;
   w.K = K;
-  w.layout = 0;
+  w.layout = NVFP4_LAYOUT_TILED;
   w.reserved = 0;
-  nvfp4_status st = check_weight(&w);
-  if (st != NVFP4_OK) return st;
   *out = w;
   return NVFP4_OK;
 }
@@ -141,12 +153,13 @@ nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvf
 }
 
 nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w,
-                                   const float* alpha, void* out, int64_t ldo, int row_tiles, int steps_per_wave,
-                                   hipStream_t stream) {
-  if (row_tiles == 0) return w4a16_checked(a, M, lda, w, alpha, out, ldo, nullptr, stream);
+                                   const float* alpha, void* out, int64_t ldo, int schedule, int ksplit,
+                                   int chunk_steps, hipStream_t stream) {
+  if (schedule == 0) return w4a16_checked(a, M, lda, w, alpha, out, ldo, nullptr, stream);
   nvfp4::W4A16Config cfg;
-  cfg.row_tiles = row_tiles;
-  cfg.steps_per_wave = steps_per_wave;
+  cfg.schedule = schedule;
+  cfg.ksplit = ksplit;
+  cfg.chunk_steps = chunk_steps;
   return w4a16_checked(a, M, lda, w, alpha, out, ldo, &cfg, stream);
 }
 
@@ -163,7 +176,7 @@ nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_
   if ((M + 127) / 128 > 65535) return NVFP4_ERR_UNSUPPORTED;
   if (M == 0 || w->N == 0) return NVFP4_OK;
   return hip_status(
-      nvfp4::launch_w4a4(a_codes, a_scales, M, w->codes, w->scales, w->N, w->K, alpha, out, ldo, stream));
+      nvfp4::launch_w4a4(a_codes, a_scales, M, w->data, w->N, w->K, alpha, out, ldo, stream));
 }
 
 int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global) {
@@ -213,8 +226,7 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
     uint8_t* scales = codes + align_up(size_t(M) * size_t(w->K / 2), 256);
     st = hip_status(nvfp4::launch_quantize(a, M, w->K, lda, g_act, codes, scales, stream));
     if (st == NVFP4_OK)
-      st = hip_status(nvfp4::launch_w4a4(codes, scales, M, w->codes, w->scales, w->N, w->K, alpha_w4a4, out, ldo,
-                                         stream));
+      st = hip_status(nvfp4::launch_w4a4(codes, scales, M, w->data, w->N, w->K, alpha_w4a4, out, ldo, stream));
   }
   if (st == NVFP4_OK && route_taken) *route_taken = route;
   return st;

@@ -2,192 +2,283 @@
 //
 // Computes out[m, n] = bf16(alpha * sum_k a[m, k] * e2m1(c[n, k]) * E4M3(s[n, k/16]))
 // with fp32 accumulation (FlashInfer PR #3597, Description: out = (a @
-// dequant(b, b_sf).T) * alpha), reading the canonical row-major [N, K/2] codes
-// and [N, K/16] scales (FreeToken PR #737, Changes: one weight copy, no repack).
+// dequant(b, b_sf).T) * alpha), on the weight re-tiled once by the prepare step.
 //
-// Design (HBM-bound: every weight byte is read once; activations stay in L2):
-//  * swap-AB bf16 MFMA 16x16x32: 16 weight rows on the MFMA's M side, up to 16
-//    tokens on its N side (tokens >= M contribute zeros);
-//  * k is permuted inside each 256-k step so that one lane's two dwordx4 code
-//    loads (32 contiguous bytes = 64 k of one row) and its one scale dword are
-//    exactly the A operands of 8 MFMAs; the activation operand uses the same
-//    permutation (8 contiguous bf16 per lane per MFMA).  A row's 128 code bytes
-//    of a step come from 4 lanes, so each wave instruction reads whole lines;
-//  * dequant: fp4 -> f32 pair (hardware convert), times the E4M3 scale, packed
-//    to bf16 -- exact, since e2m1 * E4M3 fits bf16;
-//  * the K range is split across the waves of one workgroup, which then add
-//    their partial 16x16 tiles through LDS in a fixed order (deterministic, no
-//    workspace, one launch).  This fills the GPU at small N without a second
-//    reduction kernel.
+// Arithmetic:
+//  * swap-AB bf16 MFMA 16x16x32: 16 weight rows on the MFMA's row side, up to 16
+//    tokens on its column side (token lanes >= M repeat token M-1; their output
+//    columns are never stored);
+//  * a 256-k step of a 16-row tile is one 2304-byte unit of the tiled weight;
+//    a wave reads it with two dwordx4 code loads and one dword scale load per
+//    lane, each instruction covering whole cache lines, and every lane then
+//    holds the operands of its MFMA row: lane (r, q) owns the 16-k groups
+//    4p + q (p = 0..3), so MFMA j = 2p + h multiplies codes k = 64p + 16q + 8h
+//    + (0..7) of the step -- the same k the activation lane (c, q) reads;
+//  * dequant: fp4 pair -> f32 pair (hardware convert, exact), times the E4M3
+//    scale, packed to bf16 -- exact, since every e2m1 * E4M3 product fits bf16.
+//
+// The weight is read once from HBM, every wave keeps the next units' loads in
+// flight while it dequantizes the current one, and the kernel stays within 64
+// (split) or 80 (shared) VGPRs so a CU holds enough waves to hide HBM latency.
+// Every 16-row tile needs all M x K activations (M/4.5 times the tile's weight
+// bytes), and there are two schedules for them, both one launch with a fixed
+// fp32 sum order (deterministic) and no workspace:
+//  * split -- for weights with few row tiles: a workgroup owns one tile and its
+//    `ksplit` waves split K into contiguous runs of steps, each reading its own
+//    activations from L2; the partial tiles are added through LDS in wave
+//    order.  This spreads a small weight over enough waves to fill the GPU.
+//  * shared -- for weights with many row tiles: a workgroup owns 8 tiles (one
+//    per wave) over all of K and streams the activations through LDS in
+//    double-buffered chunks of `kc` steps, so each chunk is read from L2 once
+//    per 8 tiles and from LDS by every wave.
 #include "device.hpp"
 #include "kernels.hpp"
+
+#include <algorithm>
+#include <atomic>
 
 namespace nvfp4 {
 
 namespace {
 
-// One wave: R row tiles (16 rows each) x S consecutive 256-k steps.  All of the
-// wave's weight bytes (R*S*(32 B codes + 4 B scales) per lane) are requested
-// before any arithmetic, so a CU holds tens of KB of HBM reads in flight; the
-// activation operands of step s+1 are requested while step s computes.
-template <int R, int S, int WMAX>
-__global__ __launch_bounds__(64 * WMAX) void w4a16_kernel(const uint16_t* __restrict__ a, int64_t lda, int32_t M,
-                                                          const uint8_t* __restrict__ wc,
-                                                          const uint8_t* __restrict__ ws, int32_t N, int32_t K,
-                                                          const float* __restrict__ alpha_p,
-                                                          uint16_t* __restrict__ out, int64_t ldo) {
-  extern __shared__ float red[];  // [waves][R][64][4]
+constexpr int kUnitBytes = 2304;
+constexpr int kSharedTiles = 8;
+
+struct Unit {
+  uint4 c0, c1;
+  uint32_t sc;
+};
+
+__device__ __forceinline__ Unit load_unit(const uint8_t* __restrict__ u, int lane) {
+  Unit x;
+  x.c0 = ld16_nt(u + 16 * lane);
+  x.c1 = ld16_nt(u + 1024 + 16 * lane);
+  x.sc = ld4_nt(u + 2048 + 4 * lane);
+  return x;
+}
+
+// acc += dequant(codes of MFMAs 4*half .. 4*half+3) * b[0..3].
+__device__ __forceinline__ void mma_half(const uint4& codes, uint32_t sc, int half, const uint4 (&b)[4],
+                                         f32x4_t& acc) {
+  const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
+  const float S0 = half == 0 ? e4m3_to_f32<0>(sc) : e4m3_to_f32<2>(sc);
+  const float S1 = half == 0 ? e4m3_to_f32<1>(sc) : e4m3_to_f32<3>(sc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t av[4];
+    dequant8_bf16(cw[i], i < 2 ? S0 : S1, av);
+    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
+    const bf16x8_t B = __builtin_bit_cast(bf16x8_t, b[i]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+  }
+}
+
+// Lane (c, qq) holds out[c][16 * tile + 4qq + i], i = 0..3.
+__device__ __forceinline__ void store_tile(const f32x4_t& acc, float alpha, int lane, int32_t tile, int32_t M,
+                                           int32_t N, uint16_t* __restrict__ out, int64_t ldo) {
+  const int c = lane & 15, qq = lane >> 4;
+  if (c >= M) return;
+  uint16_t* orow = out + int64_t(c) * ldo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t n = 16 * tile + 4 * qq + i;
+    if (n < N) orow[n] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] * alpha));
+  }
+}
+
+// ------------------------------------------------------------------- split
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void w4a16_split_kernel(
+    const uint16_t* __restrict__ a, int64_t lda, int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
+    int32_t steps_per_wave, const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo) {
+  extern __shared__ float red[];  // [waves][64][4]
   const int lane = int(threadIdx.x & 63);
   const int wave = int(threadIdx.x >> 6);
   const int nwaves = int(blockDim.x >> 6);
-  const int r = lane & 15, q = lane >> 4;
-  const int32_t n_base = int32_t(blockIdx.x) * 16 * R;
+  const int q = lane >> 4;
+  const int32_t tile = int32_t(blockIdx.x);
   const int32_t steps = K / 256;
-  const int32_t s0 = wave * S;
-  const int64_t code_row = K / 2, scale_row = K / 16;
+  const int32_t s0 = wave * steps_per_wave;
+  const int32_t s1 = min(steps, s0 + steps_per_wave);  // s0 < s1: the host sizes the block so
+  const uint16_t* arow = a + int64_t(min(lane & 15, M - 1)) * lda;
+  const uint8_t* wtile = wt + int64_t(tile) * steps * kUnitBytes;
 
-  uint4 cw[S][R][2];
-  uint32_t sw[S][R];
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  Unit next = load_unit(wtile + int64_t(s0) * kUnitBytes, lane);
+  for (int32_t s = s0; s < s1; ++s) {
+    const Unit cur = next;
+    if (s + 1 < s1) next = load_unit(wtile + int64_t(s + 1) * kUnitBytes, lane);
+    const uint16_t* astep = arow + 256 * int64_t(s);
 #pragma unroll
-  for (int t = 0; t < R; ++t) {
-    const int32_t n = min(n_base + 16 * t + r, N - 1);
-    const uint8_t* wrow = wc + int64_t(n) * code_row + 32 * q;
-    const uint8_t* srow = ws + int64_t(n) * scale_row + 4 * q;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int32_t st = min(s0 + s, steps - 1);  // steps past the end are loaded but unused
-      cw[s][t][0] = ld16_nt(wrow + 128 * int64_t(st));
-      cw[s][t][1] = ld16_nt(wrow + 128 * int64_t(st) + 16);
-      sw[s][t] = ld4_nt(srow + 16 * int64_t(st));
-    }
-  }
-  const bool tok = r < M;
-  const uint16_t* arow = a + int64_t(tok ? r : 0) * lda + 64 * q;
-
-  f32x4_t acc[R];
-#pragma unroll
-  for (int t = 0; t < R; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 b[2][8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) b[0][j] = make_uint4(0, 0, 0, 0);
-  if (tok && s0 < steps) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[0][j] = ld16(arow + 256 * int64_t(s0) + 8 * j);
-  }
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    if (s0 + s >= steps) break;  // wave-uniform
-    const int cur = s & 1;
-    if (s + 1 < S) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) b[cur ^ 1][j] = make_uint4(0, 0, 0, 0);
-      if (tok && s0 + s + 1 < steps) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) b[cur ^ 1][j] = ld16(arow + 256 * int64_t(s0 + s + 1) + 8 * j);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      const uint32_t cwd[8] = {cw[s][t][0].x, cw[s][t][0].y, cw[s][t][0].z, cw[s][t][0].w,
-                               cw[s][t][1].x, cw[s][t][1].y, cw[s][t][1].z, cw[s][t][1].w};
-      const float Sg[4] = {e4m3_to_f32<0>(sw[s][t]), e4m3_to_f32<1>(sw[s][t]), e4m3_to_f32<2>(sw[s][t]),
-                           e4m3_to_f32<3>(sw[s][t])};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t av[4];
-        dequant8_bf16(cwd[j], Sg[j >> 1], av);
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
-        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, b[cur][j]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int t = 0; t < R; ++t)
-    *reinterpret_cast<f32x4_t*>(&red[((wave * R + t) * 64 + lane) * 4]) = acc[t];
-  __syncthreads();
-  const float alpha = *alpha_p;
-  for (int idx = int(threadIdx.x); idx < R * 64; idx += int(blockDim.x)) {
-    const int t = idx >> 6, ln = idx & 63;
-    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-    for (int w = 0; w < nwaves; ++w) sum += *reinterpret_cast<const f32x4_t*>(&red[((w * R + t) * 64 + ln) * 4]);
-    const int c = ln & 15, qq = ln >> 4;
-    if (c < M) {
-      uint16_t* orow = out + int64_t(c) * ldo;
+    for (int half = 0; half < 2; ++half) {
+      uint4 b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int32_t n = n_base + 16 * t + 4 * qq + i;
-        if (n < N) orow[n] = __builtin_bit_cast(uint16_t, (__bf16)(sum[i] * alpha));
+        const int j = 4 * half + i;  // k = 64p + 16q + 8h, j = 2p + h
+        b[i] = ld16(astep + 64 * (j >> 1) + 16 * q + 8 * (j & 1));
       }
+      mma_half(half == 0 ? cur.c0 : cur.c1, cur.sc, half, b, acc);
+    }
+  }
+
+  if (nwaves > 1) {
+    *reinterpret_cast<f32x4_t*>(&red[(wave * 64 + lane) * 4]) = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < nwaves; ++w) acc += *reinterpret_cast<const f32x4_t*>(&red[(w * 64 + lane) * 4]);
+  }
+  store_tile(acc, *alpha_p, lane, tile, M, N, out, ldo);
+}
+
+// ------------------------------------------------------------------ shared
+// LDS holds two chunks of kc steps; a chunk is [kc steps][8 j][4 q][M c]
+// entries of 8 bf16 (only the M real token rows).
+__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ a, int64_t lda, int32_t M, int32_t s_begin,
+                                           int32_t ns, int32_t tid, uint4 (&v)[4], int32_t (&dst)[4]) {
+  const int32_t per_row = ns * 32;  // 16-byte pieces per token row in the chunk
+  const int32_t total = per_row * M;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t e = tid + i * kSharedTiles * 64;
+    dst[i] = -1;
+    if (e < total) {
+      const int32_t c = e / per_row, kk = e - c * per_row;
+      const int32_t s = kk >> 5, r5 = kk & 31;                   // step in the chunk, piece in the step
+      const int32_t p = r5 >> 3, q = (r5 >> 1) & 3, h = r5 & 1;  // k = 64p + 16q + 8h
+      v[i] = ld16(a + int64_t(c) * lda + int64_t(s_begin + s) * 256 + 8 * r5);
+      dst[i] = ((s * 8 + 2 * p + h) * 4 + q) * M + c;
     }
   }
 }
 
+__global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __restrict__ a, int64_t lda, int32_t M,
+                                                           const uint8_t* __restrict__ wt, int32_t N, int32_t K,
+                                                           int32_t kc, const float* __restrict__ alpha_p,
+                                                           uint16_t* __restrict__ out, int64_t ldo) {
+  extern __shared__ uint4 act[];  // two chunks of kc * 32 * M entries
+  const int lane = int(threadIdx.x & 63);
+  const int wave = int(threadIdx.x >> 6);
+  const int32_t tid = int32_t(threadIdx.x);
+  const int32_t tiles = (N + 15) / 16;
+  const int32_t steps = K / 256;
+  const int32_t nch = (steps + kc - 1) / kc;
+  const int32_t chunk_entries = kc * 32 * M;
+  const int32_t tile = int32_t(blockIdx.x) * kSharedTiles + wave;
+  const bool has_tile = tile < tiles;
+  const int lds_lane = (lane >> 4) * M + min(lane & 15, M - 1);
+  const uint8_t* wtile = wt + int64_t(has_tile ? tile : 0) * steps * kUnitBytes;
+
+  uint4 v[4];
+  int32_t dst[4];
+  stage_load(a, lda, M, 0, min(kc, steps), tid, v, dst);
+  // weight units of steps 0 and 1 in flight while the first chunk is staged
+  Unit n1 = load_unit(wtile, lane);
+  Unit n2 = steps > 1 ? load_unit(wtile + kUnitBytes, lane) : n1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (dst[i] >= 0) act[dst[i]] = v[i];
+  __syncthreads();
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t ch = 0; ch < nch; ++ch) {
+    const int32_t s_begin = ch * kc;
+    const int32_t ns = min(kc, steps - s_begin);
+    const bool more = ch + 1 < nch;
+    if (more) stage_load(a, lda, M, s_begin + kc, min(kc, steps - s_begin - kc), tid, v, dst);
+    const uint4* buf = act + (ch & 1) * chunk_entries;
+    for (int32_t s = 0; s < ns; ++s) {
+      const int32_t gs = s_begin + s;
+      const Unit cur = n1;
+      n1 = n2;
+      if (gs + 2 < steps) n2 = load_unit(wtile + int64_t(gs + 2) * kUnitBytes, lane);
+      const uint4* lds_step = buf + s * 32 * M;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint4 b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = lds_step[(4 * half + i) * 4 * M + lds_lane];
+        mma_half(half == 0 ? cur.c0 : cur.c1, cur.sc, half, b, acc);
+      }
+    }
+    if (more) {
+      uint4* nbuf = act + ((ch + 1) & 1) * chunk_entries;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (dst[i] >= 0) nbuf[dst[i]] = v[i];
+      __syncthreads();
+    }
+  }
+  if (has_tile) store_tile(acc, *alpha_p, lane, tile, M, N, out, ldo);
+}
+
+std::atomic<int> g_cu_count[64];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 }  // namespace
 
-// Largest waves-per-workgroup each steps-per-wave variant is compiled for.
-constexpr int wmax_for(int S) { return S == 1 ? 16 : (S == 2 ? 16 : 8); }
-
 W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
-  W4A16Config c;
   const int64_t steps = K / 256;
-  // steps per wave: keep a workgroup within 16 waves, two steps once K is long
-  c.steps_per_wave = steps <= 8 ? 1 : (steps <= 32 ? 2 : 4);
-  // row tiles per wave: as many as keep at least one workgroup per CU
-  const int64_t tiles = (N + 15) / 16;
-  c.row_tiles = 1;
-  if (tiles / 4 >= 256 && c.steps_per_wave <= 2) c.row_tiles = 4;
-  else if (tiles / 2 >= 256 || (M > 4 && tiles / 2 >= 128)) c.row_tiles = 2;
-  if (c.row_tiles == 4 && c.steps_per_wave == 2) c.row_tiles = 2;  // register budget of the 16-wave variant
+  const int64_t tiles = std::max<int64_t>(1, (N + 15) / 16);
+  const int64_t cus = cu_count();
+  W4A16Config c;
+  c.ksplit = 0;
+  c.chunk_steps = 0;
+  if (tiles >= int64_t(kSharedTiles) * cus * 3 / 2) {
+    // shared: the largest chunk whose double buffer fits in 64 KiB of LDS
+    c.schedule = 2;
+    c.chunk_steps = int(std::max<int64_t>(1, std::min<int64_t>(steps, 64 / std::max<int64_t>(1, M))));
+  } else {
+    // split: waves per tile so the launch gives every CU about 8 waves
+    c.schedule = 1;
+    const int64_t want = (8 * cus + tiles - 1) / tiles;
+    c.ksplit = int(std::max<int64_t>(1, std::min<int64_t>({want, steps, 16})));
+  }
   return c;
 }
 
-bool w4a16_config_valid(const W4A16Config& c, int64_t K) {
-  const int R = c.row_tiles, S = c.steps_per_wave;
-  if (R != 1 && R != 2 && R != 4) return false;
-  if (S != 1 && S != 2 && S != 4) return false;
-  if (R * S > 4 && !(R == 2 && S == 4)) return false;
-  const int64_t steps = K / 256;
-  const int64_t waves = (steps + S - 1) / S;
-  return waves >= 1 && waves <= wmax_for(S);
+bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K) {
+  if (c.schedule == 1) return c.ksplit >= 1 && c.ksplit <= 16;
+  if (c.schedule == 2) {
+    if (c.chunk_steps < 1) return false;
+    const int64_t kc = std::min<int64_t>(c.chunk_steps, K / 256);
+    const int64_t per_chunk = std::max<int64_t>(1, M) * kc * 32;  // 16-byte entries
+    return 2 * per_chunk * 16 <= 64 * 1024 && per_chunk <= 4 * kSharedTiles * 64;  // LDS, staging registers
+  }
+  return false;
 }
 
-namespace {
-template <int R, int S>
-void launch_rs(dim3 grid, int waves, size_t lds, hipStream_t stream, const uint16_t* A, int64_t lda, int32_t M,
-               const uint8_t* WC, const uint8_t* WS, int32_t N, int32_t K, const float* alpha, uint16_t* O,
-               int64_t ldo) {
-  hipLaunchKernelGGL((w4a16_kernel<R, S, wmax_for(S)>), grid, dim3(64 * waves), lds, stream, A, lda, M, WC, WS, N, K,
-                     alpha, O, ldo);
-}
-}  // namespace
-
-hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_codes, const void* w_scales,
-                        int64_t N, int64_t K, const float* alpha, void* out, int64_t ldo,
-                        const W4A16Config& cfg, hipStream_t stream) {
+hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_tiled, int64_t N, int64_t K,
+                        const float* alpha, void* out, int64_t ldo, const W4A16Config& cfg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t steps = K / 256;
-  const int S = cfg.steps_per_wave, R = cfg.row_tiles;
-  const int waves = int((steps + S - 1) / S);
-  const dim3 grid(uint32_t((N + 16 * R - 1) / (16 * R)));
-  const size_t lds = size_t(waves) * R * 64 * 4 * sizeof(float);
+  const int64_t tiles = (N + 15) / 16;
   const auto* A = static_cast<const uint16_t*>(a);
-  const auto* WC = static_cast<const uint8_t*>(w_codes);
-  const auto* WS = static_cast<const uint8_t*>(w_scales);
+  const auto* WT = static_cast<const uint8_t*>(w_tiled);
   auto* O = static_cast<uint16_t*>(out);
-  const int32_t m = int32_t(M), n = int32_t(N), k = int32_t(K);
-#define NVFP4_W4A16_CASE(RR, SS) \
-  if (R == RR && S == SS) launch_rs<RR, SS>(grid, waves, lds, stream, A, lda, m, WC, WS, n, k, alpha, O, ldo);
-  NVFP4_W4A16_CASE(1, 1)
-  NVFP4_W4A16_CASE(1, 2)
-  NVFP4_W4A16_CASE(1, 4)
-  NVFP4_W4A16_CASE(2, 1)
-  NVFP4_W4A16_CASE(2, 2)
-  NVFP4_W4A16_CASE(2, 4)
-  NVFP4_W4A16_CASE(4, 1)
-#undef NVFP4_W4A16_CASE
+  if (cfg.schedule == 2) {
+    const int64_t kc = std::min<int64_t>(cfg.chunk_steps, steps);
+    const size_t lds = 2 * size_t(M) * size_t(kc) * 32 * 16;
+    const int64_t groups = (tiles + kSharedTiles - 1) / kSharedTiles;
+    hipLaunchKernelGGL(w4a16_shared_kernel, dim3(uint32_t(groups)), dim3(64 * kSharedTiles), lds, stream, A, lda,
+                       int32_t(M), WT, int32_t(N), int32_t(K), int32_t(kc), alpha, O, ldo);
+    return hipGetLastError();
+  }
+  // contiguous runs of steps per wave; no wave is left without a step
+  const int64_t ks = std::min<int64_t>(cfg.ksplit, steps);
+  const int64_t per = (steps + ks - 1) / ks;
+  const int waves = int((steps + per - 1) / per);
+  const size_t lds = waves > 1 ? size_t(waves) * 64 * 4 * sizeof(float) : 0;
+  hipLaunchKernelGGL(w4a16_split_kernel, dim3(uint32_t(tiles)), dim3(64 * waves), lds, stream, A, lda, int32_t(M),
+                     WT, int32_t(N), int32_t(K), int32_t(per), alpha, O, ldo);
   return hipGetLastError();
 }
 

@@ -2,8 +2,8 @@
 //
 // Computes out[m, n] = bf16(alpha * sum_k deq(A)[m, k] * deq(W)[n, k]) with
 // alpha = 1 / (g_w * g_a), on NVFP4 activations (from the quantize kernel) and
-// the same canonical [N, K/2] + [N, K/16] weight as the W4A16 path (FreeToken
-// PR #737, Changes: W4A4 prefill on the checkpoint's row-major codes).
+// the same prepared (tiled) weight as the W4A16 path (FreeToken PR #737,
+// Changes: both linears use one weight copy).
 //
 // Arithmetic: every dequantized value e2m1 * E4M3 is exact in fp16, so the
 // tile product runs on the fp16 MFMA with exact operands and fp32
@@ -40,6 +40,25 @@ __device__ __forceinline__ Stage load_stage(const uint8_t* __restrict__ codes, c
   return s;
 }
 
+// Weight stage from the tiled layout: row n of the weight, 64-k block kb, the
+// 32 k of half `half` (scale groups 4p + q for q = 2*half, 2*half + 1 of step
+// kb/4, p = kb % 4).  Unit (t, s) holds, for lane r + 16q, the codes of groups
+// q, 4+q at byte 16*lane, of groups 8+q, 12+q at 1024 + 16*lane, and the four
+// scale bytes at 2048 + 4*lane.
+__device__ __forceinline__ Stage load_w_stage(const uint8_t* __restrict__ wt, int64_t n, int32_t steps, int kb,
+                                              int half) {
+  const int64_t t = n >> 4, r = n & 15;
+  const int s = kb >> 2, p = kb & 3;
+  const uint8_t* u = wt + (t * steps + s) * 2304;
+  const int64_t l0 = r + 16 * (2 * half), l1 = l0 + 16;
+  const uint2 a = *reinterpret_cast<const uint2*>(u + 1024 * (p >> 1) + 16 * l0 + 8 * (p & 1));
+  const uint2 b = *reinterpret_cast<const uint2*>(u + 1024 * (p >> 1) + 16 * l1 + 8 * (p & 1));
+  Stage st;
+  st.codes = make_uint4(a.x, a.y, b.x, b.y);
+  st.scales = (uint32_t(u[2048 + 4 * l0 + p]) | (uint32_t(u[2048 + 4 * l1 + p]) << 8)) << (16 * half);
+  return st;
+}
+
 __device__ __forceinline__ void store_stage(const Stage& s, int half, _Float16* dst) {
   // this thread's 32 k use scale groups 2*half and 2*half + 1
   const uint32_t sb = s.scales >> (16 * half);
@@ -58,8 +77,7 @@ __device__ __forceinline__ void store_stage(const Stage& s, int half, _Float16* 
 }
 
 __global__ __launch_bounds__(256) void w4a4_kernel(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
-                                                   int32_t M, const uint8_t* __restrict__ wc,
-                                                   const uint8_t* __restrict__ ws, int32_t N, int32_t K,
+                                                   int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
                                                    const float* __restrict__ alpha_p, uint16_t* __restrict__ out,
                                                    int64_t ldo) {
   __shared__ __attribute__((aligned(16))) _Float16 lw[BN * PITCH];
@@ -72,7 +90,8 @@ __global__ __launch_bounds__(256) void w4a4_kernel(const uint8_t* __restrict__ a
 
   // loader role: row tid/2 of both tiles, 32 k half (tid & 1)
   const int lrow = tid >> 1, half = tid & 1;
-  const int64_t wrow = min(n0 + lrow, N - 1);
+  const int32_t steps = K / 256;
+  const int64_t wrow = min(n0 + lrow, (N + 15) / 16 * 16 - 1);
   const int64_t arow = min(m0 + lrow, M - 1);
   _Float16* lw_dst = lw + lrow * PITCH + 32 * half;
   _Float16* la_dst = la + lrow * PITCH + 32 * half;
@@ -84,7 +103,7 @@ __global__ __launch_bounds__(256) void w4a4_kernel(const uint8_t* __restrict__ a
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / BK;
-  Stage sw = load_stage(wc, ws, wrow, K, 0, half);
+  Stage sw = load_w_stage(wt, wrow, steps, 0, half);
   Stage sa = load_stage(ac, as, arow, K, 0, half);
   for (int kb = 0; kb < nk; ++kb) {
     __syncthreads();
@@ -92,7 +111,7 @@ __global__ __launch_bounds__(256) void w4a4_kernel(const uint8_t* __restrict__ a
     store_stage(sa, half, la_dst);
     __syncthreads();
     if (kb + 1 < nk) {
-      sw = load_stage(wc, ws, wrow, K, kb + 1, half);
+      sw = load_w_stage(wt, wrow, steps, kb + 1, half);
       sa = load_stage(ac, as, arow, K, kb + 1, half);
     }
 #pragma unroll
@@ -129,14 +148,13 @@ __global__ __launch_bounds__(256) void w4a4_kernel(const uint8_t* __restrict__ a
 
 }  // namespace
 
-hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_codes,
-                       const void* w_scales, int64_t N, int64_t K, const float* alpha, void* out, int64_t ldo,
-                       hipStream_t stream) {
+hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
+                       int64_t K, const float* alpha, void* out, int64_t ldo, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   dim3 grid(uint32_t((N + BN - 1) / BN), uint32_t((M + BM - 1) / BM));
   hipLaunchKernelGGL(w4a4_kernel, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(a_codes),
-                     static_cast<const uint8_t*>(a_scales), int32_t(M), static_cast<const uint8_t*>(w_codes),
-                     static_cast<const uint8_t*>(w_scales), int32_t(N), int32_t(K), alpha,
+                     static_cast<const uint8_t*>(a_scales), int32_t(M), static_cast<const uint8_t*>(w_tiled),
+                     int32_t(N), int32_t(K), alpha,
                      static_cast<uint16_t*>(out), ldo);
   return hipGetLastError();
 }

@@ -26,9 +26,12 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "invalid shape", 3: "alignment", 4:
 ROUTE_W4A16, ROUTE_W4A4 = 0, 1
 
 
+LAYOUT_TILED = 1
+
+
 class Weight(C.Structure):
     """Mirror of struct nvfp4_weight."""
-    _fields_ = [("codes", P), ("scales", P), ("N", I64), ("K", I64), ("layout", C.c_int32), ("reserved", C.c_int32)]
+    _fields_ = [("data", P), ("N", I64), ("K", I64), ("layout", C.c_int32), ("reserved", C.c_int32)]
 
 
 _SIGS = {
@@ -40,7 +43,7 @@ _SIGS = {
     "nvfp4_prepared_weight_bytes": (SZ, [I64, I64]),
     "nvfp4_prepare_weight": (I32, [P, P, I64, I64, P, SZ, C.POINTER(Weight), P]),
     "nvfp4_linear_w4a16": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, P]),
-    "nvfp4_linear_w4a16_ex": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, I32, I32, P]),
+    "nvfp4_linear_w4a16_ex": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, I32, I32, I32, P]),
     "nvfp4_linear_w4a4": (I32, [P, P, I64, C.POINTER(Weight), P, P, I64, P]),
     "nvfp4_route": (I32, [I64, I64, I64, I32]),
     "nvfp4_set_route_m_max": (None, [I64]),

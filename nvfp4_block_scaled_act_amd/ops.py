@@ -44,9 +44,8 @@ def _scalar(t: torch.Tensor, name: str) -> None:
 
 @dataclass
 class Weight:
-    """A prepared NVFP4 weight: the canonical codes/scales and their descriptor."""
-    codes: torch.Tensor
-    scales: torch.Tensor
+    """A prepared NVFP4 weight: the tiled device buffer and its descriptor."""
+    data: torch.Tensor
     desc: _L.Weight
 
     @property
@@ -93,7 +92,13 @@ def quantize_act(a: torch.Tensor, g: torch.Tensor, codes: torch.Tensor | None = 
     return codes, scales
 
 
-def prepare_weight(codes: torch.Tensor, scales: torch.Tensor) -> Weight:
+def prepared_weight_bytes(N: int, K: int) -> int:
+    return int(_L.load().nvfp4_prepared_weight_bytes(N, K))
+
+
+def prepare_weight(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None) -> Weight:
+    """Re-tile canonical NVFP4 codes [N, K/2] and scales [N, K/16] into the
+    layout the linears read (one launch on the current stream)."""
     _need(codes, torch.uint8, "codes")
     _need(scales, torch.uint8, "scales")
     if not codes.is_contiguous() or not scales.is_contiguous():
@@ -102,10 +107,15 @@ def prepare_weight(codes: torch.Tensor, scales: torch.Tensor) -> Weight:
     K = 2 * half
     if tuple(scales.shape) != (N, K // 16):
         raise ValueError(f"scales must be [N, K/16] = [{N}, {K // 16}], got {tuple(scales.shape)}")
+    nbytes = prepared_weight_bytes(N, K)
+    if out is None:
+        out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
+    _need(out, torch.uint8, "out")
     desc = _L.Weight()
     _L.check("nvfp4_prepare_weight",
-             _L.load().nvfp4_prepare_weight(_ptr(codes), _ptr(scales), N, K, None, 0, C.byref(desc), _stream()))
-    return Weight(codes, scales, desc)
+             _L.load().nvfp4_prepare_weight(_ptr(codes), _ptr(scales), N, K, _ptr(out), out.numel(),
+                                            C.byref(desc), _stream()))
+    return Weight(out, desc)
 
 
 def _out(out, M, N, device):
@@ -116,7 +126,9 @@ def _out(out, M, N, device):
 
 
 def linear_w4a16(a: torch.Tensor, w: Weight, alpha_: torch.Tensor, out: torch.Tensor | None = None,
-                 row_tiles: int = 0, steps_per_wave: int = 0) -> torch.Tensor:
+                 schedule: int = 0, ksplit: int = 0, chunk_steps: int = 0) -> torch.Tensor:
+    """W4A16 linear; schedule 0 picks the default schedule for (M, N, K)
+    (1 = split with ksplit waves per tile, 2 = shared with LDS chunks)."""
     _need(a, torch.bfloat16, "a")
     _scalar(alpha_, "alpha")
     lda = _rows(a, "a")
@@ -126,7 +138,7 @@ def linear_w4a16(a: torch.Tensor, w: Weight, alpha_: torch.Tensor, out: torch.Te
     out, ldo = _out(out, M, w.N, a.device)
     _L.check("nvfp4_linear_w4a16_ex",
              _L.load().nvfp4_linear_w4a16_ex(_ptr(a), M, lda, C.byref(w.desc), _ptr(alpha_), _ptr(out), ldo,
-                                             row_tiles, steps_per_wave, _stream()))
+                                             schedule, ksplit, chunk_steps, _stream()))
     return out
 
 
@@ -172,12 +184,13 @@ def linear(a: torch.Tensor, w: Weight, g_act: torch.Tensor | None, alpha_w4a16: 
     M = a.shape[0]
     out, ldo = _out(out, M, w.N, a.device)
     need = linear_workspace_bytes(M, w.N, w.K)
-    if workspace is None and g_act is not None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
-    ws_bytes = 0 if workspace is None else workspace.numel()
+    ws = workspace
+    if ws is None and g_act is not None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if ws is None else ws.numel()
     r = C.c_int(-1)
     _L.check("nvfp4_linear",
              _L.load().nvfp4_linear(_ptr(a), M, lda, C.byref(w.desc), _ptr(g_act), _ptr(alpha_w4a16),
-                                    _ptr(alpha_w4a4), _ptr(out), ldo, _ptr(workspace), ws_bytes, C.byref(r),
+                                    _ptr(alpha_w4a4), _ptr(out), ldo, _ptr(ws), ws_bytes, C.byref(r),
                                     _stream()))
     return out, int(r.value)

@@ -34,9 +34,9 @@ def test_status_strings(nv):
     assert nv.nvfp4_version() >= 100
 
 
-def _w(N=64, K=256, codes=A16, scales=A16):
+def _w(N=64, K=256, data=A16, layout=L.LAYOUT_TILED):
     w = L.Weight()
-    w.codes, w.scales, w.N, w.K, w.layout, w.reserved = codes, scales, N, K, 0, 0
+    w.data, w.N, w.K, w.layout, w.reserved = data, N, K, layout, 0
     return w
 
 
@@ -56,14 +56,25 @@ def test_quantize_validation(nv):
 
 def test_prepare_weight_validation(nv):
     d = L.Weight()
-    assert nv.nvfp4_prepared_weight_bytes(128, 256) == 0
-    assert nv.nvfp4_prepare_weight(A16, A16, 128, 256, None, 0, C.byref(d), None) == OK
-    assert (d.N, d.K, d.layout) == (128, 256, 0) and d.codes == A16
-    assert nv.nvfp4_prepare_weight(A16, A16, 128, 24, None, 0, C.byref(d), None) == SHAPE
-    assert nv.nvfp4_prepare_weight(A16, A16, 128, 128, None, 0, C.byref(d), None) == UNSUP  # K % 256
-    assert nv.nvfp4_prepare_weight(A16 + 4, A16, 128, 256, None, 0, C.byref(d), None) == ALIGN
-    assert nv.nvfp4_prepare_weight(None, A16, 128, 256, None, 0, C.byref(d), None) == ARG
-    assert nv.nvfp4_prepare_weight(A16, A16, -1, 256, None, 0, C.byref(d), None) == SHAPE
+    # ceil(N/16) tiles x K/256 steps x 2304 bytes
+    assert nv.nvfp4_prepared_weight_bytes(128, 256) == 8 * 2304
+    assert nv.nvfp4_prepared_weight_bytes(100, 512) == 7 * 2 * 2304
+    assert nv.nvfp4_prepared_weight_bytes(62080, 5120) == 62080 * 5120 * 9 // 16
+    assert nv.nvfp4_prepared_weight_bytes(128, 24) == 0      # invalid shape
+    need = nv.nvfp4_prepared_weight_bytes(128, 256)
+    p = nv.nvfp4_prepare_weight
+    assert p(A16, A16, 128, 24, A16, need, C.byref(d), None) == SHAPE
+    assert p(A16, A16, 128, 128, A16, need, C.byref(d), None) == UNSUP   # K % 256
+    assert p(A16, A16, 128, 256, A16, need - 1, C.byref(d), None) == WS  # dst too small
+    assert p(A16, A16, 128, 256, None, need, C.byref(d), None) == ARG    # no dst
+    assert p(None, A16, 128, 256, A16, need, C.byref(d), None) == ARG
+    assert p(A16, A16, 128, 256, A16 + 8, need, C.byref(d), None) == ALIGN  # dst not 16-byte aligned
+    assert p(A16 + 4, A16, 128, 256, A16, need, C.byref(d), None) == ALIGN  # codes not 8-byte aligned
+    assert p(A16, A16, -1, 256, A16, need, C.byref(d), None) == SHAPE
+    assert p(A16, A16, 128, 256, A16, need, None, None) == ARG
+    # N = 0: nothing to re-tile, a valid empty descriptor
+    assert p(None, None, 0, 256, None, 0, C.byref(d), None) == OK
+    assert (d.N, d.K, d.layout) == (0, 256, L.LAYOUT_TILED)
 
 
 def test_w4a16_validation(nv):
@@ -82,12 +93,13 @@ def test_w4a16_validation(nv):
     wz = _w(N=0)
     assert f(A16, 4, 256, C.byref(wz), A16, A16, 1, None) == OK         # N = 0
     g = nv.nvfp4_linear_w4a16_ex
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 3, 1, None) == ARG  # row_tiles 3
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 0, None) == ARG  # steps_per_wave 0
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 3, None) == ARG  # steps_per_wave 3
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 4, 2, None) == ARG  # (4, 2) not compiled
-    wk = _w(K=256 * 20)
-    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 1, 1, None) == ARG  # 20 waves > 16
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 3, 1, 1, None) == ARG    # schedule 3
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 0, 0, None) == ARG    # split: ksplit 0
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 17, 0, None) == ARG   # split: ksplit 17
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 2, 0, 0, None) == ARG    # shared: chunk 0
+    wl = _w(N=64, K=256 * 8)
+    assert g(A16, 16, 256 * 8, C.byref(wl), A16, A16, 64, 2, 0, 5, None) == ARG  # 16 x 5 > 64
+    assert g(A16, 0, 256, C.byref(w), A16, A16, 64, 2, 0, 5, None) == OK     # empty
 
 
 def test_w4a4_validation(nv):
@@ -100,6 +112,10 @@ def test_w4a4_validation(nv):
     assert f(None, None, 0, C.byref(w), A16, None, 64, None) == OK
     wbad = _w(K=512 + 16)
     assert f(A16, A16, 8, C.byref(wbad), A16, A16, 64, None) == UNSUP
+    wlay = _w(layout=0)
+    assert f(A16, A16, 8, C.byref(wlay), A16, A16, 64, None) == UNSUP   # not a prepared weight
+    wmis = _w(data=A16 + 8)
+    assert f(A16, A16, 8, C.byref(wmis), A16, A16, 64, None) == ALIGN
 
 
 def test_route_is_a_pure_threshold(nv):

@@ -65,32 +65,76 @@ def test_w4a16_decode_sweep(ops, orc, shape_index):
         gemm_check(bf16_host(out), ref[:M], sabs[:M])
 
 
-def test_w4a16_every_kernel_config(ops, orc):
-    # ragged N, K with an odd number of 256-k steps, M between powers of two
+SCHEDULES = [(1, ks, 0) for ks in (1, 2, 3, 7, 16)] + [(2, 0, kc) for kc in (1, 2, 3, 4, 17)]
+
+
+def _schedules_for(M, K):
+    return [(0, 0, 0)] + [sch for sch in SCHEDULES if sch[0] == 1 or M * min(sch[2], K // 256) <= 64]
+
+
+def test_w4a16_every_schedule(ops, orc):
+    # ragged N (not a multiple of 16 or of a workgroup's 8 tiles), K with an odd
+    # number of 256-k steps (17: uneven chunks), M between powers of two
     N, K, M = 1000, 4352, 7
     W = synth.normal_bf16(11, N, K)
     a = synth.normal_bf16(12, M, K)
     q = Quantized(ops, orc, W)
     ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
     ad = bf16_dev(a)
-    steps = K // 256
-    for rt, spw in [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1)]:
-        if -(-steps // spw) > (8 if spw == 4 else 16):
-            with pytest.raises(ValueError):
-                ops.linear_w4a16(ad, q.w, q.alpha, row_tiles=rt, steps_per_wave=spw)
-            continue
-        out = ops.linear_w4a16(ad, q.w, q.alpha, row_tiles=rt, steps_per_wave=spw)
+    for sch, ks, kc in _schedules_for(M, K):
+        out = ops.linear_w4a16(ad, q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
         gemm_check(bf16_host(out), ref, sabs)
-    # a K with fewer steps than one wave's share, on every variant
+    # every token count on a short K, including a chunk longer than K
     K2 = 512
     W2 = synth.normal_bf16(13, 300, K2)
     a2 = synth.normal_bf16(14, 16, K2)
     q2 = Quantized(ops, orc, W2)
     ref2, _, sabs2 = orc.linear_w4a16(a2, q2.codes, q2.scales, orc.alpha(q2.g))
-    for rt, spw in [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1)]:
-        for M in (1, 5, 16):
-            out = ops.linear_w4a16(bf16_dev(a2[:M]), q2.w, q2.alpha, row_tiles=rt, steps_per_wave=spw)
+    a2d = bf16_dev(a2)
+    for M in range(1, 17):
+        for sch, ks, kc in [(0, 0, 0), (1, 2, 0), (2, 0, 1), (2, 0, 4 if M <= 16 else 1)]:
+            out = ops.linear_w4a16(a2d[:M], q2.w, q2.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
             gemm_check(bf16_host(out), ref2[:M], sabs2[:M])
+
+
+def test_w4a16_long_k(ops, orc):
+    # K/256 = 72 steps: long runs per wave, many LDS chunks
+    N, K = 200, 256 * 72
+    W = synth.normal_bf16(15, N, K)
+    a = synth.normal_bf16(16, 16, K)
+    q = Quantized(ops, orc, W)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    ad = bf16_dev(a)
+    for sch, ks, kc in [(0, 0, 0), (1, 1, 0), (1, 16, 0), (2, 0, 4), (2, 0, 3)]:
+        for M in (1, 16):
+            out = ops.linear_w4a16(ad[:M], q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
+            gemm_check(bf16_host(out), ref[:M], sabs[:M])
+    out = ops.linear_w4a16(ad[:1], q.w, q.alpha, schedule=2, chunk_steps=64)  # one chunk of 64 steps (M = 1)
+    gemm_check(bf16_host(out), ref[:1], sabs[:1])
+
+
+def test_prepared_layout(ops, orc):
+    """The tiled weight follows the documented unit layout byte for byte."""
+    N, K = 40, 512
+    W = synth.normal_bf16(17, N, K)
+    q = Quantized(ops, orc, W)
+    tiled = u8_host(q.w.data)
+    steps, tiles = K // 256, (N + 15) // 16
+    assert tiled.size >= tiles * steps * 2304
+    codes = np.zeros((tiles * 16, K // 2), np.uint8)
+    scales = np.zeros((tiles * 16, K // 16), np.uint8)
+    codes[:N], scales[:N] = q.codes, q.scales
+    for t in range(tiles):
+        for s in range(steps):
+            u = tiled[(t * steps + s) * 2304:(t * steps + s + 1) * 2304]
+            for lane in range(64):
+                r, qq = lane % 16, lane // 16
+                row = 16 * t + r
+                groups = [4 * p + qq for p in range(4)]
+                want = np.concatenate([codes[row, 128 * s + 8 * g:128 * s + 8 * g + 8] for g in groups])
+                got = np.concatenate([u[16 * lane:16 * lane + 16], u[1024 + 16 * lane:1024 + 16 * lane + 16]])
+                assert (got == want).all(), (t, s, lane)
+                assert (u[2048 + 4 * lane:2048 + 4 * lane + 4] == scales[row, 16 * s + np.array(groups)]).all()
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 12, 256), (16, 12, 512), (3, 17, 768), (9, 100, 1024), (13, 4000, 2048)])
@@ -127,9 +171,11 @@ def test_w4a16_deterministic(ops, orc):
     W = synth.normal_bf16(8, 3584, 5120)
     q = Quantized(ops, orc, W, check_rows=np.arange(0, 3584, 97))
     a = bf16_dev(synth.normal_bf16(9, 16, 5120))
-    o1 = bf16_host(ops.linear_w4a16(a, q.w, q.alpha))
-    for _ in range(3):
-        assert (bf16_host(ops.linear_w4a16(a, q.w, q.alpha)) == o1).all()
+    for sch, ks, kc in [(0, 0, 0), (1, 7, 0), (2, 0, 4)]:
+        o1 = bf16_host(ops.linear_w4a16(a, q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc))
+        for _ in range(3):
+            o2 = ops.linear_w4a16(a, q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
+            assert (bf16_host(o2) == o1).all()
 
 
 # ------------------------------------------------------------------ W4A4
