@@ -1,23 +1,26 @@
 """Benchmark of the NVFP4 quantized linear on one MI355X.
 
-Headline: W4A16 decode throughput in HBM TB/s over the decode sweep
+Headline (`value`): W4A16 decode throughput in HBM TB/s over the decode sweep
 M in {1, 2, 4, 8, 16} x (N, K) in {(3584, 5120), (8704, 5120), (5120, 1536),
-(5120, 4352)} (the shapes of 1Cat-vLLM PR #611, Test Plan), with the W4A4
-prefill GEMM at M = 8192, N = 8704, K = 5120 reported beside it in TFLOP/s.
+(5120, 4352)} -- the decode shapes of 1Cat-vLLM PR #611 (Test Plan) -- as
+total algorithmic bytes over total kernel time.  Reported beside it: the large
+fused-weight decode (N = 62080, K = 5120, M in {1, 8, 16}), the W4A4 prefill
+GEMM at M = 8192, N = 8704, K = 5120 in TFLOP/s with its activation quantizer,
+the one-time weight prepare, and the CPU oracle on a bounded sample.
 
 Method (cold weights, as the pages measure decode linears with every layer
 read from DRAM: FreeToken PR #737, Results; FlashInfer PR #4038, cold L2):
-  * every (shape, M) call cycles through C copies of its weight so that more
-    than 2 GB of other weights is read between two uses of one copy (the
-    256 MB last-level cache cannot hold them);
-  * the calls of one (shape, M) are captured in a HIP graph (C launches) and
-    replayed; one step = one replay of each of the 20 graphs;
-  * times come from HIP events on the stream the kernels run on.
-Algorithmic bytes of one W4A16 launch: N*K/2 (codes) + N*K/16 (scales) +
-2*M*K (activations) + 2*M*N (output) + 4 (alpha); of the W4A4 GEMM: 2*M*N*K
-FLOPs.
+  * every (shape, M) call cycles through C prepared copies of its weight so
+    that more than 2 GB of other weights is read between two uses of one copy
+    (the 256 MB last-level cache cannot hold them);
+  * the C calls of one (shape, M) are captured in a HIP graph and replayed;
+    one step = one replay of each graph of the sweep;
+  * times come from HIP events recorded on the stream the graphs run on.
+Algorithmic bytes of one W4A16 call: N*K/2 (codes) + N*K/16 (scales) +
+2*M*K (activations) + 2*M*N (output) + 4 (alpha); of one W4A4 GEMM: 2*M*N*K
+FLOPs; of one quantizer call: M*K*(2 + 1/2 + 1/16) bytes.
 
-Prints ONE JSON line on stdout; details go to stderr.
+Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -56,12 +59,12 @@ def kernel_source_hash(names):
 
 
 def load_traffic(kernel_key, src_hash):
-    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they
-    were taken on the current kernel source (else None)."""
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/
+    counters.json), if they were taken on the current kernel source."""
     p = os.path.join(ROOT, "profiles", "counters.json")
     try:
         d = json.load(open(p))
-    except Exception:
+    except (OSError, ValueError):
         return None
     e = d.get(kernel_key)
     if not e or e.get("source_hash") != src_hash:
@@ -69,80 +72,85 @@ def load_traffic(kernel_key, src_hash):
     return e.get("hbm_bytes_per_launch")
 
 
-def bench_w4a16(ops, torch, steps, warmup):
+def dev_bf16(torch, bits):
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def bench_w4a16(ops, torch, workload, shapes, Ms, steps, warmup, graphs=True):
+    """Cold-weight W4A16 timing of every (shape, M); returns per-call rows and
+    totals.  graphs=False launches the calls directly (for counter runs, which
+    do not see kernels replayed from a graph)."""
     from nvfp4_block_scaled_act_amd import synth
 
-    shapes = synth.W4A16_DECODE_SHAPES
-    Ms = synth.W4A16_DECODE_M
-    per_set = sum(N * K * 9 // 16 for N, K in shapes)
-    C = max(2, int(np.ceil(COLD_BYTES / per_set)))
-    log(f"[w4a16] {len(shapes)} shapes x M {Ms}; {C} cold copies per weight ({C * per_set / 1e9:.2f} GB)")
     entries = []
+    keep = []
     for si, (N, K) in enumerate(shapes):
-        W = synth.normal_bf16(synth.seed_for("w4a16_decode", synth.ROLE_W, si), N, K)
-        a = synth.normal_bf16(synth.seed_for("w4a16_decode", synth.ROLE_A, si), 16, K)
-        wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
+        W = synth.normal_bf16(synth.seed_for(workload, synth.ROLE_W, si), N, K)
+        a = synth.normal_bf16(synth.seed_for(workload, synth.ROLE_A, si), max(Ms), K)
+        wd = dev_bf16(torch, W)
         g = ops.global_scale(wd)
         codes, scales = ops.quantize_act(wd, g)
         del wd
         alpha = ops.alpha(g)
-        copies = [ops.prepare_weight(codes.clone(), scales.clone()) for _ in range(C)]
-        ad = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        C = max(2, int(np.ceil(COLD_BYTES / (N * K * 9 / 16))))
+        copies = [ops.prepare_weight(codes, scales) for _ in range(C)]
+        del codes, scales
+        ad = dev_bf16(torch, a)
+        keep.append((copies, ad, alpha))
         for M in Ms:
             out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-            entries.append(dict(N=N, K=K, M=M, a=ad[:M], alpha=alpha, out=out, copies=copies))
+            entries.append(dict(N=N, K=K, M=M, a=ad[:M], alpha=alpha, out=out, copies=copies, C=C))
     torch.cuda.synchronize()
-    # capture one graph per (shape, M): C launches over the C copies
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
+    with torch.cuda.stream(s):  # warm the code paths before capture
         for e in entries:
             for w in e["copies"][:2]:
                 ops.linear_w4a16(e["a"], w, e["alpha"], out=e["out"])
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     for e in entries:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for w in e["copies"]:
-                ops.linear_w4a16(e["a"], w, e["alpha"], out=e["out"])
-        e["graph"] = g
+        if graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for w in e["copies"]:
+                    ops.linear_w4a16(e["a"], w, e["alpha"], out=e["out"])
+            e["graph"] = g.replay
+            e["_g"] = g
+        else:
+            e["graph"] = (lambda e=e: [ops.linear_w4a16(e["a"], w, e["alpha"], out=e["out"]) for w in e["copies"]])
     torch.cuda.synchronize()
     for _ in range(warmup):
         for e in entries:
-            e["graph"].replay()
+            e["graph"]()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in entries]
     per = np.zeros(len(entries))
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
     for _ in range(steps):
         for i, e in enumerate(entries):
             evs[i][0].record()
-            e["graph"].replay()
+            e["graph"]()
             evs[i][1].record()
         torch.cuda.synchronize()
         for i in range(len(entries)):
             per[i] += evs[i][0].elapsed_time(evs[i][1])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    rows = []
-    tot_bytes = 0
-    tot_kernel_ms = 0.0
+    rows, tot_bytes, tot_ms = [], 0.0, 0.0
     for i, e in enumerate(entries):
-        us = per[i] / steps / C * 1e3
+        us = per[i] / steps / e["C"] * 1e3
         b = w4a16_bytes(e["M"], e["N"], e["K"])
         rows.append(dict(N=e["N"], K=e["K"], M=e["M"], us_per_launch=round(us, 3), tb_s=round(b / us / 1e6, 3)))
-        tot_bytes += b * C * steps
-        tot_kernel_ms += per[i]
-        log(f"[w4a16] N={e['N']:5d} K={e['K']:5d} M={e['M']:2d}: {us:7.2f} us/launch  {b / us / 1e6:6.3f} TB/s")
-    step_bytes = sum(w4a16_bytes(e["M"], e["N"], e["K"]) for e in entries) * C
+        tot_bytes += b * e["C"] * steps
+        tot_ms += per[i]
+        log(f"[{workload}] N={e['N']:5d} K={e['K']:5d} M={e['M']:2d}: {us:7.2f} us/launch  {b / us / 1e6:6.3f} TB/s")
+    launches = sum(e["C"] for e in entries)
     for e in entries:
-        del e["graph"]
-    return dict(rows=rows, C=C, total_ms=total_ms, kernel_ms=tot_kernel_ms, bytes=tot_bytes, step_bytes=step_bytes,
-                launches=len(entries) * C * steps)
+        e.pop("graph")
+        e.pop("_g", None)
+    del keep
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return dict(rows=rows, bytes=tot_bytes, kernel_ms=tot_ms, launches_per_step=launches,
+                weight_gb=sum(N * K * 9 / 16 * max(2, int(np.ceil(COLD_BYTES / (N * K * 9 / 16)))) for N, K in shapes) / 1e9)
 
 
 def bench_w4a4(ops, torch, reps=10):
@@ -153,11 +161,16 @@ def bench_w4a4(ops, torch, reps=10):
     W = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_W), N, K)
     a = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), M, K)
     cal = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_CAL), 512, K)
-    wd = torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16)
-    ad = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-    cd = torch.from_numpy(cal.view(np.int16)).cuda().view(torch.bfloat16)
+    wd, ad, cd = dev_bf16(torch, W), dev_bf16(torch, a), dev_bf16(torch, cal)
     gw, ga = ops.global_scale(wd), ops.global_scale(cd)
-    w = ops.prepare_weight(*ops.quantize_act(wd, gw))
+    codes, scales = ops.quantize_act(wd, gw)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    w = ops.prepare_weight(codes, scales)
+    t1.record()
+    torch.cuda.synchronize()
+    prepare_us = t0.elapsed_time(t1) * 1e3
     al = ops.alpha(gw, ga)
     ac, as_ = ops.quantize_act(ad, ga)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -181,65 +194,91 @@ def bench_w4a4(ops, torch, reps=10):
     flops = 2.0 * M * N * K
     qbytes = M * K * (2 + 0.5 + 1 / 16)
     log(f"[w4a4] M={M} N={N} K={K}: gemm {gemm_us:.1f} us = {flops / gemm_us / 1e6:.1f} TFLOP/s; "
-        f"quantize {quant_us:.1f} us = {qbytes / quant_us / 1e3:.1f} GB/s")
+        f"quantize {quant_us:.1f} us = {qbytes / quant_us / 1e3:.1f} GB/s; prepare {prepare_us:.1f} us")
     return dict(M=M, N=N, K=K, gemm_us=gemm_us, quant_us=quant_us, tflops=flops / gemm_us / 1e6,
-                linear_tflops=flops / (gemm_us + quant_us) / 1e6, quant_gbs=qbytes / quant_us / 1e3)
+                linear_tflops=flops / (gemm_us + quant_us) / 1e6, quant_gbs=qbytes / quant_us / 1e3,
+                prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16)
 
 
 def cpu_baseline(target_s=15.0):
-    """The oracle (untuned) on a bounded sample of the W4A16 decode sweep:
-    shape (8704, 5120) at M = 16 over a prefix of the weight rows."""
+    """The oracle (as it stands) on a bounded sample of the headline workload:
+    the W4A16 call N=8704, K=5120, M=16 restricted to its first 512 weight
+    rows, repeated for about target_s seconds on the host cores."""
     import oracle
     from nvfp4_block_scaled_act_amd import synth
 
-    N, K, M = 8704, 5120, 16
-    rows_w = 512
+    K, M, rows_w = 5120, 16, 512
     W = synth.normal_bf16(synth.seed_for("w4a16_decode", synth.ROLE_W, 1), rows_w, K)
     a = synth.normal_bf16(synth.seed_for("w4a16_decode", synth.ROLE_A, 1), M, K)
     g = oracle.global_scale(W)
     c, s = oracle.quantize(W, g)
     al = oracle.alpha(g)
+    oracle.linear_w4a16(a, c[:8], s[:8], al)  # load the library outside the timed loop
     t0 = time.perf_counter()
-    n_done = 0
-    while True:
+    passes = 0
+    while time.perf_counter() - t0 < target_s:
         oracle.linear_w4a16(a, c, s, al)
-        n_done += rows_w
-        if time.perf_counter() - t0 > target_s or n_done >= 64 * rows_w:
-            break
+        passes += 1
     dt = time.perf_counter() - t0
-    b = (w4a16_bytes(M, rows_w, K)) * (n_done // rows_w)
+    b = w4a16_bytes(M, rows_w, K) * passes
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return dict(value=b / dt / 1e12, unit="TB/s", cores=cores, kind="oracle",
-                sample=f"W4A16 N=8704,K=5120,M=16 on {rows_w} weight rows x {n_done // rows_w} passes, {dt:.1f} s")
+                sample=f"W4A16 N=512 rows of (8704, 5120), M=16, {passes} passes in {dt:.1f} s")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--skip-w4a4", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch the W4A16 calls directly (counter runs)")
+    ap.add_argument("--only", choices=["all", "headline", "fused", "w4a4", "copy"], default="all",
+                    help="run one part (for profiler runs); 'copy' times a plain 256 MiB device copy, the "
+                         "reference for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the NVFP4 linear has no multi-GPU path here); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only: the NVFP4 linear here has no multi-GPU path (got --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     import torch
 
-    from nvfp4_block_scaled_act_amd import ops
+    from nvfp4_block_scaled_act_amd import ops, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    r16 = bench_w4a16(ops, torch, args.steps, args.warmup)
-    r4 = None if args.skip_w4a4 else bench_w4a4(ops, torch)
-    value_tbs = r16["bytes"] / (r16["kernel_ms"] * 1e-3) / 1e12
+    if args.only == "copy":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        print(json.dumps({"copy_bytes": 256 << 20, "us": round(us, 2), "read_write_gb_s": round(2 * (256 << 20) / us / 1e3, 1)}))
+        return
+    if args.only in ("fused", "w4a4"):
+        if args.only == "fused":
+            fl = synth.FUSED_LARGE
+            r3 = bench_w4a16(ops, torch, "fused_large", [(fl["N"], fl["K"])], [1, 8, 16], args.steps, args.warmup,
+                             graphs=not args.no_graph)
+            print(json.dumps({"fused_large_decode": r3["rows"]}))
+        else:
+            r4 = bench_w4a4(ops, torch, reps=args.steps)
+            print(json.dumps({"w4a4_prefill": {k: round(v, 3) if isinstance(v, float) else v for k, v in r4.items()}}))
+        return
+    shapes = synth.W4A16_DECODE_SHAPES
+    Ms = synth.W4A16_DECODE_M
+    log(f"[w4a16_decode] {len(shapes)} shapes x M {Ms}, cold rotation over >= {COLD_BYTES / 1e9:.1f} GB per shape")
+    r16 = bench_w4a16(ops, torch, "w4a16_decode", shapes, Ms, args.steps, args.warmup, graphs=not args.no_graph)
     achieved_gbs = r16["bytes"] / (r16["kernel_ms"] * 1e-3) / 1e9
     src16 = kernel_source_hash(["w4a16.hip", "device.hpp"])
-    traffic = load_traffic("w4a16_decode_sweep", src16)
     res = {
         "metric": METRIC,
-        "value": round(value_tbs, 4),
+        "value": round(achieved_gbs / 1e3, 4),
         "unit": "TB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -252,18 +291,28 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "W4A16 decode sweep: M in {1,2,4,8,16} x (N,K) in {(3584,5120),(8704,5120),(5120,1536),"
-                        "(5120,4352)}, NVFP4 weights N(0,1), cold (rotated over %d copies, %.1f GB)"
-                        % (r16["C"], r16["C"] * sum(N * K * 9 / 16 for N, K in [(3584, 5120), (8704, 5120),
-                                                                            (5120, 1536), (5120, 4352)]) / 1e9),
-            "launches_per_step": len(r16["rows"]) * r16["C"],
+                        "(5120,4352)}, NVFP4 weights from N(0,1), cold (each weight rotated over copies, %.1f GB)"
+                        % r16["weight_gb"],
+            "launches_per_step": r16["launches_per_step"],
             "parallelism": "single GPU",
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "w4a16_kernel", "source_hash": src16},
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("w4a16_decode_sweep", src16),
+                     "kernel": "w4a16_split_kernel (every decode shape)", "source_hash": src16},
         "per_shape": r16["rows"],
     }
-    if r4 is not None:
+    if args.only == "headline":
+        print(json.dumps({"value_tb_s": res["value"], "per_shape": res["per_shape"]}))
+        return
+    if args.only == "all":
+        fl = synth.FUSED_LARGE
+        r3 = bench_w4a16(ops, torch, "fused_large", [(fl["N"], fl["K"])], [1, 8, 16], max(2, args.steps // 2), 1)
+        gbs3 = r3["bytes"] / (r3["kernel_ms"] * 1e-3) / 1e9
+        res["fused_large_decode"] = {
+            "workload": "W4A16 N=62080 K=5120 M in {1,8,16}, cold", "tb_s": round(gbs3 / 1e3, 4),
+            "frac_of_hbm_peak": round(gbs3 / HBM_PEAK_GBS, 4), "kernel": "w4a16_shared_kernel", "per_m": r3["rows"]}
+        r4 = bench_w4a4(ops, torch)
         res["w4a4_prefill"] = {
             "workload": "W4A4 M=8192 N=8704 K=5120, NVFP4 activations (static global, 512-row calibration)",
             "tflops": round(r4["tflops"], 2), "unit": "TFLOP/s", "gemm_us": round(r4["gemm_us"], 2),
@@ -274,7 +323,10 @@ def main():
                          "unit": "TFLOP/s", "frac": round(r4["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                          "traffic": load_traffic("w4a4_prefill_m8192", kernel_source_hash(["w4a4.hip", "device.hpp"]))},
         }
-    if not args.no_cpu_baseline:
+        res["prepare_weight"] = {"workload": "re-tile N=8704 K=5120 (one time, not in value)",
+                                 "us": round(r4["prepare_us"], 2),
+                                 "gb_s": round(r4["prepare_bytes"] / r4["prepare_us"] / 1e3, 1)}
+    if not args.no_cpu_baseline and args.only == "all":
         res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)
 
