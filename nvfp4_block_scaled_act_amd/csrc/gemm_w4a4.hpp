@@ -1,0 +1,219 @@
+// Block-scaled NVFP4 x NVFP4 GEMM main loop for gfx950, shared by the dense
+// W4A4 linear and the two grouped GEMMs of the MoE expert layer.
+//
+// Computes, for a workgroup tile of 256 weight rows x 256 activation rows,
+//   acc[row][tok] = sum_k deq(W)[row, k] * deq(A)[tok, k]
+// with deq(x) = e2m1(code) * E4M3(scale of its 16-k group).  Every such value
+// has at most 6 significant bits and lies in [2^-10, 2688], so it is exact in
+// fp16, the products are exact in fp32 and the MFMA (32x32x16 fp16, fp32
+// accumulate) adds exact terms.  (gfx950's fp4 MFMA scales by powers of two
+// per 32 k and cannot carry NVFP4's per-16 E4M3 scales.)
+//
+// Per 64-k step the workgroup dequantizes both operand tiles once into LDS
+// (fp16, row-major, double-buffered): the weight tile from the tiled weight
+// (the step's 64 k of a 16-row tile are groups 4b..4b+3 of its unit, 8 code
+// bytes and one scale byte per (row, group)), the activation tile from the
+// canonical [rows, K/2] codes and [rows, K/16] scales.  The next step's loads
+// are in flight while the MFMAs of the current one run; one barrier per step.
+// Waves are laid out 2 (weight rows) x 4 (activation rows); each owns 128 x 64
+// outputs as 4 x 2 MFMA tiles of 32 x 32 (the 32x32x16 shape runs at about
+// 1.6 times the rate of 16x16x32 on gfx950).  Register i of lane l in tile
+// (t, u) holds weight row row0(t) + 8*(i/4) + 4*(l/32) + i%4 for activation
+// row 32u + l%32 of the wave's 64.
+#pragma once
+
+#include "device.hpp"
+
+namespace nvfp4 {
+namespace gemm {
+
+constexpr int BN = 256;  // weight rows per workgroup (16 tiles of 16)
+constexpr int BM = 256;  // activation rows per workgroup
+constexpr int BK = 64;   // k per step
+constexpr int PITCH = BK + 8;  // fp16 per LDS row; the pad staggers rows across banks
+constexpr int kThreads = 512;
+constexpr int kUnitBytes = 2304;
+constexpr int kLdsHalves = 2 * (BN + BM) * PITCH;  // both buffers of both operands
+
+struct Acc {
+  f32x16_t v[4][2];  // [wave 32-row weight tile t][32-row activation tile u]
+};
+
+// Staged (not yet dequantized) operand bytes of one step for this thread.
+struct Stage {
+  uint2 w[2];      // weight: two (row, group) items of 16 codes
+  uint32_t ws[2];  // their scale bytes
+  uint4 a;         // activation: 32 codes of row tid/2, k 32*(tid&1) .. +32
+  uint32_t as;     // its two scale bytes (low 16 bits)
+};
+
+// Weight item i (0..1023) of a step = (local tile lt = i / 64, lane slot
+// l = i % 64 = r + 16q): row 16*lt + r, group 4b + q of the step's unit, b =
+// the step within the unit.
+template <typename WTile>
+__device__ __forceinline__ Stage load_stage(const uint8_t* __restrict__ wt, WTile wtile, int32_t steps256,
+                                            const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+                                            int64_t arow, int32_t K, int32_t step) {
+  const int tid = int(threadIdx.x);
+  const int b = step & 3;
+  Stage s;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + kThreads * j;
+    const int lt = i >> 6, l = i & 63;
+    const uint8_t* u = wt + (wtile(lt) * steps256 + (step >> 2)) * kUnitBytes;
+    s.w[j] = *reinterpret_cast<const uint2*>(u + 1024 * (b >> 1) + 16 * l + 8 * (b & 1));
+    s.ws[j] = u[2048 + 4 * l + b];
+  }
+  const int half = tid & 1;
+  s.a = ld16(a_codes + arow * (K / 2) + int64_t(step) * (BK / 2) + 16 * half);
+  s.as = *reinterpret_cast<const uint16_t*>(a_scales + arow * (K / 16) + int64_t(step) * (BK / 16) + 2 * half);
+  return s;
+}
+
+// Dequantizes part `part` (0..3) of a staged step into LDS: parts 0 and 1 are
+// the thread's two weight items, parts 2 and 3 the two 16-k groups of its
+// activation piece.  Split in four so the work interleaves with the MFMAs.
+__device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* __restrict__ wbuf,
+                                           _Float16* __restrict__ abuf) {
+  const int tid = int(threadIdx.x);
+  uint32_t v0[4], v1[4];
+  if (part < 2) {
+    const int i = tid + kThreads * part;
+    const int lt = i >> 6, l = i & 63, r = l & 15, q = l >> 4;
+    const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(s.ws[part], 0));
+    dequant8_f16(s.w[part].x, S2, v0);
+    dequant8_f16(s.w[part].y, S2, v1);
+    uint4* d = reinterpret_cast<uint4*>(wbuf + (16 * lt + r) * PITCH + 16 * q);
+    d[0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+    d[1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+  } else {
+    const int g = part - 2;  // 16-k group of the thread's 32 k
+    const int row = tid >> 1, half = tid & 1;
+    const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(s.as >> (8 * g), 0));
+    dequant8_f16(g == 0 ? s.a.x : s.a.z, S2, v0);
+    dequant8_f16(g == 0 ? s.a.y : s.a.w, S2, v1);
+    uint4* d = reinterpret_cast<uint4*>(abuf + row * PITCH + 32 * half + 16 * g);
+    d[0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+    d[1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+  }
+}
+
+// acc += W tile x A tile over one step (four 16-k MFMA blocks); after block
+// kk, part kk of the next step's staged operands is dequantized into the other
+// LDS buffer (when `next` is set), so the VALU work runs under the MFMAs.
+// wave_row0(t) = first LDS weight row of the wave's 32-row tile t.
+template <typename WaveRow0>
+__device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ wbuf, const _Float16* __restrict__ abuf,
+                                         WaveRow0 wave_row0, int wm, int lane, const Stage& next, bool has_next,
+                                         _Float16* __restrict__ wnext, _Float16* __restrict__ anext) {
+  const int r = lane & 31, h = lane >> 5;
+  // operands of block kk + 1 are read from LDS while the MFMAs of block kk run
+  f16x8_t A[2][4], B[2][2];
+  auto read = [&](int kk, int slot) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      B[slot][u] = *reinterpret_cast<const f16x8_t*>(abuf + (wm * 64 + 32 * u + r) * PITCH + 16 * kk + 8 * h);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      A[slot][t] = *reinterpret_cast<const f16x8_t*>(wbuf + (wave_row0(t) + r) * PITCH + 16 * kk + 8 * h);
+  };
+  read(0, 0);
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < BK / 16) read(kk + 1, cur ^ 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc.v[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][t], B[cur][u], acc.v[t][u], 0, 0, 0);
+    if (has_next) store_part(next, kk, wnext, anext);
+  }
+}
+
+// The whole K loop of one workgroup tile.
+//   a_row(i)    global activation row of tile row i (0..255): always a valid row
+//   wtile(lt)   tile index in the tiled weight of LDS weight tile lt (0..15): always valid
+//   wave_row0(t) first LDS weight row of the calling wave's 32-row tile t (0..3)
+template <typename ARow, typename WTile, typename WaveRow0>
+__device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, const uint8_t* __restrict__ a_codes,
+                                         const uint8_t* __restrict__ a_scales, ARow a_row,
+                                         const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K) {
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int wm = wave >> 1;
+  const int32_t steps = K / BK, steps256 = K / 256;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc.v[t][u][i] = 0.f;
+  const int64_t arow = a_row(int(threadIdx.x >> 1));
+  // buffer b of the weight tile at lds + b * BN * PITCH, of the activation
+  // tile at lds + 2 * BN * PITCH + b * BM * PITCH (offsets, so that the
+  // compiler keeps every access in the LDS address space)
+  _Float16* const abase = lds + 2 * BN * PITCH;
+
+  // Step s+1's operands are staged in registers during step s-1 and
+  // dequantized into LDS during step s: the loads have a whole step to land.
+  Stage st1 = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, 0);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) store_part(st1, part, lds, abase);
+  if (steps > 1) st1 = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, 1);
+  __syncthreads();
+  for (int32_t s = 0; s < steps; ++s) {
+    Stage st2;
+    if (s + 2 < steps) st2 = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, s + 2);
+    const int cur = s & 1;
+    mma_step(acc, lds + cur * (BN * PITCH), abase + cur * (BM * PITCH), wave_row0, wm, lane, st1, s + 1 < steps,
+             lds + (cur ^ 1) * (BN * PITCH), abase + (cur ^ 1) * (BM * PITCH));
+    __syncthreads();
+    st1 = st2;
+  }
+}
+
+// Writes the bf16 tile out[m][n] (activation row m, weight row n) of the
+// workgroup through LDS so that global stores are whole 16-byte pieces of
+// output rows.  value(t, u, i) = the output value of accumulator register i of
+// wave tile (t, u); rows beyond M and columns beyond N are not written.
+// Needs out and ldo*2 aligned to 16 bytes and n0 % 8 == 0 (else store_tile_direct).
+template <typename Value>
+__device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Value value, uint16_t* __restrict__ out,
+                                               int64_t ldo, int32_t m0, int32_t M, int32_t n0, int32_t N) {
+  constexpr int OP = BN + 8;  // bf16 per LDS output row
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(lds);
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int mloc = wm * 64 + 32 * u + (lane & 31);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nloc = 128 * wn + 32 * t + 8 * g + 4 * h;
+        const uint32_t lo = pack_bf16x2(value(t, u, 4 * g), value(t, u, 4 * g + 1));
+        const uint32_t hi = pack_bf16x2(value(t, u, 4 * g + 2), value(t, u, 4 * g + 3));
+        *reinterpret_cast<uint2*>(t16 + mloc * OP + nloc) = make_uint2(lo, hi);
+      }
+  }
+  __syncthreads();
+  // 256 rows x 32 pieces of 8 bf16
+  for (int e = int(threadIdx.x); e < BM * (BN / 8); e += kThreads) {
+    const int mloc = e >> 5, piece = e & 31;
+    const int32_t m = m0 + mloc, n = n0 + 8 * piece;
+    if (m >= M || n >= N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(t16 + mloc * OP + 8 * piece);
+    uint16_t* dst = out + int64_t(m) * ldo + n;
+    if (n + 8 <= N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint16_t* vv = reinterpret_cast<const uint16_t*>(&v);
+      for (int i = 0; i < N - n; ++i) dst[i] = vv[i];
+    }
+  }
+}
+
+}  // namespace gemm
+}  // namespace nvfp4
