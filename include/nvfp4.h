@@ -223,6 +223,70 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
                           const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo, void* ws,
                           size_t ws_bytes, int* route_taken, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * NVFP4 MoE expert layer, W4A4 on both GEMMs (FreeToken PR #736, Changes and
+ * Results: both expert GEMMs take NVFP4 activations with static input scales,
+ * the gate_up epilogue applies the gated activation and quantizes its output
+ * to NVFP4, the down epilogue applies the routing weight and sums the routes;
+ * FreeToken PR #733, Changes: the layer runs align, gate_up, activation, down
+ * and the route sum).  For token t, route r < top_k, e = topk_ids[t, r]:
+ *   z      = alpha_gu[e] * (dequant(q(x_t; g1)) @ dequant(W_gu[e]).T)   [2I]
+ *   h      = SiLU(z[0:I]) * z[I:2I], SiLU(v) = v / (1 + exp(-v)), fp32
+ *   y      = alpha_dn[e] * (dequant(q(h; g2)) @ dequant(W_dn[e]).T)     [K]
+ *   out[t] = bf16(sum_r topk_w[t, r] * y_r), the sum in fp32
+ * q(.; g) is the NVFP4 quantization of nvfp4_quantize_act (h is never rounded
+ * to bf16).  Rows [0, I) of an expert's gate_up weight are the gate, [I, 2I)
+ * the up projection.  A pair whose id lies outside [0, E) is skipped: it adds
+ * nothing to its token's sum (expert-parallel callers pass -1 for experts they
+ * do not hold).
+ *   x          bf16 [T, K], row stride ldx (>= K, multiple of 8), 16-byte aligned
+ *   topk_ids   device int32 [T, top_k]; topk_w device fp32 [T, top_k]
+ *   gate_up    prepared weight of the E stacked [2I, K] banks (N = E*2I, K)
+ *   down       prepared weight of the E stacked [K, I] banks (N = E*K, K = I)
+ *   g1, g2     device fp32[1]: static globals of x and of h
+ *   alpha_gu, alpha_dn  device fp32[E]: 1/(g_gu[e] g1), 1/(g_dn[e] g2)
+ *   out        bf16 [T, K], row stride ldo (multiple of 8), 16-byte aligned
+ *   ws         device workspace >= nvfp4_moe_workspace_bytes, 256-byte aligned
+ *   h_amax     device fp32[1] or NULL: receives max |h| over the pairs (the
+ *              calibration of a static g2 runs the layer on a calibration
+ *              batch with any g2 and sets g2 = 2688 / h_amax)
+ * Needs K % 256 == 0, I % 256 == 0, 1 <= E <= 1024, T*top_k < 2^31 and
+ * T*top_k/256 + E <= 65535.  Eight launches on the stream, no host sync; the
+ * route sum uses fp32 atomics, so its order (and the last bit of an output)
+ * can vary from call to call.
+ * After the call the workspace holds, at the offsets nvfp4_moe_workspace_layout
+ * reports, the align results and h (for inspection):
+ *   sorted     int32 [T*top_k]: pair index t*top_k + r at each slot, pairs
+ *              grouped by expert, in pair order within an expert
+ *   offsets    int32 [E + 1]: first slot of each expert, [E] = pairs kept
+ *   tiles      int32 [max_tiles, 4]: (expert, first slot, rows, 0) of each
+ *              tile of up to 256 slots, rows == 0 past the last tile
+ *   h_codes    uint8 [T*top_k, I/2], h_scales uint8 [T*top_k, I/16], by slot
+ * Errors: INVALID_ARGUMENT (null, top_k < 1, E out of range), INVALID_SHAPE
+ * (descriptor shapes disagree, strides), UNSUPPORTED (K or I % 256, sizes
+ * beyond the limits), WORKSPACE, ALIGNMENT, HIP.
+ * ------------------------------------------------------------------------- */
+typedef struct nvfp4_moe_layout {
+  int64_t x_codes, x_scales;  /* quantized x [T, K/2], [T, K/16] */
+  int64_t counts;             /* int32 [chunks, E] scratch */
+  int64_t offsets;            /* int32 [E + 1] */
+  int64_t tiles;              /* int32 [max_tiles, 4] */
+  int64_t sorted;             /* int32 [T*top_k] */
+  int64_t h_codes, h_scales;  /* uint8 [T*top_k, I/2], [T*top_k, I/16] */
+  int64_t acc;                /* fp32 [T, K] route sum */
+  int64_t max_tiles;
+  int64_t total_bytes;
+} nvfp4_moe_layout;
+
+size_t nvfp4_moe_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I);
+nvfp4_status nvfp4_moe_workspace_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I,
+                                        nvfp4_moe_layout* out);
+nvfp4_status nvfp4_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t* topk_ids, const float* topk_w,
+                            int64_t top_k, int64_t E, int64_t I, const nvfp4_weight* gate_up,
+                            const nvfp4_weight* down, const float* g1, const float* g2, const float* alpha_gu,
+                            const float* alpha_dn, void* out, int64_t ldo, void* ws, size_t ws_bytes,
+                            float* h_amax, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

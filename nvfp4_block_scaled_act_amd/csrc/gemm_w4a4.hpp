@@ -19,7 +19,10 @@
 // outputs as 4 x 2 MFMA tiles of 32 x 32 (the 32x32x16 shape runs at about
 // 1.6 times the rate of 16x16x32 on gfx950).  Register i of lane l in tile
 // (t, u) holds weight row row0(t) + 8*(i/4) + 4*(l/32) + i%4 for activation
-// row 32u + l%32 of the wave's 64.
+// row 32u + l%32 of the wave's 64; with kSwap (operands exchanged in the
+// MFMA) it holds weight row row0(t) + l%32 for activation row 32u + 8*(i/4) +
+// 4*(l/32) + i%4, so that a register's 32 lanes cover 32 consecutive outputs
+// of one activation row.
 #pragma once
 
 #include "device.hpp"
@@ -103,7 +106,7 @@ __device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* _
 // kk, part kk of the next step's staged operands is dequantized into the other
 // LDS buffer (when `next` is set), so the VALU work runs under the MFMAs.
 // wave_row0(t) = first LDS weight row of the wave's 32-row tile t.
-template <typename WaveRow0>
+template <bool kSwap, typename WaveRow0>
 __device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ wbuf, const _Float16* __restrict__ abuf,
                                          WaveRow0 wave_row0, int wm, int lane, const Stage& next, bool has_next,
                                          _Float16* __restrict__ wnext, _Float16* __restrict__ anext) {
@@ -127,7 +130,8 @@ __device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ 
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        acc.v[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][t], B[cur][u], acc.v[t][u], 0, 0, 0);
+        acc.v[t][u] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_f16(B[cur][u], A[cur][t], acc.v[t][u], 0, 0, 0)
+                            : __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][t], B[cur][u], acc.v[t][u], 0, 0, 0);
     if (has_next) store_part(next, kk, wnext, anext);
   }
 }
@@ -136,7 +140,7 @@ __device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ 
 //   a_row(i)    global activation row of tile row i (0..255): always a valid row
 //   wtile(lt)   tile index in the tiled weight of LDS weight tile lt (0..15): always valid
 //   wave_row0(t) first LDS weight row of the calling wave's 32-row tile t (0..3)
-template <typename ARow, typename WTile, typename WaveRow0>
+template <bool kSwap = false, typename ARow, typename WTile, typename WaveRow0>
 __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, const uint8_t* __restrict__ a_codes,
                                          const uint8_t* __restrict__ a_scales, ARow a_row,
                                          const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K) {
@@ -166,7 +170,7 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
     Stage st2;
     if (s + 2 < steps) st2 = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, s + 2);
     const int cur = s & 1;
-    mma_step(acc, lds + cur * (BN * PITCH), abase + cur * (BM * PITCH), wave_row0, wm, lane, st1, s + 1 < steps,
+    mma_step<kSwap>(acc, lds + cur * (BN * PITCH), abase + cur * (BM * PITCH), wave_row0, wm, lane, st1, s + 1 < steps,
              lds + (cur ^ 1) * (BN * PITCH), abase + (cur ^ 1) * (BM * PITCH));
     __syncthreads();
     st1 = st2;

@@ -33,4 +33,28 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
 hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
                        int64_t K, const float* alpha, void* out, int64_t ldo, hipStream_t stream);
 
+// NVFP4 MoE expert layer (W4A4 gate_up with SiLU gate and NVFP4 re-quantization,
+// W4A4 down with routing weights and an fp32 route sum).  The workspace holds,
+// at the offsets moe_layout gives (256-byte aligned parts):
+struct MoeTile {
+  int32_t expert, slot0, rows, pad;  // rows == 0: unused entry
+};
+struct MoeLayout {
+  int64_t chunks;     // align chunks of 1024 pairs
+  int64_t max_tiles;  // tile table length: T*top_k/256 + E
+  int64_t x_codes, x_scales;  // quantized hidden states [T, K/2], [T, K/16]
+  int64_t counts;     // int32 [chunks, E]: per-chunk counts, then scatter bases
+  int64_t offsets;    // int32 [E + 1]: first slot of each expert's pairs, [E] = pairs kept
+  int64_t tiles;      // MoeTile [max_tiles]
+  int64_t sorted;     // int32 [T*top_k]: pair index t*top_k + r at each slot
+  int64_t h_codes, h_scales;  // NVFP4 h by slot [T*top_k, I/2], [T*top_k, I/16]
+  int64_t acc;        // fp32 [T, K]: route sum
+  int64_t total;      // bytes
+};
+MoeLayout moe_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I);
+hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t* ids, const float* topk_w,
+                           int64_t top_k, int64_t E, int64_t I, const void* w_gate_up, const void* w_down, int64_t K,
+                           const float* g1, const float* g2, const float* alpha_gu, const float* alpha_dn, void* out,
+                           int64_t ldo, void* ws, float* h_amax, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -1,0 +1,335 @@
+// NVFP4 MoE expert layer (W4A4 on both GEMMs) on gfx950.
+//
+// Layer flow (FreeToken PR #733, Changes: align, gate_up, activation, down,
+// sum; FreeToken PR #736, Changes: both GEMMs take NVFP4 activations, the
+// gate_up epilogue applies the gated activation and quantizes to NVFP4, the
+// down epilogue applies the routing weight and sums the routes):
+//   align    group the T*top_k (token, route) pairs by expert, stable in pair
+//            order; cut each expert's segment into tiles of up to 256 pairs
+//   gate_up  z = alpha_gu[e] * deq(q(x_t)) . deq(W_gu[e])^T   (2I outputs)
+//            h = SiLU(z[:I]) * z[I:]  in fp32, quantized to NVFP4 with g2
+//   down     y = alpha_dn[e] * deq(h) . deq(W_dn[e])^T       (K outputs)
+//            acc[t] += w[t, r] * y  (fp32 atomics), then out = bf16(acc)
+// Both GEMMs run gemm::mainloop on one 256-pair tile and 256 weight rows per
+// workgroup.  The tile table has a fixed maximum length (every expert can
+// leave one partial tile), so no launch depends on counts read back to the
+// host; workgroups past the table's live entries exit at once.
+#include <algorithm>
+
+#include "gemm_w4a4.hpp"
+#include "kernels.hpp"
+#include "quant_exact.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kChunk = 1024;  // pairs per align workgroup (one per thread)
+
+// The pair's expert, or E for a pair that is skipped (id outside [0, E)).
+__device__ __forceinline__ int expert_of(const int32_t* __restrict__ ids, int64_t p, int32_t E) {
+  const int32_t e = ids[p];
+  return (e >= 0 && e < E) ? e : E;
+}
+
+// counts[c][e] = pairs of chunk c routed to expert e.
+__global__ __launch_bounds__(kChunk) void moe_count_kernel(const int32_t* __restrict__ ids, int64_t P, int32_t E,
+                                                           int32_t* __restrict__ counts) {
+  extern __shared__ int32_t cnt[];
+  for (int e = int(threadIdx.x); e < E; e += kChunk) cnt[e] = 0;
+  __syncthreads();
+  const int64_t p = int64_t(blockIdx.x) * kChunk + threadIdx.x;
+  if (p < P) {
+    const int e = expert_of(ids, p, E);
+    if (e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = int(threadIdx.x); e < E; e += kChunk) counts[int64_t(blockIdx.x) * E + e] = cnt[e];
+}
+
+// Exclusive prefix sum over the 1024 threads of the workgroup (tmp: 16 ints).
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* tmp, int32_t& total) {
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  int32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int32_t before = 0;
+  total = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int32_t t = tmp[w];
+    if (w < wave) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
+
+// One workgroup: per-expert totals, segment starts, the per-chunk bases the
+// scatter adds its ranks to (written over the counts), and the tile table.
+__global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ counts, int32_t chunks, int32_t E,
+                                                        int32_t* __restrict__ offsets, MoeTile* __restrict__ tiles,
+                                                        int32_t max_tiles) {
+  __shared__ int32_t tmp[16];
+  const int e = int(threadIdx.x);
+  int32_t total = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int32_t c = 0; c < chunks; ++c) total += counts[int64_t(c) * E + e];
+  }
+  const int32_t ntile = (total + gemm::BM - 1) / gemm::BM;
+  int32_t pairs = 0, ntiles = 0;
+  const int32_t seg = block_exclusive_scan(total, tmp, pairs);
+  const int32_t tile0 = block_exclusive_scan(ntile, tmp, ntiles);
+  if (e < E) {
+    int32_t base = seg;
+    for (int32_t c = 0; c < chunks; ++c) {
+      const int64_t i = int64_t(c) * E + e;
+      const int32_t v = counts[i];
+      counts[i] = base;
+      base += v;
+    }
+    offsets[e] = seg;
+    for (int32_t j = 0; j < ntile; ++j) {
+      MoeTile t;
+      t.expert = e;
+      t.slot0 = seg + gemm::BM * j;
+      t.rows = min(gemm::BM, total - gemm::BM * j);
+      t.pad = 0;
+      tiles[tile0 + j] = t;
+    }
+  }
+  if (e == 0) offsets[E] = pairs;
+  for (int32_t j = ntiles + e; j < max_tiles; j += 1024) tiles[j] = MoeTile{0, 0, 0, 0};
+}
+
+// sorted[base[c][e] + rank] = p, rank = number of earlier pairs of the chunk
+// with the same expert (so the order within an expert is the pair order).
+__global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int32_t E,
+                                                             const int32_t* __restrict__ bases,
+                                                             int32_t* __restrict__ sorted) {
+  extern __shared__ int32_t wave_count[];  // [16][E]
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  for (int i = int(threadIdx.x); i < 16 * E; i += kChunk) wave_count[i] = 0;
+  __syncthreads();
+  const int64_t p = int64_t(blockIdx.x) * kChunk + threadIdx.x;
+  const int e = p < P ? expert_of(ids, p, E) : E;
+  // lanes of the wave with the same expert value: one ballot per bit
+  uint64_t same = ~0ull;
+  for (int b = 0; (1 << b) <= E; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ball = __ballot(bit);
+    same &= bit ? ball : ~ball;
+  }
+  const uint64_t lower = same & ((1ull << lane) - 1ull);
+  if (e < E && lower == 0) wave_count[wave * E + e] = __popcll(same);
+  __syncthreads();
+  if (e < E) {
+    int32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_count[w * E + e];
+    sorted[bases[int64_t(blockIdx.x) * E + e] + before + __popcll(lower)] = int32_t(p);
+  }
+}
+
+// Zeroes the fp32 route sum (and the h amax, if requested).
+__global__ __launch_bounds__(256) void moe_zero_kernel(float4* __restrict__ acc, int64_t n4,
+                                                       uint32_t* __restrict__ h_amax) {
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += stride) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (h_amax && blockIdx.x == 0 && threadIdx.x == 0) *h_amax = 0u;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// gate_up GEMM of one tile of pairs x 128 gate rows (+ the matching 128 up
+// rows) of its expert, with the SiLU gate and NVFP4 quantization of h.
+// blockIdx.x = 128-row block c of the expert's I gate rows, blockIdx.y = tile.
+__global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
+    const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int32_t K, int32_t top_k,
+    const int32_t* __restrict__ sorted, const MoeTile* __restrict__ tiles, const uint8_t* __restrict__ wt, int32_t I,
+    const float* __restrict__ alpha_gu, const float* __restrict__ g2_p, uint8_t* __restrict__ hc,
+    uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
+  const MoeTile tile = tiles[blockIdx.y];
+  if (tile.rows == 0) return;
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
+  const int32_t c = int32_t(blockIdx.x);
+  // LDS weight tiles 0..7: gate rows 128c..128c+127, 8..15: the up rows I + the same
+  const int32_t gate_tile0 = tile.expert * (2 * I / 16) + 8 * c, up_tile0 = gate_tile0 + I / 16;
+  gemm::Acc acc;
+  gemm::mainloop(
+      acc, lds, xc, xs, [&](int i) { return int64_t(sorted[tile.slot0 + min(i, tile.rows - 1)] / top_k); }, wt,
+      [&](int lt) { return int64_t(lt < 8 ? gate_tile0 + lt : up_tile0 + lt - 8); },
+      // the wave's tiles 0, 1 are gate rows 64wn..64wn+63, tiles 2, 3 the up rows under them
+      [&](int t) { return t < 2 ? 64 * wn + 32 * t : 128 + 64 * wn + 32 * (t - 2); }, K);
+
+  const float alpha = alpha_gu[tile.expert], g2 = *g2_p;
+  float hmax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int32_t m = wm * 64 + 32 * u + (lane & 31);  // pair row of the tile
+    const int64_t slot = int64_t(tile.slot0) + m;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // h of gate rows 8(i/4) + 4h + i%4 of the wave's 32-row tile t
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = silu(alpha * acc.v[t][u][i]) * (alpha * acc.v[t + 2][u][i]);
+      // lane half h gathers the 16-row block h of the tile: it keeps its own
+      // registers of that block and takes the partner half's
+      float x[16];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float own = h ? v[8 + j] : v[j];
+        const float recv = __shfl_xor(h ? v[j] : v[8 + j], 32, 64);
+        const float lo = h ? recv : own, hi = h ? own : recv;
+        x[(j & 4) * 2 + (j & 3)] = lo;
+        x[(j & 4) * 2 + 4 + (j & 3)] = hi;
+      }
+      if (m < tile.rows) {
+        uint32_t c0, c1;
+        const uint32_t s = quantize16_exact(x, g2, c0, c1);
+        const int32_t i0 = 128 * c + 64 * wn + 32 * t + 16 * h;  // first h element of the block
+        *reinterpret_cast<uint2*>(hc + slot * (I / 2) + i0 / 2) = make_uint2(c0, c1);
+        hs[slot * (I / 16) + i0 / 16] = uint8_t(s);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) hmax = __builtin_fmaxf(hmax, __builtin_fabsf(x[i]));
+      }
+    }
+  }
+  if (h_amax) {
+    uint32_t bits = __float_as_uint(hmax);
+    for (int o = 32; o > 0; o >>= 1) bits = max(bits, uint32_t(__shfl_xor(int(bits), o, 64)));
+    if (lane == 0) atomicMax(h_amax, bits);
+  }
+}
+
+// down GEMM of one tile of pairs x 256 outputs of its expert, scaled by
+// alpha_dn[e] * w[pair] and added into the token's fp32 row.
+// blockIdx.x = 256-output block of K, blockIdx.y = tile.
+__global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
+    const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs, int32_t I, const int32_t* __restrict__ sorted,
+    const MoeTile* __restrict__ tiles, const float* __restrict__ topk_w, int32_t top_k,
+    const uint8_t* __restrict__ wt, int32_t K, const float* __restrict__ alpha_dn, float* __restrict__ acc32) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
+  const MoeTile tile = tiles[blockIdx.y];
+  if (tile.rows == 0) return;
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
+  const int32_t wtile0 = tile.expert * (K / 16) + int32_t(blockIdx.x) * 16;
+  gemm::Acc acc;
+  gemm::mainloop<true>(
+      acc, lds, hc, hs, [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); }, wt,
+      [&](int lt) { return int64_t(wtile0 + lt); }, [&](int t) { return 128 * wn + 32 * t; }, I);
+
+  // the tile's tokens and scales, through LDS (free after the main loop)
+  int32_t* s_tok = reinterpret_cast<int32_t*>(lds);
+  float* s_scale = reinterpret_cast<float*>(lds) + gemm::BM;
+  const float alpha = alpha_dn[tile.expert];
+  if (threadIdx.x < gemm::BM) {
+    const int m = int(threadIdx.x);
+    const int32_t p = sorted[tile.slot0 + min(m, tile.rows - 1)];
+    s_tok[m] = p / top_k;
+    s_scale[m] = alpha * topk_w[p];
+  }
+  __syncthreads();
+  const int32_t n = int32_t(blockIdx.x) * 256 + 128 * wn + (lane & 31);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = wm * 64 + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (m >= tile.rows) continue;
+      float* row = acc32 + int64_t(s_tok[m]) * K + n;
+      const float sc = s_scale[m];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) unsafeAtomicAdd(row + 32 * t, sc * acc.v[t][u][i]);
+    }
+}
+
+// out[t][k] = bf16(acc[t][k]), eight outputs per thread.
+__global__ __launch_bounds__(256) void moe_convert_kernel(const float* __restrict__ acc32, int64_t T, int32_t K,
+                                                          uint16_t* __restrict__ out, int64_t ldo) {
+  const int64_t per_row = K / 8;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= T * per_row) return;
+  const int64_t t = i / per_row, k = (i - t * per_row) * 8;
+  const float4 a = *reinterpret_cast<const float4*>(acc32 + t * K + k);
+  const float4 b = *reinterpret_cast<const float4*>(acc32 + t * K + k + 4);
+  uint16_t* dst = out + t * ldo + k;
+  const uint4 v = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+  *reinterpret_cast<uint4*>(dst) = v;
+}
+
+}  // namespace
+
+MoeLayout moe_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I) {
+  MoeLayout L{};
+  const int64_t P = T * top_k;
+  L.chunks = (P + kChunk - 1) / kChunk;
+  L.max_tiles = P / gemm::BM + E;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  L.x_codes = take(T * K / 2);
+  L.x_scales = take(T * K / 16);
+  L.counts = take(4 * L.chunks * E);
+  L.offsets = take(4 * (E + 1));
+  L.tiles = take(int64_t(sizeof(MoeTile)) * L.max_tiles);
+  L.sorted = take(4 * P);
+  L.h_codes = take(P * I / 2);
+  L.h_scales = take(P * I / 16);
+  L.acc = take(4 * T * K);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t* ids, const float* topk_w,
+                           int64_t top_k, int64_t E, int64_t I, const void* w_gate_up, const void* w_down, int64_t K,
+                           const float* g1, const float* g2, const float* alpha_gu, const float* alpha_dn, void* out,
+                           int64_t ldo, void* ws, float* h_amax, hipStream_t stream) {
+  const MoeLayout L = moe_layout(T, top_k, E, K, I);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* xc = base + L.x_codes;
+  uint8_t* xs = base + L.x_scales;
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  MoeTile* tiles = reinterpret_cast<MoeTile*>(base + L.tiles);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  uint8_t* hc = base + L.h_codes;
+  uint8_t* hs = base + L.h_scales;
+  float* acc32 = reinterpret_cast<float*>(base + L.acc);
+  const int64_t P = T * top_k;
+  hipError_t err = launch_quantize(x, T, K, ldx, g1, xc, xs, stream);
+  if (err != hipSuccess) return err;
+  const uint32_t chunks = uint32_t(L.chunks);
+  hipLaunchKernelGGL(moe_count_kernel, dim3(chunks), dim3(kChunk), size_t(4 * E), stream, ids, P, int32_t(E), counts);
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, int32_t(L.chunks), int32_t(E), offsets,
+                     tiles, int32_t(L.max_tiles));
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(chunks), dim3(kChunk), size_t(4 * 16 * E), stream, ids, P, int32_t(E),
+                     counts, sorted);
+  const int64_t n4 = T * K / 4;
+  const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(moe_zero_kernel, dim3(uint32_t(std::max<int64_t>(zblocks, 1))), dim3(256), 0, stream,
+                     reinterpret_cast<float4*>(acc32), n4, reinterpret_cast<uint32_t*>(h_amax));
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(uint32_t(I / 128), uint32_t(L.max_tiles)), dim3(gemm::kThreads), 0, stream,
+                     xc, xs, int32_t(K), int32_t(top_k), sorted, tiles, static_cast<const uint8_t*>(w_gate_up),
+                     int32_t(I), alpha_gu, g2, hc, hs, reinterpret_cast<uint32_t*>(h_amax));
+  hipLaunchKernelGGL(moe_down_kernel, dim3(uint32_t(K / 256), uint32_t(L.max_tiles)), dim3(gemm::kThreads), 0, stream,
+                     hc, hs, int32_t(I), sorted, tiles, topk_w, int32_t(top_k), static_cast<const uint8_t*>(w_down),
+                     int32_t(K), alpha_dn, acc32);
+  const int64_t items = T * (K / 8);
+  hipLaunchKernelGGL(moe_convert_kernel, dim3(uint32_t((items + 255) / 256)), dim3(256), 0, stream, acc32, T,
+                     int32_t(K), static_cast<uint16_t*>(out), ldo);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -34,6 +34,12 @@ class Weight(C.Structure):
     _fields_ = [("data", P), ("N", I64), ("K", I64), ("layout", C.c_int32), ("reserved", C.c_int32)]
 
 
+class MoeLayout(C.Structure):
+    """Mirror of struct nvfp4_moe_layout (byte offsets into the MoE workspace)."""
+    _fields_ = [(n, I64) for n in ("x_codes", "x_scales", "counts", "offsets", "tiles", "sorted", "h_codes",
+                                   "h_scales", "acc", "max_tiles", "total_bytes")]
+
+
 _SIGS = {
     "nvfp4_status_str": (C.c_char_p, [I32]),
     "nvfp4_version": (I32, []),
@@ -51,8 +57,9 @@ _SIGS = {
     "nvfp4_linear_workspace_bytes": (SZ, [I64, I64, I64]),
     "nvfp4_linear": (I32, [P, I64, I64, C.POINTER(Weight), P, P, P, P, I64, P, SZ, C.POINTER(I32), P]),
     "nvfp4_moe_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
-    "nvfp4_moe_w4a4": (I32, [P, I64, I64, P, P, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P]),
-    "nvfp4_moe_act2_amax": (I32, [P, I64, I64, P, I64, I64, I64, P, P, P, P, P, SZ, P]),
+    "nvfp4_moe_workspace_layout": (I32, [I64, I64, I64, I64, I64, C.POINTER(MoeLayout)]),
+    "nvfp4_moe_w4a4": (I32, [P, I64, I64, P, P, I64, I64, I64, C.POINTER(Weight), C.POINTER(Weight), P, P, P, P,
+                             P, I64, P, SZ, P, P]),
 }
 
 

@@ -152,3 +152,56 @@ def test_linear_dispatch_validation(nv):
     r.value = -1
     assert f(A16, 0, 256, C.byref(w), None, A16, None, A16, 64, None, 0, C.byref(r), None) == OK
     assert r.value == 0
+
+
+def test_moe_workspace_layout(nv):
+    T, top_k, E, K, I = 8192, 8, 128, 2048, 768
+    lay = L.MoeLayout()
+    assert nv.nvfp4_moe_workspace_layout(T, top_k, E, K, I, C.byref(lay)) == OK
+    P = T * top_k
+    parts = [("x_codes", T * K // 2), ("x_scales", T * K // 16), ("counts", 4 * 64 * E), ("offsets", 4 * (E + 1)),
+             ("tiles", 16 * lay.max_tiles), ("sorted", 4 * P), ("h_codes", P * I // 2), ("h_scales", P * I // 16),
+             ("acc", 4 * T * K)]
+    assert lay.max_tiles == P // 256 + E
+    end = 0
+    for name, size in parts:
+        off = getattr(lay, name)
+        assert off % 256 == 0 and off >= end, name
+        end = off + size
+    assert lay.total_bytes >= end
+    assert nv.nvfp4_moe_workspace_bytes(T, top_k, E, K, I) == lay.total_bytes
+    # invalid shapes report 0 bytes / an error
+    assert nv.nvfp4_moe_workspace_bytes(T, top_k, E, K, 100) == 0
+    assert nv.nvfp4_moe_workspace_layout(T, top_k, E, K, 128, C.byref(lay)) == UNSUP   # I % 256
+    assert nv.nvfp4_moe_workspace_layout(T, 0, E, K, I, C.byref(lay)) == ARG          # top_k
+    assert nv.nvfp4_moe_workspace_layout(T, top_k, 1025, K, I, C.byref(lay)) == ARG   # E > 1024
+    assert nv.nvfp4_moe_workspace_layout(T, top_k, E, K, I, None) == ARG
+
+
+def test_moe_validation(nv):
+    T, top_k, E, K, I = 64, 2, 4, 512, 256
+    gu, dn = _w(N=E * 2 * I, K=K), _w(N=E * K, K=I)
+    need = nv.nvfp4_moe_workspace_bytes(T, top_k, E, K, I)
+    WS0 = 0x100000  # 256-byte aligned fake address
+
+    def call(x=A16, T=T, ldx=K, ids=A16, w=A16, top_k=top_k, E=E, I=I, gu=gu, dn=dn, g1=A16, g2=A16, agu=A16,
+             adn=A16, out=A16, ldo=K, ws=WS0, ws_bytes=need, h_amax=None):
+        return nv.nvfp4_moe_w4a4(x, T, ldx, ids, w, top_k, E, I, C.byref(gu) if gu is not None else None,
+                                 C.byref(dn) if dn is not None else None, g1, g2, agu, adn, out, ldo, ws, ws_bytes,
+                                 h_amax, None)
+
+    assert call(gu=None) == ARG
+    assert call(g2=None) == ARG
+    assert call(ids=None) == ARG
+    assert call(top_k=0) == ARG
+    assert call(E=2000) == ARG
+    assert call(dn=_w(N=E * K, K=512)) == SHAPE          # down K != I
+    assert call(gu=_w(N=E * 2 * I - 16, K=K)) == SHAPE   # gate_up N != E*2I
+    assert call(I=128, gu=_w(N=E * 256, K=K), dn=_w(N=E * K, K=128)) == UNSUP  # I % 256
+    assert call(ldx=K - 8) == SHAPE
+    assert call(ldo=K + 4) == ALIGN
+    assert call(out=A16 + 2) == ALIGN
+    assert call(ws=WS0 + 16) == ALIGN
+    assert call(ws_bytes=need - 1) == WS
+    assert call(ws=None) == WS
+    assert call(x=None, T=0, ids=None, w=None, out=None, ws=None, ws_bytes=0) == OK   # empty batch

@@ -1,0 +1,290 @@
+"""GPU parity of the NVFP4 MoE expert layer against the oracle.
+
+Stage-wise check (the GPU's h is fp32, the oracle's fp64, so h's NVFP4 codes
+may legitimately differ where h sits on a rounding boundary):
+  align    bit-exact: pairs grouped by expert in pair order (a stable sort of
+           the expert ids), expert offsets, tile table
+  h        codes and scales per pair equal the oracle's, except benign flips:
+           the oracle's exact value within a small relative margin of the
+           boundary it straddles (scale flips may change the whole block)
+  out      rel-L2 <= 1e-3 over all checked tokens, and the per-element bar
+           (2 bf16 ulp with the Sabs floor) on every token whose h has no flip
+"""
+import numpy as np
+import pytest
+
+from nvfp4_block_scaled_act_amd import synth
+
+from helpers import bf16_dev, bf16_host, f32_dev, gemm_check, to_dev, u8_host
+
+pytestmark = pytest.mark.gpu
+
+# A flip of an h code or scale is benign when the oracle's exact |h|*g2/S (or
+# amax*g2/6) lies within this relative distance of the boundary it straddles.
+BENIGN_MARGIN = 2.0 ** -14
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from nvfp4_block_scaled_act_amd import ops as O
+
+    return O
+
+
+class Banks:
+    """Expert banks quantized per expert on the GPU (one global per expert
+    tensor) and prepared as one stacked weight each; the oracle quantizes the
+    same bf16 banks itself, and the two are compared on `check_experts`.
+    Without g2, g2 is calibrated by the oracle on `cal` = (x, ids, w):
+    g2 = fp32(2688 / max |h|) over the calibration batch's routed pairs."""
+
+    def __init__(self, ops, orc, gate_up, down, g1, g2=None, cal=None, check_experts=None):
+        import torch
+
+        E, twoI, K = gate_up.shape
+        I = twoI // 2
+        self.E, self.K, self.I = E, K, I
+        g1 = np.float32(g1)
+        og_gu = [orc.global_scale(gate_up[e]) for e in range(E)]
+        og_dn = [orc.global_scale(down[e]) for e in range(E)]
+        self.o_gu = (np.empty((E, twoI, K // 2), np.uint8), np.empty((E, twoI, K // 16), np.uint8))
+        self.o_dn = (np.empty((E, K, I // 2), np.uint8), np.empty((E, K, I // 16), np.uint8))
+        for e in range(E):
+            self.o_gu[0][e], self.o_gu[1][e] = orc.quantize(gate_up[e], og_gu[e])
+            self.o_dn[0][e], self.o_dn[1][e] = orc.quantize(down[e], og_dn[e])
+        self.o_alpha_gu = np.array([orc.alpha(g, g1) for g in og_gu], np.float32)
+        if g2 is None:
+            a_dn1 = np.array([orc.alpha(g, np.float32(1.0)) for g in og_dn], np.float32)
+            xc, ic, wc = cal
+            res = orc.moe_w4a4(xc, ic, wc, self.o_gu[0], self.o_gu[1], self.o_dn[0], self.o_dn[1], g1,
+                               np.float32(1.0), self.o_alpha_gu, a_dn1)
+            g2 = orc.global_scale_from_amax(res["h_amax"])
+        g2 = np.float32(g2)
+        self.g1, self.g2 = g1, g2
+        self.o_alpha_dn = np.array([orc.alpha(g, g2) for g in og_dn], np.float32)
+
+        g1d, g2d = f32_dev(g1), f32_dev(g2)
+        self.alpha_gu = torch.empty(E, dtype=torch.float32, device="cuda")
+        self.alpha_dn = torch.empty(E, dtype=torch.float32, device="cuda")
+        check = range(E) if check_experts is None else check_experts
+        prepared = []
+        for bank, g_in_dev, alphas, o_codes in ((gate_up, g1d, self.alpha_gu, self.o_gu),
+                                                (down, g2d, self.alpha_dn, self.o_dn)):
+            rows = bank.shape[1]
+            dev = bf16_dev(bank.reshape(E * rows, bank.shape[2]))
+            codes = torch.empty((E * rows, bank.shape[2] // 2), dtype=torch.uint8, device="cuda")
+            scales = torch.empty((E * rows, bank.shape[2] // 16), dtype=torch.uint8, device="cuda")
+            for e in range(E):
+                sl = slice(e * rows, (e + 1) * rows)
+                g = ops.global_scale(dev[sl])
+                ops.quantize_act(dev[sl], g, codes=codes[sl], scales=scales[sl])
+                ops.alpha(g, g_in_dev, out=alphas[e:e + 1])
+            hc, hs = u8_host(codes), u8_host(scales)
+            for e in check:
+                sl = slice(e * rows, (e + 1) * rows)
+                assert (hc[sl] == o_codes[0][e]).all(), f"weight codes of expert {e}"
+                assert (hs[sl] == o_codes[1][e]).all(), f"weight scales of expert {e}"
+            del dev
+            prepared.append(ops.prepare_weight(codes, scales))
+        assert (self.alpha_gu.cpu().numpy() == self.o_alpha_gu).all()
+        assert (self.alpha_dn.cpu().numpy() == self.o_alpha_dn).all()
+        self.w_gu, self.w_dn = prepared
+
+    def run(self, ops, x, ids, w, h_amax=None, workspace=None):
+        import torch
+
+        T = x.shape[0]
+        top_k = ids.shape[1]
+        if workspace is None:
+            workspace = torch.empty(max(1, ops.moe_workspace_bytes(T, top_k, self.E, self.K, self.I)),
+                                    dtype=torch.uint8, device="cuda")
+        out = ops.moe_w4a4(bf16_dev(x), to_dev(ids), to_dev(w), self.w_gu, self.w_dn, self.E, f32_dev(self.g1),
+                           f32_dev(self.g2), self.alpha_gu, self.alpha_dn, workspace=workspace, h_amax=h_amax)
+        torch.cuda.synchronize()
+        return out, workspace
+
+    def oracle(self, orc, x, ids, w, tokens=None):
+        return orc.moe_w4a4(x, ids, w, self.o_gu[0], self.o_gu[1], self.o_dn[0], self.o_dn[1], self.g1, self.g2,
+                            self.o_alpha_gu, self.o_alpha_dn, tokens=tokens)
+
+
+def expected_align(ids, E):
+    flat = ids.reshape(-1).astype(np.int64)
+    valid = (flat >= 0) & (flat < E)
+    idx = np.nonzero(valid)[0]
+    order = idx[np.argsort(flat[idx], kind="stable")]
+    counts = np.bincount(flat[idx], minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    tiles = []
+    for e in range(E):
+        for j in range(0, counts[e], 256):
+            tiles.append((e, offsets[e] + j, min(256, counts[e] - j), 0))
+    return order, offsets, tiles
+
+
+def check_align(views, ids, E):
+    order, offsets, tiles = expected_align(ids, E)
+    n = len(order)
+    got_sorted = views["sorted"].cpu().numpy()
+    assert (got_sorted[:n] == order).all(), "sorted pairs differ from a stable sort by expert"
+    assert (views["offsets"].cpu().numpy() == offsets).all(), "expert offsets"
+    tt = views["tiles"].cpu().numpy()
+    assert len(tiles) <= tt.shape[0]
+    assert (tt[:len(tiles)] == np.array(tiles, np.int64).reshape(-1, 4)).all(), "tile table"
+    assert (tt[len(tiles):, 2] == 0).all(), "entries past the last tile must be empty"
+    inv = np.full(ids.size, -1, np.int64)
+    inv[order] = np.arange(n)
+    return inv
+
+
+def check_h(views, inv, res, tokens, top_k, I):
+    """h codes/scales of the tokens' pairs; returns the set of tokens with a
+    (benign) flip.  Any flip outside the margin fails."""
+    hc = views["h_codes"].cpu().numpy()
+    hs = views["h_scales"].cpu().numpy()
+    flipped = set()
+    n_code_flips = n_scale_flips = 0
+    for tt, t in enumerate(tokens):
+        for r in range(top_k):
+            p = t * top_k + r
+            slot = inv[p]
+            if slot < 0:
+                continue
+            q = tt * top_k + r
+            g_s, o_s = hs[slot], res["h_scales"][q]
+            scale_bad = g_s != o_s
+            if scale_bad.any():
+                m = res["h_scale_margin"][q][scale_bad]
+                assert (m <= BENIGN_MARGIN).all(), f"token {t} route {r}: scale mismatch with margin {m.min()}"
+                n_scale_flips += int(scale_bad.sum())
+                flipped.add(t)
+            g_c = np.stack([hc[slot] & 15, hc[slot] >> 4], 1).reshape(-1)
+            o_c = np.stack([res["h_codes"][q] & 15, res["h_codes"][q] >> 4], 1).reshape(-1)
+            code_bad = (g_c != o_c) & ~np.repeat(scale_bad, 16)
+            if code_bad.any():
+                m = res["h_code_margin"][q][code_bad]
+                assert (m <= BENIGN_MARGIN).all(), (
+                    f"token {t} route {r}: h code mismatch at {np.nonzero(code_bad)[0][:8]} margin {m.max()}")
+                n_code_flips += int(code_bad.sum())
+                flipped.add(t)
+    return flipped, n_code_flips, n_scale_flips
+
+
+def check_out(out_bits, res, tokens, flipped):
+    keep = np.array([i for i, t in enumerate(tokens) if t not in flipped], np.int64)
+    g = out_bits[tokens]
+    ref = res["out"]
+    # rel-L2 over every checked token
+    stats = gemm_check(g, ref, res["sabs"], max_ulp=float("inf"))
+    if len(keep):
+        stats = gemm_check(g[keep], ref[keep], res["sabs"][keep])
+    return stats
+
+
+def _small_case(seed, T, E, top_k, K, I, bias=None, calib_rows=64):
+    x = synth.normal_bf16(seed, T, K)
+    logits = synth.normal_f32(seed + 1, T, E)
+    cal = synth.normal_bf16(seed + 2, calib_rows, K)
+    cal_logits = synth.normal_f32(seed + 3, calib_rows, E)
+    if bias is not None:
+        logits = logits + bias
+        cal_logits = cal_logits + bias
+    ids, w = synth.route_top_k(logits, top_k)
+    cids, cw = synth.route_top_k(cal_logits, top_k)
+    gate_up = synth.normal_bf16(seed + 4, E * 2 * I, K).reshape(E, 2 * I, K)
+    down = synth.normal_bf16(seed + 5, E * K, I).reshape(E, K, I)
+    return x, ids, w, cal, cids, cw, gate_up, down
+
+
+def test_moe_small_multi_tile(ops, orc):
+    # 8 experts, top-2, K=512, I=256, T=700: expert 0 draws most tokens (3
+    # tiles, the last ragged), expert 7 none; every other expert one ragged tile
+    E, top_k, K, I, T = 8, 2, 512, 256, 700
+    bias = np.zeros(E, np.float32)
+    bias[0], bias[7] = 2.5, -30.0
+    x, ids, w, cal, cids, cw, gate_up, down = _small_case(101, T, E, top_k, K, I, bias)
+    banks = Banks(ops, orc, gate_up, down, orc.global_scale(cal), cal=(cal, cids, cw))
+    import torch
+
+    h_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out, ws = banks.run(ops, x, ids, w, h_amax=h_amax)
+    views = ops.moe_workspace_views(ws, T, top_k, E, K, I)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    assert counts[0] > 512 and counts[7] == 0
+    inv = check_align(views, ids, E)
+    tokens = np.arange(T)
+    res = banks.oracle(orc, x, ids, w)
+    flipped, ncf, nsf = check_h(views, inv, res, tokens, top_k, I)
+    stats = check_out(bf16_host(out), res, tokens, flipped)
+    assert abs(h_amax.item() - res["h_amax"]) <= 1e-5 * res["h_amax"]
+    print(f"flipped tokens {len(flipped)}/{T}, code flips {ncf}, scale flips {nsf}, {stats}")
+
+
+def test_moe_skipped_ids_and_repeat(ops, orc):
+    # ids outside [0, E) add nothing; a second call on the same workspace gives
+    # the same h and outputs within the fp32 atomics' reordering
+    E, top_k, K, I, T = 4, 3, 256, 256, 130
+    x, ids, w, cal, cids, cw, gate_up, down = _small_case(202, T, E, top_k, K, I)
+    ids = ids.copy()
+    ids[::7, 0] = -1
+    ids[3::11, 2] = E
+    banks = Banks(ops, orc, gate_up, down, orc.global_scale(cal), cal=(cal, cids, cw))
+    out1, ws = banks.run(ops, x, ids, w)
+    views = ops.moe_workspace_views(ws, T, top_k, E, K, I)
+    inv = check_align(views, ids, E)
+    h1 = views["h_codes"].cpu().numpy().copy()
+    out2, _ = banks.run(ops, x, ids, w, workspace=ws)
+    n = int(views["offsets"].cpu().numpy()[E])
+    assert (views["h_codes"].cpu().numpy()[:n] == h1[:n]).all()
+    # oracle: a skipped pair = expert 0 with routing weight 0
+    skip = (ids < 0) | (ids >= E)
+    oid = np.where(skip, 0, ids).astype(np.int32)
+    ow = np.where(skip, 0, w).astype(np.float32)
+    res = banks.oracle(orc, x, oid, ow)
+    flipped, _, _ = check_h(views, inv, res, np.arange(T), top_k, I)
+    for out in (out1, out2):
+        check_out(bf16_host(out), res, np.arange(T), flipped)
+
+
+def test_moe_empty(ops, orc):
+    import torch
+
+    E, top_k, K, I = 2, 2, 256, 256
+    gate_up = synth.normal_bf16(5, E * 2 * I, K).reshape(E, 2 * I, K)
+    down = synth.normal_bf16(6, E * K, I).reshape(E, K, I)
+    banks = Banks(ops, orc, gate_up, down, 1.0, 1.0)
+    x = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, top_k), dtype=torch.float32, device="cuda")
+    out = ops.moe_w4a4(x, ids, w, banks.w_gu, banks.w_dn, E, f32_dev(1.0), f32_dev(1.0), banks.alpha_gu,
+                       banks.alpha_dn)
+    assert out.shape == (0, K)
+
+
+def test_moe_full_size_sampled(ops, orc):
+    # the MoE workload (E=128, top-8, K=2048, I=768, T=8192): align checked on
+    # all 65536 pairs, h and outputs on sampled tokens; g2 calibrated by the
+    # oracle on the first 64 rows of the calibration batch
+    import torch
+
+    m = synth.MOE
+    d = synth.moe_inputs()
+    E, top_k, K, I, T = m["E"], m["top_k"], m["K"], m["I"], m["T"]
+    cal_n = 64
+    sample_e = sorted(set(d["ids"][[0, 1, T // 2, T - 1]].reshape(-1).tolist()) | {0, E - 1})
+    banks = Banks(ops, orc, d["gate_up"], d["down"], orc.global_scale(d["cal"]),
+                  cal=(d["cal"][:cal_n], d["cal_ids"][:cal_n], d["cal_w"][:cal_n]), check_experts=sample_e)
+    h_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out, ws = banks.run(ops, d["x"], d["ids"], d["w"], h_amax=h_amax)
+    views = ops.moe_workspace_views(ws, T, top_k, E, K, I)
+    inv = check_align(views, d["ids"], E)
+    rng = np.random.Generator(np.random.PCG64(7))
+    tokens = np.unique(np.concatenate([[0, 1, T // 2, T - 1], rng.choice(T, 12, replace=False)]))
+    res = banks.oracle(orc, d["x"], d["ids"], d["w"], tokens=tokens)
+    flipped, ncf, nsf = check_h(views, inv, res, tokens, top_k, I)
+    stats = check_out(bf16_host(out), res, tokens, flipped)
+    assert h_amax.item() >= res["h_amax"] * (1 - 1e-5)
+    print(f"flipped tokens {len(flipped)}/{len(tokens)}, code flips {ncf}, scale flips {nsf}, {stats}")
