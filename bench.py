@@ -200,6 +200,77 @@ def bench_w4a4(ops, torch, reps=10):
                 prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16)
 
 
+def moe_flops(T, top_k, K, I):
+    """FLOPs of the MoE layer as the pages count them: 2*T*top_k*3*K*I
+    (gate_up 2I x K plus down K x I per routed pair; FreeToken PR #736, Results)."""
+    return 2.0 * T * top_k * 3 * K * I
+
+
+def bench_moe(ops, torch, reps=10):
+    """The NVFP4 MoE layer (E=128, top-8, K=2048, I=768, T=8192): whole-layer
+    time of nvfp4_moe_w4a4 (quantize x, align, gate_up, down, route sum) with
+    HIP events.  Banks are quantized per expert on the GPU; g1 comes from the
+    512-row calibration batch's amax, g2 from the h amax of the layer run on
+    that batch (the layer's own calibration output)."""
+    from nvfp4_block_scaled_act_amd import synth
+
+    m = synth.MOE
+    E, top_k, K, I, T = m["E"], m["top_k"], m["K"], m["I"], m["T"]
+    d = synth.moe_inputs()
+    t_setup = time.perf_counter()
+    prepared, globals_ = [], []
+    for bank in (d["gate_up"], d["down"]):
+        rows, cols = bank.shape[1], bank.shape[2]
+        dev = dev_bf16(torch, bank.reshape(E * rows, cols))
+        codes = torch.empty((E * rows, cols // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((E * rows, cols // 16), dtype=torch.uint8, device="cuda")
+        gs = torch.empty(E, dtype=torch.float32, device="cuda")
+        for e in range(E):
+            sl = slice(e * rows, (e + 1) * rows)
+            ops.global_scale(dev[sl], out=gs[e:e + 1])
+            ops.quantize_act(dev[sl], gs[e:e + 1], codes=codes[sl], scales=scales[sl])
+        del dev
+        prepared.append(ops.prepare_weight(codes, scales))
+        del codes, scales
+        globals_.append(gs)
+    w_gu, w_dn = prepared
+    g1 = ops.global_scale(dev_bf16(torch, d["cal"]))
+    a_gu = torch.empty(E, dtype=torch.float32, device="cuda")
+    a_dn = torch.empty(E, dtype=torch.float32, device="cuda")
+    for e in range(E):
+        ops.alpha(globals_[0][e:e + 1], g1, out=a_gu[e:e + 1])
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    for e in range(E):
+        ops.alpha(globals_[1][e:e + 1], one, out=a_dn[e:e + 1])
+    h_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ops.moe_w4a4(dev_bf16(torch, d["cal"]), torch.from_numpy(d["cal_ids"]).cuda(),
+                 torch.from_numpy(d["cal_w"]).cuda(), w_gu, w_dn, E, g1, one, a_gu, a_dn, h_amax=h_amax)
+    g2 = (torch.full((1,), 2688.0, dtype=torch.float32, device="cuda") / h_amax).contiguous()
+    for e in range(E):
+        ops.alpha(globals_[1][e:e + 1], g2, out=a_dn[e:e + 1])
+    x = dev_bf16(torch, d["x"])
+    ids = torch.from_numpy(d["ids"]).cuda()
+    w = torch.from_numpy(d["w"]).cuda()
+    ws = torch.empty(ops.moe_workspace_bytes(T, top_k, E, K, I), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[moe] setup {time.perf_counter() - t_setup:.1f} s, g2 = {g2.item():.6g}")
+    for _ in range(2):
+        ops.moe_w4a4(x, ids, w, w_gu, w_dn, E, g1, g2, a_gu, a_dn, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ops.moe_w4a4(x, ids, w, w_gu, w_dn, E, g1, g2, a_gu, a_dn, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    layer_us = e0.elapsed_time(e1) * 1e3 / reps
+    flops = moe_flops(T, top_k, K, I)
+    log(f"[moe] T={T} E={E} top_k={top_k} K={K} I={I}: layer {layer_us:.1f} us = "
+        f"{flops / layer_us / 1e6:.1f} TFLOP/s")
+    return dict(T=T, E=E, top_k=top_k, K=K, I=I, layer_us=layer_us, tflops=flops / layer_us / 1e6)
+
+
 def cpu_baseline(target_s=15.0):
     """The oracle (as it stands) on a bounded sample of the headline workload:
     the W4A16 call N=8704, K=5120, M=16 restricted to its first 512 weight
@@ -233,7 +304,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the W4A16 calls directly (counter runs)")
-    ap.add_argument("--only", choices=["all", "headline", "fused", "w4a4", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "headline", "fused", "w4a4", "moe", "copy"], default="all",
                     help="run one part (for profiler runs); 'copy' times a plain 256 MiB device copy, the "
                          "reference for the HBM byte counters")
     args = ap.parse_args()
@@ -259,6 +330,10 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.steps
         print(json.dumps({"copy_bytes": 256 << 20, "us": round(us, 2), "read_write_gb_s": round(2 * (256 << 20) / us / 1e3, 1)}))
+        return
+    if args.only == "moe":
+        r5 = bench_moe(ops, torch, reps=args.steps)
+        print(json.dumps({"moe": {k: round(v, 3) if isinstance(v, float) else v for k, v in r5.items()}}))
         return
     if args.only in ("fused", "w4a4"):
         if args.only == "fused":
@@ -321,11 +396,20 @@ def main():
             "quantize_us": round(r4["quant_us"], 2), "quantize_gb_s": round(r4["quant_gbs"], 1),
             "roofline": {"bound": "mfma", "achieved": round(r4["tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(r4["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
-                         "traffic": load_traffic("w4a4_prefill_m8192", kernel_source_hash(["w4a4.hip", "device.hpp"]))},
+                         "traffic": load_traffic("w4a4_prefill_m8192",
+                                                 kernel_source_hash(["w4a4.hip", "gemm_w4a4.hpp", "device.hpp"]))},
         }
         res["prepare_weight"] = {"workload": "re-tile N=8704 K=5120 (one time, not in value)",
                                  "us": round(r4["prepare_us"], 2),
                                  "gb_s": round(r4["prepare_bytes"] / r4["prepare_us"] / 1e3, 1)}
+        r5 = bench_moe(ops, torch)
+        res["moe_layer"] = {
+            "workload": "NVFP4 MoE W4A4, E=128, top-8, K=2048, I=768, T=8192 (whole layer: quantize, align, "
+                        "gate_up + SiLU gate + NVFP4 quantize, down + routing weight + top-8 sum)",
+            "tflops": round(r5["tflops"], 2), "unit": "TFLOP/s", "layer_us": round(r5["layer_us"], 2),
+            "flops": moe_flops(r5["T"], r5["top_k"], r5["K"], r5["I"]),
+            "frac_of_fp16_mfma_peak": round(r5["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+        }
     if not args.no_cpu_baseline and args.only == "all":
         res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)
