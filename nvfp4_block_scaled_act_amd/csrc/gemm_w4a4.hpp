@@ -104,11 +104,12 @@ __device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* _
 
 // acc += W tile x A tile over one step (four 16-k MFMA blocks); after block
 // kk, part kk of the next step's staged operands is dequantized into the other
-// LDS buffer (when `next` is set), so the VALU work runs under the MFMAs.
+// LDS buffer, so the VALU work runs under the MFMAs.  (After the last step the
+// staged set is a re-read of it and lands in a buffer nobody reads.)
 // wave_row0(t) = first LDS weight row of the wave's 32-row tile t.
 template <bool kSwap, typename WaveRow0>
 __device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ wbuf, const _Float16* __restrict__ abuf,
-                                         WaveRow0 wave_row0, int wm, int lane, const Stage& next, bool has_next,
+                                         WaveRow0 wave_row0, int wm, int lane, const Stage& next,
                                          _Float16* __restrict__ wnext, _Float16* __restrict__ anext) {
   const int r = lane & 31, h = lane >> 5;
   // operands of block kk + 1 are read from LDS while the MFMAs of block kk run
@@ -132,7 +133,7 @@ __device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ 
       for (int u = 0; u < 2; ++u)
         acc.v[t][u] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_f16(B[cur][u], A[cur][t], acc.v[t][u], 0, 0, 0)
                             : __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][t], B[cur][u], acc.v[t][u], 0, 0, 0);
-    if (has_next) store_part(next, kk, wnext, anext);
+    store_part(next, kk, wnext, anext);
   }
 }
 
@@ -161,19 +162,31 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
 
   // Step s+1's operands are staged in registers during step s-1 and
   // dequantized into LDS during step s: the loads have a whole step to land.
-  Stage st1 = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, 0);
+  // The two staging sets alternate by name (the loop runs two steps per
+  // iteration), so no staged register is copied while its load is in flight,
+  // and every step issues the same loads (past the last step they re-read it,
+  // unused): the compiler's wait counts then stay exact around the loop rather
+  // than draining the memory pipeline once per step.
+  Stage sa = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, 0);
 #pragma unroll
-  for (int part = 0; part < 4; ++part) store_part(st1, part, lds, abase);
-  if (steps > 1) st1 = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, 1);
+  for (int part = 0; part < 4; ++part) store_part(sa, part, lds, abase);
+  sa = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, min(1, steps - 1));
   __syncthreads();
-  for (int32_t s = 0; s < steps; ++s) {
-    Stage st2;
-    if (s + 2 < steps) st2 = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, s + 2);
-    const int cur = s & 1;
-    mma_step<kSwap>(acc, lds + cur * (BN * PITCH), abase + cur * (BM * PITCH), wave_row0, wm, lane, st1, s + 1 < steps,
-             lds + (cur ^ 1) * (BN * PITCH), abase + (cur ^ 1) * (BM * PITCH));
+  _Float16* const w0 = lds;
+  _Float16* const w1 = lds + BN * PITCH;
+  _Float16* const a0 = abase;
+  _Float16* const a1 = abase + BM * PITCH;
+  for (int32_t s = 0;; s += 2) {
+    // step s from buffer 0; step s+1 (in sa) goes to buffer 1
+    const Stage sb = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, min(s + 2, steps - 1));
+    mma_step<kSwap>(acc, w0, a0, wave_row0, wm, lane, sa, w1, a1);
     __syncthreads();
-    st1 = st2;
+    if (s + 1 >= steps) break;
+    // step s+1 from buffer 1; step s+2 (in sb) goes to buffer 0
+    sa = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, min(s + 3, steps - 1));
+    mma_step<kSwap>(acc, w1, a1, wave_row0, wm, lane, sb, w0, a0);
+    __syncthreads();
+    if (s + 2 >= steps) break;
   }
 }
 

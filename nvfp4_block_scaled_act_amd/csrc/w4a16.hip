@@ -17,16 +17,20 @@
 //  * dequant: fp4 pair -> f32 pair (hardware convert, exact), times the E4M3
 //    scale, packed to bf16 -- exact, since every e2m1 * E4M3 product fits bf16.
 //
-// The weight is read once from HBM, every wave keeps the next units' loads in
-// flight while it dequantizes the current one, and the kernel stays within 64
-// (split) or 80 (shared) VGPRs so a CU holds enough waves to hide HBM latency.
-// Every 16-row tile needs all M x K activations (M/4.5 times the tile's weight
-// bytes), and there are two schedules for them, both one launch with a fixed
-// fp32 sum order (deterministic) and no workspace:
+// The weight is read once from HBM.  Every 16-row tile needs all M x K
+// activations (M/4.5 times the tile's weight bytes), and there are two
+// schedules for them, both one launch with a fixed fp32 sum order
+// (deterministic) and no workspace:
 //  * split -- for weights with few row tiles: a workgroup owns one tile and its
-//    `ksplit` waves split K into contiguous runs of steps, each reading its own
-//    activations from L2; the partial tiles are added through LDS in wave
-//    order.  This spreads a small weight over enough waves to fill the GPU.
+//    `ksplit` waves split K, each reading its own activations through L1/L2;
+//    the partial tiles are added through LDS in wave order.  This spreads a
+//    small weight over enough waves to fill the GPU.  The fixed-step form
+//    (at most 8 steps per wave) is fully unrolled so that the next step's
+//    loads stay in flight under the current step's waits; its interleaved
+//    variant gives wave w the steps w, w + waves, ... so the waves on a CU
+//    read the same activation steps at a time.  With more than 4 token rows
+//    the activation loads are issued in a cache-line-friendly lane order and
+//    moved to their MFMA lanes by a cross-lane permute.
 //  * shared -- for weights with many row tiles: a workgroup owns 8 tiles (one
 //    per wave) over all of K and streams the activations through LDS in
 //    double-buffered chunks of `kc` steps, so each chunk is read from L2 once
@@ -58,11 +62,14 @@ __device__ __forceinline__ Unit load_unit(const uint8_t* __restrict__ u, int lan
 }
 
 // acc += dequant(codes of MFMAs 4*half .. 4*half+3) * b[0..3].
+// A step that is not live (a re-read past the wave's last step) gets zero
+// scales, so its products add nothing.
 __device__ __forceinline__ void mma_half(const uint4& codes, uint32_t sc, int half, const uint4 (&b)[4],
-                                         f32x4_t& acc) {
+                                         f32x4_t& acc, bool live = true) {
   const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
-  const float S0 = half == 0 ? e4m3_to_f32<0>(sc) : e4m3_to_f32<2>(sc);
-  const float S1 = half == 0 ? e4m3_to_f32<1>(sc) : e4m3_to_f32<3>(sc);
+  float S0 = half == 0 ? e4m3_to_f32<0>(sc) : e4m3_to_f32<2>(sc);
+  float S1 = half == 0 ? e4m3_to_f32<1>(sc) : e4m3_to_f32<3>(sc);
+  if (!live) S0 = S1 = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t av[4];
@@ -87,7 +94,120 @@ __device__ __forceinline__ void store_tile(const f32x4_t& acc, float alpha, int 
 }
 
 // ------------------------------------------------------------------- split
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void w4a16_split_kernel(
+// Activation operands of the 8 MFMAs of one 256-k step for lane (c, q): token
+// row c's k = 64p + 16q + 8h + (0..7) for MFMA j = 2p + h.
+struct StepB {
+  uint4 v[8];
+};
+
+__device__ __forceinline__ StepB load_b(const uint16_t* __restrict__ astep, int q) {
+  StepB b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b.v[j] = ld16(astep + 64 * (j >> 1) + 16 * q + 8 * (j & 1));
+  return b;
+}
+
+// With several token rows, lane (c, q) of the MFMA layout puts 16 different
+// rows in every group of 4 neighbouring lanes, and the texture unit then
+// looks up 4 cache lines per group.  The permuted load has lane 4c + q read
+// what lane c + 16q needs (4 neighbours, one row, one line); one LDS-crossbar
+// permute per dword (no LDS storage) then moves it to its MFMA lane.
+__device__ __forceinline__ uint4 to_mfma_lane(const uint4& v, int src_byte) {
+  return make_uint4(uint32_t(__builtin_amdgcn_ds_bpermute(src_byte, int(v.x))),
+                    uint32_t(__builtin_amdgcn_ds_bpermute(src_byte, int(v.y))),
+                    uint32_t(__builtin_amdgcn_ds_bpermute(src_byte, int(v.z))),
+                    uint32_t(__builtin_amdgcn_ds_bpermute(src_byte, int(v.w))));
+}
+
+__device__ __forceinline__ void mma_step(const Unit& u, const StepB& b, f32x4_t& acc, bool live = true) {
+  const uint4 b0[4] = {b.v[0], b.v[1], b.v[2], b.v[3]};
+  const uint4 b1[4] = {b.v[4], b.v[5], b.v[6], b.v[7]};
+  mma_half(u.c0, u.sc, 0, b0, acc, live);
+  mma_half(u.c1, u.sc, 1, b1, acc, live);
+}
+
+__device__ __forceinline__ void mma_step_perm(const Unit& u, const StepB& b, int src_byte, f32x4_t& acc, bool live) {
+  const uint4 b0[4] = {to_mfma_lane(b.v[0], src_byte), to_mfma_lane(b.v[1], src_byte), to_mfma_lane(b.v[2], src_byte),
+                       to_mfma_lane(b.v[3], src_byte)};
+  mma_half(u.c0, u.sc, 0, b0, acc, live);
+  const uint4 b1[4] = {to_mfma_lane(b.v[4], src_byte), to_mfma_lane(b.v[5], src_byte), to_mfma_lane(b.v[6], src_byte),
+                       to_mfma_lane(b.v[7], src_byte)};
+  mma_half(u.c1, u.sc, 1, b1, acc, live);
+}
+
+// Partial tiles of the waves added through LDS in wave order, then stored.
+__device__ __forceinline__ void reduce_store(f32x4_t acc, float* red, int wave, int nwaves, int lane, int32_t tile,
+                                             int32_t M, int32_t N, const float* __restrict__ alpha_p,
+                                             uint16_t* __restrict__ out, int64_t ldo) {
+  if (nwaves > 1) {
+    *reinterpret_cast<f32x4_t*>(&red[(wave * 64 + lane) * 4]) = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < nwaves; ++w) acc += *reinterpret_cast<const f32x4_t*>(&red[(w * 64 + lane) * 4]);
+  }
+  store_tile(acc, *alpha_p, lane, tile, M, N, out, ldo);
+}
+
+// Split with at most PER steps per wave, fully unrolled: step i+1's weight
+// unit and activation operands are issued before step i is computed, in the
+// order they are consumed (loads complete in issue order), and a scheduling
+// barrier keeps the compiler from sinking them below step i's waits.  Steps
+// past a wave's share re-read a valid step with zero scales.
+// INTERLEAVE: wave w takes steps w, w + waves, w + 2*waves, ... instead of a
+// contiguous run, so the waves of every workgroup on a CU read the same few
+// activation steps at a time and share them in the L1 cache.
+constexpr int kSplitMaxPer = 8;
+
+template <int PER, bool INTERLEAVE, bool PERM>
+__global__ __launch_bounds__(1024) void w4a16_split_fixed_kernel(
+    const uint16_t* __restrict__ a, int64_t lda, int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
+    int32_t steps_per_wave, const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo) {
+  extern __shared__ float red[];  // [waves][64][4]
+  const int lane = int(threadIdx.x & 63);
+  const int wave = int(threadIdx.x >> 6);
+  const int nwaves = int(blockDim.x >> 6);
+  const int q = lane >> 4;
+  const int32_t tile = int32_t(blockIdx.x);
+  const int32_t steps = K / 256;
+  const int32_t s0 = INTERLEAVE ? wave : wave * steps_per_wave;
+  const int32_t ds = INTERLEAVE ? nwaves : 1;
+  const int32_t s1 = INTERLEAVE ? steps : min(steps, s0 + steps_per_wave);
+  // the lane's load row and 16-k piece (PERM: lane 4c + q loads for MFMA lane c + 16q)
+  const int lrow = PERM ? (lane >> 2) : (lane & 15), lq = PERM ? (lane & 3) : q;
+  const int src_byte = 4 * (4 * (lane & 15) + q);
+  const uint16_t* arow = a + int64_t(min(lrow, M - 1)) * lda;
+  const uint8_t* wtile = wt + int64_t(tile) * steps * kUnitBytes;
+  auto unit_at = [&](int32_t st) { return load_unit(wtile + int64_t(min(st, steps - 1)) * kUnitBytes, lane); };
+  auto b_at = [&](int32_t st) { return load_b(arow + 256 * int64_t(min(st, steps - 1)), lq); };
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  Unit w[2];
+  StepB b[2];
+  w[0] = unit_at(s0);
+  b[0] = b_at(s0);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (i + 1 < PER) {
+      w[(i + 1) & 1] = unit_at(s0 + (i + 1) * ds);
+      b[(i + 1) & 1] = b_at(s0 + (i + 1) * ds);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (PERM)
+      mma_step_perm(w[i & 1], b[i & 1], src_byte, acc, s0 + i * ds < s1);
+    else
+      mma_step(w[i & 1], b[i & 1], acc, s0 + i * ds < s1);
+  }
+  reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha_p, out, ldo);
+}
+
+// Each wave runs steps [s0, s1) of one tile.  Step s+1's weight unit and
+// activation operands are loaded before step s is computed.  Loads complete in
+// issue order, so they are issued in the order they are consumed, and every
+// step issues the same loads (past s1 they re-read the last step, unused):
+// the waits then only cover the step being computed and the next step's loads
+// stay in flight.  Two register sets alternate by name (two steps per
+// iteration), so nothing is copied while its load is outstanding.
+__global__ __launch_bounds__(1024) void w4a16_split_kernel(
     const uint16_t* __restrict__ a, int64_t lda, int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
     int32_t steps_per_wave, const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo) {
   extern __shared__ float red[];  // [waves][64][4]
@@ -101,32 +221,28 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
   const int32_t s1 = min(steps, s0 + steps_per_wave);  // s0 < s1: the host sizes the block so
   const uint16_t* arow = a + int64_t(min(lane & 15, M - 1)) * lda;
   const uint8_t* wtile = wt + int64_t(tile) * steps * kUnitBytes;
+  auto unit_at = [&](int32_t st) { return load_unit(wtile + int64_t(min(st, s1 - 1)) * kUnitBytes, lane); };
+  auto b_at = [&](int32_t st) { return load_b(arow + 256 * int64_t(min(st, s1 - 1)), q); };
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  Unit next = load_unit(wtile + int64_t(s0) * kUnitBytes, lane);
-  for (int32_t s = s0; s < s1; ++s) {
-    const Unit cur = next;
-    if (s + 1 < s1) next = load_unit(wtile + int64_t(s + 1) * kUnitBytes, lane);
-    const uint16_t* astep = arow + 256 * int64_t(s);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint4 b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * half + i;  // k = 64p + 16q + 8h, j = 2p + h
-        b[i] = ld16(astep + 64 * (j >> 1) + 16 * q + 8 * (j & 1));
-      }
-      mma_half(half == 0 ? cur.c0 : cur.c1, cur.sc, half, b, acc);
-    }
+  Unit wa = unit_at(s0);
+  StepB ba = b_at(s0);
+  // (the scheduling barriers keep the compiler from sinking the next step's
+  // loads below the current step's waits)
+  for (int32_t s = s0;; s += 2) {
+    const Unit wb = unit_at(s + 1);
+    const StepB bb = b_at(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step(wa, ba, acc);
+    if (s + 1 >= s1) break;
+    wa = unit_at(s + 2);
+    ba = b_at(s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step(wb, bb, acc);
+    if (s + 2 >= s1) break;
   }
 
-  if (nwaves > 1) {
-    *reinterpret_cast<f32x4_t*>(&red[(wave * 64 + lane) * 4]) = acc;
-    __syncthreads();
-    if (wave != 0) return;
-    for (int w = 1; w < nwaves; ++w) acc += *reinterpret_cast<const f32x4_t*>(&red[(w * 64 + lane) * 4]);
-  }
-  store_tile(acc, *alpha_p, lane, tile, M, N, out, ldo);
+  reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha_p, out, ldo);
 }
 
 // ------------------------------------------------------------------ shared
@@ -237,16 +353,23 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
     c.schedule = 2;
     c.chunk_steps = int(std::max<int64_t>(1, std::min<int64_t>(steps, 64 / std::max<int64_t>(1, M))));
   } else {
-    // split: waves per tile so the launch gives every CU about 8 waves
-    c.schedule = 1;
+    // split: waves per tile so the launch gives every CU about 8 waves;
+    // interleaved steps while a wave has at most kSplitMaxPer of them
     const int64_t want = (8 * cus + tiles - 1) / tiles;
     c.ksplit = int(std::max<int64_t>(1, std::min<int64_t>({want, steps, 16})));
+    const int64_t ks = std::min<int64_t>(c.ksplit, steps);
+    c.schedule = (steps + ks - 1) / ks <= kSplitMaxPer ? 3 : 1;
   }
   return c;
 }
 
 bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K) {
   if (c.schedule == 1) return c.ksplit >= 1 && c.ksplit <= 16;
+  if (c.schedule == 3) {
+    const int64_t steps = K / 256;
+    const int64_t ks = std::min<int64_t>(c.ksplit, steps);
+    return c.ksplit >= 1 && c.ksplit <= 16 && (steps + ks - 1) / ks <= kSplitMaxPer;
+  }
   if (c.schedule == 2) {
     if (c.chunk_steps < 1) return false;
     const int64_t kc = std::min<int64_t>(c.chunk_steps, K / 256);
@@ -277,8 +400,36 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
   const int64_t per = (steps + ks - 1) / ks;
   const int waves = int((steps + per - 1) / per);
   const size_t lds = waves > 1 ? size_t(waves) * 64 * 4 * sizeof(float) : 0;
-  hipLaunchKernelGGL(w4a16_split_kernel, dim3(uint32_t(tiles)), dim3(64 * waves), lds, stream, A, lda, int32_t(M),
-                     WT, int32_t(N), int32_t(K), int32_t(per), alpha, O, ldo);
+  const dim3 grid{uint32_t(tiles)}, block{uint32_t(64 * waves)};
+  // permuted activation loads once several token rows share a load group
+  const bool perm = M > 4;
+#define NVFP4_SPLIT_LAUNCH(P, IL, PM)                                                                           \
+  hipLaunchKernelGGL((w4a16_split_fixed_kernel<P, IL, PM>), grid, block, lds, stream, A, lda, int32_t(M), WT,   \
+                     int32_t(N), int32_t(K), int32_t(per), alpha, O, ldo)
+#define NVFP4_SPLIT_FIXED(P)                                                                                    \
+  case P:                                                                                                       \
+    if (cfg.schedule == 3) {                                                                                    \
+      if (perm) NVFP4_SPLIT_LAUNCH(P, true, true); else NVFP4_SPLIT_LAUNCH(P, true, false);                     \
+    } else {                                                                                                    \
+      if (perm) NVFP4_SPLIT_LAUNCH(P, false, true); else NVFP4_SPLIT_LAUNCH(P, false, false);                   \
+    }                                                                                                           \
+    return hipGetLastError();
+  switch (per) {
+    NVFP4_SPLIT_FIXED(1)
+    NVFP4_SPLIT_FIXED(2)
+    NVFP4_SPLIT_FIXED(3)
+    NVFP4_SPLIT_FIXED(4)
+    NVFP4_SPLIT_FIXED(5)
+    NVFP4_SPLIT_FIXED(6)
+    NVFP4_SPLIT_FIXED(7)
+    NVFP4_SPLIT_FIXED(8)
+    default:
+      break;
+  }
+#undef NVFP4_SPLIT_FIXED
+#undef NVFP4_SPLIT_LAUNCH
+  hipLaunchKernelGGL(w4a16_split_kernel, grid, block, lds, stream, A, lda, int32_t(M), WT, int32_t(N), int32_t(K),
+                     int32_t(per), alpha, O, ldo);
   return hipGetLastError();
 }
 

@@ -65,11 +65,22 @@ def test_w4a16_decode_sweep(ops, orc, shape_index):
         gemm_check(bf16_host(out), ref[:M], sabs[:M])
 
 
-SCHEDULES = [(1, ks, 0) for ks in (1, 2, 3, 7, 16)] + [(2, 0, kc) for kc in (1, 2, 3, 4, 17)]
+SCHEDULES = ([(1, ks, 0) for ks in (1, 2, 3, 7, 16)] + [(2, 0, kc) for kc in (1, 2, 3, 4, 17)]
+             + [(3, ks, 0) for ks in (1, 3, 7, 16)])
+
+
+def _valid(sch, M, K):
+    steps = K // 256
+    if sch[0] == 2:
+        return M * min(sch[2], steps) <= 64
+    if sch[0] == 3:
+        ks = min(sch[1], steps)
+        return -(-steps // ks) <= 8
+    return True
 
 
 def _schedules_for(M, K):
-    return [(0, 0, 0)] + [sch for sch in SCHEDULES if sch[0] == 1 or M * min(sch[2], K // 256) <= 64]
+    return [(0, 0, 0)] + [sch for sch in SCHEDULES if _valid(sch, M, K)]
 
 
 def test_w4a16_every_schedule(ops, orc):
