@@ -173,7 +173,8 @@ nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_
   if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
   if (M > kInt32Max || M * (w->K / 16) > INT64_MAX / 16) return NVFP4_ERR_INVALID_SHAPE;
   if (!aligned16(a_codes) || !aligned16(a_scales)) return NVFP4_ERR_ALIGNMENT;
-  if ((M + 127) / 128 > 65535) return NVFP4_ERR_UNSUPPORTED;
+  // grid rows of 256 activation rows; 32-bit byte offsets into the codes
+  if ((M + 255) / 256 > 65535 || M * (w->K / 2) >= (int64_t(1) << 32)) return NVFP4_ERR_UNSUPPORTED;
   if (M == 0 || w->N == 0) return NVFP4_OK;
   return hip_status(
       nvfp4::launch_w4a4(a_codes, a_scales, M, w->data, w->N, w->K, alpha, out, ldo, stream));
@@ -220,7 +221,8 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
     const size_t need = nvfp4_linear_workspace_bytes(M, w->N, w->K);
     if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned16(ws)) return NVFP4_ERR_ALIGNMENT;
-    if (M * (w->K / 16) > kInt32Max || (M + 3) / 4 > 65535 || (M + 127) / 128 > 65535)
+    if (M * (w->K / 16) > kInt32Max || (M + 3) / 4 > 65535 || (M + 255) / 256 > 65535 ||
+        M * (w->K / 2) >= (int64_t(1) << 32))
       return NVFP4_ERR_UNSUPPORTED;
     uint8_t* codes = static_cast<uint8_t*>(ws);
     uint8_t* scales = codes + align_up(size_t(M) * size_t(w->K / 2), 256);
@@ -243,6 +245,8 @@ nvfp4_status moe_shape(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I
   if (K % 256 != 0 || I % 256 != 0) return NVFP4_ERR_UNSUPPORTED;
   if (K > (1 << 20) || I > (1 << 20) || T > kInt32Max || top_k > 1024) return NVFP4_ERR_UNSUPPORTED;
   if (T * top_k > kInt32Max || T * top_k / 256 + E > 65535) return NVFP4_ERR_UNSUPPORTED;
+  // 32-bit byte offsets into the quantized x and h
+  if (T * (K / 2) >= (int64_t(1) << 32) || T * top_k * (I / 2) >= (int64_t(1) << 32)) return NVFP4_ERR_UNSUPPORTED;
   if (E * 2 * I > kInt32Max - 15 || E * K > kInt32Max - 15) return NVFP4_ERR_UNSUPPORTED;
   return NVFP4_OK;
 }

@@ -50,27 +50,65 @@ struct Stage {
   uint32_t as;     // its two scale bytes (low 16 bits)
 };
 
+// The operands are read with buffer loads: a descriptor (scalar registers)
+// holds the base address, each thread keeps the byte offsets of its pieces
+// that do not depend on the step (one VGPR each), and the step adds a uniform
+// offset in a scalar register -- no per-load address arithmetic.  Offsets are
+// 32-bit: the weight descriptor starts at the workgroup's first weight tile
+// (wtile(lt) >= wtile(0) for every lt), the activation one at row 0, and the
+// callers keep both spans below 4 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(0xFFFFFFFF), 0x00020000);
+}
+
 // Weight item i (0..1023) of a step = (local tile lt = i / 64, lane slot
 // l = i % 64 = r + 16q): row 16*lt + r, group 4b + q of the step's unit, b =
 // the step within the unit.
-template <typename WTile>
-__device__ __forceinline__ Stage load_stage(const uint8_t* __restrict__ wt, WTile wtile, int32_t steps256,
-                                            const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
-                                            int64_t arow, int32_t K, int32_t step) {
+struct StageOffsets {
+  uint32_t w[2];   // item's unit row start (relative to the descriptor) + 16*l
+  uint32_t ws[2];  // the same + 2048 + 4*l (scale bytes)
+  uint32_t a;      // activation codes of row tid/2, k 32*(tid&1)
+  uint32_t as;     // its scale bytes
+};
+
+template <typename WTile, typename ARow>
+__device__ __forceinline__ StageOffsets stage_offsets(WTile wtile, ARow a_row, int32_t steps256, int32_t K) {
   const int tid = int(threadIdx.x);
-  const int b = step & 3;
-  Stage s;
+  const int64_t t0 = wtile(0);
+  StageOffsets o;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int i = tid + kThreads * j;
     const int lt = i >> 6, l = i & 63;
-    const uint8_t* u = wt + (wtile(lt) * steps256 + (step >> 2)) * kUnitBytes;
-    s.w[j] = *reinterpret_cast<const uint2*>(u + 1024 * (b >> 1) + 16 * l + 8 * (b & 1));
-    s.ws[j] = u[2048 + 4 * l + b];
+    const uint32_t unit0 = uint32_t(wtile(lt) - t0) * uint32_t(steps256) * uint32_t(kUnitBytes);
+    o.w[j] = unit0 + 16u * uint32_t(l);
+    o.ws[j] = unit0 + 2048u + 4u * uint32_t(l);
   }
-  const int half = tid & 1;
-  s.a = ld16(a_codes + arow * (K / 2) + int64_t(step) * (BK / 2) + 16 * half);
-  s.as = *reinterpret_cast<const uint16_t*>(a_scales + arow * (K / 16) + int64_t(step) * (BK / 16) + 2 * half);
+  const uint32_t arow = uint32_t(a_row(tid >> 1)), half = uint32_t(tid & 1);
+  o.a = arow * uint32_t(K / 2) + 16u * half;
+  o.as = arow * uint32_t(K / 16) + 2u * half;
+  return o;
+}
+
+struct StageSrc {
+  __amdgpu_buffer_rsrc_t w, a, as;
+};
+
+__device__ __forceinline__ Stage load_stage(const StageSrc& src, const StageOffsets& o, int32_t step) {
+  const int b = step & 3;
+  // uniform parts: the step's unit within a tile row and its place in the unit
+  const int32_t wu = (step >> 2) * kUnitBytes;
+  const int32_t wc = wu + 1024 * (b >> 1) + 8 * (b & 1);
+  Stage s;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.w, o.w[j], wc, 0);
+    s.w[j] = make_uint2(v[0], v[1]);
+    s.ws[j] = __builtin_amdgcn_raw_buffer_load_b8(src.w, o.ws[j], wu + b, 0);
+  }
+  const auto a = __builtin_amdgcn_raw_buffer_load_b128(src.a, o.a, step * (BK / 2), 0);
+  s.a = make_uint4(a[0], a[1], a[2], a[3]);
+  s.as = __builtin_amdgcn_raw_buffer_load_b16(src.as, o.as, step * (BK / 16), 0);
   return s;
 }
 
@@ -134,6 +172,18 @@ __device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ 
         acc.v[t][u] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_f16(B[cur][u], A[cur][t], acc.v[t][u], 0, 0, 0)
                             : __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][t], B[cur][u], acc.v[t][u], 0, 0, 0);
     store_part(next, kk, wnext, anext);
+    // One MFMA, then a few VALU instructions of the staged dequant (and the
+    // next block's LDS reads): the wave keeps its MFMA pipe busy while its own
+    // VALU work issues in the MFMAs' shadow, instead of issuing the MFMAs
+    // back to back and the VALU work after them.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // LDS write
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -154,7 +204,11 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc.v[t][u][i] = 0.f;
-  const int64_t arow = a_row(int(threadIdx.x >> 1));
+  const StageOffsets so = stage_offsets(wtile, a_row, steps256, K);
+  StageSrc src;
+  src.w = buffer_rsrc(wt + wtile(0) * steps256 * kUnitBytes);
+  src.a = buffer_rsrc(a_codes);
+  src.as = buffer_rsrc(a_scales);
   // buffer b of the weight tile at lds + b * BN * PITCH, of the activation
   // tile at lds + 2 * BN * PITCH + b * BM * PITCH (offsets, so that the
   // compiler keeps every access in the LDS address space)
@@ -167,10 +221,10 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
   // and every step issues the same loads (past the last step they re-read it,
   // unused): the compiler's wait counts then stay exact around the loop rather
   // than draining the memory pipeline once per step.
-  Stage sa = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, 0);
+  Stage sa = load_stage(src, so, 0);
 #pragma unroll
   for (int part = 0; part < 4; ++part) store_part(sa, part, lds, abase);
-  sa = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, min(1, steps - 1));
+  sa = load_stage(src, so, min(1, steps - 1));
   __syncthreads();
   _Float16* const w0 = lds;
   _Float16* const w1 = lds + BN * PITCH;
@@ -178,12 +232,12 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
   _Float16* const a1 = abase + BM * PITCH;
   for (int32_t s = 0;; s += 2) {
     // step s from buffer 0; step s+1 (in sa) goes to buffer 1
-    const Stage sb = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, min(s + 2, steps - 1));
+    const Stage sb = load_stage(src, so, min(s + 2, steps - 1));
     mma_step<kSwap>(acc, w0, a0, wave_row0, wm, lane, sa, w1, a1);
     __syncthreads();
     if (s + 1 >= steps) break;
     // step s+1 from buffer 1; step s+2 (in sb) goes to buffer 0
-    sa = load_stage(wt, wtile, steps256, a_codes, a_scales, arow, K, min(s + 3, steps - 1));
+    sa = load_stage(src, so, min(s + 3, steps - 1));
     mma_step<kSwap>(acc, w1, a1, wave_row0, wm, lane, sb, w0, a0);
     __syncthreads();
     if (s + 2 >= steps) break;
