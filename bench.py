@@ -191,13 +191,27 @@ def bench_w4a4(ops, torch, reps=10):
         tg += e1.elapsed_time(e2)
     gemm_us = tg / reps * 1e3
     quant_us = tq / reps * 1e3
+    # the smaller prefill batches of the same workload (prefixes of a)
+    sweep = []
+    for Ms in synth.W4A4_PREFILL["M"]:
+        o = out[:Ms]
+        ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o)
+        torch.cuda.synchronize()
+        e1.record()
+        for _ in range(reps):
+            ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o)
+        e2.record()
+        torch.cuda.synchronize()
+        us = e1.elapsed_time(e2) / reps * 1e3
+        sweep.append(dict(M=Ms, gemm_us=round(us, 2), tflops=round(2.0 * Ms * N * K / us / 1e6, 1)))
+        log(f"[w4a4] M={Ms}: gemm {us:.1f} us = {2.0 * Ms * N * K / us / 1e6:.1f} TFLOP/s")
     flops = 2.0 * M * N * K
     qbytes = M * K * (2 + 0.5 + 1 / 16)
     log(f"[w4a4] M={M} N={N} K={K}: gemm {gemm_us:.1f} us = {flops / gemm_us / 1e6:.1f} TFLOP/s; "
         f"quantize {quant_us:.1f} us = {qbytes / quant_us / 1e3:.1f} GB/s; prepare {prepare_us:.1f} us")
     return dict(M=M, N=N, K=K, gemm_us=gemm_us, quant_us=quant_us, tflops=flops / gemm_us / 1e6,
                 linear_tflops=flops / (gemm_us + quant_us) / 1e6, quant_gbs=qbytes / quant_us / 1e3,
-                prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16)
+                prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16, m_sweep=sweep)
 
 
 def moe_flops(T, top_k, K, I):
@@ -394,6 +408,7 @@ def main():
             "frac_of_fp16_mfma_peak": round(r4["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
             "linear_tflops_incl_quantize": round(r4["linear_tflops"], 2),
             "quantize_us": round(r4["quant_us"], 2), "quantize_gb_s": round(r4["quant_gbs"], 1),
+            "m_sweep": r4["m_sweep"],
             "roofline": {"bound": "mfma", "achieved": round(r4["tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(r4["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                          "traffic": load_traffic("w4a4_prefill_m8192",

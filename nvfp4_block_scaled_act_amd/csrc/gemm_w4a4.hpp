@@ -38,6 +38,45 @@ constexpr int kThreads = 512;
 constexpr int kUnitBytes = 2304;
 constexpr int kLdsHalves = 2 * (BN + BM) * PITCH;  // both buffers of both operands
 
+// Workgroup -> output tile, XCD-aware.  Workgroups are dispatched to the 8
+// XCDs in turn (id % 8), and each XCD has its own L2.  So workgroup id goes to
+// position id / 8 of XCD id % 8's contiguous share of the tile order, and the
+// order walks groups of kGroupM activation-row blocks with the rows fastest:
+// the workgroups an XCD runs at once cover a compact block of tiles whose
+// operand panels they share through that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;
+
+__host__ __device__ inline int32_t xcd_grid(int32_t total) { return (total + kXcds - 1) / kXcds * kXcds; }
+
+__device__ __forceinline__ bool xcd_tile(int32_t id, int32_t nt, int32_t mt, int32_t& n, int32_t& m) {
+  const int32_t total = nt * mt;
+  const int32_t per = (total + kXcds - 1) / kXcds;
+  const int32_t L = (id % kXcds) * per + id / kXcds;
+  if (L >= total) return false;
+  const int32_t gsize = kGroupM * nt;
+  const int32_t first = (L / gsize) * kGroupM;
+  const int32_t gm = min(mt - first, kGroupM);
+  const int32_t r = L % gsize;
+  m = first + r % gm;
+  n = r / gm;
+  return true;
+}
+
+// Grouped GEMMs: workgroup -> (tile-table row y, output block n) with all
+// `nb` blocks of a row on one XCD (they share the row's gathered activation
+// panel through its L2) and rows dealt to the XCDs in turn, so the live rows
+// of a partly filled table are spread evenly.  Grid: xcd_rows_grid(rows, nb).
+__host__ __device__ inline int32_t xcd_rows_grid(int32_t rows, int32_t nb) {
+  return (rows + kXcds - 1) / kXcds * kXcds * nb;
+}
+
+__device__ __forceinline__ void xcd_row_block(int32_t id, int32_t nb, int32_t& y, int32_t& n) {
+  const int32_t local = id / kXcds;
+  y = (local / nb) * kXcds + id % kXcds;
+  n = local % nb;
+}
+
 struct Acc {
   f32x16_t v[4][2];  // [wave 32-row weight tile t][32-row activation tile u]
 };

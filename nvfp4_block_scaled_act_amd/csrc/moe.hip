@@ -147,18 +147,21 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // gate_up GEMM of one tile of pairs x 128 gate rows (+ the matching 128 up
 // rows) of its expert, with the SiLU gate and NVFP4 quantization of h.
-// blockIdx.x = 128-row block c of the expert's I gate rows, blockIdx.y = tile.
+// Workgroup -> (tile, 128-row block c of the expert's I gate rows) by
+// gemm::xcd_row_block.
 __global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int32_t K, int32_t top_k,
-    const int32_t* __restrict__ sorted, const MoeTile* __restrict__ tiles, const uint8_t* __restrict__ wt, int32_t I,
-    const float* __restrict__ alpha_gu, const float* __restrict__ g2_p, uint8_t* __restrict__ hc,
-    uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
+    const int32_t* __restrict__ sorted, const MoeTile* __restrict__ tiles, int32_t max_tiles,
+    const uint8_t* __restrict__ wt, int32_t I, const float* __restrict__ alpha_gu, const float* __restrict__ g2_p,
+    uint8_t* __restrict__ hc, uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
-  const MoeTile tile = tiles[blockIdx.y];
+  int32_t ty, c;
+  gemm::xcd_row_block(int32_t(blockIdx.x), I / 128, ty, c);
+  if (ty >= max_tiles) return;
+  const MoeTile tile = tiles[ty];
   if (tile.rows == 0) return;
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
-  const int32_t c = int32_t(blockIdx.x);
   // LDS weight tiles 0..7: gate rows 128c..128c+127, 8..15: the up rows I + the same
   const int32_t gate_tile0 = tile.expert * (2 * I / 16) + 8 * c, up_tile0 = gate_tile0 + I / 16;
   gemm::Acc acc;
@@ -211,17 +214,20 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
 
 // down GEMM of one tile of pairs x 256 outputs of its expert, scaled by
 // alpha_dn[e] * w[pair] and added into the token's fp32 row.
-// blockIdx.x = 256-output block of K, blockIdx.y = tile.
+// Workgroup -> (tile, 256-output block of K) by gemm::xcd_row_block.
 __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
     const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs, int32_t I, const int32_t* __restrict__ sorted,
-    const MoeTile* __restrict__ tiles, const float* __restrict__ topk_w, int32_t top_k,
+    const MoeTile* __restrict__ tiles, int32_t max_tiles, const float* __restrict__ topk_w, int32_t top_k,
     const uint8_t* __restrict__ wt, int32_t K, const float* __restrict__ alpha_dn, float* __restrict__ acc32) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
-  const MoeTile tile = tiles[blockIdx.y];
+  int32_t ty, nblk;
+  gemm::xcd_row_block(int32_t(blockIdx.x), K / 256, ty, nblk);
+  if (ty >= max_tiles) return;
+  const MoeTile tile = tiles[ty];
   if (tile.rows == 0) return;
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
-  const int32_t wtile0 = tile.expert * (K / 16) + int32_t(blockIdx.x) * 16;
+  const int32_t wtile0 = tile.expert * (K / 16) + nblk * 16;
   gemm::Acc acc;
   gemm::mainloop<true>(
       acc, lds, hc, hs, [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); }, wt,
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
     s_scale[m] = alpha * topk_w[p];
   }
   __syncthreads();
-  const int32_t n = int32_t(blockIdx.x) * 256 + 128 * wn + (lane & 31);
+  const int32_t n = nblk * 256 + 128 * wn + (lane & 31);
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -320,12 +326,14 @@ hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t*
   const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 4096);
   hipLaunchKernelGGL(moe_zero_kernel, dim3(uint32_t(std::max<int64_t>(zblocks, 1))), dim3(256), 0, stream,
                      reinterpret_cast<float4*>(acc32), n4, reinterpret_cast<uint32_t*>(h_amax));
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(uint32_t(I / 128), uint32_t(L.max_tiles)), dim3(gemm::kThreads), 0, stream,
-                     xc, xs, int32_t(K), int32_t(top_k), sorted, tiles, static_cast<const uint8_t*>(w_gate_up),
-                     int32_t(I), alpha_gu, g2, hc, hs, reinterpret_cast<uint32_t*>(h_amax));
-  hipLaunchKernelGGL(moe_down_kernel, dim3(uint32_t(K / 256), uint32_t(L.max_tiles)), dim3(gemm::kThreads), 0, stream,
-                     hc, hs, int32_t(I), sorted, tiles, topk_w, int32_t(top_k), static_cast<const uint8_t*>(w_down),
-                     int32_t(K), alpha_dn, acc32);
+  const int32_t mt = int32_t(L.max_tiles);
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(uint32_t(gemm::xcd_rows_grid(mt, int32_t(I / 128)))),
+                     dim3(gemm::kThreads), 0, stream, xc, xs, int32_t(K), int32_t(top_k), sorted, tiles, mt,
+                     static_cast<const uint8_t*>(w_gate_up), int32_t(I), alpha_gu, g2, hc, hs,
+                     reinterpret_cast<uint32_t*>(h_amax));
+  hipLaunchKernelGGL(moe_down_kernel, dim3(uint32_t(gemm::xcd_rows_grid(mt, int32_t(K / 256)))),
+                     dim3(gemm::kThreads), 0, stream, hc, hs, int32_t(I), sorted, tiles, mt, topk_w, int32_t(top_k),
+                     static_cast<const uint8_t*>(w_down), int32_t(K), alpha_dn, acc32);
   const int64_t items = T * (K / 8);
   hipLaunchKernelGGL(moe_convert_kernel, dim3(uint32_t((items + 255) / 256)), dim3(256), 0, stream, acc32, T,
                      int32_t(K), static_cast<uint16_t*>(out), ldo);

@@ -22,8 +22,11 @@ __global__ __launch_bounds__(gemm::kThreads) void w4a4_kernel(const uint8_t* __r
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int32_t tiles = (N + 15) / 16;
-  const int32_t tb = int32_t(blockIdx.x) * (gemm::BN / 16);  // first weight tile of the workgroup
-  const int32_t m0 = int32_t(blockIdx.y) * gemm::BM;
+  int32_t nblk, mblk;
+  if (!gemm::xcd_tile(int32_t(blockIdx.x), (N + gemm::BN - 1) / gemm::BN, (M + gemm::BM - 1) / gemm::BM, nblk, mblk))
+    return;
+  const int32_t tb = nblk * (gemm::BN / 16);  // first weight tile of the workgroup
+  const int32_t m0 = mblk * gemm::BM;
   gemm::Acc acc;
   gemm::mainloop(
       acc, lds, ac, as, [&](int i) { return int64_t(min(m0 + i, M - 1)); }, wt,
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(gemm::kThreads) void w4a4_kernel(const uint8_t* __r
 hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
                        int64_t K, const float* alpha, void* out, int64_t ldo, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  dim3 grid(uint32_t((N + gemm::BN - 1) / gemm::BN), uint32_t((M + gemm::BM - 1) / gemm::BM));
+  const dim3 grid(uint32_t(gemm::xcd_grid(int32_t((N + gemm::BN - 1) / gemm::BN) * int32_t((M + gemm::BM - 1) / gemm::BM))));
   // whole 16-byte output pieces when the rows are 16-byte aligned
   const int vec_store = (reinterpret_cast<uintptr_t>(out) % 16 == 0 && (ldo * 2) % 16 == 0) ? 1 : 0;
   hipLaunchKernelGGL(w4a4_kernel, grid, dim3(gemm::kThreads), 0, stream, static_cast<const uint8_t*>(a_codes),
