@@ -1,7 +1,9 @@
 // Block-scaled NVFP4 x NVFP4 GEMM main loop for gfx950, shared by the dense
 // W4A4 linear and the two grouped GEMMs of the MoE expert layer.
 //
-// Computes, for a workgroup tile of 256 weight rows x 256 activation rows,
+// Computes, for a workgroup tile of 256 weight rows x BMT activation rows
+// (BMT = 256, or 128 for tiles that would be mostly empty or for a final
+// partial round),
 //   acc[row][tok] = sum_k deq(W)[row, k] * deq(A)[tok, k]
 // with deq(x) = e2m1(code) * E4M3(scale of its 16-k group).  Every such value
 // has at most 6 significant bits and lies in [2^-10, 2688], so it is exact in
@@ -15,11 +17,11 @@
 // bytes and one scale byte per (row, group)), the activation tile from the
 // canonical [rows, K/2] codes and [rows, K/16] scales.  The next step's loads
 // are in flight while the MFMAs of the current one run; one barrier per step.
-// Waves are laid out 2 (weight rows) x 4 (activation rows); each owns 128 x 64
-// outputs as 4 x 2 MFMA tiles of 32 x 32 (the 32x32x16 shape runs at about
+// Waves are laid out 2 (weight rows) x 4 (activation rows); each owns 128 x
+// BMT/4 outputs as 4 x BMT/128 MFMA tiles of 32 x 32 (the 32x32x16 shape runs at about
 // 1.6 times the rate of 16x16x32 on gfx950).  Register i of lane l in tile
 // (t, u) holds weight row row0(t) + 8*(i/4) + 4*(l/32) + i%4 for activation
-// row 32u + l%32 of the wave's 64; with kSwap (operands exchanged in the
+// row 32u + l%32 of the wave's BMT/4; with kSwap (operands exchanged in the
 // MFMA) it holds weight row row0(t) + l%32 for activation row 32u + 8*(i/4) +
 // 4*(l/32) + i%4, so that a register's 32 lanes cover 32 consecutive outputs
 // of one activation row.
@@ -49,6 +51,26 @@ constexpr int kGroupM = 4;
 
 __host__ __device__ inline int32_t xcd_grid(int32_t total) { return (total + kXcds - 1) / kXcds * kXcds; }
 
+// Tile L (0 <= L < nt*mt) of the grouped order -> (n, m).
+__device__ __forceinline__ void grouped_tile(int32_t L, int32_t nt, int32_t mt, int32_t& n, int32_t& m) {
+  const int32_t gsize = kGroupM * nt;
+  const int32_t first = (L / gsize) * kGroupM;
+  const int32_t gm = min(mt - first, kGroupM);
+  const int32_t r = L % gsize;
+  m = first + r % gm;
+  n = r / gm;
+}
+
+// The first `count` tiles of the grouped order, dealt to the XCDs as above;
+// false for the padding workgroups of xcd_grid(count).
+__device__ __forceinline__ bool xcd_tile(int32_t id, int32_t nt, int32_t mt, int32_t count, int32_t& n, int32_t& m) {
+  const int32_t per = (count + kXcds - 1) / kXcds;
+  const int32_t L = (id % kXcds) * per + id / kXcds;
+  if (L >= count) return false;
+  grouped_tile(L, nt, mt, n, m);
+  return true;
+}
+
 __device__ __forceinline__ bool xcd_tile(int32_t id, int32_t nt, int32_t mt, int32_t& n, int32_t& m) {
   const int32_t total = nt * mt;
   const int32_t per = (total + kXcds - 1) / kXcds;
@@ -77,9 +99,11 @@ __device__ __forceinline__ void xcd_row_block(int32_t id, int32_t nb, int32_t& y
   n = local % nb;
 }
 
-struct Acc {
-  f32x16_t v[4][2];  // [wave 32-row weight tile t][32-row activation tile u]
+template <int BMT>
+struct AccT {
+  f32x16_t v[4][BMT / 128];  // [wave 32-row weight tile t][32-row activation tile u]
 };
+using Acc = AccT<BM>;
 
 // Staged (not yet dequantized) operand bytes of one step for this thread.
 struct Stage {
@@ -154,6 +178,7 @@ __device__ __forceinline__ Stage load_stage(const StageSrc& src, const StageOffs
 // Dequantizes part `part` (0..3) of a staged step into LDS: parts 0 and 1 are
 // the thread's two weight items, parts 2 and 3 the two 16-k groups of its
 // activation piece.  Split in four so the work interleaves with the MFMAs.
+template <int BMT>
 __device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* __restrict__ wbuf,
                                            _Float16* __restrict__ abuf) {
   const int tid = int(threadIdx.x);
@@ -170,6 +195,9 @@ __device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* _
   } else {
     const int g = part - 2;  // 16-k group of the thread's 32 k
     const int row = tid >> 1, half = tid & 1;
+    // narrow tiles stage fewer activation rows: waves BMT/32.. have none (a
+    // wave-uniform test, so it is a scalar branch)
+    if (BMT < BM && __builtin_amdgcn_readfirstlane(tid >> 6) >= BMT / 32) return;
     const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(s.as >> (8 * g), 0));
     dequant8_f16(g == 0 ? s.a.x : s.a.z, S2, v0);
     dequant8_f16(g == 0 ? s.a.y : s.a.w, S2, v1);
@@ -184,17 +212,18 @@ __device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* _
 // LDS buffer, so the VALU work runs under the MFMAs.  (After the last step the
 // staged set is a re-read of it and lands in a buffer nobody reads.)
 // wave_row0(t) = first LDS weight row of the wave's 32-row tile t.
-template <bool kSwap, typename WaveRow0>
-__device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ wbuf, const _Float16* __restrict__ abuf,
+template <bool kSwap, int BMT, typename WaveRow0>
+__device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restrict__ wbuf, const _Float16* __restrict__ abuf,
                                          WaveRow0 wave_row0, int wm, int lane, const Stage& next,
                                          _Float16* __restrict__ wnext, _Float16* __restrict__ anext) {
   const int r = lane & 31, h = lane >> 5;
   // operands of block kk + 1 are read from LDS while the MFMAs of block kk run
-  f16x8_t A[2][4], B[2][2];
+  constexpr int U = BMT / 128;
+  f16x8_t A[2][4], B[2][U];
   auto read = [&](int kk, int slot) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      B[slot][u] = *reinterpret_cast<const f16x8_t*>(abuf + (wm * 64 + 32 * u + r) * PITCH + 16 * kk + 8 * h);
+    for (int u = 0; u < U; ++u)
+      B[slot][u] = *reinterpret_cast<const f16x8_t*>(abuf + (wm * (BMT / 4) + 32 * u + r) * PITCH + 16 * kk + 8 * h);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       A[slot][t] = *reinterpret_cast<const f16x8_t*>(wbuf + (wave_row0(t) + r) * PITCH + 16 * kk + 8 * h);
@@ -207,16 +236,16 @@ __device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ 
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < U; ++u)
         acc.v[t][u] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_f16(B[cur][u], A[cur][t], acc.v[t][u], 0, 0, 0)
                             : __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][t], B[cur][u], acc.v[t][u], 0, 0, 0);
-    store_part(next, kk, wnext, anext);
+    store_part<BMT>(next, kk, wnext, anext);
     // One MFMA, then a few VALU instructions of the staged dequant (and the
     // next block's LDS reads): the wave keeps its MFMA pipe busy while its own
     // VALU work issues in the MFMAs' shadow, instead of issuing the MFMAs
     // back to back and the VALU work after them.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4 * U; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
@@ -228,10 +257,11 @@ __device__ __forceinline__ void mma_step(Acc& acc, const _Float16* __restrict__ 
 
 // The whole K loop of one workgroup tile.
 //   a_row(i)    global activation row of tile row i (0..255): always a valid row
+//               (rows BMT..255 are loaded but not used by a narrow tile)
 //   wtile(lt)   tile index in the tiled weight of LDS weight tile lt (0..15): always valid
 //   wave_row0(t) first LDS weight row of the calling wave's 32-row tile t (0..3)
-template <bool kSwap = false, typename ARow, typename WTile, typename WaveRow0>
-__device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, const uint8_t* __restrict__ a_codes,
+template <bool kSwap = false, int BMT = BM, typename ARow, typename WTile, typename WaveRow0>
+__device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ lds, const uint8_t* __restrict__ a_codes,
                                          const uint8_t* __restrict__ a_scales, ARow a_row,
                                          const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K) {
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
@@ -240,7 +270,7 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < BMT / 128; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc.v[t][u][i] = 0.f;
   const StageOffsets so = stage_offsets(wtile, a_row, steps256, K);
@@ -249,7 +279,7 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
   src.a = buffer_rsrc(a_codes);
   src.as = buffer_rsrc(a_scales);
   // buffer b of the weight tile at lds + b * BN * PITCH, of the activation
-  // tile at lds + 2 * BN * PITCH + b * BM * PITCH (offsets, so that the
+  // tile at lds + 2 * BN * PITCH + b * BMT * PITCH (offsets, so that the
   // compiler keeps every access in the LDS address space)
   _Float16* const abase = lds + 2 * BN * PITCH;
 
@@ -262,22 +292,22 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
   // than draining the memory pipeline once per step.
   Stage sa = load_stage(src, so, 0);
 #pragma unroll
-  for (int part = 0; part < 4; ++part) store_part(sa, part, lds, abase);
+  for (int part = 0; part < 4; ++part) store_part<BMT>(sa, part, lds, abase);
   sa = load_stage(src, so, min(1, steps - 1));
   __syncthreads();
   _Float16* const w0 = lds;
   _Float16* const w1 = lds + BN * PITCH;
   _Float16* const a0 = abase;
-  _Float16* const a1 = abase + BM * PITCH;
+  _Float16* const a1 = abase + BMT * PITCH;
   for (int32_t s = 0;; s += 2) {
     // step s from buffer 0; step s+1 (in sa) goes to buffer 1
     const Stage sb = load_stage(src, so, min(s + 2, steps - 1));
-    mma_step<kSwap>(acc, w0, a0, wave_row0, wm, lane, sa, w1, a1);
+    mma_step<kSwap, BMT>(acc, w0, a0, wave_row0, wm, lane, sa, w1, a1);
     __syncthreads();
     if (s + 1 >= steps) break;
     // step s+1 from buffer 1; step s+2 (in sb) goes to buffer 0
     sa = load_stage(src, so, min(s + 3, steps - 1));
-    mma_step<kSwap>(acc, w1, a1, wave_row0, wm, lane, sb, w0, a0);
+    mma_step<kSwap, BMT>(acc, w1, a1, wave_row0, wm, lane, sb, w0, a0);
     __syncthreads();
     if (s + 2 >= steps) break;
   }
@@ -288,7 +318,7 @@ __device__ __forceinline__ void mainloop(Acc& acc, _Float16* __restrict__ lds, c
 // output rows.  value(t, u, i) = the output value of accumulator register i of
 // wave tile (t, u); rows beyond M and columns beyond N are not written.
 // Needs out and ldo*2 aligned to 16 bytes and n0 % 8 == 0 (else store_tile_direct).
-template <typename Value>
+template <int BMT = BM, typename Value>
 __device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Value value, uint16_t* __restrict__ out,
                                                int64_t ldo, int32_t m0, int32_t M, int32_t n0, int32_t N) {
   constexpr int OP = BN + 8;  // bf16 per LDS output row
@@ -296,8 +326,8 @@ __device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Value
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int mloc = wm * 64 + 32 * u + (lane & 31);
+  for (int u = 0; u < BMT / 128; ++u) {
+    const int mloc = wm * (BMT / 4) + 32 * u + (lane & 31);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -309,8 +339,8 @@ __device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Value
       }
   }
   __syncthreads();
-  // 256 rows x 32 pieces of 8 bf16
-  for (int e = int(threadIdx.x); e < BM * (BN / 8); e += kThreads) {
+  // BMT rows x 32 pieces of 8 bf16
+  for (int e = int(threadIdx.x); e < BMT * (BN / 8); e += kThreads) {
     const int mloc = e >> 5, piece = e & 31;
     const int32_t m = m0 + mloc, n = n0 + 8 * piece;
     if (m >= M || n >= N) continue;

@@ -13,6 +13,9 @@ hipError_t launch_global_scale(const void* x, int64_t rows, int64_t cols, int64_
                                hipStream_t stream);
 hipError_t launch_alpha(const float* g_w, const float* g_a, float* alpha, hipStream_t stream);
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 // Re-tiling of a canonical [N, K/2] + [N, K/16] weight into the tiled layout
 // both linears read (K % 256 == 0); tiled_weight_bytes is its size.
 int64_t tiled_weight_bytes(int64_t N, int64_t K);

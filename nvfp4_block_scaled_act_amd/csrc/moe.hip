@@ -145,37 +145,31 @@ __global__ __launch_bounds__(256) void moe_zero_kernel(float4* __restrict__ acc,
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// gate_up GEMM of one tile of pairs x 128 gate rows (+ the matching 128 up
-// rows) of its expert, with the SiLU gate and NVFP4 quantization of h.
-// Workgroup -> (tile, 128-row block c of the expert's I gate rows) by
-// gemm::xcd_row_block.
-__global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
-    const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int32_t K, int32_t top_k,
-    const int32_t* __restrict__ sorted, const MoeTile* __restrict__ tiles, int32_t max_tiles,
-    const uint8_t* __restrict__ wt, int32_t I, const float* __restrict__ alpha_gu, const float* __restrict__ g2_p,
-    uint8_t* __restrict__ hc, uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
-  int32_t ty, c;
-  gemm::xcd_row_block(int32_t(blockIdx.x), I / 128, ty, c);
-  if (ty >= max_tiles) return;
-  const MoeTile tile = tiles[ty];
-  if (tile.rows == 0) return;
+// gate_up of one tile of pairs x 128 gate rows (block c, + the matching 128
+// up rows) of its expert, with the SiLU gate and NVFP4 quantization of h.
+// BMT = pair rows the workgroup computes (256, or 128 for a tile that fits).
+template <int BMT>
+__device__ __forceinline__ void gate_up_tile(_Float16* __restrict__ lds, const MoeTile& tile, int32_t c,
+                                             const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+                                             int32_t K, int32_t top_k, const int32_t* __restrict__ sorted,
+                                             const uint8_t* __restrict__ wt, int32_t I, float alpha, float g2,
+                                             uint8_t* __restrict__ hc, uint8_t* __restrict__ hs,
+                                             uint32_t* __restrict__ h_amax) {
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
   // LDS weight tiles 0..7: gate rows 128c..128c+127, 8..15: the up rows I + the same
   const int32_t gate_tile0 = tile.expert * (2 * I / 16) + 8 * c, up_tile0 = gate_tile0 + I / 16;
-  gemm::Acc acc;
-  gemm::mainloop(
+  gemm::AccT<BMT> acc;
+  gemm::mainloop<false, BMT>(
       acc, lds, xc, xs, [&](int i) { return int64_t(sorted[tile.slot0 + min(i, tile.rows - 1)] / top_k); }, wt,
       [&](int lt) { return int64_t(lt < 8 ? gate_tile0 + lt : up_tile0 + lt - 8); },
       // the wave's tiles 0, 1 are gate rows 64wn..64wn+63, tiles 2, 3 the up rows under them
       [&](int t) { return t < 2 ? 64 * wn + 32 * t : 128 + 64 * wn + 32 * (t - 2); }, K);
 
-  const float alpha = alpha_gu[tile.expert], g2 = *g2_p;
   float hmax = 0.0f;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int32_t m = wm * 64 + 32 * u + (lane & 31);  // pair row of the tile
+  for (int u = 0; u < BMT / 128; ++u) {
+    const int32_t m = wm * (BMT / 4) + 32 * u + (lane & 31);  // pair row of the tile
     const int64_t slot = int64_t(tile.slot0) + m;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -212,9 +206,68 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
   }
 }
 
-// down GEMM of one tile of pairs x 256 outputs of its expert, scaled by
-// alpha_dn[e] * w[pair] and added into the token's fp32 row.
-// Workgroup -> (tile, 256-output block of K) by gemm::xcd_row_block.
+// Workgroup -> (tile, 128-row block c of the expert's I gate rows) by
+// gemm::xcd_row_block; tiles of at most 128 pairs take the 128-row path.
+__global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
+    const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int32_t K, int32_t top_k,
+    const int32_t* __restrict__ sorted, const MoeTile* __restrict__ tiles, int32_t max_tiles,
+    const uint8_t* __restrict__ wt, int32_t I, const float* __restrict__ alpha_gu, const float* __restrict__ g2_p,
+    uint8_t* __restrict__ hc, uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
+  int32_t ty, c;
+  gemm::xcd_row_block(int32_t(blockIdx.x), I / 128, ty, c);
+  if (ty >= max_tiles) return;
+  const MoeTile tile = tiles[ty];
+  if (tile.rows == 0) return;
+  const float alpha = alpha_gu[tile.expert], g2 = *g2_p;
+  if (tile.rows <= gemm::BM / 2)
+    gate_up_tile<gemm::BM / 2>(lds, tile, c, xc, xs, K, top_k, sorted, wt, I, alpha, g2, hc, hs, h_amax);
+  else
+    gate_up_tile<gemm::BM>(lds, tile, c, xc, xs, K, top_k, sorted, wt, I, alpha, g2, hc, hs, h_amax);
+}
+
+// down of one tile of pairs x 256 outputs (block nblk of K) of its expert,
+// scaled by alpha_dn[e] * w[pair] and added into the token's fp32 row.
+template <int BMT>
+__device__ __forceinline__ void down_tile(_Float16* __restrict__ lds, const MoeTile& tile, int32_t nblk,
+                                          const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs, int32_t I,
+                                          const int32_t* __restrict__ sorted, const float* __restrict__ topk_w,
+                                          int32_t top_k, const uint8_t* __restrict__ wt, int32_t K, float alpha,
+                                          float* __restrict__ acc32) {
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
+  const int32_t wtile0 = tile.expert * (K / 16) + nblk * 16;
+  gemm::AccT<BMT> acc;
+  gemm::mainloop<true, BMT>(
+      acc, lds, hc, hs, [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); }, wt,
+      [&](int lt) { return int64_t(wtile0 + lt); }, [&](int t) { return 128 * wn + 32 * t; }, I);
+
+  // the tile's tokens and scales, through LDS (free after the main loop)
+  int32_t* s_tok = reinterpret_cast<int32_t*>(lds);
+  float* s_scale = reinterpret_cast<float*>(lds) + gemm::BM;
+  if (threadIdx.x < BMT) {
+    const int m = int(threadIdx.x);
+    const int32_t p = sorted[tile.slot0 + min(m, tile.rows - 1)];
+    s_tok[m] = p / top_k;
+    s_scale[m] = alpha * topk_w[p];
+  }
+  __syncthreads();
+  const int32_t n = nblk * 256 + 128 * wn + (lane & 31);
+#pragma unroll
+  for (int u = 0; u < BMT / 128; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = wm * (BMT / 4) + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (m >= tile.rows) continue;
+      float* row = acc32 + int64_t(s_tok[m]) * K + n;
+      const float sc = s_scale[m];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) unsafeAtomicAdd(row + 32 * t, sc * acc.v[t][u][i]);
+    }
+}
+
+// Workgroup -> (tile, 256-output block of K) by gemm::xcd_row_block; tiles of
+// at most 128 pairs take the 128-row path.
 __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
     const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs, int32_t I, const int32_t* __restrict__ sorted,
     const MoeTile* __restrict__ tiles, int32_t max_tiles, const float* __restrict__ topk_w, int32_t top_k,
@@ -225,37 +278,11 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
   if (ty >= max_tiles) return;
   const MoeTile tile = tiles[ty];
   if (tile.rows == 0) return;
-  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
-  const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
-  const int32_t wtile0 = tile.expert * (K / 16) + nblk * 16;
-  gemm::Acc acc;
-  gemm::mainloop<true>(
-      acc, lds, hc, hs, [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); }, wt,
-      [&](int lt) { return int64_t(wtile0 + lt); }, [&](int t) { return 128 * wn + 32 * t; }, I);
-
-  // the tile's tokens and scales, through LDS (free after the main loop)
-  int32_t* s_tok = reinterpret_cast<int32_t*>(lds);
-  float* s_scale = reinterpret_cast<float*>(lds) + gemm::BM;
   const float alpha = alpha_dn[tile.expert];
-  if (threadIdx.x < gemm::BM) {
-    const int m = int(threadIdx.x);
-    const int32_t p = sorted[tile.slot0 + min(m, tile.rows - 1)];
-    s_tok[m] = p / top_k;
-    s_scale[m] = alpha * topk_w[p];
-  }
-  __syncthreads();
-  const int32_t n = nblk * 256 + 128 * wn + (lane & 31);
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = wm * 64 + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (m >= tile.rows) continue;
-      float* row = acc32 + int64_t(s_tok[m]) * K + n;
-      const float sc = s_scale[m];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) unsafeAtomicAdd(row + 32 * t, sc * acc.v[t][u][i]);
-    }
+  if (tile.rows <= gemm::BM / 2)
+    down_tile<gemm::BM / 2>(lds, tile, nblk, hc, hs, I, sorted, topk_w, top_k, wt, K, alpha, acc32);
+  else
+    down_tile<gemm::BM>(lds, tile, nblk, hc, hs, I, sorted, topk_w, top_k, wt, K, alpha, acc32);
 }
 
 // out[t][k] = bf16(acc[t][k]), eight outputs per thread.

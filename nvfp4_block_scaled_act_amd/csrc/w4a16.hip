@@ -328,7 +328,9 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
 
 std::atomic<int> g_cu_count[64];
 
-int cu_count() {
+}  // namespace
+
+int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   int n = g_cu_count[dev].load(std::memory_order_relaxed);
@@ -338,6 +340,10 @@ int cu_count() {
   }
   return n;
 }
+
+namespace {
+
+int cu_count() { return device_cu_count(); }
 
 }  // namespace
 

@@ -237,6 +237,20 @@ def test_w4a4_prefill_sampled(ops, orc, M):
     _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols, check_rows=cols)
 
 
+def test_w4a4_split_final_round(ops, orc):
+    # 17 x 16 tiles of 256 x 256 on 256 CUs: the 16 tiles of the final round
+    # run as 128-row halves (rows 3072.., cols 3328.. in the grouped tile
+    # order); checked in full there, and on sampled rows elsewhere
+    N, K, M = 4352, 1024, 4096
+    W = synth.normal_bf16(81, N, K)
+    a = synth.normal_bf16(82, M, K)
+    cal = synth.normal_bf16(83, 64, K)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(3072, 4096), rng.integers(0, 3072, 64)]))
+    cols = np.unique(np.concatenate([np.arange(3328, 4352), rng.integers(0, 3328, 64)]))
+    _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 16, 256), (130, 200, 512), (127, 129, 768), (300, 1000, 1024), (17, 8, 256)])
 def test_w4a4_ragged(ops, orc, M, N, K):
     W = synth.normal_bf16(40 + N, N, K)
