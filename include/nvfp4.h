@@ -253,9 +253,10 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
  *              calibration of a static g2 runs the layer on a calibration
  *              batch with any g2 and sets g2 = 2688 / h_amax)
  * Needs K % 256 == 0, I % 256 == 0, 1 <= E <= 1024, T*top_k < 2^31 and
- * T*top_k/256 + E <= 65535.  Eight launches on the stream, no host sync; the
- * route sum uses fp32 atomics, so its order (and the last bit of an output)
- * can vary from call to call.
+ * T*top_k/256 + E <= 65535.  Seven launches on the stream, no host sync.  The
+ * down GEMM stores each pair's routing-weighted y in fp32 by slot and a last
+ * launch adds a token's routes in the order r = 0, 1, ...: the outputs are
+ * the same bits on every call.
  * After the call the workspace holds, at the offsets nvfp4_moe_workspace_layout
  * reports, the align results and h (for inspection):
  *   sorted     int32 [T*top_k]: pair index t*top_k + r at each slot, pairs
@@ -264,6 +265,7 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
  *   tiles      int32 [max_tiles, 4]: (expert, first slot, rows, 0) of each
  *              tile of up to 256 slots, rows == 0 past the last tile
  *   h_codes    uint8 [T*top_k, I/2], h_scales uint8 [T*top_k, I/16], by slot
+ *   inv        int32 [T*top_k]: slot of pair t*top_k + r, -1 for a skipped pair
  * Errors: INVALID_ARGUMENT (null, top_k < 1, E out of range), INVALID_SHAPE
  * (descriptor shapes disagree, strides), UNSUPPORTED (K or I % 256, sizes
  * beyond the limits), WORKSPACE, ALIGNMENT, HIP.
@@ -275,7 +277,8 @@ typedef struct nvfp4_moe_layout {
   int64_t tiles;              /* int32 [max_tiles, 4] */
   int64_t sorted;             /* int32 [T*top_k] */
   int64_t h_codes, h_scales;  /* uint8 [T*top_k, I/2], [T*top_k, I/16] */
-  int64_t acc;                /* fp32 [T, K] route sum */
+  int64_t inv;                /* int32 [T*top_k]: slot of each pair, -1 if skipped */
+  int64_t ys;                 /* fp32 [T*top_k, K]: routing-weighted y by slot */
   int64_t max_tiles;
   int64_t total_bytes;
 } nvfp4_moe_layout;

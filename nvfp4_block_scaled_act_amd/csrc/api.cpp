@@ -274,7 +274,8 @@ nvfp4_status nvfp4_moe_workspace_layout(int64_t T, int64_t top_k, int64_t E, int
   out->sorted = L.sorted;
   out->h_codes = L.h_codes;
   out->h_scales = L.h_scales;
-  out->acc = L.acc;
+  out->inv = L.inv;
+  out->ys = L.ys;
   out->max_tiles = L.max_tiles;
   out->total_bytes = L.total;
   return NVFP4_OK;

@@ -37,7 +37,7 @@ hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, con
                        int64_t K, const float* alpha, void* out, int64_t ldo, hipStream_t stream);
 
 // NVFP4 MoE expert layer (W4A4 gate_up with SiLU gate and NVFP4 re-quantization,
-// W4A4 down with routing weights and an fp32 route sum).  The workspace holds,
+// W4A4 down with routing weights, fp32 route sum in a fixed order).  The workspace holds,
 // at the offsets moe_layout gives (256-byte aligned parts):
 struct MoeTile {
   int32_t expert, slot0, rows, pad;  // rows == 0: unused entry
@@ -51,7 +51,8 @@ struct MoeLayout {
   int64_t tiles;      // MoeTile [max_tiles]
   int64_t sorted;     // int32 [T*top_k]: pair index t*top_k + r at each slot
   int64_t h_codes, h_scales;  // NVFP4 h by slot [T*top_k, I/2], [T*top_k, I/16]
-  int64_t acc;        // fp32 [T, K]: route sum
+  int64_t inv;        // int32 [T*top_k]: slot of each pair, -1 if skipped
+  int64_t ys;         // fp32 [T*top_k, K]: routing-weighted down outputs by slot
   int64_t total;      // bytes
 };
 MoeLayout moe_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I);

@@ -9,7 +9,9 @@
 //   gate_up  z = alpha_gu[e] * deq(q(x_t)) . deq(W_gu[e])^T   (2I outputs)
 //            h = SiLU(z[:I]) * z[I:]  in fp32, quantized to NVFP4 with g2
 //   down     y = alpha_dn[e] * deq(h) . deq(W_dn[e])^T       (K outputs)
-//            acc[t] += w[t, r] * y  (fp32 atomics), then out = bf16(acc)
+//            ys[slot] = w[t, r] * y in fp32, by slot
+//   sum      out[t] = bf16(sum_r ys[slot of (t, r)]), routes in order r = 0..
+// (a fixed summation order: the layer's output bits are reproducible)
 // Both GEMMs run gemm::mainloop on one 256-pair tile and 256 weight rows per
 // workgroup.  The tile table has a fixed maximum length (every expert can
 // leave one partial tile), so no launch depends on counts read back to the
@@ -33,9 +35,11 @@ __device__ __forceinline__ int expert_of(const int32_t* __restrict__ ids, int64_
 }
 
 // counts[c][e] = pairs of chunk c routed to expert e.
+// Also clears the h amax (when requested) for the gate_up kernel.
 __global__ __launch_bounds__(kChunk) void moe_count_kernel(const int32_t* __restrict__ ids, int64_t P, int32_t E,
-                                                           int32_t* __restrict__ counts) {
+                                                           int32_t* __restrict__ counts, uint32_t* __restrict__ h_amax) {
   extern __shared__ int32_t cnt[];
+  if (h_amax && blockIdx.x == 0 && threadIdx.x == 0) *h_amax = 0u;
   for (int e = int(threadIdx.x); e < E; e += kChunk) cnt[e] = 0;
   __syncthreads();
   const int64_t p = int64_t(blockIdx.x) * kChunk + threadIdx.x;
@@ -109,9 +113,10 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ co
 
 // sorted[base[c][e] + rank] = p, rank = number of earlier pairs of the chunk
 // with the same expert (so the order within an expert is the pair order).
+// inv[p] = the slot of pair p, -1 for a skipped pair.
 __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int32_t E,
                                                              const int32_t* __restrict__ bases,
-                                                             int32_t* __restrict__ sorted) {
+                                                             int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
   extern __shared__ int32_t wave_count[];  // [16][E]
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   for (int i = int(threadIdx.x); i < 16 * E; i += kChunk) wave_count[i] = 0;
@@ -131,16 +136,12 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __re
   if (e < E) {
     int32_t before = 0;
     for (int w = 0; w < wave; ++w) before += wave_count[w * E + e];
-    sorted[bases[int64_t(blockIdx.x) * E + e] + before + __popcll(lower)] = int32_t(p);
+    const int32_t slot = bases[int64_t(blockIdx.x) * E + e] + before + __popcll(lower);
+    sorted[slot] = int32_t(p);
+    inv[p] = slot;
+  } else if (p < P) {
+    inv[p] = -1;
   }
-}
-
-// Zeroes the fp32 route sum (and the h amax, if requested).
-__global__ __launch_bounds__(256) void moe_zero_kernel(float4* __restrict__ acc, int64_t n4,
-                                                       uint32_t* __restrict__ h_amax) {
-  const int64_t stride = int64_t(gridDim.x) * 256;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += stride) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (h_amax && blockIdx.x == 0 && threadIdx.x == 0) *h_amax = 0u;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -227,13 +228,13 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
 }
 
 // down of one tile of pairs x 256 outputs (block nblk of K) of its expert,
-// scaled by alpha_dn[e] * w[pair] and added into the token's fp32 row.
+// scaled by alpha_dn[e] * w[pair] and stored by slot (fp32).
 template <int BMT>
 __device__ __forceinline__ void down_tile(_Float16* __restrict__ lds, const MoeTile& tile, int32_t nblk,
                                           const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs, int32_t I,
                                           const int32_t* __restrict__ sorted, const float* __restrict__ topk_w,
                                           int32_t top_k, const uint8_t* __restrict__ wt, int32_t K, float alpha,
-                                          float* __restrict__ acc32) {
+                                          float* __restrict__ ys) {
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
   const int32_t wtile0 = tile.expert * (K / 16) + nblk * 16;
@@ -242,14 +243,11 @@ __device__ __forceinline__ void down_tile(_Float16* __restrict__ lds, const MoeT
       acc, lds, hc, hs, [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); }, wt,
       [&](int lt) { return int64_t(wtile0 + lt); }, [&](int t) { return 128 * wn + 32 * t; }, I);
 
-  // the tile's tokens and scales, through LDS (free after the main loop)
-  int32_t* s_tok = reinterpret_cast<int32_t*>(lds);
-  float* s_scale = reinterpret_cast<float*>(lds) + gemm::BM;
+  // the tile's routing-weight scales, through LDS (free after the main loop)
+  float* s_scale = reinterpret_cast<float*>(lds);
   if (threadIdx.x < BMT) {
     const int m = int(threadIdx.x);
-    const int32_t p = sorted[tile.slot0 + min(m, tile.rows - 1)];
-    s_tok[m] = p / top_k;
-    s_scale[m] = alpha * topk_w[p];
+    s_scale[m] = alpha * topk_w[sorted[tile.slot0 + min(m, tile.rows - 1)]];
   }
   __syncthreads();
   const int32_t n = nblk * 256 + 128 * wn + (lane & 31);
@@ -259,10 +257,10 @@ __device__ __forceinline__ void down_tile(_Float16* __restrict__ lds, const MoeT
     for (int i = 0; i < 16; ++i) {
       const int m = wm * (BMT / 4) + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3);
       if (m >= tile.rows) continue;
-      float* row = acc32 + int64_t(s_tok[m]) * K + n;
+      float* row = ys + (int64_t(tile.slot0) + m) * K + n;
       const float sc = s_scale[m];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) unsafeAtomicAdd(row + 32 * t, sc * acc.v[t][u][i]);
+      for (int t = 0; t < 4; ++t) row[32 * t] = sc * acc.v[t][u][i];
     }
 }
 
@@ -271,7 +269,7 @@ __device__ __forceinline__ void down_tile(_Float16* __restrict__ lds, const MoeT
 __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
     const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs, int32_t I, const int32_t* __restrict__ sorted,
     const MoeTile* __restrict__ tiles, int32_t max_tiles, const float* __restrict__ topk_w, int32_t top_k,
-    const uint8_t* __restrict__ wt, int32_t K, const float* __restrict__ alpha_dn, float* __restrict__ acc32) {
+    const uint8_t* __restrict__ wt, int32_t K, const float* __restrict__ alpha_dn, float* __restrict__ ys) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
   int32_t ty, nblk;
   gemm::xcd_row_block(int32_t(blockIdx.x), K / 256, ty, nblk);
@@ -280,23 +278,32 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
   if (tile.rows == 0) return;
   const float alpha = alpha_dn[tile.expert];
   if (tile.rows <= gemm::BM / 2)
-    down_tile<gemm::BM / 2>(lds, tile, nblk, hc, hs, I, sorted, topk_w, top_k, wt, K, alpha, acc32);
+    down_tile<gemm::BM / 2>(lds, tile, nblk, hc, hs, I, sorted, topk_w, top_k, wt, K, alpha, ys);
   else
-    down_tile<gemm::BM>(lds, tile, nblk, hc, hs, I, sorted, topk_w, top_k, wt, K, alpha, acc32);
+    down_tile<gemm::BM>(lds, tile, nblk, hc, hs, I, sorted, topk_w, top_k, wt, K, alpha, ys);
 }
 
-// out[t][k] = bf16(acc[t][k]), eight outputs per thread.
-__global__ __launch_bounds__(256) void moe_convert_kernel(const float* __restrict__ acc32, int64_t T, int32_t K,
-                                                          uint16_t* __restrict__ out, int64_t ldo) {
+// out[t][k] = bf16(sum over the token's routes r = 0.. of ys[inv[t*top_k + r]][k])
+// in fp32, eight outputs per thread; skipped routes (inv < 0) add nothing.
+__global__ __launch_bounds__(256) void moe_sum_kernel(const float* __restrict__ ys, const int32_t* __restrict__ inv,
+                                                      int64_t T, int32_t top_k, int32_t K, uint16_t* __restrict__ out,
+                                                      int64_t ldo) {
   const int64_t per_row = K / 8;
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= T * per_row) return;
   const int64_t t = i / per_row, k = (i - t * per_row) * 8;
-  const float4 a = *reinterpret_cast<const float4*>(acc32 + t * K + k);
-  const float4 b = *reinterpret_cast<const float4*>(acc32 + t * K + k + 4);
-  uint16_t* dst = out + t * ldo + k;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+  for (int32_t r = 0; r < top_k; ++r) {
+    const int32_t slot = inv[t * top_k + r];
+    if (slot < 0) continue;
+    const float* src = ys + int64_t(slot) * K + k;
+    const float4 x = *reinterpret_cast<const float4*>(src);
+    const float4 y = *reinterpret_cast<const float4*>(src + 4);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+  }
   const uint4 v = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
-  *reinterpret_cast<uint4*>(dst) = v;
+  *reinterpret_cast<uint4*>(out + t * ldo + k) = v;
 }
 
 }  // namespace
@@ -320,7 +327,8 @@ MoeLayout moe_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I) 
   L.sorted = take(4 * P);
   L.h_codes = take(P * I / 2);
   L.h_scales = take(P * I / 16);
-  L.acc = take(4 * T * K);
+  L.inv = take(4 * P);
+  L.ys = take(4 * P * K);
   L.total = off;
   return L;
 }
@@ -339,20 +347,18 @@ hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t*
   int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
   uint8_t* hc = base + L.h_codes;
   uint8_t* hs = base + L.h_scales;
-  float* acc32 = reinterpret_cast<float*>(base + L.acc);
+  int32_t* inv = reinterpret_cast<int32_t*>(base + L.inv);
+  float* ys = reinterpret_cast<float*>(base + L.ys);
   const int64_t P = T * top_k;
   hipError_t err = launch_quantize(x, T, K, ldx, g1, xc, xs, stream);
   if (err != hipSuccess) return err;
   const uint32_t chunks = uint32_t(L.chunks);
-  hipLaunchKernelGGL(moe_count_kernel, dim3(chunks), dim3(kChunk), size_t(4 * E), stream, ids, P, int32_t(E), counts);
+  hipLaunchKernelGGL(moe_count_kernel, dim3(chunks), dim3(kChunk), size_t(4 * E), stream, ids, P, int32_t(E), counts,
+                     reinterpret_cast<uint32_t*>(h_amax));
   hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, int32_t(L.chunks), int32_t(E), offsets,
                      tiles, int32_t(L.max_tiles));
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(chunks), dim3(kChunk), size_t(4 * 16 * E), stream, ids, P, int32_t(E),
-                     counts, sorted);
-  const int64_t n4 = T * K / 4;
-  const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 4096);
-  hipLaunchKernelGGL(moe_zero_kernel, dim3(uint32_t(std::max<int64_t>(zblocks, 1))), dim3(256), 0, stream,
-                     reinterpret_cast<float4*>(acc32), n4, reinterpret_cast<uint32_t*>(h_amax));
+                     counts, sorted, inv);
   const int32_t mt = int32_t(L.max_tiles);
   hipLaunchKernelGGL(moe_gate_up_kernel, dim3(uint32_t(gemm::xcd_rows_grid(mt, int32_t(I / 128)))),
                      dim3(gemm::kThreads), 0, stream, xc, xs, int32_t(K), int32_t(top_k), sorted, tiles, mt,
@@ -360,10 +366,10 @@ hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t*
                      reinterpret_cast<uint32_t*>(h_amax));
   hipLaunchKernelGGL(moe_down_kernel, dim3(uint32_t(gemm::xcd_rows_grid(mt, int32_t(K / 256)))),
                      dim3(gemm::kThreads), 0, stream, hc, hs, int32_t(I), sorted, tiles, mt, topk_w, int32_t(top_k),
-                     static_cast<const uint8_t*>(w_down), int32_t(K), alpha_dn, acc32);
+                     static_cast<const uint8_t*>(w_down), int32_t(K), alpha_dn, ys);
   const int64_t items = T * (K / 8);
-  hipLaunchKernelGGL(moe_convert_kernel, dim3(uint32_t((items + 255) / 256)), dim3(256), 0, stream, acc32, T,
-                     int32_t(K), static_cast<uint16_t*>(out), ldo);
+  hipLaunchKernelGGL(moe_sum_kernel, dim3(uint32_t((items + 255) / 256)), dim3(256), 0, stream, ys, inv, T,
+                     int32_t(top_k), int32_t(K), static_cast<uint16_t*>(out), ldo);
   return hipGetLastError();
 }
 

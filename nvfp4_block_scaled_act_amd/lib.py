@@ -37,7 +37,7 @@ class Weight(C.Structure):
 class MoeLayout(C.Structure):
     """Mirror of struct nvfp4_moe_layout (byte offsets into the MoE workspace)."""
     _fields_ = [(n, I64) for n in ("x_codes", "x_scales", "counts", "offsets", "tiles", "sorted", "h_codes",
-                                   "h_scales", "acc", "max_tiles", "total_bytes")]
+                                   "h_scales", "inv", "ys", "max_tiles", "total_bytes")]
 
 
 _SIGS = {

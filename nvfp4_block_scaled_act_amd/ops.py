@@ -222,6 +222,7 @@ def moe_workspace_views(ws: torch.Tensor, T: int, top_k: int, E: int, K: int, I:
         tiles=part("tiles", 16 * lay["max_tiles"]).view(torch.int32).view(lay["max_tiles"], 4),
         h_codes=part("h_codes", P * I // 2).view(P, I // 2),
         h_scales=part("h_scales", P * I // 16).view(P, I // 16),
+        inv=part("inv", 4 * P).view(torch.int32),
         x_codes=part("x_codes", T * K // 2).view(T, K // 2),
         x_scales=part("x_scales", T * K // 16).view(T, K // 16),
     )

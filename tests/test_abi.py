@@ -164,7 +164,7 @@ def test_moe_workspace_layout(nv):
     P = T * top_k
     parts = [("x_codes", T * K // 2), ("x_scales", T * K // 16), ("counts", 4 * 64 * E), ("offsets", 4 * (E + 1)),
              ("tiles", 16 * lay.max_tiles), ("sorted", 4 * P), ("h_codes", P * I // 2), ("h_scales", P * I // 16),
-             ("acc", 4 * T * K)]
+             ("inv", 4 * P), ("ys", 4 * P * K)]
     assert lay.max_tiles == P // 256 + E
     end = 0
     for name, size in parts:
