@@ -76,18 +76,21 @@ __device__ __forceinline__ void dequant8_bf16(uint32_t codes, float S, uint32_t 
   out[3] = pack_bf16x2(p3.x * S, p3.y * S);
 }
 
-// Same, to fp16: the codes go to fp16 unscaled, then one packed fp16 multiply
-// per pair applies S (both factors and the product are exact in fp16).
+// Two e2m1 codes (byte SEL of word) -> two fp16 values (low nibble first),
+// exact, by gfx950's packed fp4 -> fp16 convert (scale 1.0: unscaled).
+template <int SEL>
+__device__ __forceinline__ f16x2_t e2m1x2_to_f16(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, SEL);
+}
+
+// Same, to fp16: two codes per convert, then one packed fp16 multiply per pair
+// applies S (both factors and the product are exact in fp16).
 __device__ __forceinline__ void dequant8_f16(uint32_t codes, uint32_t S2 /* S as f16x2 */, uint32_t out[4]) {
-  const f32x2_t p0 = e2m1x2_to_f32<0>(codes);
-  const f32x2_t p1 = e2m1x2_to_f32<1>(codes);
-  const f32x2_t p2 = e2m1x2_to_f32<2>(codes);
-  const f32x2_t p3 = e2m1x2_to_f32<3>(codes);
   const f16x2_t s = __builtin_bit_cast(f16x2_t, S2);
-  out[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pack_f16x2_rtz(p0.x, p0.y)) * s);
-  out[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pack_f16x2_rtz(p1.x, p1.y)) * s);
-  out[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pack_f16x2_rtz(p2.x, p2.y)) * s);
-  out[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pack_f16x2_rtz(p3.x, p3.y)) * s);
+  out[0] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16<0>(codes) * s);
+  out[1] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16<1>(codes) * s);
+  out[2] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16<2>(codes) * s);
+  out[3] = __builtin_bit_cast(uint32_t, e2m1x2_to_f16<3>(codes) * s);
 }
 
 __device__ __forceinline__ uint32_t f32_to_f16x2_splat(float s) {
