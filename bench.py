@@ -174,32 +174,35 @@ def bench_w4a4(ops, torch, reps=10):
     al = ops.alpha(gw, ga)
     ac, as_ = ops.quantize_act(ad, ga)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = ops.w4a4_workspace()  # stream-K finish of the last round of tiles
     for _ in range(2):
         ops.quantize_act(ad, ga, ac, as_)
-        ops.linear_w4a4(ac, as_, w, al, out=out)
+        ops.linear_w4a4(ac, as_, w, al, out=out, workspace=ws)
     torch.cuda.synchronize()
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    tq = tg = 0.0
-    for _ in range(reps):
-        e0.record()
+    # quantize -> GEMM pairs issued back to back (as consecutive prefill
+    # layers would), one event before each call, one host sync at the end
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 1)]
+    for i in range(reps):
+        ev[2 * i].record()
         ops.quantize_act(ad, ga, ac, as_)
-        e1.record()
-        ops.linear_w4a4(ac, as_, w, al, out=out)
-        e2.record()
-        torch.cuda.synchronize()
-        tq += e0.elapsed_time(e1)
-        tg += e1.elapsed_time(e2)
+        ev[2 * i + 1].record()
+        ops.linear_w4a4(ac, as_, w, al, out=out, workspace=ws)
+    ev[2 * reps].record()
+    torch.cuda.synchronize()
+    tq = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps))
+    tg = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(reps))
+    e1, e2 = ev[0], ev[1]
     gemm_us = tg / reps * 1e3
     quant_us = tq / reps * 1e3
     # the smaller prefill batches of the same workload (prefixes of a)
     sweep = []
     for Ms in synth.W4A4_PREFILL["M"]:
         o = out[:Ms]
-        ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o)
+        ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o, workspace=ws)
         torch.cuda.synchronize()
         e1.record()
         for _ in range(reps):
-            ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o)
+            ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o, workspace=ws)
         e2.record()
         torch.cuda.synchronize()
         us = e1.elapsed_time(e2) / reps * 1e3

@@ -255,7 +255,8 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restr
   }
 }
 
-// The whole K loop of one workgroup tile.
+// The K loop of one workgroup tile over the 64-k steps [s_begin, s_end)
+// (default: all of K).
 //   a_row(i)    global activation row of tile row i (0..255): always a valid row
 //               (rows BMT..255 are loaded but not used by a narrow tile)
 //   wtile(lt)   tile index in the tiled weight of LDS weight tile lt (0..15): always valid
@@ -263,10 +264,11 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restr
 template <bool kSwap = false, int BMT = BM, typename ARow, typename WTile, typename WaveRow0>
 __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ lds, const uint8_t* __restrict__ a_codes,
                                          const uint8_t* __restrict__ a_scales, ARow a_row,
-                                         const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K) {
+                                         const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K,
+                                         int32_t s_begin = 0, int32_t s_end = -1) {
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wm = wave >> 1;
-  const int32_t steps = K / BK, steps256 = K / 256;
+  const int32_t steps = s_end < 0 ? K / BK : s_end, steps256 = K / 256;  // steps: one past the last step
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -290,16 +292,16 @@ __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ 
   // and every step issues the same loads (past the last step they re-read it,
   // unused): the compiler's wait counts then stay exact around the loop rather
   // than draining the memory pipeline once per step.
-  Stage sa = load_stage(src, so, 0);
+  Stage sa = load_stage(src, so, s_begin);
 #pragma unroll
   for (int part = 0; part < 4; ++part) store_part<BMT>(sa, part, lds, abase);
-  sa = load_stage(src, so, min(1, steps - 1));
+  sa = load_stage(src, so, min(s_begin + 1, steps - 1));
   __syncthreads();
   _Float16* const w0 = lds;
   _Float16* const w1 = lds + BN * PITCH;
   _Float16* const a0 = abase;
   _Float16* const a1 = abase + BMT * PITCH;
-  for (int32_t s = 0;; s += 2) {
+  for (int32_t s = s_begin;; s += 2) {
     // step s from buffer 0; step s+1 (in sa) goes to buffer 1
     const Stage sb = load_stage(src, so, min(s + 2, steps - 1));
     mma_step<kSwap, BMT>(acc, w0, a0, wave_row0, wm, lane, sa, w1, a1);
@@ -315,11 +317,14 @@ __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ 
 
 // Writes the bf16 tile out[m][n] (activation row m, weight row n) of the
 // workgroup through LDS so that global stores are whole 16-byte pieces of
-// output rows.  value(t, u, i) = the output value of accumulator register i of
-// wave tile (t, u); rows beyond M and columns beyond N are not written.
-// Needs out and ldo*2 aligned to 16 bytes and n0 % 8 == 0 (else store_tile_direct).
-template <int BMT = BM, typename Value>
-__device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Value value, uint16_t* __restrict__ out,
+// output rows.  chunk(t, u, g) = the output values of accumulator registers
+// 4g .. 4g+3 of wave tile (t, u) (a float4); rows beyond M and columns beyond
+// N are not written.
+// Needs out and ldo*2 aligned to 16 bytes and n0 % 8 == 0 (else a direct store).
+// kCpol != 0: the global stores are buffer stores with that cache policy (the
+// output then spans less than 2 GiB).
+template <int BMT = BM, int kCpol = 0, typename Chunk>
+__device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Chunk chunk, uint16_t* __restrict__ out,
                                                int64_t ldo, int32_t m0, int32_t M, int32_t n0, int32_t N) {
   constexpr int OP = BN + 8;  // bf16 per LDS output row
   uint16_t* t16 = reinterpret_cast<uint16_t*>(lds);
@@ -333,9 +338,8 @@ __device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Value
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int nloc = 128 * wn + 32 * t + 8 * g + 4 * h;
-        const uint32_t lo = pack_bf16x2(value(t, u, 4 * g), value(t, u, 4 * g + 1));
-        const uint32_t hi = pack_bf16x2(value(t, u, 4 * g + 2), value(t, u, 4 * g + 3));
-        *reinterpret_cast<uint2*>(t16 + mloc * OP + nloc) = make_uint2(lo, hi);
+        const float4 v = chunk(t, u, g);
+        *reinterpret_cast<uint2*>(t16 + mloc * OP + nloc) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
       }
   }
   __syncthreads();
@@ -346,11 +350,25 @@ __device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Value
     if (m >= M || n >= N) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(t16 + mloc * OP + 8 * piece);
     uint16_t* dst = out + int64_t(m) * ldo + n;
-    if (n + 8 <= N) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (kCpol != 0) {
+      const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(out);
+      const int32_t off = int32_t((int64_t(m) * ldo + n) * 2);
+      if (n + 8 <= N) {
+        const u32x4_t vv = {v.x, v.y, v.z, v.w};
+        __builtin_amdgcn_raw_buffer_store_b128(vv, rsrc, off, 0, kCpol);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (n + i < N)
+            __builtin_amdgcn_raw_buffer_store_b16(uint16_t(w[i >> 1] >> (16 * (i & 1))), rsrc, off + 2 * i, 0, kCpol);
+      }
+    } else if (n + 8 <= N) {
       *reinterpret_cast<uint4*>(dst) = v;
     } else {
-      const uint16_t* vv = reinterpret_cast<const uint16_t*>(&v);
-      for (int i = 0; i < N - n; ++i) dst[i] = vv[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (n + i < N) dst[i] = uint16_t(w[i >> 1] >> (16 * (i & 1)));
     }
   }
 }

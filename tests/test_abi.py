@@ -105,6 +105,18 @@ def test_w4a16_validation(nv):
     assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 2, 0, None) == ARG  # burst: 10 steps per wave > 8
 
 
+def test_w4a4_ws_validation(nv):
+    f = nv.nvfp4_linear_w4a4_ws
+    need = nv.nvfp4_linear_w4a4_workspace_bytes()
+    assert need >= 256 * 1024  # at least one 256 x 256 fp32 partial tile
+    w = _w()
+    assert f(A16, A16, 8, C.byref(w), A16, A16, 64, None, need, None) == WS          # no workspace
+    assert f(A16, A16, 8, C.byref(w), A16, A16, 64, A16, need - 1, None) == WS       # too small
+    assert f(A16, A16, 8, C.byref(w), A16, A16, 64, A16 + 16, need, None) == ALIGN   # not 256-aligned
+    assert f(A16, A16, 0, C.byref(w), A16, A16, 64, None, 0, None) == OK             # empty batch
+    assert f(A16, A16 + 4, 8, C.byref(w), A16, A16, 64, A16, need, None) == ALIGN
+
+
 def test_w4a4_validation(nv):
     f = nv.nvfp4_linear_w4a4
     w = _w()

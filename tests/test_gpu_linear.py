@@ -5,7 +5,7 @@ import pytest
 
 from nvfp4_block_scaled_act_amd import synth
 
-from helpers import bf16_dev, bf16_host, f32_dev, gemm_check, u8_host
+from helpers import bf16_dev, bf16_f64, bf16_host, f32_dev, gemm_check, u8_host
 
 pytestmark = pytest.mark.gpu
 
@@ -191,7 +191,7 @@ def test_w4a16_deterministic(ops, orc):
 
 # ------------------------------------------------------------------ W4A4
 
-def _w4a4_case(ops, orc, W, a, cal, rows=None, cols=None, check_rows=None):
+def _w4a4_case(ops, orc, W, a, cal, rows=None, cols=None, check_rows=None, ws=None):
     q = Quantized(ops, orc, W, check_rows=check_rows)
     ga = orc.global_scale(cal)
     gad = ops.global_scale(bf16_dev(cal))
@@ -200,7 +200,9 @@ def _w4a4_case(ops, orc, W, a, cal, rows=None, cols=None, check_rows=None):
     ac, as_ = ops.quantize_act(ad, gad)
     al = ops.alpha(q.g_dev, gad)
     assert al.item() == orc.alpha(q.g, ga)
-    out = bf16_host(ops.linear_w4a4(ac, as_, q.w, al))
+    out = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=ws))
+    if ws is not None:
+        check_ws_clean(ops, ws)
     oac, oas = orc.quantize(a if rows is None else a[rows], ga)
     if rows is None:
         assert (u8_host(ac) == oac).all() and (u8_host(as_) == oas).all()
@@ -269,6 +271,79 @@ def test_w4a4_deterministic(ops, orc):
     o1 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al))
     for _ in range(3):
         assert (bf16_host(ops.linear_w4a4(ac, as_, q.w, al)) == o1).all()
+
+
+# ------------------------------------------------------- W4A4, stream-K finish
+
+def check_ws_clean(ops, ws):
+    """After a call the stream-K flags and the timed-out-wait count are zero."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tail = ws[cus * 256 * 1024:cus * 256 * 1024 + 4 * cus + 4].cpu().numpy()
+    assert (tail == 0).all(), "stream-K flags left set or a wait timed out"
+
+
+def test_w4a4_streamk_full_rounds(ops, orc):
+    # 9 x 34 = 306 tiles: a whole round, then 50 leftover tiles cut between
+    # the CUs (on a 256-CU device); checked in full
+    N, K, M = 8704, 1024, 2304
+    W = synth.normal_bf16(84, N, K)
+    a = synth.normal_bf16(85, M, K)
+    cal = synth.normal_bf16(86, 64, K)
+    _w4a4_case(ops, orc, W, a, cal, ws=ops.w4a4_workspace())
+
+
+def test_w4a4_streamk_small_full(ops, orc):
+    # 32 tiles, each cut into 4 pieces of 20 steps; checked in full
+    N, K, M = 2048, 5120, 1024
+    W = synth.normal_bf16(87, N, K)
+    a = synth.normal_bf16(88, M, K)
+    cal = synth.normal_bf16(89, 64, K)
+    _w4a4_case(ops, orc, W, a, cal, ws=ops.w4a4_workspace())
+
+
+def test_w4a4_streamk_m4096_sampled(ops, orc):
+    # 544 tiles: two whole rounds, then the 32 tiles of grouped positions
+    # 512.. (rows 3072.., cols 6656.. on a 256-CU device) split 8 ways
+    N, K, M = 8704, 5120, 4096
+    W = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_W), N, K)
+    a = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), 8192, K)[:M]
+    cal = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_CAL), 512, K)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([rng.integers(3072, M, 64), rng.integers(0, 3072, 32), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(6656, N, 256), rng.integers(0, 6656, 96), [0, N - 1]]))
+    _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols, check_rows=cols, ws=ops.w4a4_workspace())
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (130, 200, 512), (300, 1000, 1024), (700, 520, 2048)])
+def test_w4a4_streamk_ragged(ops, orc, M, N, K):
+    # fewer tiles than CUs: each tile cut into up to 8 pieces of a few steps
+    W = synth.normal_bf16(40 + N, N, K)
+    a = synth.normal_bf16(50 + M, M, K)
+    cal = synth.normal_bf16(60 + M, 64, K)
+    _w4a4_case(ops, orc, W, a, cal, ws=ops.w4a4_workspace())
+
+
+def test_w4a4_streamk_reuse_and_deterministic(ops, orc):
+    # one workspace across calls of different shapes: repeated calls give the
+    # same bits, and the stream-K result matches the workspace-free one to
+    # fp32 rounding
+    ws = ops.w4a4_workspace()
+    W = synth.normal_bf16(72, 1000, 2048)
+    q = Quantized(ops, orc, W)
+    g = f32_dev(400.0)
+    al = ops.alpha(q.g_dev, g)
+    for M in (300, 1024, 5, 300):
+        a = bf16_dev(synth.normal_bf16(73 + M, M, 2048))
+        ac, as_ = ops.quantize_act(a, g)
+        o1 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=ws))
+        check_ws_clean(ops, ws)
+        o2 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=ws))
+        assert (o1 == o2).all()
+        ref = bf16_f64(bf16_host(ops.linear_w4a4(ac, as_, q.w, al)))
+        got = bf16_f64(o1)
+        assert np.linalg.norm(got - ref) <= 1e-3 * np.linalg.norm(ref)
 
 
 # ------------------------------------------------------------------ dispatch
