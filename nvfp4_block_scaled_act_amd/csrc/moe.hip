@@ -284,26 +284,46 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
 }
 
 // out[t][k] = bf16(sum over the token's routes r = 0.. of ys[inv[t*top_k + r]][k])
-// in fp32, eight outputs per thread; skipped routes (inv < 0) add nothing.
+// in fp32, four outputs per thread; skipped routes (inv < 0) add nothing.
+// TK > 0: top_k == TK, and the loads of all the token's routes are issued
+// before the sum (a skipped route re-reads slot 0 and is not added); TK == 0:
+// any top_k, one route at a time.  Same sum order either way.
+template <int TK>
 __global__ __launch_bounds__(256) void moe_sum_kernel(const float* __restrict__ ys, const int32_t* __restrict__ inv,
                                                       int64_t T, int32_t top_k, int32_t K, uint16_t* __restrict__ out,
                                                       int64_t ldo) {
-  const int64_t per_row = K / 8;
+  const int64_t per_row = K / 4;
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= T * per_row) return;
-  const int64_t t = i / per_row, k = (i - t * per_row) * 8;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  for (int32_t r = 0; r < top_k; ++r) {
-    const int32_t slot = inv[t * top_k + r];
-    if (slot < 0) continue;
-    const float* src = ys + int64_t(slot) * K + k;
-    const float4 x = *reinterpret_cast<const float4*>(src);
-    const float4 y = *reinterpret_cast<const float4*>(src + 4);
-    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
-    b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+  const int64_t t = i / per_row, k = (i - t * per_row) * 4;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (TK > 0) {
+    int32_t slot[TK > 0 ? TK : 1];
+    float4 x[TK > 0 ? TK : 1];
+#pragma unroll
+    for (int r = 0; r < TK; ++r) slot[r] = inv[t * TK + r];
+#pragma unroll
+    for (int r = 0; r < TK; ++r) x[r] = *reinterpret_cast<const float4*>(ys + int64_t(max(slot[r], 0)) * K + k);
+#pragma unroll
+    for (int r = 0; r < TK; ++r) {
+      const bool take = slot[r] >= 0;
+      a.x = take ? a.x + x[r].x : a.x;
+      a.y = take ? a.y + x[r].y : a.y;
+      a.z = take ? a.z + x[r].z : a.z;
+      a.w = take ? a.w + x[r].w : a.w;
+    }
+  } else {
+    for (int32_t r = 0; r < top_k; ++r) {
+      const int32_t slot = inv[t * top_k + r];
+      if (slot < 0) continue;
+      const float4 x = *reinterpret_cast<const float4*>(ys + int64_t(slot) * K + k);
+      a.x += x.x;
+      a.y += x.y;
+      a.z += x.z;
+      a.w += x.w;
+    }
   }
-  const uint4 v = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
-  *reinterpret_cast<uint4*>(out + t * ldo + k) = v;
+  *reinterpret_cast<uint2*>(out + t * ldo + k) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
 }
 
 }  // namespace
@@ -367,9 +387,19 @@ hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t*
   hipLaunchKernelGGL(moe_down_kernel, dim3(uint32_t(gemm::xcd_rows_grid(mt, int32_t(K / 256)))),
                      dim3(gemm::kThreads), 0, stream, hc, hs, int32_t(I), sorted, tiles, mt, topk_w, int32_t(top_k),
                      static_cast<const uint8_t*>(w_down), int32_t(K), alpha_dn, ys);
-  const int64_t items = T * (K / 8);
-  hipLaunchKernelGGL(moe_sum_kernel, dim3(uint32_t((items + 255) / 256)), dim3(256), 0, stream, ys, inv, T,
-                     int32_t(top_k), int32_t(K), static_cast<uint16_t*>(out), ldo);
+  const dim3 sum_grid{uint32_t((T * (K / 4) + 255) / 256)};
+#define NVFP4_SUM(TK)                                                                                            \
+  hipLaunchKernelGGL(moe_sum_kernel<TK>, sum_grid, dim3(256), 0, stream, ys, inv, T, int32_t(top_k), int32_t(K), \
+                     static_cast<uint16_t*>(out), ldo)
+  switch (top_k) {
+    case 1: NVFP4_SUM(1); break;
+    case 2: NVFP4_SUM(2); break;
+    case 4: NVFP4_SUM(4); break;
+    case 6: NVFP4_SUM(6); break;
+    case 8: NVFP4_SUM(8); break;
+    default: NVFP4_SUM(0); break;
+  }
+#undef NVFP4_SUM
   return hipGetLastError();
 }
 
