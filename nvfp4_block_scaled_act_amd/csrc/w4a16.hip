@@ -283,45 +283,59 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
   const int lds_lane = (lane >> 4) * M + min(lane & 15, M - 1);
   const uint8_t* wtile = wt + int64_t(has_tile ? tile : 0) * steps * kUnitBytes;
 
+  // The weight units of the next kSharedDepth steps are in flight while a
+  // step is computed: four named slots, each reloaded (unconditionally,
+  // clamped to the last step) right after the step that consumed it.  Loads
+  // complete in issue order, so the wait for a step's unit leaves the three
+  // younger ones in flight; nothing is copied out of a slot whose load is
+  // outstanding (that would wait for it, and for everything older).
+  auto unit_at = [&](int32_t st) { return load_unit(wtile + int64_t(min(st, steps - 1)) * kUnitBytes, lane); };
   uint4 v[4];
   int32_t dst[4];
   stage_load(a, lda, M, 0, min(kc, steps), tid, v, dst);
-  // weight units of steps 0 and 1 in flight while the first chunk is staged
-  Unit n1 = load_unit(wtile, lane);
-  Unit n2 = steps > 1 ? load_unit(wtile + kUnitBytes, lane) : n1;
+  Unit w0 = unit_at(0), w1 = unit_at(1), w2 = unit_at(2), w3 = unit_at(3);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (dst[i] >= 0) act[dst[i]] = v[i];
   __syncthreads();
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t ch = 0; ch < nch; ++ch) {
-    const int32_t s_begin = ch * kc;
-    const int32_t ns = min(kc, steps - s_begin);
-    const bool more = ch + 1 < nch;
-    if (more) stage_load(a, lda, M, s_begin + kc, min(kc, steps - s_begin - kc), tid, v, dst);
-    const uint4* buf = act + (ch & 1) * chunk_entries;
-    for (int32_t s = 0; s < ns; ++s) {
-      const int32_t gs = s_begin + s;
-      const Unit cur = n1;
-      n1 = n2;
-      if (gs + 2 < steps) n2 = load_unit(wtile + int64_t(gs + 2) * kUnitBytes, lane);
-      const uint4* lds_step = buf + s * 32 * M;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint4 b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = lds_step[(4 * half + i) * 4 * M + lds_lane];
-        mma_half(half == 0 ? cur.c0 : cur.c1, cur.sc, half, b, acc);
-      }
-    }
-    if (more) {
-      uint4* nbuf = act + ((ch + 1) & 1) * chunk_entries;
+  // step gs of chunk ch = gs / kc.  At a chunk's first step the chunk staged
+  // during the previous one is written to its LDS buffer (every wave is past
+  // the chunk before it, which used that buffer) and the next chunk's loads
+  // are issued.
+  auto step = [&](int32_t gs, const Unit& cur) {
+    const int32_t ch = gs / kc, s = gs - ch * kc;
+    if (s == 0 && ch > 0) {
+      uint4* nbuf = act + (ch & 1) * chunk_entries;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (dst[i] >= 0) nbuf[dst[i]] = v[i];
       __syncthreads();
     }
+    if (s == 0 && ch + 1 < nch) stage_load(a, lda, M, gs + kc, min(kc, steps - gs - kc), tid, v, dst);
+    const uint4* lds_step = act + (ch & 1) * chunk_entries + s * 32 * M;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint4 bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bb[i] = lds_step[(4 * half + i) * 4 * M + lds_lane];
+      mma_half(half == 0 ? cur.c0 : cur.c1, cur.sc, half, bb, acc);
+    }
+  };
+  for (int32_t gs = 0; gs < steps; gs += 4) {
+    step(gs, w0);
+    w0 = unit_at(gs + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    if (gs + 1 < steps) step(gs + 1, w1);
+    w1 = unit_at(gs + 5);
+    __builtin_amdgcn_sched_barrier(0);
+    if (gs + 2 < steps) step(gs + 2, w2);
+    w2 = unit_at(gs + 6);
+    __builtin_amdgcn_sched_barrier(0);
+    if (gs + 3 < steps) step(gs + 3, w3);
+    w3 = unit_at(gs + 7);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (has_tile) store_tile(acc, *alpha_p, lane, tile, M, N, out, ldo);
 }
