@@ -288,6 +288,77 @@ def bench_moe(ops, torch, reps=10):
     return dict(T=T, E=E, top_k=top_k, K=K, I=I, layer_us=layer_us, tflops=flops / layer_us / 1e6)
 
 
+def bench_fused_sweep(ops, torch, reps=2):
+    """The large fused-weight linear through the dispatch (nvfp4_linear) at
+    every M of its sweep, over rotated weight copies (cold weights), and the
+    W4A4 route forced at M <= 16 (quantize + GEMM) to show where the routes
+    cross.  Per call: us, route, TB/s (W4A16: algorithmic bytes) or TFLOP/s
+    (W4A4: 2*M*N*K over quantize + GEMM)."""
+    from nvfp4_block_scaled_act_amd import synth
+    from nvfp4_block_scaled_act_amd.lib import ROUTE_W4A16
+
+    fl = synth.FUSED_LARGE
+    N, K, Ms = fl["N"], fl["K"], fl["M"]
+    W = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_W), N, K)
+    a = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_A), max(Ms), K)
+    cal = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_CAL), fl["calib_rows"], K)
+    wd = dev_bf16(torch, W)
+    gw = ops.global_scale(wd)
+    codes, scales = ops.quantize_act(wd, gw)
+    del wd
+    C = max(2, int(np.ceil(COLD_BYTES / (N * K * 9 / 16))))
+    copies = [ops.prepare_weight(codes, scales) for _ in range(C)]
+    del codes, scales
+    ad = dev_bf16(torch, a)
+    ga = ops.global_scale(dev_bf16(torch, cal))
+    a16, a4 = ops.alpha(gw), ops.alpha(gw, ga)
+    ws = torch.empty(ops.linear_workspace_bytes(max(Ms), N, K), dtype=torch.uint8, device="cuda")
+    qc = torch.empty((16, K // 2), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((16, K // 16), dtype=torch.uint8, device="cuda")
+    ops.set_route_m_max(16)
+
+    def timed(fn):
+        for w in copies[:2]:
+            fn(w)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for w in copies:
+                fn(w)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * C)
+
+    rows = []
+    for M in Ms:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        route = [None]
+
+        def disp(w):
+            route[0] = ops.linear(ad[:M], w, ga, a16, a4, out=out, workspace=ws)[1]
+
+        us = timed(disp)
+        r = dict(M=M, route="w4a16" if route[0] == ROUTE_W4A16 else "w4a4", us=round(us, 2))
+        if r["route"] == "w4a16":
+            r["tb_s"] = round(w4a16_bytes(M, N, K) / us / 1e6, 3)
+        else:
+            r["tflops"] = round(2.0 * M * N * K / us / 1e6, 1)
+        if M <= 16:
+            def forced(w):
+                ops.quantize_act(ad[:M], ga, codes=qc[:M], scales=qs[:M])
+                ops.linear_w4a4(qc[:M], qs[:M], w, a4, out=out)
+
+            r["w4a4_forced_us"] = round(timed(forced), 2)
+        rows.append(r)
+        extra = f", W4A4 forced {r['w4a4_forced_us']:.1f} us" if M <= 16 else ""
+        rate = f"{r['tb_s']:.3f} TB/s" if "tb_s" in r else f"{r['tflops']:.1f} TFLOP/s"
+        log(f"[fused_sweep] N={N} K={K} M={M:5d}: {r['route']} {us:9.2f} us ({rate}){extra}")
+    del copies
+    torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(target_s=15.0):
     """The oracle (as it stands) on a bounded sample of the headline workload:
     the W4A16 call N=8704, K=5120, M=16 restricted to its first 512 weight
@@ -321,7 +392,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the W4A16 calls directly (counter runs)")
-    ap.add_argument("--only", choices=["all", "headline", "fused", "w4a4", "moe", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "headline", "fused", "fused_sweep", "w4a4", "moe", "copy"], default="all",
                     help="run one part (for profiler runs); 'copy' times a plain 256 MiB device copy, the "
                          "reference for the HBM byte counters")
     args = ap.parse_args()
@@ -351,6 +422,9 @@ def main():
     if args.only == "moe":
         r5 = bench_moe(ops, torch, reps=args.steps)
         print(json.dumps({"moe": {k: round(v, 3) if isinstance(v, float) else v for k, v in r5.items()}}))
+        return
+    if args.only == "fused_sweep":
+        print(json.dumps({"fused_large_sweep": bench_fused_sweep(ops, torch)}))
         return
     if args.only in ("fused", "w4a4"):
         if args.only == "fused":
@@ -404,6 +478,10 @@ def main():
         res["fused_large_decode"] = {
             "workload": "W4A16 N=62080 K=5120 M in {1,8,16}, cold", "tb_s": round(gbs3 / 1e3, 4),
             "frac_of_hbm_peak": round(gbs3 / HBM_PEAK_GBS, 4), "kernel": "w4a16_shared_kernel", "per_m": r3["rows"]}
+        res["fused_large_sweep"] = {
+            "workload": "dispatched linear N=62080 K=5120 at every M of the sweep (route reported), cold weights; "
+                        "W4A4 forced at M <= 16 for the crossover",
+            "route_m_max": 16, "per_m": bench_fused_sweep(ops, torch)}
         r4 = bench_w4a4(ops, torch)
         res["w4a4_prefill"] = {
             "workload": "W4A4 M=8192 N=8704 K=5120, NVFP4 activations (static global, 512-row calibration)",
