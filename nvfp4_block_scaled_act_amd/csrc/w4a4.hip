@@ -160,9 +160,9 @@ __host__ __device__ inline int32_t sk_owner(int64_t u, int64_t units, int32_t G)
 //    stores (sc0 sc1, written through) and takes an agent-scope release (an
 //    L2 write-back queued behind its own stores), then one atomic swap
 //    raises the flag;
-//  * finish: the flags are taken with compare-and-swap (1 -> 0), and the
-//    partials are read with system-scope loads, which bypass the L1 and the
-//    XCD's L2 and so need no cache-wide invalidate.
+//  * finish: the flags are taken with compare-and-swap (1 -> 0), then every
+//    wave takes an agent-scope acquire (invalidating its L1 and its XCD's
+//    L2) and reads the partials with ordinary loads.
 // Every flag access is a read-modify-write atomic, which the device resolves
 // coherently (a plain load could hit a stale line of a fresh workspace).  The
 // finishing workgroups write their output through as well, so the
@@ -227,6 +227,10 @@ __device__ __forceinline__ void sk_segment(_Float16* __restrict__ lds, const uin
         }
       }
       __syncthreads();  // every flag seen
+      // each wave invalidates its L1 and its XCD's L2 before reading: a clean
+      // but stale copy of a partial (say from the workspace's fill) could
+      // still be cached there, and system-scope loads do not bypass it
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     // own sum plus the partials of workgroups j-1 down to jf (a fixed order),
     // added chunk by chunk as the tile is stored (the adds are unrolled over
@@ -249,7 +253,7 @@ __device__ __forceinline__ void sk_segment(_Float16* __restrict__ lds, const uin
 #pragma unroll
             for (int k = 0; k < kMaxPartials; ++k) {
               const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(
-                  prsrc, voff, (j - 1 - min(k, np - 1)) * int32_t(kPartialBytes), kSysScope);
+                  prsrc, voff, (j - 1 - min(k, np - 1)) * int32_t(kPartialBytes), 0);
               const bool take = k < np;
               v.x = take ? v.x + __uint_as_float(q[0]) : v.x;
               v.y = take ? v.y + __uint_as_float(q[1]) : v.y;

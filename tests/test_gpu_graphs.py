@@ -82,9 +82,15 @@ def test_graph_w4a4_streamk(ops):
     eager = bf16_host(ops.linear_w4a4(ac, as_, w, al, workspace=ws))
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     gr = _capture(torch, lambda: ops.linear_w4a4(ac, as_, w, al, out=out, workspace=ws))
-    # eager calls on the same workspace between replays, too
-    _replays_match(torch, gr, out, eager, lambda: ops.linear_w4a4(ac, as_, w, al, workspace=ws))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def between():
+        # eager calls on the same workspace between replays, and NaN in every
+        # partial slot before each replay (a stale partial would show)
+        ops.linear_w4a4(ac, as_, w, al, workspace=ws)
+        ws[:cus * 256 * 1024].fill_(0xFF)
+
+    _replays_match(torch, gr, out, eager, between)
     assert (ws[cus * 256 * 1024:cus * 256 * 1024 + 4 * cus + 4].cpu().numpy() == 0).all()
 
 

@@ -275,6 +275,19 @@ def test_w4a4_deterministic(ops, orc):
 
 # ------------------------------------------------------- W4A4, stream-K finish
 
+def poisoned_ws(ops, ws=None):
+    """A stream-K workspace whose partial slots hold NaN (flags zero), so a
+    finishing workgroup that read a stale copy of a partial instead of the
+    one just published would produce NaN, not a plausible sum."""
+    import torch
+
+    if ws is None:
+        ws = ops.w4a4_workspace()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ws[:cus * 256 * 1024].fill_(0xFF)
+    return ws
+
+
 def check_ws_clean(ops, ws):
     """After a call the stream-K flags and the timed-out-wait count are zero."""
     import torch
@@ -291,7 +304,7 @@ def test_w4a4_streamk_full_rounds(ops, orc):
     W = synth.normal_bf16(84, N, K)
     a = synth.normal_bf16(85, M, K)
     cal = synth.normal_bf16(86, 64, K)
-    _w4a4_case(ops, orc, W, a, cal, ws=ops.w4a4_workspace())
+    _w4a4_case(ops, orc, W, a, cal, ws=poisoned_ws(ops))
 
 
 def test_w4a4_streamk_small_full(ops, orc):
@@ -300,7 +313,7 @@ def test_w4a4_streamk_small_full(ops, orc):
     W = synth.normal_bf16(87, N, K)
     a = synth.normal_bf16(88, M, K)
     cal = synth.normal_bf16(89, 64, K)
-    _w4a4_case(ops, orc, W, a, cal, ws=ops.w4a4_workspace())
+    _w4a4_case(ops, orc, W, a, cal, ws=poisoned_ws(ops))
 
 
 def test_w4a4_streamk_m4096_sampled(ops, orc):
@@ -313,7 +326,7 @@ def test_w4a4_streamk_m4096_sampled(ops, orc):
     rng = np.random.default_rng(11)
     rows = np.unique(np.concatenate([rng.integers(3072, M, 64), rng.integers(0, 3072, 32), [0, M - 1]]))
     cols = np.unique(np.concatenate([rng.integers(6656, N, 256), rng.integers(0, 6656, 96), [0, N - 1]]))
-    _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols, check_rows=cols, ws=ops.w4a4_workspace())
+    _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols, check_rows=cols, ws=poisoned_ws(ops))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 256), (130, 200, 512), (300, 1000, 1024), (700, 520, 2048)])
@@ -322,7 +335,7 @@ def test_w4a4_streamk_ragged(ops, orc, M, N, K):
     W = synth.normal_bf16(40 + N, N, K)
     a = synth.normal_bf16(50 + M, M, K)
     cal = synth.normal_bf16(60 + M, 64, K)
-    _w4a4_case(ops, orc, W, a, cal, ws=ops.w4a4_workspace())
+    _w4a4_case(ops, orc, W, a, cal, ws=poisoned_ws(ops))
 
 
 def test_w4a4_streamk_reuse_and_deterministic(ops, orc):
@@ -337,9 +350,9 @@ def test_w4a4_streamk_reuse_and_deterministic(ops, orc):
     for M in (300, 1024, 5, 300):
         a = bf16_dev(synth.normal_bf16(73 + M, M, 2048))
         ac, as_ = ops.quantize_act(a, g)
-        o1 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=ws))
+        o1 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=poisoned_ws(ops, ws)))
         check_ws_clean(ops, ws)
-        o2 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=ws))
+        o2 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=poisoned_ws(ops, ws)))
         assert (o1 == o2).all()
         ref = bf16_f64(bf16_host(ops.linear_w4a4(ac, as_, q.w, al)))
         got = bf16_f64(o1)
