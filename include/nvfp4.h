@@ -174,6 +174,9 @@ nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvf
  *                  256-k steps; needs M * min(chunk_steps, K/256) <= 64
  *   schedule 3     split with interleaved steps (wave w takes steps w,
  *                  w + waves, ...); needs ceil(K/256 / ksplit) <= 8
+ *   schedule 4     dot: schedule 3's work split with the products on the
+ *                  VALU (bf16 dot products, activations broadcast across
+ *                  lanes); needs M <= 4 and ceil(K/256 / ksplit) <= 8
  * Other values return INVALID_ARGUMENT.  The result bits depend on (M, N, K)
  * and the schedule. */
 nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w,

@@ -23,8 +23,9 @@ hipError_t launch_retile(const void* codes, const void* scales, int64_t N, int64
 
 // W4A16 skinny kernel: out[M, N] = bf16(alpha * a[M, K] @ dequant(W)^T), M <= 16.
 struct W4A16Config {
-  int schedule;     // 1 = split (one tile per workgroup, K split over its waves), 2 = shared (8 tiles, all of K)
-  int ksplit;       // split: waves per tile, 1..16
+  int schedule;     // 1 = split (one tile per workgroup, K split over its waves), 2 = shared (8 tiles, all of K),
+                    // 3 = split with interleaved steps, 4 = dot (split on the VALU, M <= 4)
+  int ksplit;       // split, dot: waves per tile, 1..16
   int chunk_steps;  // shared: 256-k steps per LDS activation chunk
 };
 W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K);

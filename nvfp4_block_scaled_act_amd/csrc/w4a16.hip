@@ -18,8 +18,8 @@
 //    scale, packed to bf16 -- exact, since every e2m1 * E4M3 product fits bf16.
 //
 // The weight is read once from HBM.  Every 16-row tile needs all M x K
-// activations (M/4.5 times the tile's weight bytes), and there are two
-// schedules for them, both one launch with a fixed fp32 sum order
+// activations (M/4.5 times the tile's weight bytes), and there are three
+// schedules for them, each one launch with a fixed fp32 sum order
 // (deterministic) and no workspace:
 //  * split -- for weights with few row tiles: a workgroup owns one tile and its
 //    `ksplit` waves split K, each reading its own activations through L1/L2;
@@ -35,6 +35,10 @@
 //    per wave) over all of K and streams the activations through LDS in
 //    double-buffered chunks of `kc` steps, so each chunk is read from L2 once
 //    per 8 tiles and from LDS by every wave.
+//  * dot -- up to 4 tokens, the split schedule's work split on the VALU
+//    instead of the MFMA: each lane loads 4 activations per token and step
+//    (no duplicates), the dot-product instruction broadcasts them across the
+//    lane's row, and the dequant is one convert per code pair.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -93,6 +97,13 @@ __device__ __forceinline__ void store_tile(const f32x4_t& acc, float alpha, int 
   }
 }
 
+// The alpha operand lives in device memory (so that a captured call can take a
+// new value).  Its load is issued with a kernel's first weight loads and
+// awaited right after them, where its latency hides under theirs: waiting for
+// it only in the epilogue would add a dependent memory round trip to the end
+// of every (short) decode call.
+__device__ __forceinline__ void settle(float& alpha) { asm volatile("" : "+s"(alpha)); }
+
 // ------------------------------------------------------------------- split
 // Activation operands of the 8 MFMAs of one 256-k step for lane (c, q): token
 // row c's k = 64p + 16q + 8h + (0..7) for MFMA j = 2p + h.
@@ -137,15 +148,15 @@ __device__ __forceinline__ void mma_step_perm(const Unit& u, const StepB& b, int
 
 // Partial tiles of the waves added through LDS in wave order, then stored.
 __device__ __forceinline__ void reduce_store(f32x4_t acc, float* red, int wave, int nwaves, int lane, int32_t tile,
-                                             int32_t M, int32_t N, const float* __restrict__ alpha_p,
-                                             uint16_t* __restrict__ out, int64_t ldo) {
+                                             int32_t M, int32_t N, float alpha, uint16_t* __restrict__ out,
+                                             int64_t ldo) {
   if (nwaves > 1) {
     *reinterpret_cast<f32x4_t*>(&red[(wave * 64 + lane) * 4]) = acc;
     __syncthreads();
     if (wave != 0) return;
     for (int w = 1; w < nwaves; ++w) acc += *reinterpret_cast<const f32x4_t*>(&red[(w * 64 + lane) * 4]);
   }
-  store_tile(acc, *alpha_p, lane, tile, M, N, out, ldo);
+  store_tile(acc, alpha, lane, tile, M, N, out, ldo);
 }
 
 // Split with at most PER steps per wave, fully unrolled: step i+1's weight
@@ -183,8 +194,11 @@ __global__ __launch_bounds__(1024) void w4a16_split_fixed_kernel(
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   Unit w[2];
   StepB b[2];
+  float alpha = *alpha_p;
   w[0] = unit_at(s0);
   b[0] = b_at(s0);
+  __builtin_amdgcn_sched_barrier(0);
+  settle(alpha);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (i + 1 < PER) {
@@ -197,7 +211,7 @@ __global__ __launch_bounds__(1024) void w4a16_split_fixed_kernel(
     else
       mma_step(w[i & 1], b[i & 1], acc, s0 + i * ds < s1);
   }
-  reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha_p, out, ldo);
+  reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha, out, ldo);
 }
 
 // Each wave runs steps [s0, s1) of one tile.  Step s+1's weight unit and
@@ -225,8 +239,11 @@ __global__ __launch_bounds__(1024) void w4a16_split_kernel(
   auto b_at = [&](int32_t st) { return load_b(arow + 256 * int64_t(min(st, s1 - 1)), q); };
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float alpha = *alpha_p;
   Unit wa = unit_at(s0);
   StepB ba = b_at(s0);
+  __builtin_amdgcn_sched_barrier(0);
+  settle(alpha);
   // (the scheduling barriers keep the compiler from sinking the next step's
   // loads below the current step's waits)
   for (int32_t s = s0;; s += 2) {
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(1024) void w4a16_split_kernel(
     if (s + 2 >= s1) break;
   }
 
-  reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha_p, out, ldo);
+  reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha, out, ldo);
 }
 
 // ------------------------------------------------------------------ shared
@@ -292,8 +309,11 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
   auto unit_at = [&](int32_t st) { return load_unit(wtile + int64_t(min(st, steps - 1)) * kUnitBytes, lane); };
   uint4 v[4];
   int32_t dst[4];
+  float alpha = *alpha_p;
   stage_load(a, lda, M, 0, min(kc, steps), tid, v, dst);
   Unit w0 = unit_at(0), w1 = unit_at(1), w2 = unit_at(2), w3 = unit_at(3);
+  __builtin_amdgcn_sched_barrier(0);
+  settle(alpha);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (dst[i] >= 0) act[dst[i]] = v[i];
@@ -337,7 +357,178 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
     w3 = unit_at(gs + 7);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (has_tile) store_tile(acc, *alpha_p, lane, tile, M, N, out, ldo);
+  if (has_tile) store_tile(acc, alpha, lane, tile, M, N, out, ldo);
+}
+
+// --------------------------------------------------------------------- dot
+// A few tokens: the MFMA would spend most of its work on repeated token
+// columns and the split kernel's texture unit on duplicate activation loads
+// (eight 16-byte loads per wave and step whatever M is), so each lane computes
+// plain dot products on the VALU.  Lane
+// (r, q) of a unit holds row r's codes of the 16-k groups 4p + q (p = 0..3);
+// its row of 16 lanes (q) needs the 64 activations k = 64p + 16q + 8h + i
+// (h = 0..1, i = 0..7), and lane n of that row loads 4 of them (p = n / 4,
+// h = (n / 2) % 2, i = 4 (n % 2) + 0..3) with one 8-byte load.  The
+// dot-product instruction reads them from lane 4p + 2h + i / 4 of the row
+// through its DPP row broadcast, so no lane holds a copy of another lane's
+// activations.  The codes are converted to bf16 pairs (exact), each 16-k
+// block's partial dot (fp32) is multiplied by the block scale as it is added
+// to the lane's sum, the 4 lanes of a row are added (q order fixed), then the
+// waves in wave order.
+
+// The 32 products of a unit for one token: part[p] += dot(activation pair
+// broadcast from lane 4p + s / 2 of the row (register x for even s, y for odd
+// s), weight pair s of block p), s = 0..7.  A DPP instruction must not read a
+// VGPR (any operand, the accumulator included) that a VALU instruction wrote
+// in the two instructions before it, so the four blocks' chains are
+// interleaved (each accumulator is read 3 instructions after its write) and a
+// leading s_nop covers the operands written just before the block.
+constexpr int kDotMaxM = 4;
+
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t word) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL));
+}
+
+__device__ __forceinline__ void dot_unit(const uint2& x, const Unit& u, float (&part)[4]) {
+  const uint32_t c[8] = {u.c0.x, u.c0.y, u.c0.z, u.c0.w, u.c1.x, u.c1.y, u.c1.z, u.c1.w};
+  uint32_t w[32];  // w[8p + s]: pair s of block p (s < 4: low code dword, byte s; s >= 4: high dword, byte s - 4)
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    w[8 * pp + 0] = e2m1x2_to_bf16<0>(c[2 * pp]);
+    w[8 * pp + 1] = e2m1x2_to_bf16<1>(c[2 * pp]);
+    w[8 * pp + 2] = e2m1x2_to_bf16<2>(c[2 * pp]);
+    w[8 * pp + 3] = e2m1x2_to_bf16<3>(c[2 * pp]);
+    w[8 * pp + 4] = e2m1x2_to_bf16<0>(c[2 * pp + 1]);
+    w[8 * pp + 5] = e2m1x2_to_bf16<1>(c[2 * pp + 1]);
+    w[8 * pp + 6] = e2m1x2_to_bf16<2>(c[2 * pp + 1]);
+    w[8 * pp + 7] = e2m1x2_to_bf16<3>(c[2 * pp + 1]);
+  }
+  asm volatile(
+  "s_nop 1\n"
+  "v_dot2c_f32_bf16_dpp %0, %4, %6 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %1, %4, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %2, %4, %22 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %3, %4, %30 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %0, %5, %7 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %1, %5, %15 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %2, %5, %23 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %3, %5, %31 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %0, %4, %8 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %1, %4, %16 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %2, %4, %24 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %3, %4, %32 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %0, %5, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %1, %5, %17 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %2, %5, %25 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %3, %5, %33 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %0, %4, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %1, %4, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %2, %4, %26 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %3, %4, %34 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %0, %5, %11 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %1, %5, %19 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %2, %5, %27 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %3, %5, %35 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %0, %4, %12 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %1, %4, %20 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %2, %4, %28 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %3, %4, %36 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %0, %5, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %1, %5, %21 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %2, %5, %29 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+  "v_dot2c_f32_bf16_dpp %3, %5, %37 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      : "+v"(part[0]), "+v"(part[1]), "+v"(part[2]), "+v"(part[3])
+      : "v"(x.x), "v"(x.y), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]),
+        "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]), "v"(w[16]),
+        "v"(w[17]), "v"(w[18]), "v"(w[19]), "v"(w[20]), "v"(w[21]), "v"(w[22]), "v"(w[23]), "v"(w[24]), "v"(w[25]),
+        "v"(w[26]), "v"(w[27]), "v"(w[28]), "v"(w[29]), "v"(w[30]), "v"(w[31]));
+}
+
+// acc[m] += sum over the lane's 64 k of the unit of token m: the 16-k blocks'
+// partial dots times their block scales.
+template <int MT>
+__device__ __forceinline__ void dot_step(const Unit& u, const uint2 (&x)[MT], float (&acc)[MT]) {
+  const float S[4] = {e4m3_to_f32<0>(u.sc), e4m3_to_f32<1>(u.sc), e4m3_to_f32<2>(u.sc), e4m3_to_f32<3>(u.sc)};
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    dot_unit(x[m], u, part);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) acc[m] = __builtin_fmaf(S[pp], part[pp], acc[m]);
+  }
+}
+
+// Wave w takes steps w, w + waves, ... (PER of them; the ones past K are
+// skipped) of the workgroup's tile, with the units and activations of two
+// steps in flight while one is computed.
+template <int PER, int MT>
+__global__ __launch_bounds__(1024) void w4a16_dot_kernel(
+    const uint16_t* __restrict__ a, int64_t lda, int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
+    const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo) {
+  extern __shared__ float dot_red[];  // [waves][MT][16]
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6), nwaves = int(blockDim.x >> 6);
+  const int q = lane >> 4, n = lane & 15;
+  const int32_t tile = int32_t(blockIdx.x), steps = K / 256;
+  const uint8_t* wtile = wt + int64_t(tile) * steps * kUnitBytes;
+  const int koff = 64 * (n >> 2) + 16 * q + 8 * ((n >> 1) & 1) + 4 * (n & 1);
+  const uint16_t* arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) arow[m] = a + int64_t(min(m, M - 1)) * lda + koff;
+  auto unit_at = [&](int32_t st) { return load_unit(wtile + int64_t(min(st, steps - 1)) * kUnitBytes, lane); };
+  auto act_at = [&](int32_t st, uint2 (&x)[MT]) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) x[m] = *reinterpret_cast<const uint2*>(arow[m] + 256 * int64_t(min(st, steps - 1)));
+  };
+
+  float alpha = *alpha_p;
+  Unit w[2];
+  uint2 x[2][MT];
+  act_at(wave, x[0]);
+  w[0] = unit_at(wave);
+  if (PER > 1) {
+    act_at(wave + nwaves, x[1]);
+    w[1] = unit_at(wave + nwaves);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  settle(alpha);
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (wave + i * nwaves < steps) dot_step<MT>(w[i & 1], x[i & 1], acc);
+    if (i + 2 < PER) {
+      act_at(wave + (i + 2) * nwaves, x[i & 1]);
+      w[i & 1] = unit_at(wave + (i + 2) * nwaves);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the row's 4 lanes (q), then the waves in order
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    acc[m] += __shfl_xor(acc[m], 16, 64);
+    acc[m] += __shfl_xor(acc[m], 32, 64);
+  }
+  if (nwaves > 1) {
+    if (q == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) dot_red[(wave * MT + m) * 16 + n] = acc[m];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      acc[m] = dot_red[m * 16 + n];
+      for (int k = 1; k < nwaves; ++k) acc[m] += dot_red[(k * MT + m) * 16 + n];
+    }
+  }
+  const int32_t row = 16 * tile + n;
+  if (q == 0 && row < N) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (m < M) out[int64_t(m) * ldo + row] = __builtin_bit_cast(uint16_t, (__bf16)(acc[m] * alpha));
+  }
 }
 
 std::atomic<int> g_cu_count[64];
@@ -361,6 +552,21 @@ int cu_count() { return device_cu_count(); }
 
 }  // namespace
 
+namespace {
+
+// Steps per wave and waves per workgroup for a requested ksplit (no wave is
+// left without a step).
+struct SplitShape {
+  int64_t per, waves;
+};
+SplitShape split_shape(int64_t ksplit, int64_t steps) {
+  const int64_t ks = std::min<int64_t>(ksplit, steps);
+  const int64_t per = (steps + ks - 1) / ks;
+  return {per, (steps + per - 1) / per};
+}
+
+}  // namespace
+
 W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
   const int64_t steps = K / 256;
   const int64_t tiles = std::max<int64_t>(1, (N + 15) / 16);
@@ -368,6 +574,15 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
   W4A16Config c;
   c.ksplit = 0;
   c.chunk_steps = 0;
+  if (tiles < int64_t(kSharedTiles) * cus * 3 / 2 && (M <= 2 || (M == 3 && tiles * steps >= 20 * cus))) {
+    // dot: waves per tile so the launch gives every CU about 8 waves, and at
+    // most 2 steps per wave while there are at most 2 tiles per CU
+    int64_t ks = std::max<int64_t>((8 * cus + tiles - 1) / tiles, (steps + kSplitMaxPer - 1) / kSplitMaxPer);
+    if (tiles <= 2 * cus) ks = std::max<int64_t>(ks, (steps + 1) / 2);
+    c.schedule = 4;
+    c.ksplit = int(std::min<int64_t>({ks, steps, 16}));
+    return c;
+  }
   if (tiles >= int64_t(kSharedTiles) * cus * 3 / 2) {
     // shared: the largest chunk whose double buffer fits in 64 KiB of LDS
     c.schedule = 2;
@@ -389,6 +604,10 @@ bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K) {
     const int64_t steps = K / 256;
     const int64_t ks = std::min<int64_t>(c.ksplit, steps);
     return c.ksplit >= 1 && c.ksplit <= 16 && (steps + ks - 1) / ks <= kSplitMaxPer;
+  }
+  if (c.schedule == 4) {
+    if (M > kDotMaxM || c.ksplit < 1 || c.ksplit > 16) return false;
+    return split_shape(c.ksplit, K / 256).per <= kSplitMaxPer;
   }
   if (c.schedule == 2) {
     if (c.chunk_steps < 1) return false;
@@ -414,6 +633,33 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
     hipLaunchKernelGGL(w4a16_shared_kernel, dim3(uint32_t(groups)), dim3(64 * kSharedTiles), lds, stream, A, lda,
                        int32_t(M), WT, int32_t(N), int32_t(K), int32_t(kc), alpha, O, ldo);
     return hipGetLastError();
+  }
+  if (cfg.schedule == 4) {
+    const SplitShape sh = split_shape(cfg.ksplit, steps);
+    const size_t lds = size_t(sh.waves) * kDotMaxM * 16 * sizeof(float);
+    const dim3 grid{uint32_t(tiles)}, block{uint32_t(64 * sh.waves)};
+#define NVFP4_DOT_LAUNCH(P, MT)                                                                                  \
+  hipLaunchKernelGGL((w4a16_dot_kernel<P, MT>), grid, block, lds, stream, A, lda, int32_t(M), WT, int32_t(N),    \
+                     int32_t(K), alpha, O, ldo)
+#define NVFP4_DOT(P)                                                                                             \
+  case P:                                                                                                        \
+    if (M == 1) NVFP4_DOT_LAUNCH(P, 1); else if (M == 2) NVFP4_DOT_LAUNCH(P, 2);                                 \
+    else if (M == 3) NVFP4_DOT_LAUNCH(P, 3); else NVFP4_DOT_LAUNCH(P, 4);                                        \
+    return hipGetLastError();
+    switch (sh.per) {
+      NVFP4_DOT(1)
+      NVFP4_DOT(2)
+      NVFP4_DOT(3)
+      NVFP4_DOT(4)
+      NVFP4_DOT(5)
+      NVFP4_DOT(6)
+      NVFP4_DOT(7)
+      NVFP4_DOT(8)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef NVFP4_DOT
+#undef NVFP4_DOT_LAUNCH
   }
   // contiguous runs of steps per wave; no wave is left without a step
   const int64_t ks = std::min<int64_t>(cfg.ksplit, steps);

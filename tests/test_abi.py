@@ -93,7 +93,10 @@ def test_w4a16_validation(nv):
     wz = _w(N=0)
     assert f(A16, 4, 256, C.byref(wz), A16, A16, 1, None) == OK         # N = 0
     g = nv.nvfp4_linear_w4a16_ex
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 4, 1, 1, None) == ARG    # schedule 4
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 5, 1, 1, None) == ARG    # schedule 5
+    assert g(A16, 5, 256, C.byref(w), A16, A16, 64, 4, 1, 0, None) == ARG    # dot: M > 4
+    assert g(A16, 2, 256, C.byref(w), A16, A16, 64, 4, 0, 0, None) == ARG    # dot: ksplit 0
+    assert g(A16, 2, 256, C.byref(w), A16, A16, 64, 4, 17, 0, None) == ARG   # dot: ksplit 17
     assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 0, 0, None) == ARG    # split: ksplit 0
     assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 17, 0, None) == ARG   # split: ksplit 17
     assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 2, 0, 0, None) == ARG    # shared: chunk 0
@@ -103,6 +106,7 @@ def test_w4a16_validation(nv):
     assert g(A16, 4, 256 * 8, C.byref(wl), A16, A16, 64, 3, 0, 0, None) == ARG   # burst: ksplit 0
     wk = _w(N=64, K=256 * 20)
     assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 2, 0, None) == ARG  # burst: 10 steps per wave > 8
+    assert g(A16, 1, 256 * 20, C.byref(wk), A16, A16, 64, 4, 2, 0, None) == ARG  # dot: 10 steps per wave > 8
 
 
 def test_w4a4_ws_validation(nv):

@@ -66,7 +66,7 @@ def test_w4a16_decode_sweep(ops, orc, shape_index):
 
 
 SCHEDULES = ([(1, ks, 0) for ks in (1, 2, 3, 7, 16)] + [(2, 0, kc) for kc in (1, 2, 3, 4, 17)]
-             + [(3, ks, 0) for ks in (1, 3, 7, 16)])
+             + [(3, ks, 0) for ks in (1, 3, 7, 16)] + [(4, ks, 0) for ks in (1, 3, 7, 16)])
 
 
 def _valid(sch, M, K):
@@ -76,6 +76,9 @@ def _valid(sch, M, K):
     if sch[0] == 3:
         ks = min(sch[1], steps)
         return -(-steps // ks) <= 8
+    if sch[0] == 4:  # dot: M <= 4, <= 8 steps per wave
+        ks = min(sch[1], steps)
+        return M <= 4 and -(-steps // ks) <= 8
     return True
 
 
@@ -103,7 +106,8 @@ def test_w4a16_every_schedule(ops, orc):
     ref2, _, sabs2 = orc.linear_w4a16(a2, q2.codes, q2.scales, orc.alpha(q2.g))
     a2d = bf16_dev(a2)
     for M in range(1, 17):
-        for sch, ks, kc in [(0, 0, 0), (1, 2, 0), (2, 0, 1), (2, 0, 4 if M <= 16 else 1)]:
+        dot = [(4, 2, 0), (4, 1, 0)] if M <= 4 else []
+        for sch, ks, kc in [(0, 0, 0), (1, 2, 0), (2, 0, 1), (2, 0, 4 if M <= 16 else 1)] + dot:
             out = ops.linear_w4a16(a2d[:M], q2.w, q2.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
             gemm_check(bf16_host(out), ref2[:M], sabs2[:M])
 
@@ -122,6 +126,10 @@ def test_w4a16_long_k(ops, orc):
             gemm_check(bf16_host(out), ref[:M], sabs[:M])
     out = ops.linear_w4a16(ad[:1], q.w, q.alpha, schedule=2, chunk_steps=64)  # one chunk of 64 steps (M = 1)
     gemm_check(bf16_host(out), ref[:1], sabs[:1])
+    for sch, ks, r in ((4, 16, 0), (4, 9, 0)):  # dot: 72 steps over 15 / 8 waves
+        for M in (1, 2, 3, 4):
+            out = ops.linear_w4a16(ad[:M], q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=r)
+            gemm_check(bf16_host(out), ref[:M], sabs[:M])
 
 
 def test_prepared_layout(ops, orc):
@@ -182,10 +190,10 @@ def test_w4a16_deterministic(ops, orc):
     W = synth.normal_bf16(8, 3584, 5120)
     q = Quantized(ops, orc, W, check_rows=np.arange(0, 3584, 97))
     a = bf16_dev(synth.normal_bf16(9, 16, 5120))
-    for sch, ks, kc in [(0, 0, 0), (1, 7, 0), (2, 0, 4)]:
-        o1 = bf16_host(ops.linear_w4a16(a, q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc))
+    for M, sch, ks, kc in [(16, 0, 0, 0), (16, 1, 7, 0), (16, 2, 0, 4), (4, 0, 0, 0), (4, 4, 7, 0), (1, 0, 0, 0), (2, 4, 7, 0)]:
+        o1 = bf16_host(ops.linear_w4a16(a[:M], q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc))
         for _ in range(3):
-            o2 = ops.linear_w4a16(a, q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
+            o2 = ops.linear_w4a16(a[:M], q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
             assert (bf16_host(o2) == o1).all()
 
 
