@@ -465,7 +465,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic("w4a16_decode_sweep", src16),
-                     "kernel": "w4a16_split_fixed_kernel (every decode shape)", "source_hash": src16},
+                     "kernel": "w4a16_dot_kernel (M <= 2), w4a16_split_fixed_kernel (M >= 4)", "source_hash": src16},
         "per_shape": r16["rows"],
     }
     if args.only == "headline":
