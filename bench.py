@@ -16,6 +16,10 @@ read from DRAM: FreeToken PR #737, Results; FlashInfer PR #4038, cold L2):
   * the C calls of one (shape, M) are captured in a HIP graph and replayed;
     one step = one replay of each graph of the sweep;
   * times come from HIP events recorded on the stream the graphs run on.
+Beside `value`, `read_floor` times a plain streaming read (nvfp4_stream_read:
+one 16-byte nontemporal load per thread, nothing computed) of each call's weight
+bytes over the same copies and graphs: what launching a kernel and reading those
+bytes from cold memory costs at these sizes, the attainable bound for the sweep.
 Algorithmic bytes of one W4A16 call: N*K/2 (codes) + N*K/16 (scales) +
 2*M*K (activations) + 2*M*N (output) + 4 (alpha); of one W4A4 GEMM: 2*M*N*K
 FLOPs; of one quantizer call: M*K*(2 + 1/2 + 1/16) bytes.
@@ -119,6 +123,17 @@ def bench_w4a16(ops, torch, workload, shapes, Ms, steps, warmup, graphs=True):
             e["_g"] = g
         else:
             e["graph"] = (lambda e=e: [ops.linear_w4a16(e["a"], w, e["alpha"], out=e["out"]) for w in e["copies"]])
+    # the read floor: a plain streaming read of each call's weight bytes over
+    # the same copies, captured and replayed the same way (graphs only)
+    floor = {}
+    if graphs:
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for copies, _, _ in keep:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for w in copies:
+                    ops.stream_read(w.data, sink)
+            floor[id(copies)] = g
     torch.cuda.synchronize()
     for _ in range(warmup):
         for e in entries:
@@ -134,22 +149,44 @@ def bench_w4a16(ops, torch, workload, shapes, Ms, steps, warmup, graphs=True):
         torch.cuda.synchronize()
         for i in range(len(entries)):
             per[i] += evs[i][0].elapsed_time(evs[i][1])
-    rows, tot_bytes, tot_ms = [], 0.0, 0.0
+    fper = {}
+    if floor:
+        fev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in floor}
+        fper = {k: 0.0 for k in floor}
+        for g in floor.values():
+            g.replay()
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            for k, g in floor.items():
+                fev[k][0].record()
+                g.replay()
+                fev[k][1].record()
+            torch.cuda.synchronize()
+            for k in floor:
+                fper[k] += fev[k][0].elapsed_time(fev[k][1])
+    rows, tot_bytes, tot_ms, floor_ms = [], 0.0, 0.0, 0.0
     for i, e in enumerate(entries):
         us = per[i] / steps / e["C"] * 1e3
         b = w4a16_bytes(e["M"], e["N"], e["K"])
-        rows.append(dict(N=e["N"], K=e["K"], M=e["M"], us_per_launch=round(us, 3), tb_s=round(b / us / 1e6, 3)))
+        row = dict(N=e["N"], K=e["K"], M=e["M"], us_per_launch=round(us, 3), tb_s=round(b / us / 1e6, 3))
+        extra = ""
+        if fper:
+            fus = fper[id(e["copies"])] / steps / e["C"] * 1e3
+            row["read_floor_us"] = round(fus, 3)
+            floor_ms += fus * e["C"] * steps / 1e3
+            extra = f"  (read floor {fus:5.2f} us)"
+        rows.append(row)
         tot_bytes += b * e["C"] * steps
         tot_ms += per[i]
-        log(f"[{workload}] N={e['N']:5d} K={e['K']:5d} M={e['M']:2d}: {us:7.2f} us/launch  {b / us / 1e6:6.3f} TB/s")
+        log(f"[{workload}] N={e['N']:5d} K={e['K']:5d} M={e['M']:2d}: {us:7.2f} us/launch  {b / us / 1e6:6.3f} TB/s{extra}")
     launches = sum(e["C"] for e in entries)
     for e in entries:
         e.pop("graph")
         e.pop("_g", None)
-    del keep
+    del keep, floor
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    return dict(rows=rows, bytes=tot_bytes, kernel_ms=tot_ms, launches_per_step=launches,
+    return dict(rows=rows, bytes=tot_bytes, kernel_ms=tot_ms, floor_ms=floor_ms, launches_per_step=launches,
                 weight_gb=sum(N * K * 9 / 16 * max(2, int(np.ceil(COLD_BYTES / (N * K * 9 / 16)))) for N, K in shapes) / 1e9)
 
 
@@ -468,8 +505,15 @@ def main():
                      "kernel": "w4a16_dot_kernel (M <= 2), w4a16_split_fixed_kernel (M >= 4)", "source_hash": src16},
         "per_shape": r16["rows"],
     }
+    if r16["floor_ms"] > 0:
+        floor_gbs = r16["bytes"] / (r16["floor_ms"] * 1e-3) / 1e9
+        res["read_floor"] = {
+            "what": "nvfp4_stream_read of each call's weight bytes (one 16-byte nontemporal load per thread, no "
+                    "compute) over the same copies, graphs and order: the launch plus the cold read at these sizes",
+            "tb_s": round(floor_gbs / 1e3, 4), "frac_of_hbm_peak": round(floor_gbs / HBM_PEAK_GBS, 4),
+            "value_over_floor": round(achieved_gbs / floor_gbs, 4)}
     if args.only == "headline":
-        print(json.dumps({"value_tb_s": res["value"], "per_shape": res["per_shape"]}))
+        print(json.dumps({"value_tb_s": res["value"], "read_floor": res.get("read_floor"), "per_shape": res["per_shape"]}))
         return
     if args.only == "all":
         fl = synth.FUSED_LARGE

@@ -316,6 +316,22 @@ nvfp4_status nvfp4_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t
                             const float* alpha_dn, void* out, int64_t ldo, void* ws, size_t ws_bytes,
                             float* h_amax, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * nvfp4_stream_read -- a measurement aid, not part of the NVFP4 method: reads
+ * `bytes` of device memory once (one 16-byte nontemporal load per thread, the
+ * way the W4A16 kernels read their weight units) and computes nothing from the
+ * data, except that a 4-byte value is written to *sink in the rare case the
+ * XOR of a 16-byte piece equals a fixed constant.  Timed over the same buffers
+ * and launch sequence as a set of W4A16 calls, it measures what launching a
+ * kernel and reading those bytes from cold memory costs at that size.
+ *   src    device pointer, 16-byte aligned
+ *   bytes  a multiple of 16 (0: no launch)
+ *   sink   device uint32 (4-byte aligned), owned by the caller
+ * Errors: INVALID_ARGUMENT (null src or sink with bytes > 0), INVALID_SHAPE
+ * (bytes % 16), ALIGNMENT, HIP.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -334,4 +334,13 @@ nvfp4_status nvfp4_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t
                                            g1, g2, alpha_gu, alpha_dn, out, ldo, ws, h_amax, stream));
 }
 
+nvfp4_status nvfp4_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes == 0) return NVFP4_OK;
+  if (!src || !sink) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (bytes % 16 != 0 || bytes > size_t(INT64_MAX)) return NVFP4_ERR_INVALID_SHAPE;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return NVFP4_ERR_ALIGNMENT;
+  if (bytes / 16 > size_t(0xffffff00u)) return NVFP4_ERR_UNSUPPORTED;  // 32-bit dispatch size in threads
+  return hip_status(nvfp4::launch_stream_read(src, int64_t(bytes), sink, stream));
+}
+
 }  // extern "C"

@@ -43,6 +43,9 @@ int64_t w4a4_workspace_bytes();
 hipError_t launch_w4a4_sk(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
                           int64_t K, const float* alpha, void* out, int64_t ldo, void* ws, hipStream_t stream);
 
+// Streaming-read diagnostic: reads `bytes` (a multiple of 16) once.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // NVFP4 MoE expert layer (W4A4 gate_up with SiLU gate and NVFP4 re-quantization,
 // W4A4 down with routing weights, fp32 route sum in a fixed order).  The workspace holds,
 // at the offsets moe_layout gives (256-byte aligned parts):

@@ -144,6 +144,17 @@ def linear_w4a16(a: torch.Tensor, w: Weight, alpha_: torch.Tensor, out: torch.Te
     return out
 
 
+def stream_read(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None) -> None:
+    """Measurement aid: read the first nbytes (default: all) of src once, as
+    the W4A16 kernels read weights, computing nothing (see nvfp4_stream_read)."""
+    if not src.is_cuda or not sink.is_cuda or sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ValueError("src must be a CUDA tensor and sink a CUDA int32 tensor")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size():
+        raise ValueError("nbytes beyond src")
+    _L.check("nvfp4_stream_read", _L.load().nvfp4_stream_read(_ptr(src), n, _ptr(sink), _stream()))
+
+
 def w4a4_workspace(device=None) -> torch.Tensor:
     """A zero-filled workspace for linear_w4a4(..., workspace=...) (stream-K
     finish of the last round of tiles); every call leaves it zero-filled."""

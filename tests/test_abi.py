@@ -224,3 +224,14 @@ def test_moe_validation(nv):
     assert call(ws_bytes=need - 1) == WS
     assert call(ws=None) == WS
     assert call(x=None, T=0, ids=None, w=None, out=None, ws=None, ws_bytes=0) == OK   # empty batch
+
+
+def test_stream_read_validation(nv):
+    f = nv.nvfp4_stream_read
+    assert f(None, 0, None, None) == OK              # nothing to read
+    assert f(None, 16, A16, None) == ARG             # null source
+    assert f(A16, 16, None, None) == ARG             # null sink
+    assert f(A16, 24, A16, None) == SHAPE            # bytes % 16
+    assert f(A16 + 8, 16, A16, None) == ALIGN        # source alignment
+    assert f(A16, 16, A16 + 2, None) == ALIGN        # sink alignment
+

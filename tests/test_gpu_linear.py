@@ -394,3 +394,32 @@ def test_dispatch_routes_and_numerics(ops, orc):
     # no activation global: always W4A16
     out, route = ops.linear(ad[:8], q.w, None, a16, None)
     assert route == 0
+
+
+# ------------------------------------------------------ read diagnostic
+
+def test_stream_read_reads_every_piece(ops):
+    """The streaming-read diagnostic loads every 16-byte piece: a piece whose
+    dwords XOR to the kernel's constant, placed anywhere (the first, a middle
+    and the last piece), is seen; a buffer without one leaves the sink alone.
+    The buffer is left unchanged."""
+    import torch
+
+    n = 1 << 20  # bytes: 65536 pieces, 256 workgroups
+    for where in (None, 0, 12345, n // 16 - 1):
+        buf = torch.zeros(n // 4, dtype=torch.int32, device="cuda")
+        if where is not None:
+            buf[4 * where] = np.int32(np.uint32(0x6A09E667).view(np.int32))
+        before = buf.clone()
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ops.stream_read(buf, sink)
+        torch.cuda.synchronize()
+        got = int(np.int32(sink.item()).view(np.uint32))
+        assert got == (0 if where is None else 0x6A09E667), where
+        assert torch.equal(buf, before)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    buf = torch.zeros(64, dtype=torch.int32, device="cuda")
+    buf[60] = np.int32(np.uint32(0x6A09E667).view(np.int32))
+    ops.stream_read(buf, sink, nbytes=224)  # the last piece is past nbytes
+    torch.cuda.synchronize()
+    assert sink.item() == 0
