@@ -173,7 +173,10 @@ nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvf
  *                  activations streamed through LDS in chunks of chunk_steps
  *                  256-k steps; needs M * min(chunk_steps, K/256) <= 64
  *   schedule 3     split with interleaved steps (wave w takes steps w,
- *                  w + waves, ...); needs ceil(K/256 / ksplit) <= 8
+ *                  w + waves, ...); needs ceil(K/256 / ksplit) <= 8.  Here
+ *                  chunk_steps is the tiles per workgroup: 0 or 1, or 2
+ *                  (each step's activation operands serve both tiles; at
+ *                  most 8 waves)
  *   schedule 4     dot: schedule 3's work split with the products on the
  *                  VALU (bf16 dot products, activations broadcast across
  *                  lanes); needs M <= 4 and ceil(K/256 / ksplit) <= 8

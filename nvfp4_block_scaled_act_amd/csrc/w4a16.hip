@@ -169,16 +169,39 @@ __device__ __forceinline__ void reduce_store(f32x4_t acc, float* red, int wave, 
 // activation steps at a time and share them in the L1 cache.
 constexpr int kSplitMaxPer = 8;
 
-template <int PER, bool INTERLEAVE, bool PERM>
-__global__ __launch_bounds__(1024) void w4a16_split_fixed_kernel(
+// R tiles per workgroup (R = 2 where a CU would otherwise hold two or more
+// one-tile workgroups): each step's activation operands are loaded (and
+// permuted) once and serve the R tiles' weight units.
+template <int R>
+__device__ __forceinline__ void reduce_store_tiles(const f32x4_t (&acc)[R], float* red, int wave, int nwaves, int lane,
+                                                   int32_t tile0, int32_t tiles, int32_t M, int32_t N, float alpha,
+                                                   uint16_t* __restrict__ out, int64_t ldo) {
+  if (nwaves == 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (tile0 + r < tiles) store_tile(acc[r], alpha, lane, tile0 + r, M, N, out, ldo);
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) *reinterpret_cast<f32x4_t*>(&red[((wave * R + r) * 64 + lane) * 4]) = acc[r];
+  __syncthreads();
+  if (wave >= R || tile0 + wave >= tiles) return;  // nwaves >= 2 >= R: wave r adds up tile r
+  f32x4_t sum = *reinterpret_cast<const f32x4_t*>(&red[(wave * 64 + lane) * 4]);
+  for (int w = 1; w < nwaves; ++w) sum += *reinterpret_cast<const f32x4_t*>(&red[((w * R + wave) * 64 + lane) * 4]);
+  store_tile(sum, alpha, lane, tile0 + wave, M, N, out, ldo);
+}
+
+template <int PER, bool INTERLEAVE, bool PERM, int R>
+__global__ __launch_bounds__(R == 1 ? 1024 : 512) void w4a16_split_fixed_kernel(
     const uint16_t* __restrict__ a, int64_t lda, int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
     int32_t steps_per_wave, const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo) {
-  extern __shared__ float red[];  // [waves][64][4]
+  extern __shared__ float red[];  // [waves][R][64][4]
   const int lane = int(threadIdx.x & 63);
   const int wave = int(threadIdx.x >> 6);
   const int nwaves = int(blockDim.x >> 6);
   const int q = lane >> 4;
-  const int32_t tile = int32_t(blockIdx.x);
+  const int32_t tiles = (N + 15) / 16;
+  const int32_t tile0 = int32_t(blockIdx.x) * R;
   const int32_t steps = K / 256;
   const int32_t s0 = INTERLEAVE ? wave : wave * steps_per_wave;
   const int32_t ds = INTERLEAVE ? nwaves : 1;
@@ -187,31 +210,54 @@ __global__ __launch_bounds__(1024) void w4a16_split_fixed_kernel(
   const int lrow = PERM ? (lane >> 2) : (lane & 15), lq = PERM ? (lane & 3) : q;
   const int src_byte = 4 * (4 * (lane & 15) + q);
   const uint16_t* arow = a + int64_t(min(lrow, M - 1)) * lda;
-  const uint8_t* wtile = wt + int64_t(tile) * steps * kUnitBytes;
-  auto unit_at = [&](int32_t st) { return load_unit(wtile + int64_t(min(st, steps - 1)) * kUnitBytes, lane); };
+  // tiles past the last re-read the last tile; their results are not stored
+  auto unit_at = [&](int r, int32_t st) {
+    const int32_t t = min(tile0 + r, tiles - 1);
+    return load_unit(wt + (int64_t(t) * steps + min(st, steps - 1)) * kUnitBytes, lane);
+  };
   auto b_at = [&](int32_t st) { return load_b(arow + 256 * int64_t(min(st, steps - 1)), lq); };
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  Unit w[2];
+  f32x4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Unit w[2][R];
   StepB b[2];
   float alpha = *alpha_p;
-  w[0] = unit_at(s0);
+#pragma unroll
+  for (int r = 0; r < R; ++r) w[0][r] = unit_at(r, s0);
   b[0] = b_at(s0);
   __builtin_amdgcn_sched_barrier(0);
   settle(alpha);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (i + 1 < PER) {
-      w[(i + 1) & 1] = unit_at(s0 + (i + 1) * ds);
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[(i + 1) & 1][r] = unit_at(r, s0 + (i + 1) * ds);
       b[(i + 1) & 1] = b_at(s0 + (i + 1) * ds);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (PERM)
-      mma_step_perm(w[i & 1], b[i & 1], src_byte, acc, s0 + i * ds < s1);
-    else
-      mma_step(w[i & 1], b[i & 1], acc, s0 + i * ds < s1);
+    const bool live = s0 + i * ds < s1;
+    if (R == 1) {
+      if (PERM)
+        mma_step_perm(w[i & 1][0], b[i & 1], src_byte, acc[0], live);
+      else
+        mma_step(w[i & 1][0], b[i & 1], acc[0], live);
+    } else {
+      const StepB& bs = b[i & 1];
+      uint4 b0[4], b1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b0[j] = PERM ? to_mfma_lane(bs.v[j], src_byte) : bs.v[j];
+        b1[j] = PERM ? to_mfma_lane(bs.v[4 + j], src_byte) : bs.v[4 + j];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        mma_half(w[i & 1][r].c0, w[i & 1][r].sc, 0, b0, acc[r], live);
+        mma_half(w[i & 1][r].c1, w[i & 1][r].sc, 1, b1, acc[r], live);
+      }
+    }
   }
-  reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha, out, ldo);
+  reduce_store_tiles<R>(acc, red, wave, nwaves, lane, tile0, tiles, M, N, alpha, out, ldo);
 }
 
 // Each wave runs steps [s0, s1) of one tile.  Step s+1's weight unit and
@@ -589,11 +635,20 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
     c.chunk_steps = int(std::max<int64_t>(1, std::min<int64_t>(steps, 64 / std::max<int64_t>(1, M))));
   } else {
     // split: waves per tile so the launch gives every CU about 8 waves;
-    // interleaved steps while a wave has at most kSplitMaxPer of them
+    // interleaved steps while a wave has at most kSplitMaxPer of them.  With
+    // between one and two tiles per CU, two tiles per workgroup on 4 waves
+    // (each step's activation operands serve both; measured 4-20 % faster at
+    // 320 tiles, slower at 224 and within noise at 544)
     const int64_t want = (8 * cus + tiles - 1) / tiles;
     c.ksplit = int(std::max<int64_t>(1, std::min<int64_t>({want, steps, 16})));
     const int64_t ks = std::min<int64_t>(c.ksplit, steps);
     c.schedule = (steps + ks - 1) / ks <= kSplitMaxPer ? 3 : 1;
+    if (c.schedule == 3 && tiles > cus && tiles <= 2 * cus) {
+      W4A16Config two = c;
+      two.chunk_steps = 2;
+      two.ksplit = int(std::max<int64_t>(std::min<int64_t>(4, steps), (steps + kSplitMaxPer - 1) / kSplitMaxPer));
+      if (w4a16_config_valid(two, M, K)) c = two;
+    }
   }
   return c;
 }
@@ -601,9 +656,11 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
 bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K) {
   if (c.schedule == 1) return c.ksplit >= 1 && c.ksplit <= 16;
   if (c.schedule == 3) {
+    // chunk_steps: tiles per workgroup (0 or 1: one; 2: two, at most 8 waves)
     const int64_t steps = K / 256;
-    const int64_t ks = std::min<int64_t>(c.ksplit, steps);
-    return c.ksplit >= 1 && c.ksplit <= 16 && (steps + ks - 1) / ks <= kSplitMaxPer;
+    if (c.ksplit < 1 || c.ksplit > 16 || c.chunk_steps < 0 || c.chunk_steps > 2) return false;
+    const SplitShape sh = split_shape(c.ksplit, steps);
+    return sh.per <= kSplitMaxPer && (c.chunk_steps < 2 || sh.waves <= 8);
   }
   if (c.schedule == 4) {
     if (M > kDotMaxM || c.ksplit < 1 || c.ksplit > 16) return false;
@@ -665,19 +722,22 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
   const int64_t ks = std::min<int64_t>(cfg.ksplit, steps);
   const int64_t per = (steps + ks - 1) / ks;
   const int waves = int((steps + per - 1) / per);
-  const size_t lds = waves > 1 ? size_t(waves) * 64 * 4 * sizeof(float) : 0;
-  const dim3 grid{uint32_t(tiles)}, block{uint32_t(64 * waves)};
+  const int R = cfg.schedule == 3 && cfg.chunk_steps == 2 ? 2 : 1;  // tiles per workgroup
+  const size_t lds = waves > 1 ? size_t(waves) * R * 64 * 4 * sizeof(float) : 0;
+  const dim3 grid{uint32_t((tiles + R - 1) / R)}, block{uint32_t(64 * waves)};
   // permuted activation loads once several token rows share a load group
   const bool perm = M > 4;
-#define NVFP4_SPLIT_LAUNCH(P, IL, PM)                                                                           \
-  hipLaunchKernelGGL((w4a16_split_fixed_kernel<P, IL, PM>), grid, block, lds, stream, A, lda, int32_t(M), WT,   \
-                     int32_t(N), int32_t(K), int32_t(per), alpha, O, ldo)
+#define NVFP4_SPLIT_LAUNCH(P, IL, PM, RR)                                                                       \
+  hipLaunchKernelGGL((w4a16_split_fixed_kernel<P, IL, PM, RR>), grid, block, lds, stream, A, lda, int32_t(M),   \
+                     WT, int32_t(N), int32_t(K), int32_t(per), alpha, O, ldo)
 #define NVFP4_SPLIT_FIXED(P)                                                                                    \
   case P:                                                                                                       \
-    if (cfg.schedule == 3) {                                                                                    \
-      if (perm) NVFP4_SPLIT_LAUNCH(P, true, true); else NVFP4_SPLIT_LAUNCH(P, true, false);                     \
+    if (cfg.schedule == 3 && R == 2) {                                                                          \
+      if (perm) NVFP4_SPLIT_LAUNCH(P, true, true, 2); else NVFP4_SPLIT_LAUNCH(P, true, false, 2);               \
+    } else if (cfg.schedule == 3) {                                                                             \
+      if (perm) NVFP4_SPLIT_LAUNCH(P, true, true, 1); else NVFP4_SPLIT_LAUNCH(P, true, false, 1);               \
     } else {                                                                                                    \
-      if (perm) NVFP4_SPLIT_LAUNCH(P, false, true); else NVFP4_SPLIT_LAUNCH(P, false, false);                   \
+      if (perm) NVFP4_SPLIT_LAUNCH(P, false, true, 1); else NVFP4_SPLIT_LAUNCH(P, false, false, 1);             \
     }                                                                                                           \
     return hipGetLastError();
   switch (per) {

@@ -129,7 +129,8 @@ def linear_w4a16(a: torch.Tensor, w: Weight, alpha_: torch.Tensor, out: torch.Te
                  schedule: int = 0, ksplit: int = 0, chunk_steps: int = 0) -> torch.Tensor:
     """W4A16 linear; schedule 0 picks the default schedule for (M, N, K)
     (1 = split with ksplit waves per tile, 2 = shared with LDS chunks of
-    chunk_steps steps, 3 = split with interleaved steps, 4 = dot: split on
+    chunk_steps steps, 3 = split with interleaved steps and chunk_steps (1 or
+    2) tiles per workgroup, 4 = dot: split on
     the VALU, M <= 4)."""
     _need(a, torch.bfloat16, "a")
     _scalar(alpha_, "alpha")

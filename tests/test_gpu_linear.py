@@ -66,16 +66,18 @@ def test_w4a16_decode_sweep(ops, orc, shape_index):
 
 
 SCHEDULES = ([(1, ks, 0) for ks in (1, 2, 3, 7, 16)] + [(2, 0, kc) for kc in (1, 2, 3, 4, 17)]
-             + [(3, ks, 0) for ks in (1, 3, 7, 16)] + [(4, ks, 0) for ks in (1, 3, 7, 16)])
+             + [(3, ks, 0) for ks in (1, 3, 7, 16)] + [(3, ks, 2) for ks in (1, 3, 7, 8)]
+             + [(4, ks, 0) for ks in (1, 3, 7, 16)])
 
 
 def _valid(sch, M, K):
     steps = K // 256
     if sch[0] == 2:
         return M * min(sch[2], steps) <= 64
-    if sch[0] == 3:
+    if sch[0] == 3:  # chunk_steps 2: two tiles per workgroup, at most 8 waves
         ks = min(sch[1], steps)
-        return -(-steps // ks) <= 8
+        per = -(-steps // ks)
+        return per <= 8 and (sch[2] < 2 or -(-steps // per) <= 8)
     if sch[0] == 4:  # dot: M <= 4, <= 8 steps per wave
         ks = min(sch[1], steps)
         return M <= 4 and -(-steps // ks) <= 8
@@ -106,7 +108,7 @@ def test_w4a16_every_schedule(ops, orc):
     ref2, _, sabs2 = orc.linear_w4a16(a2, q2.codes, q2.scales, orc.alpha(q2.g))
     a2d = bf16_dev(a2)
     for M in range(1, 17):
-        dot = [(4, 2, 0), (4, 1, 0)] if M <= 4 else []
+        dot = ([(4, 2, 0), (4, 1, 0)] if M <= 4 else []) + [(3, 2, 2)]
         for sch, ks, kc in [(0, 0, 0), (1, 2, 0), (2, 0, 1), (2, 0, 4 if M <= 16 else 1)] + dot:
             out = ops.linear_w4a16(a2d[:M], q2.w, q2.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
             gemm_check(bf16_host(out), ref2[:M], sabs2[:M])
@@ -190,7 +192,7 @@ def test_w4a16_deterministic(ops, orc):
     W = synth.normal_bf16(8, 3584, 5120)
     q = Quantized(ops, orc, W, check_rows=np.arange(0, 3584, 97))
     a = bf16_dev(synth.normal_bf16(9, 16, 5120))
-    for M, sch, ks, kc in [(16, 0, 0, 0), (16, 1, 7, 0), (16, 2, 0, 4), (4, 0, 0, 0), (4, 4, 7, 0), (1, 0, 0, 0), (2, 4, 7, 0)]:
+    for M, sch, ks, kc in [(16, 0, 0, 0), (16, 1, 7, 0), (16, 2, 0, 4), (4, 0, 0, 0), (4, 4, 7, 0), (1, 0, 0, 0), (2, 4, 7, 0), (16, 3, 4, 2), (8, 3, 7, 2)]:
         o1 = bf16_host(ops.linear_w4a16(a[:M], q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc))
         for _ in range(3):
             o2 = ops.linear_w4a16(a[:M], q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
