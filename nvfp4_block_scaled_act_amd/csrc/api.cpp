@@ -100,7 +100,7 @@ nvfp4_status nvfp4_quantize_act(const void* a, int64_t M, int64_t K, int64_t lda
   if (st != NVFP4_OK) return st;
   if (!aligned16(codes)) return NVFP4_ERR_ALIGNMENT;
   if (M * (K / 16) > kInt32Max) return NVFP4_ERR_INVALID_SHAPE;
-  if ((M + 3) / 4 > 65535) return NVFP4_ERR_UNSUPPORTED;  // grid.y limit of the row mapping
+  if ((M + 3) / 4 > 65535) return NVFP4_ERR_UNSUPPORTED;  // row mapping (grid.y), with margin
   if (M == 0) return NVFP4_OK;
   return hip_status(nvfp4::launch_quantize(a, M, K, lda, g, codes, scales, stream));
 }

@@ -12,7 +12,7 @@
 // Both roundings decide on the exact real values amax*g/6 and |x|*g/S.
 //
 // Mapping: one lane per 16-element block; a wave covers 64 consecutive blocks
-// of one row (2 KB of contiguous bf16 through dwordx4 loads), a workgroup four
+// (2 KB of contiguous bf16 through dwordx4 loads) of 4 rows, a workgroup 16
 // rows.  The block max is an integer max over bf16 magnitude bits.
 //
 // Rounding of the codes: the fast path forms w = x * fl(g/S) and lets the
@@ -36,27 +36,49 @@ __device__ __forceinline__ uint32_t cvt_pair(uint32_t acc, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, a, b, 1.0f, SEL);
 }
 
-__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ a, int64_t lda,
-                                                       int32_t rows, int32_t blocks_per_row,
-                                                       const float* __restrict__ g_ptr,
-                                                       uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
-  const int32_t j = int32_t(blockIdx.x) * 64 + int32_t(threadIdx.x & 63);
-  const int32_t row = int32_t(blockIdx.y) * 4 + int32_t(threadIdx.x >> 6);
-  if (j >= blocks_per_row || row >= rows) return;
-  const uint16_t* src = a + int64_t(row) * lda + int64_t(j) * 16;
-  const uint4 v0 = ld16_nt(src);
-  const uint4 v1 = ld16_nt(src + 8);
-  const float g = *g_ptr;
-  const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+// Per-call tables, indexed by the scale byte s = 0..126, built once per
+// workgroup in LDS (exact: the same operations the per-block code would do):
+//   val[s]  = E4M3 value of s
+//   gs[s]   = fl(g / val[s]) (0 for s = 0)
+//   mid6[s] = 3 * (val[s-1] + val[s]) = 6 x the midpoint below s (s >= 1)
+struct ScaleTables {
+  float val[128], gs[128], mid6[128];
+};
 
+// The E4M3 byte nearest to the exact amax*g/6: the same decision as
+// scale_byte(), with the values and midpoints read from the tables.
+__device__ __forceinline__ uint32_t scale_byte_lut(float amax, float g, const ScaleTables& T) {
+  const float t = amax * g * (1.0f / 6.0f);
+  uint32_t s;
+  if (!(t < 464.0f)) {
+    s = 126;
+  } else if (t < 0x1p-6f) {
+    s = uint32_t(__builtin_rintf(t * 512.0f));  // subnormal range, 0..8
+  } else {
+    uint32_t u = __float_as_uint(t);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the fp32 mantissa to 3 bits
+    s = min(((u >> 23) - 120u) * 8u + ((u >> 20) & 7u), 126u);
+  }
+  if (s > 0) {
+    const float d = __builtin_fmaf(amax, g, -T.mid6[s]);
+    if (d < 0.0f || (d == 0.0f && ((s - 1) & 1u) == 0)) s -= 1;
+  }
+  if (s < 126) {
+    const float d = __builtin_fmaf(amax, g, -T.mid6[s + 1]);
+    if (d > 0.0f || (d == 0.0f && ((s + 1) & 1u) == 0)) s += 1;
+  }
+  return s;
+}
+
+// Codes and scale of one 16-element block (eight bf16 pairs in d).
+__device__ __forceinline__ void quantize_block(const uint32_t (&d)[8], float g, const ScaleTables& T, uint32_t& c0,
+                                               uint32_t& c1, uint32_t& s) {
   uint32_t mbits = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) mbits = max(mbits, max(d[i] & 0x7FFFu, (d[i] >> 16) & 0x7FFFu));
   const float amax = bf16_bits_to_f32(mbits);
-  const uint32_t s = scale_byte(amax, g);
-  const float S = e4m3_pos_value(s);
-  const float G = (s == 0) ? 0.0f : g / S;
+  s = scale_byte_lut(amax, g, T);
+  const float G = T.gs[s];
 
   float x[16];
 #pragma unroll
@@ -64,14 +86,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     x[2 * i] = __uint_as_float(d[i] << 16);
     x[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
   }
-  uint32_t c0 = 0, c1 = 0;
-  bool near = false;
+  c0 = 0;
+  c1 = 0;
+  // near_threshold() for all 16 at once: (bits + 4) << 11 keeps the low 21
+  // bits plus 4, scaled to the top of the word; w is within 4 ulps of a value
+  // whose low 21 bits are zero iff that is below 9 << 11
   float w[16];
+  uint32_t dmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     w[i] = x[i] * G;
-    near |= near_threshold(w[i]);
+    dmin = min(dmin, (__float_as_uint(w[i]) << 11) + (4u << 11));
   }
+  const bool near = dmin < (9u << 11);
   c0 = cvt_pair<0>(c0, w[0], w[1]);
   c0 = cvt_pair<1>(c0, w[2], w[3]);
   c0 = cvt_pair<2>(c0, w[4], w[5]);
@@ -82,6 +109,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   c1 = cvt_pair<3>(c1, w[14], w[15]);
 
   if (near && s != 0) {
+    const float S = T.val[s];
     c0 = 0;
     c1 = 0;
 #pragma unroll
@@ -90,10 +118,53 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
       c1 |= exact_code(x[8 + i], g, S) << (4 * i);
     }
   }
+}
+
+// A wave takes kRowsPerWave rows of one 64-block column range; all their
+// loads are issued before the tables are built and the first block is
+// computed (rows past the last re-read it and are not stored).
+constexpr int kRowsPerWave = 4;
+
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ a, int64_t lda,
+                                                       int32_t rows, int32_t blocks_per_row,
+                                                       const float* __restrict__ g_ptr,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  __shared__ ScaleTables T;
+  const int32_t j = int32_t(blockIdx.x) * 64 + int32_t(threadIdx.x & 63);
+  const int32_t row0 = (int32_t(blockIdx.y) * 4 + int32_t(threadIdx.x >> 6)) * kRowsPerWave;
+  const bool active = j < blocks_per_row && row0 < rows;
+  uint4 v[kRowsPerWave][2];
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      const uint16_t* src = a + int64_t(min(row0 + r, rows - 1)) * lda + int64_t(j) * 16;
+      v[r][0] = ld16_nt(src);
+      v[r][1] = ld16_nt(src + 8);
+    }
+  }
+  const float g = *g_ptr;
+  if (threadIdx.x < 128) {
+    const uint32_t sb = min(uint32_t(threadIdx.x), 126u);
+    const float val = e4m3_pos_value(sb);
+    T.val[threadIdx.x] = val;
+    T.gs[threadIdx.x] = sb == 0 ? 0.0f : g / val;
+    T.mid6[threadIdx.x] = sb == 0 ? 0.0f : 3.0f * (e4m3_pos_value(sb - 1) + val);
+  }
+  __syncthreads();
+  if (!active) return;
   const int32_t half_k = blocks_per_row * 8;
-  uint2* dst = reinterpret_cast<uint2*>(codes + int64_t(row) * half_k + int64_t(j) * 8);
-  *dst = make_uint2(c0, c1);
-  scales[int64_t(row) * blocks_per_row + j] = uint8_t(s);
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const uint32_t d[8] = {v[r][0].x, v[r][0].y, v[r][0].z, v[r][0].w, v[r][1].x, v[r][1].y, v[r][1].z, v[r][1].w};
+    uint32_t c0, c1, s;
+    quantize_block(d, g, T, c0, c1, s);
+    const int32_t row = row0 + r;
+    if (row < rows) {
+      *reinterpret_cast<uint2*>(codes + int64_t(row) * half_k + int64_t(j) * 8) = make_uint2(c0, c1);
+      scales[int64_t(row) * blocks_per_row + j] = uint8_t(s);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- calibration
@@ -137,7 +208,7 @@ hipError_t launch_quantize(const void* a, int64_t M, int64_t K, int64_t lda, con
                            void* scales, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int32_t bpr = int32_t(K / 16);
-  dim3 grid((bpr + 63) / 64, uint32_t((M + 3) / 4));
+  dim3 grid((bpr + 63) / 64, uint32_t((M + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave)));
   hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a), lda,
                      int32_t(M), bpr, g, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales));
   return hipGetLastError();
