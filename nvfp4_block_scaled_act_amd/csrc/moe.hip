@@ -198,7 +198,7 @@ __device__ __forceinline__ void gate_up_tile(_Float16* __restrict__ lds, const M
       }
       if (m < tile.rows) {
         uint32_t c0, c1;
-        const uint32_t s = quantize16_exact(x, g2, c0, c1);
+        const uint32_t s = quantize16_fast(x, g2, c0, c1);
         const int32_t i0 = 128 * c + 64 * wn + 32 * t + 16 * h;  // first h element of the block
         *reinterpret_cast<uint2*>(hc + slot * (I / 2) + i0 / 2) = make_uint2(c0, c1);
         hs[slot * (I / 16) + i0 / 16] = uint8_t(s);

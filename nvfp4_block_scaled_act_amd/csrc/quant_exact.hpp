@@ -81,4 +81,45 @@ __device__ __forceinline__ uint32_t quantize16_exact(const float x[16], float g,
   return s;
 }
 
+// Same result as quantize16_exact() with the codes from the hardware
+// f32 -> e2m1 convert (round to nearest even, saturating, sign kept) of
+// w = x * fl(g/S), which lies within two fp32 ulps of the exact x*g/S; the
+// exact comparisons run only for a block holding a w within 4 ulps of a
+// rounding threshold (0.25 .. 5, all with their low 21 mantissa bits zero).
+__device__ __forceinline__ uint32_t quantize16_fast(const float x[16], float g, uint32_t& c0, uint32_t& c1) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  const uint32_t s = scale_byte(amax, g);
+  const float S = e4m3_pos_value(s);
+  const float G = s == 0 ? 0.0f : g / S;
+  float w[16];
+  uint32_t dmin = 0xFFFFFFFFu;  // (bits + 4) << 11: below 9 << 11 iff within 4 ulps of a threshold
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    w[i] = x[i] * G;
+    dmin = min(dmin, (__float_as_uint(w[i]) << 11) + (4u << 11));
+  }
+  c0 = 0;
+  c1 = 0;
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, w[0], w[1], 1.0f, 0);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, w[2], w[3], 1.0f, 1);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, w[4], w[5], 1.0f, 2);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, w[6], w[7], 1.0f, 3);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, w[8], w[9], 1.0f, 0);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, w[10], w[11], 1.0f, 1);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, w[12], w[13], 1.0f, 2);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, w[14], w[15], 1.0f, 3);
+  if (dmin < (9u << 11) && s != 0) {
+    c0 = 0;
+    c1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c0 |= exact_code(x[i], g, S) << (4 * i);
+      c1 |= exact_code(x[8 + i], g, S) << (4 * i);
+    }
+  }
+  return s;
+}
+
 }  // namespace nvfp4
