@@ -620,10 +620,13 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
   W4A16Config c;
   c.ksplit = 0;
   c.chunk_steps = 0;
-  if (tiles < int64_t(kSharedTiles) * cus * 3 / 2 && (M <= 2 || (M == 3 && tiles * steps >= 20 * cus))) {
-    // dot: waves per tile so the launch gives every CU about 8 waves, and at
-    // most 2 steps per wave while there are at most 2 tiles per CU
-    int64_t ks = std::max<int64_t>((8 * cus + tiles - 1) / tiles, (steps + kSplitMaxPer - 1) / kSplitMaxPer);
+  if (M <= 2 || (M == 3 && tiles * steps >= 20 * cus && tiles < int64_t(kSharedTiles) * cus * 3 / 2)) {
+    // dot: waves per tile so the launch gives every CU about 8 waves (at
+    // least 4 per workgroup), and at most 2 steps per wave while there are at
+    // most 2 tiles per CU.  At one or two tokens this also beats the shared
+    // schedule on many tiles (N = 62080: the time of a plain read of the
+    // weight at M = 1)
+    int64_t ks = std::max<int64_t>({(8 * cus + tiles - 1) / tiles, (steps + kSplitMaxPer - 1) / kSplitMaxPer, 4});
     if (tiles <= 2 * cus) ks = std::max<int64_t>(ks, (steps + 1) / 2);
     c.schedule = 4;
     c.ksplit = int(std::min<int64_t>({ks, steps, 16}));
