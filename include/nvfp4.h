@@ -160,7 +160,9 @@ nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t
  *   out    bf16 [M, N], ldo >= N
  * One launch, no workspace.  Deterministic: the fp32 sum order depends only
  * on (M, N, K).
- * Errors: as above; UNSUPPORTED for M > 16.
+ * Errors: as above; UNSUPPORTED for M > 16, or when a's last row ends 2^31 -
+ * 4096 bytes or more past its first element ((M-1)*lda*2 + 2*K; the kernels
+ * address the activations with 32-bit offsets).
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* alpha,
                                 void* out, int64_t ldo, hipStream_t stream);

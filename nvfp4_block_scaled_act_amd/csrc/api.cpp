@@ -63,6 +63,7 @@ nvfp4_status w4a16_checked(const void* a, int64_t M, int64_t lda, const nvfp4_we
   if ((st = check_bf16_input(a, M, w->K, lda)) != NVFP4_OK) return st;
   if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
   if (M > 16) return NVFP4_ERR_UNSUPPORTED;
+  if ((M - 1) * lda * 2 + 2 * w->K > (int64_t(1) << 31) - 4096) return NVFP4_ERR_UNSUPPORTED;  // 32-bit offsets
   if (cfg_in && !nvfp4::w4a16_config_valid(*cfg_in, M, w->K)) return NVFP4_ERR_INVALID_ARGUMENT;
   if (w->N == 0) return NVFP4_OK;
   const nvfp4::W4A16Config cfg = cfg_in ? *cfg_in : nvfp4::w4a16_default_config(M, w->N, w->K);

@@ -118,6 +118,31 @@ __device__ __forceinline__ StepB load_b(const uint16_t* __restrict__ astep, int 
   return b;
 }
 
+// The same operands through a buffer resource whose lanes of token rows >= M
+// point past its end: the load returns zeros there without reading, and
+// those lanes' operand columns only make output columns that are never
+// stored.  (The host keeps every real offset below 2^31.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(const uint16_t* a) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a), short(0), int(0x7fffffff), 0x00020000);
+}
+
+// byte offset of the lane's row and 16-k piece, or past the end
+__device__ __forceinline__ uint32_t act_off(int64_t lda, int32_t M, int row, int q) {
+  return row < M ? uint32_t(row) * uint32_t(lda) * 2u + 32u * uint32_t(q) : 0x80000000u;
+}
+
+__device__ __forceinline__ StepB load_b_rows(__amdgpu_buffer_rsrc_t r, uint32_t off, int32_t st) {
+  StepB b;
+  const uint32_t o = off + uint32_t(st) * 512u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4_t v = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, o + 128u * (j >> 1) + 16u * (j & 1), 0, 0));
+    b.v[j] = make_uint4(v.x, v.y, v.z, v.w);
+  }
+  return b;
+}
+
 // With several token rows, lane (c, q) of the MFMA layout puts 16 different
 // rows in every group of 4 neighbouring lanes, and the texture unit then
 // looks up 4 cache lines per group.  The permuted load has lane 4c + q read
@@ -209,13 +234,14 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void w4a16_split_fixed_kernel(
   // the lane's load row and 16-k piece (PERM: lane 4c + q loads for MFMA lane c + 16q)
   const int lrow = PERM ? (lane >> 2) : (lane & 15), lq = PERM ? (lane & 3) : q;
   const int src_byte = 4 * (4 * (lane & 15) + q);
-  const uint16_t* arow = a + int64_t(min(lrow, M - 1)) * lda;
+  const __amdgpu_buffer_rsrc_t arsrc = act_rsrc(a);
+  const uint32_t aoff = act_off(lda, M, lrow, lq);
   // tiles past the last re-read the last tile; their results are not stored
   auto unit_at = [&](int r, int32_t st) {
     const int32_t t = min(tile0 + r, tiles - 1);
     return load_unit(wt + (int64_t(t) * steps + min(st, steps - 1)) * kUnitBytes, lane);
   };
-  auto b_at = [&](int32_t st) { return load_b(arow + 256 * int64_t(min(st, steps - 1)), lq); };
+  auto b_at = [&](int32_t st) { return load_b_rows(arsrc, aoff, min(st, steps - 1)); };
 
   f32x4_t acc[R];
 #pragma unroll

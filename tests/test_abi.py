@@ -81,6 +81,7 @@ def test_w4a16_validation(nv):
     f = nv.nvfp4_linear_w4a16
     w = _w()
     assert f(A16, 17, 256, C.byref(w), A16, A16, 64, None) == UNSUP    # M > 16
+    assert f(A16, 16, 1 << 27, C.byref(w), A16, A16, 64, None) == UNSUP  # offsets past 2^31 bytes
     assert f(A16, 4, 256, C.byref(w), None, A16, 64, None) == ARG      # alpha
     assert f(A16, 4, 256, C.byref(w), A16, A16, 63, None) == SHAPE     # ldo < N
     assert f(A16, 4, 255, C.byref(w), A16, A16, 64, None) == SHAPE     # lda < K
