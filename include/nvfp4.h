@@ -322,6 +322,47 @@ nvfp4_status nvfp4_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t
                             float* h_amax, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * nvfp4_moe_w4a16 -- the same expert layer with W4A16 on both GEMMs (bf16
+ * activations, NVFP4 banks), for decode-sized batches: the pages' layer keeps
+ * W4A16 below 4 tokens per expert and for decode, on the same banks as the
+ * W4A4 path (FreeToken PR #736, Changes; FreeToken PR #733, Changes: align,
+ * gate_up, activation, down, sum).  For token t, route r, e = topk_ids[t, r]:
+ *   z      = alpha_gu[e] * (x_t @ dequant(W_gu[e]).T)          [2I], fp32 sums
+ *   h      = bf16(SiLU(z[0:I]) * z[I:2I]), SiLU in fp32
+ *   y      = alpha_dn[e] * (h @ dequant(W_dn[e]).T)             [K], fp32 sums
+ *   out[t] = bf16(sum_r topk_w[t, r] * y_r), the sum in fp32, r = 0, 1, ...
+ * alpha_gu[e] = 1/g_gu[e], alpha_dn[e] = 1/g_dn[e] (no activation globals).
+ * A pair whose id lies outside [0, E) is skipped.  Arguments as
+ * nvfp4_moe_w4a4 without g1, g2 and h_amax; ws >= nvfp4_moe_w4a16_workspace_bytes.
+ * The align cuts each expert's pairs into entries of up to 16; both GEMMs run
+ * one workgroup per (entry, 16-row tile of the expert's weight), so a call
+ * reads the banks of the experts it routes to, each once per 16 of its pairs.
+ * Five launches, no host sync; the outputs are the same bits on every call.
+ * After the call the workspace holds, at the offsets
+ * nvfp4_moe_w4a16_workspace_layout reports: sorted, offsets, inv (as for
+ * nvfp4_moe_w4a4), tiles (entries of up to 16 slots) and h (bf16 [T*top_k, I]
+ * by slot).
+ * Needs K % 256 == 0, I % 256 == 0, K and I <= 16384, 1 <= E <= 1024,
+ * T*top_k < 2^31, h below 2^31 bytes and x's last row ending below 2^31 bytes.
+ * Errors as nvfp4_moe_w4a4.
+ * ------------------------------------------------------------------------- */
+typedef struct nvfp4_moe_w4a16_layout {
+  int64_t counts, offsets, tiles, sorted, inv;  /* as nvfp4_moe_layout */
+  int64_t h;                                    /* bf16 [T*top_k, I] by slot */
+  int64_t ys;                                   /* fp32 [T*top_k, K]: routing-weighted y by slot */
+  int64_t max_tiles;
+  int64_t total_bytes;
+} nvfp4_moe_w4a16_layout;
+
+size_t nvfp4_moe_w4a16_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I);
+nvfp4_status nvfp4_moe_w4a16_workspace_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I,
+                                              nvfp4_moe_w4a16_layout* out);
+nvfp4_status nvfp4_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_t* topk_ids, const float* topk_w,
+                             int64_t top_k, int64_t E, int64_t I, const nvfp4_weight* gate_up,
+                             const nvfp4_weight* down, const float* alpha_gu, const float* alpha_dn, void* out,
+                             int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * nvfp4_stream_read -- a measurement aid, not part of the NVFP4 method: reads
  * `bytes` of device memory once (one 16-byte nontemporal load per thread, the
  * way the W4A16 kernels read their weight units) and computes nothing from the

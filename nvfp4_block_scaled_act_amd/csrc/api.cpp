@@ -2,6 +2,7 @@
 // and the calls into the gfx950 kernels.  Every check runs before any launch.
 #include "../../include/nvfp4.h"
 
+#include <algorithm>
 #include <atomic>
 
 #include "kernels.hpp"
@@ -333,6 +334,82 @@ nvfp4_status nvfp4_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return NVFP4_ERR_ALIGNMENT;
   return hip_status(nvfp4::launch_moe_w4a4(x, T, ldx, topk_ids, topk_w, top_k, E, I, gate_up->data, down->data, K,
                                            g1, g2, alpha_gu, alpha_dn, out, ldo, ws, h_amax, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+nvfp4_status moe_w4a16_shape(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I) {
+  if (T < 0 || K <= 0 || I <= 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (top_k < 1 || E < 1 || E > 1024) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (K % 16 != 0 || I % 16 != 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (K % 256 != 0 || I % 256 != 0) return NVFP4_ERR_UNSUPPORTED;
+  // at most 8 steps per wave over 8 waves
+  if (K > 64 * 256 || I > 64 * 256 || T > kInt32Max || top_k > 1024) return NVFP4_ERR_UNSUPPORTED;
+  const int64_t P = T * top_k;
+  if (P > kInt32Max) return NVFP4_ERR_UNSUPPORTED;
+  // one workgroup per (entry, 16-row tile); 32-bit offsets into h
+  const int64_t entries = std::min<int64_t>(P / nvfp4::kW4A16Rows + E, P);
+  if (entries * (std::max(K, I) / 16) > kInt32Max) return NVFP4_ERR_UNSUPPORTED;
+  if (P * I * 2 > (int64_t(1) << 31) - 4096) return NVFP4_ERR_UNSUPPORTED;
+  if (E * 2 * I > kInt32Max - 15 || E * K > kInt32Max - 15) return NVFP4_ERR_UNSUPPORTED;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_moe_w4a16_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I) {
+  if (moe_w4a16_shape(T, top_k, E, K, I) != NVFP4_OK) return 0;
+  return size_t(nvfp4::moe_w4a16_layout(T, top_k, E, K, I).total);
+}
+
+nvfp4_status nvfp4_moe_w4a16_workspace_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I,
+                                              nvfp4_moe_w4a16_layout* out) {
+  if (!out) return NVFP4_ERR_INVALID_ARGUMENT;
+  const nvfp4_status st = moe_w4a16_shape(T, top_k, E, K, I);
+  if (st != NVFP4_OK) return st;
+  const nvfp4::MoeW4A16Layout L = nvfp4::moe_w4a16_layout(T, top_k, E, K, I);
+  out->counts = L.counts;
+  out->offsets = L.offsets;
+  out->tiles = L.tiles;
+  out->sorted = L.sorted;
+  out->inv = L.inv;
+  out->h = L.h;
+  out->ys = L.ys;
+  out->max_tiles = L.max_tiles;
+  out->total_bytes = L.total;
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_t* topk_ids, const float* topk_w,
+                             int64_t top_k, int64_t E, int64_t I, const nvfp4_weight* gate_up,
+                             const nvfp4_weight* down, const float* alpha_gu, const float* alpha_dn, void* out,
+                             int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!gate_up || !down) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_weight(gate_up);
+  if (st != NVFP4_OK) return st;
+  if ((st = check_weight(down)) != NVFP4_OK) return st;
+  const int64_t K = gate_up->K;
+  if ((st = moe_w4a16_shape(T, top_k, E, K, I)) != NVFP4_OK) return st;
+  if (gate_up->N != E * 2 * I || down->N != E * K || down->K != I) return NVFP4_ERR_INVALID_SHAPE;
+  if (!alpha_gu || !alpha_dn) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (T == 0) return NVFP4_OK;  // x, ids, out and ws may be null
+  if (!topk_ids || !topk_w || !out) return NVFP4_ERR_INVALID_ARGUMENT;
+  if ((st = check_bf16_input(x, T, K, ldx)) != NVFP4_OK) return st;
+  if ((T - 1) * ldx * 2 + 2 * K > (int64_t(1) << 31) - 4096) return NVFP4_ERR_UNSUPPORTED;  // 32-bit offsets
+  if (ldo < K) return NVFP4_ERR_INVALID_SHAPE;
+  if (ldo > (INT64_MAX / 2) / T) return NVFP4_ERR_INVALID_SHAPE;
+  if (!aligned16(out) || ldo % 8 != 0) return NVFP4_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(topk_ids) & 3u) || (reinterpret_cast<uintptr_t>(topk_w) & 3u) ||
+      (reinterpret_cast<uintptr_t>(alpha_gu) & 3u) || (reinterpret_cast<uintptr_t>(alpha_dn) & 3u))
+    return NVFP4_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < nvfp4_moe_w4a16_workspace_bytes(T, top_k, E, K, I)) return NVFP4_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return NVFP4_ERR_ALIGNMENT;
+  return hip_status(nvfp4::launch_moe_w4a16(x, T, ldx, topk_ids, topk_w, top_k, E, I, gate_up->data, down->data, K,
+                                            alpha_gu, alpha_dn, out, ldo, ws, stream));
 }
 
 nvfp4_status nvfp4_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {

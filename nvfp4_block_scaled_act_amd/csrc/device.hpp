@@ -98,6 +98,16 @@ __device__ __forceinline__ uint32_t f32_to_f16x2_splat(float s) {
   return h;
 }
 
+// SiLU(z) = z / (1 + e^-z) with the hardware base-2 exponential and
+// reciprocal: a few ulp of relative error, far below the distances to the
+// rounding boundaries of h that matter (an h within about 2^-14 of an NVFP4
+// boundary may round either way against an fp64 reference anyway; a bf16 h
+// keeps 8 bits).  Large |z| saturates correctly: e^-z = inf gives -0, e^-z =
+// 0 gives z.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;

@@ -71,4 +71,27 @@ hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t*
                            const float* g1, const float* g2, const float* alpha_gu, const float* alpha_dn, void* out,
                            int64_t ldo, void* ws, float* h_amax, hipStream_t stream);
 
+// The same layer with W4A16 on both GEMMs (bf16 x, bf16 h), for decode-sized
+// batches: entries of up to kW4A16Rows pairs of one expert.
+constexpr int kW4A16Rows = 16;
+struct MoeW4A16Layout {
+  int64_t chunks, max_tiles;  // align chunks; tile table length T*top_k/16 + E
+  int64_t counts, offsets, tiles, sorted, inv;  // as MoeLayout
+  int64_t h;      // bf16 [T*top_k, I] by slot
+  int64_t ys;     // fp32 [T*top_k, K]: routing-weighted down outputs by slot
+  int64_t total;  // bytes
+};
+MoeW4A16Layout moe_w4a16_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I);
+hipError_t launch_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_t* ids, const float* topk_w,
+                            int64_t top_k, int64_t E, int64_t I, const void* w_gate_up, const void* w_down,
+                            int64_t K, const float* alpha_gu, const float* alpha_dn, void* out, int64_t ldo, void* ws,
+                            hipStream_t stream);
+// Grouped W4A16 over the entries of a tile table (gated: gate_up with SiLU
+// gate into bf16 h; else down into routing-weighted fp32 y), one workgroup
+// per (entry, 16-row output tile).
+hipError_t launch_w4a16_grouped(bool gated, const void* a, int64_t lda, const int32_t* sorted, int64_t top_k,
+                                const MoeTile* entries, int64_t n_entries, int64_t out_tiles, const void* w_tiled,
+                                int64_t rows_per_expert, int64_t K, const float* alpha_e, const float* topk_w,
+                                void* out, int64_t ldo, hipStream_t stream);
+
 }  // namespace nvfp4

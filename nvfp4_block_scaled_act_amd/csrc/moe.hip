@@ -74,10 +74,11 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* tmp,
 }
 
 // One workgroup: per-expert totals, segment starts, the per-chunk bases the
-// scatter adds its ranks to (written over the counts), and the tile table.
+// scatter adds its ranks to (written over the counts), and the tile table of
+// up to tile_rows pairs per entry (256 for the W4A4 GEMMs, 16 for W4A16).
 __global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ counts, int32_t chunks, int32_t E,
                                                         int32_t* __restrict__ offsets, MoeTile* __restrict__ tiles,
-                                                        int32_t max_tiles) {
+                                                        int32_t max_tiles, int32_t tile_rows) {
   __shared__ int32_t tmp[16];
   const int e = int(threadIdx.x);
   int32_t total = 0;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ co
 #pragma unroll 8
     for (int32_t c = 0; c < chunks; ++c) total += counts[int64_t(c) * E + e];
   }
-  const int32_t ntile = (total + gemm::BM - 1) / gemm::BM;
+  const int32_t ntile = (total + tile_rows - 1) / tile_rows;
   int32_t pairs = 0, ntiles = 0;
   const int32_t seg = block_exclusive_scan(total, tmp, pairs);
   const int32_t tile0 = block_exclusive_scan(ntile, tmp, ntiles);
@@ -101,8 +102,8 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ co
     for (int32_t j = 0; j < ntile; ++j) {
       MoeTile t;
       t.expert = e;
-      t.slot0 = seg + gemm::BM * j;
-      t.rows = min(gemm::BM, total - gemm::BM * j);
+      t.slot0 = seg + tile_rows * j;
+      t.rows = min(tile_rows, total - tile_rows * j);
       t.pad = 0;
       tiles[tile0 + j] = t;
     }
@@ -142,15 +143,6 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __re
   } else if (p < P) {
     inv[p] = -1;
   }
-}
-
-// z / (1 + e^-z) with the hardware base-2 exponential and reciprocal: a few
-// ulp of relative error, far below the distances to the NVFP4 rounding
-// boundaries of h that matter (an h within about 2^-14 of a boundary may
-// round either way against an fp64 reference anyway).  Large |z| saturates
-// correctly: e^-z = inf gives -0, e^-z = 0 gives z.
-__device__ __forceinline__ float silu(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
 }
 
 // gate_up of one tile of pairs x 128 gate rows (block c, + the matching 128
@@ -333,6 +325,25 @@ __global__ __launch_bounds__(256) void moe_sum_kernel(const float* __restrict__ 
   *reinterpret_cast<uint2*>(out + t * ldo + k) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
 }
 
+// out[t] = bf16(sum of the token's routes in the order r = 0, 1, ...).
+hipError_t launch_route_sum(const float* ys, const int32_t* inv, int64_t T, int64_t top_k, int64_t K, void* out,
+                            int64_t ldo, hipStream_t stream) {
+  const dim3 sum_grid{uint32_t((T * (K / 4) + 255) / 256)};
+#define NVFP4_SUM(TK)                                                                                            \
+  hipLaunchKernelGGL(moe_sum_kernel<TK>, sum_grid, dim3(256), 0, stream, ys, inv, T, int32_t(top_k), int32_t(K), \
+                     static_cast<uint16_t*>(out), ldo)
+  switch (top_k) {
+    case 1: NVFP4_SUM(1); break;
+    case 2: NVFP4_SUM(2); break;
+    case 4: NVFP4_SUM(4); break;
+    case 6: NVFP4_SUM(6); break;
+    case 8: NVFP4_SUM(8); break;
+    default: NVFP4_SUM(0); break;
+  }
+#undef NVFP4_SUM
+  return hipGetLastError();
+}
+
 }  // namespace
 
 MoeLayout moe_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I) {
@@ -383,7 +394,7 @@ hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t*
   hipLaunchKernelGGL(moe_count_kernel, dim3(chunks), dim3(kChunk), size_t(4 * E), stream, ids, P, int32_t(E), counts,
                      reinterpret_cast<uint32_t*>(h_amax));
   hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, int32_t(L.chunks), int32_t(E), offsets,
-                     tiles, int32_t(L.max_tiles));
+                     tiles, int32_t(L.max_tiles), int32_t(gemm::BM));
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(chunks), dim3(kChunk), size_t(4 * 16 * E), stream, ids, P, int32_t(E),
                      counts, sorted, inv);
   const int32_t mt = int32_t(L.max_tiles);
@@ -394,20 +405,63 @@ hipError_t launch_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t*
   hipLaunchKernelGGL(moe_down_kernel, dim3(uint32_t(gemm::xcd_rows_grid(mt, int32_t(K / 256)))),
                      dim3(gemm::kThreads), 0, stream, hc, hs, int32_t(I), sorted, tiles, mt, topk_w, int32_t(top_k),
                      static_cast<const uint8_t*>(w_down), int32_t(K), alpha_dn, ys);
-  const dim3 sum_grid{uint32_t((T * (K / 4) + 255) / 256)};
-#define NVFP4_SUM(TK)                                                                                            \
-  hipLaunchKernelGGL(moe_sum_kernel<TK>, sum_grid, dim3(256), 0, stream, ys, inv, T, int32_t(top_k), int32_t(K), \
-                     static_cast<uint16_t*>(out), ldo)
-  switch (top_k) {
-    case 1: NVFP4_SUM(1); break;
-    case 2: NVFP4_SUM(2); break;
-    case 4: NVFP4_SUM(4); break;
-    case 6: NVFP4_SUM(6); break;
-    case 8: NVFP4_SUM(8); break;
-    default: NVFP4_SUM(0); break;
-  }
-#undef NVFP4_SUM
-  return hipGetLastError();
+  return launch_route_sum(ys, inv, T, top_k, K, out, ldo, stream);
+}
+
+MoeW4A16Layout moe_w4a16_layout(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I) {
+  MoeW4A16Layout L{};
+  const int64_t P = T * top_k;
+  L.chunks = (P + kChunk - 1) / kChunk;
+  L.max_tiles = P / kW4A16Rows + E;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  L.counts = take(4 * L.chunks * E);
+  L.offsets = take(4 * (E + 1));
+  L.tiles = take(int64_t(sizeof(MoeTile)) * L.max_tiles);
+  L.sorted = take(4 * P);
+  L.h = take(2 * P * I);
+  L.inv = take(4 * P);
+  L.ys = take(4 * P * K);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_t* ids, const float* topk_w,
+                            int64_t top_k, int64_t E, int64_t I, const void* w_gate_up, const void* w_down,
+                            int64_t K, const float* alpha_gu, const float* alpha_dn, void* out, int64_t ldo, void* ws,
+                            hipStream_t stream) {
+  const MoeW4A16Layout L = moe_w4a16_layout(T, top_k, E, K, I);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  MoeTile* tiles = reinterpret_cast<MoeTile*>(base + L.tiles);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);
+  int32_t* inv = reinterpret_cast<int32_t*>(base + L.inv);
+  float* ys = reinterpret_cast<float*>(base + L.ys);
+  const int64_t P = T * top_k;
+  const uint32_t chunks = uint32_t(L.chunks);
+  hipLaunchKernelGGL(moe_count_kernel, dim3(chunks), dim3(kChunk), size_t(4 * E), stream, ids, P, int32_t(E), counts,
+                     nullptr);
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, int32_t(L.chunks), int32_t(E), offsets,
+                     tiles, int32_t(L.max_tiles), int32_t(kW4A16Rows));
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(chunks), dim3(kChunk), size_t(4 * 16 * E), stream, ids, P, int32_t(E),
+                     counts, sorted, inv);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // every live entry holds at least one pair
+  const int64_t entries = std::min<int64_t>(L.max_tiles, P);
+  err = launch_w4a16_grouped(true, x, ldx, sorted, top_k, tiles, entries, I / 16, w_gate_up, 2 * I, K, alpha_gu,
+                             nullptr, h, I, stream);
+  if (err != hipSuccess) return err;
+  err = launch_w4a16_grouped(false, h, I, sorted, top_k, tiles, entries, K / 16, w_down, K, I, alpha_dn, topk_w, ys,
+                             K, stream);
+  if (err != hipSuccess) return err;
+  return launch_route_sum(ys, inv, T, top_k, K, out, ldo, stream);
 }
 
 }  // namespace nvfp4

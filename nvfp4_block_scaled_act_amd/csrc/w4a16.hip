@@ -334,6 +334,112 @@ __global__ __launch_bounds__(1024) void w4a16_split_kernel(
   reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha, out, ldo);
 }
 
+// ---------------------------------------------------------------- grouped
+// W4A16 on the experts of an MoE layer for decode-sized batches (the W4A16
+// side of the layer's tokens-per-expert dispatch, FreeToken PR #736,
+// Changes).  The align step cuts each expert's pairs into entries of up to 16
+// (MoeTile); one workgroup computes one 16-row output tile of one entry, its
+// waves taking interleaved 256-k steps, and the activation rows of a lane's
+// token column are gathered by slot (x by token for gate_up, h by slot for
+// down).  Lanes past the entry's pairs read nothing (out-of-range buffer
+// offsets) and their columns are not stored.
+//   GATED (gate_up): the workgroup computes gate tile t and up tile I/16 + t
+//     of the expert (each step's activation operands serve both) and stores
+//     h = bf16(SiLU(z_g) * z_u), z = alpha_e * acc, by slot;
+//   else (down): it stores the routing-weighted y = w * (alpha_e * acc) in
+//     fp32 by slot for the route sum.
+template <int PER, bool GATED>
+__global__ __launch_bounds__(512) void w4a16_grouped_kernel(
+    const uint16_t* __restrict__ a, int64_t lda, const int32_t* __restrict__ sorted, int32_t top_k,
+    const MoeTile* __restrict__ entries, int32_t out_tiles, const uint8_t* __restrict__ wt, int32_t rows_per_expert,
+    int32_t K, const float* __restrict__ alpha_e, const float* __restrict__ topk_w, void* __restrict__ out,
+    int64_t ldo) {
+  constexpr int R = GATED ? 2 : 1;
+  extern __shared__ float red[];  // [waves][R][64][4]
+  const int32_t entry = int32_t(blockIdx.x) / out_tiles, t = int32_t(blockIdx.x) - entry * out_tiles;
+  const MoeTile ent = entries[entry];
+  if (ent.rows <= 0) return;
+  const int lane = int(threadIdx.x & 63);
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int nwaves = int(blockDim.x >> 6);
+  const int q = lane >> 4;
+  const int32_t steps = K / 256;
+  const int32_t tiles_e = rows_per_expert / 16;
+  const int32_t wtile0 = ent.expert * tiles_e + t, wtile1 = wtile0 + tiles_e / 2;  // gate, up
+  // permuted activation loads: lane 4c + q loads what MFMA lane c + 16q needs
+  const int lrow = lane >> 2, lq = lane & 3;
+  const int src_byte = 4 * (4 * (lane & 15) + q);
+  int32_t arow = -1;
+  if (lrow < ent.rows) arow = GATED ? sorted[ent.slot0 + lrow] / top_k : ent.slot0 + lrow;
+  const __amdgpu_buffer_rsrc_t arsrc = act_rsrc(a);
+  const uint32_t aoff = arow >= 0 ? uint32_t(arow) * uint32_t(lda) * 2u + 32u * uint32_t(lq) : 0x80000000u;
+  auto unit_at = [&](int r, int32_t st) {
+    return load_unit(wt + (int64_t(r == 0 ? wtile0 : wtile1) * steps + min(st, steps - 1)) * kUnitBytes, lane);
+  };
+  auto b_at = [&](int32_t st) { return load_b_rows(arsrc, aoff, min(st, steps - 1)); };
+
+  f32x4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Unit w[2][R];
+  StepB b[2];
+  float alpha = alpha_e[ent.expert];
+#pragma unroll
+  for (int r = 0; r < R; ++r) w[0][r] = unit_at(r, wave);
+  b[0] = b_at(wave);
+  __builtin_amdgcn_sched_barrier(0);
+  settle(alpha);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (i + 1 < PER) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[(i + 1) & 1][r] = unit_at(r, wave + (i + 1) * nwaves);
+      b[(i + 1) & 1] = b_at(wave + (i + 1) * nwaves);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool live = wave + i * nwaves < steps;
+    const StepB& bs = b[i & 1];
+    uint4 b0[4], b1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b0[j] = to_mfma_lane(bs.v[j], src_byte);
+      b1[j] = to_mfma_lane(bs.v[4 + j], src_byte);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      mma_half(w[i & 1][r].c0, w[i & 1][r].sc, 0, b0, acc[r], live);
+      mma_half(w[i & 1][r].c1, w[i & 1][r].sc, 1, b1, acc[r], live);
+    }
+  }
+  // partial tiles added through LDS in wave order
+  if (nwaves > 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) *reinterpret_cast<f32x4_t*>(&red[((wave * R + r) * 64 + lane) * 4]) = acc[r];
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w2 = 1; w2 < nwaves; ++w2)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] += *reinterpret_cast<const f32x4_t*>(&red[((w2 * R + r) * 64 + lane) * 4]);
+  }
+  // lane (c, qq) holds rows 16t + 4qq + i of token column c
+  const int c = lane & 15, qq = lane >> 4;
+  if (c >= ent.rows) return;
+  const int32_t slot = ent.slot0 + c;
+  const int64_t at = int64_t(slot) * ldo + 16 * t + 4 * qq;
+  if (GATED) {
+    float h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = silu(alpha * acc[0][i]) * (alpha * acc[R - 1][i]);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + at) =
+        make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+  } else {
+    const float wr = topk_w[sorted[slot]];
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + at) =
+        make_float4(wr * (alpha * acc[0][0]), wr * (alpha * acc[0][1]), wr * (alpha * acc[0][2]),
+                    wr * (alpha * acc[0][3]));
+  }
+}
+
 // ------------------------------------------------------------------ shared
 // LDS holds two chunks of kc steps; a chunk is [kc steps][8 j][4 q][M c]
 // entries of 8 bf16 (only the M real token rows).
@@ -786,6 +892,44 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
   hipLaunchKernelGGL(w4a16_split_kernel, grid, block, lds, stream, A, lda, int32_t(M), WT, int32_t(N), int32_t(K),
                      int32_t(per), alpha, O, ldo);
   return hipGetLastError();
+}
+
+hipError_t launch_w4a16_grouped(bool gated, const void* a, int64_t lda, const int32_t* sorted, int64_t top_k,
+                                const MoeTile* entries, int64_t n_entries, int64_t out_tiles, const void* w_tiled,
+                                int64_t rows_per_expert, int64_t K, const float* alpha_e, const float* topk_w,
+                                void* out, int64_t ldo, hipStream_t stream) {
+  if (n_entries == 0 || out_tiles == 0) return hipSuccess;
+  const int64_t steps = K / 256;
+  const int64_t waves = std::min<int64_t>(steps, 8);
+  const int64_t per = (steps + waves - 1) / waves;
+  const size_t lds = waves > 1 ? size_t(waves) * (gated ? 2 : 1) * 64 * 4 * sizeof(float) : 0;
+  const dim3 grid{uint32_t(n_entries * out_tiles)}, block{uint32_t(64 * waves)};
+  const auto* A = static_cast<const uint16_t*>(a);
+  const auto* WT = static_cast<const uint8_t*>(w_tiled);
+#define NVFP4_GROUPED(P)                                                                                       \
+  case P:                                                                                                      \
+    if (gated)                                                                                                 \
+      hipLaunchKernelGGL((w4a16_grouped_kernel<P, true>), grid, block, lds, stream, A, lda, sorted,            \
+                         int32_t(top_k), entries, int32_t(out_tiles), WT, int32_t(rows_per_expert), int32_t(K), \
+                         alpha_e, topk_w, out, ldo);                                                           \
+    else                                                                                                       \
+      hipLaunchKernelGGL((w4a16_grouped_kernel<P, false>), grid, block, lds, stream, A, lda, sorted,           \
+                         int32_t(top_k), entries, int32_t(out_tiles), WT, int32_t(rows_per_expert), int32_t(K), \
+                         alpha_e, topk_w, out, ldo);                                                           \
+    return hipGetLastError();
+  switch (per) {
+    NVFP4_GROUPED(1)
+    NVFP4_GROUPED(2)
+    NVFP4_GROUPED(3)
+    NVFP4_GROUPED(4)
+    NVFP4_GROUPED(5)
+    NVFP4_GROUPED(6)
+    NVFP4_GROUPED(7)
+    NVFP4_GROUPED(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef NVFP4_GROUPED
 }
 
 }  // namespace nvfp4

@@ -40,6 +40,12 @@ class MoeLayout(C.Structure):
                                    "h_scales", "inv", "ys", "max_tiles", "total_bytes")]
 
 
+class MoeW4A16Layout(C.Structure):
+    """Mirror of struct nvfp4_moe_w4a16_layout (byte offsets into the W4A16 MoE workspace)."""
+    _fields_ = [(n, I64) for n in ("counts", "offsets", "tiles", "sorted", "inv", "h", "ys", "max_tiles",
+                                   "total_bytes")]
+
+
 _SIGS = {
     "nvfp4_status_str": (C.c_char_p, [I32]),
     "nvfp4_version": (I32, []),
@@ -59,6 +65,10 @@ _SIGS = {
     "nvfp4_linear_workspace_bytes": (SZ, [I64, I64, I64]),
     "nvfp4_linear": (I32, [P, I64, I64, C.POINTER(Weight), P, P, P, P, I64, P, SZ, C.POINTER(I32), P]),
     "nvfp4_stream_read": (I32, [P, SZ, P, P]),
+    "nvfp4_moe_w4a16_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
+    "nvfp4_moe_w4a16_workspace_layout": (I32, [I64, I64, I64, I64, I64, C.POINTER(MoeW4A16Layout)]),
+    "nvfp4_moe_w4a16": (I32, [P, I64, I64, P, P, I64, I64, I64, C.POINTER(Weight), C.POINTER(Weight), P, P, P,
+                              I64, P, SZ, P]),
     "nvfp4_moe_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
     "nvfp4_moe_workspace_layout": (I32, [I64, I64, I64, I64, I64, C.POINTER(MoeLayout)]),
     "nvfp4_moe_w4a4": (I32, [P, I64, I64, P, P, I64, I64, I64, C.POINTER(Weight), C.POINTER(Weight), P, P, P, P,

@@ -296,3 +296,71 @@ def moe_w4a4(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate
                                       _ptr(alpha_gu), _ptr(alpha_dn), _ptr(out), ldo, _ptr(ws), ws.numel(),
                                       _ptr(h_amax), _stream()))
     return out
+
+
+def moe_w4a16_workspace_layout(T: int, top_k: int, E: int, K: int, I: int) -> dict:
+    """Byte offsets of the W4A16 MoE workspace's parts (and max_tiles, total_bytes)."""
+    lay = _L.MoeW4A16Layout()
+    _L.check("nvfp4_moe_w4a16_workspace_layout",
+             _L.load().nvfp4_moe_w4a16_workspace_layout(T, top_k, E, K, I, C.byref(lay)))
+    return {name: int(getattr(lay, name)) for name, _ in _L.MoeW4A16Layout._fields_}
+
+
+def moe_w4a16_workspace_bytes(T: int, top_k: int, E: int, K: int, I: int) -> int:
+    return int(_L.load().nvfp4_moe_w4a16_workspace_bytes(T, top_k, E, K, I))
+
+
+def moe_w4a16_workspace_views(ws: torch.Tensor, T: int, top_k: int, E: int, K: int, I: int) -> dict:
+    """Views of what a W4A16 MoE call leaves in its workspace: the align
+    results (sorted pairs, expert offsets, entries of up to 16 pairs, slot of
+    each pair) and h (bf16 bits) by slot."""
+    lay = moe_w4a16_workspace_layout(T, top_k, E, K, I)
+    P = T * top_k
+
+    def part(name, nbytes):
+        return ws[lay[name]:lay[name] + nbytes]
+
+    return dict(
+        sorted=part("sorted", 4 * P).view(torch.int32),
+        offsets=part("offsets", 4 * (E + 1)).view(torch.int32),
+        tiles=part("tiles", 16 * lay["max_tiles"]).view(torch.int32).view(lay["max_tiles"], 4),
+        h=part("h", 2 * P * I).view(torch.int16).view(P, I),
+        inv=part("inv", 4 * P).view(torch.int32),
+    )
+
+
+def moe_w4a16(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate_up: Weight, down: Weight,
+              num_experts: int, alpha_gu: torch.Tensor, alpha_dn: torch.Tensor, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """NVFP4 MoE expert layer with W4A16 on both GEMMs (bf16 x and h), for
+    decode-sized batches: gate_up with SiLU gate into bf16 h, down, fp32 route
+    sum.  alpha_gu[e] = 1/g_gu[e], alpha_dn[e] = 1/g_dn[e]."""
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_w, torch.float32, "topk_w")
+    E = int(num_experts)
+    for t, n in ((alpha_gu, "alpha_gu"), (alpha_dn, "alpha_dn")):
+        _need(t, torch.float32, n)
+        if t.numel() < E or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous fp32 tensor of E values")
+    ldx = _rows(x, "x")
+    T, K = x.shape
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != T or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous [T, top_k] tensor")
+    if tuple(topk_w.shape) != tuple(topk_ids.shape) or not topk_w.is_contiguous():
+        raise ValueError("topk_w must be a contiguous tensor shaped like topk_ids")
+    top_k = topk_ids.shape[1]
+    I = down.K
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out")
+    ldo = _rows(out, "out")
+    ws = workspace
+    if ws is None:
+        need = moe_w4a16_workspace_bytes(T, top_k, E, K, I)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _L.check("nvfp4_moe_w4a16",
+             _L.load().nvfp4_moe_w4a16(_ptr(x), T, ldx, _ptr(topk_ids), _ptr(topk_w), top_k, E, I,
+                                       C.byref(gate_up.desc), C.byref(down.desc), _ptr(alpha_gu), _ptr(alpha_dn),
+                                       _ptr(out), ldo, _ptr(ws), ws.numel(), _stream()))
+    return out

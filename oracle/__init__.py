@@ -2,7 +2,7 @@
 
 A ctypes wrapper around ``nvfp4_oracle.cpp``: a plain, slow, obviously correct
 C++ definition of activation quantization, the W4A16 and W4A4 linears and the
-NVFP4 MoE expert layer.  Only the tests, ``__graft_entry__.smoke()`` and the
+NVFP4 MoE expert layer (W4A4, and W4A16 for decode-sized batches).  Only the tests, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
 never loads it, and the two share no code.
 
@@ -79,6 +79,9 @@ def lib():
             L.orc_moe_w4a4.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
                                        C.c_float, C.c_float, _P, _P, _P, _I64,
                                        _P, _P, _P, _P, _P, _P, _P, _P]
+            L.orc_moe_w4a16.restype = None
+            L.orc_moe_w4a16.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
+                                        _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]
             _LIB = L
     return _LIB
 
@@ -239,4 +242,42 @@ def moe_w4a4(x_bf16, ids, rw, gu_codes, gu_scales, dn_codes, dn_scales, g1, g2,
                        _ptr(res["h_scale_margin"]), _ptr(amax), _ptr(res["out"]), _ptr(res["ref"]),
                        _ptr(res["sabs"]))
     res["h_amax"] = float(amax[0])
+    return res
+
+
+def moe_w4a16(x_bf16, ids, rw, gu_codes, gu_scales, dn_codes, dn_scales, alpha_gu, alpha_dn, tokens=None,
+              h_in=None):
+    """NVFP4 MoE layer with W4A16 on both GEMMs on selected tokens.  Returns a
+    dict with out/ref/sabs [n_tok, K] and, per pair q = tt*top_k + r, the
+    oracle's h as bf16 bits, in fp64 and its error scale ("h", "h_ref",
+    "h_sabs", [n_tok*top_k, I]).  h_in (bf16 bits, same shape) replaces the
+    oracle's own h in the down projection."""
+    x = _c(x_bf16, np.uint16)
+    T, K = x.shape
+    ids = _c(ids, np.int32)
+    rw = _c(rw, np.float32)
+    top_k = ids.shape[1]
+    guc = _c(gu_codes, np.uint8)
+    gus = _c(gu_scales, np.uint8)
+    dnc = _c(dn_codes, np.uint8)
+    dns = _c(dn_scales, np.uint8)
+    E, twoI = guc.shape[0], guc.shape[1]
+    I = twoI // 2
+    agu = _c(alpha_gu, np.float32)
+    adn = _c(alpha_dn, np.float32)
+    t, nt = _idx(tokens, T)
+    P = nt * top_k
+    hin = None if h_in is None else _c(h_in, np.uint16).reshape(P, I)
+    res = {
+        "h": np.empty((P, I), np.uint16),
+        "h_ref": np.empty((P, I), np.float64),
+        "h_sabs": np.empty((P, I), np.float64),
+        "out": np.empty((nt, K), np.uint16),
+        "ref": np.empty((nt, K), np.float64),
+        "sabs": np.empty((nt, K), np.float64),
+    }
+    lib().orc_moe_w4a16(_ptr(x), T, K, _ptr(ids), _ptr(rw), top_k, E, I, _ptr(guc), _ptr(gus), _ptr(dnc),
+                        _ptr(dns), _ptr(agu), _ptr(adn), _ptr(t), nt, _ptr(hin), _ptr(res["h"]),
+                        _ptr(res["h_ref"]), _ptr(res["h_sabs"]), _ptr(res["out"]), _ptr(res["ref"]),
+                        _ptr(res["sabs"]))
     return res

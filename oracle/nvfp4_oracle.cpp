@@ -449,4 +449,90 @@ void orc_moe_w4a4(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, c
   if (h_amax) *h_amax = amax_all;
 }
 
+// NVFP4 MoE expert layer with W4A16 on both GEMMs (bf16 x and h), for
+// selected tokens; banks and ids/w as orc_moe_w4a4, alpha_gu[e] =
+// fp32(1/g_gu[e]), alpha_dn[e] = fp32(1/g_dn[e]).  For each selected token t
+// and route r whose id e lies in [0, E) (other ids are skipped):
+//   z[j]   = alpha_gu[e] * sum_k x[t, k] * dequant(gate_up[e])[j, k]   (fp64)
+//   h[i]   = SiLU(z[i]) * z[I + i]                                     (fp64)
+//   hb[i]  = bf16_rne(h[i]), or h_in[pair][i] when h_in is given
+//   y[n]   = alpha_dn[e] * sum_i hb[i] * dequant(down[e])[n, i]        (fp64)
+//   out[t] = bf16_rne(sum_r w[t, r] * y_r)                             (fp64 sum)
+// Per pair q = tt*top_k + r (tt: index into tokens): h_bits[q] = bf16_rne(h),
+// h_ref[q] = h, and h_sabs[q] = |SiLU'(z_g)| |z_u| Sg + |SiLU(z_g)| Su, Sg
+// and Su being alpha_gu * sum |x w| of the two dot products (the scale of h's
+// error from fp32 sums); zeros for a skipped pair.  ref/sabs as the linears.
+void orc_moe_w4a16(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, const float* rw,
+                   int64_t top_k, int64_t E, int64_t I,
+                   const uint8_t* gu_codes, const uint8_t* gu_scales,
+                   const uint8_t* dn_codes, const uint8_t* dn_scales,
+                   const float* alpha_gu, const float* alpha_dn, const int64_t* tokens, int64_t n_tok,
+                   const uint16_t* h_in, uint16_t* h_bits, double* h_ref, double* h_sabs,
+                   uint16_t* out, double* ref, double* sabs) {
+  (void)T;
+  const int64_t twoI = 2 * I;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t tt = 0; tt < n_tok; ++tt) {
+    const int64_t t = tokens ? tokens[tt] : tt;
+    std::vector<double> xv(K);
+    for (int64_t k = 0; k < K; ++k) xv[k] = bf16_to_double(x[t * K + k]);
+    std::vector<double> acc(K, 0.0), acc_abs(K, 0.0);
+    for (int64_t r = 0; r < top_k; ++r) {
+      const int64_t q = tt * top_k + r;
+      const int64_t e = ids[t * top_k + r];
+      if (e < 0 || e >= E) {
+        for (int64_t i = 0; i < I; ++i) {
+          if (h_bits) h_bits[q * I + i] = 0;
+          if (h_ref) h_ref[q * I + i] = 0.0;
+          if (h_sabs) h_sabs[q * I + i] = 0.0;
+        }
+        continue;
+      }
+      const uint8_t* guc = gu_codes + e * twoI * (K / 2);
+      const uint8_t* gus = gu_scales + e * twoI * (K / 16);
+      std::vector<double> z(twoI), za(twoI);
+      for (int64_t j = 0; j < twoI; ++j) {
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          const double p = xv[k] * dequant(guc + j * (K / 2), gus + j * (K / 16), k);  // exact product
+          s += p;
+          sa += std::fabs(p);
+        }
+        z[j] = double(alpha_gu[e]) * s;
+        za[j] = double(alpha_gu[e]) * sa;
+      }
+      std::vector<double> hb(I);
+      for (int64_t i = 0; i < I; ++i) {
+        const double zg = z[i], zu = z[I + i];
+        const double sig = 1.0 / (1.0 + std::exp(-zg));
+        const double h = silu(zg) * zu;
+        const double dsilu = sig + zg * sig * (1.0 - sig);
+        const uint16_t bits = bf16_rne(h);
+        if (h_bits) h_bits[q * I + i] = bits;
+        if (h_ref) h_ref[q * I + i] = h;
+        if (h_sabs) h_sabs[q * I + i] = std::fabs(dsilu) * std::fabs(zu) * za[i] + std::fabs(silu(zg)) * za[I + i];
+        hb[i] = bf16_to_double(h_in ? h_in[q * I + i] : bits);
+      }
+      const uint8_t* dnc = dn_codes + e * K * (I / 2);
+      const uint8_t* dns = dn_scales + e * K * (I / 16);
+      for (int64_t n = 0; n < K; ++n) {
+        double s = 0.0, sa = 0.0;
+        for (int64_t i = 0; i < I; ++i) {
+          const double p = hb[i] * dequant(dnc + n * (I / 2), dns + n * (I / 16), i);  // exact product
+          s += p;
+          sa += std::fabs(p);
+        }
+        const double wr = double(rw[t * top_k + r]);
+        acc[n] += wr * (double(alpha_dn[e]) * s);
+        acc_abs[n] += std::fabs(wr) * double(alpha_dn[e]) * sa;
+      }
+    }
+    for (int64_t n = 0; n < K; ++n) {
+      if (ref) ref[tt * K + n] = acc[n];
+      if (sabs) sabs[tt * K + n] = acc_abs[n];
+      if (out) out[tt * K + n] = bf16_rne(acc[n]);
+    }
+  }
+}
+
 }  // extern "C"

@@ -238,3 +238,44 @@ def test_stream_read_validation(nv):
     assert f(A16 + 8, 16, A16, None) == ALIGN        # source alignment
     assert f(A16, 16, A16 + 2, None) == ALIGN        # sink alignment
 
+
+
+def test_moe_w4a16_workspace_and_validation(nv):
+    T, top_k, E, K, I = 16, 8, 128, 2048, 768
+    lay = L.MoeW4A16Layout()
+    assert nv.nvfp4_moe_w4a16_workspace_layout(T, top_k, E, K, I, C.byref(lay)) == OK
+    P = T * top_k
+    assert lay.max_tiles == P // 16 + E
+    end = 0
+    for name, size in [("counts", 4 * E), ("offsets", 4 * (E + 1)), ("tiles", 16 * lay.max_tiles),
+                       ("sorted", 4 * P), ("h", 2 * P * I), ("inv", 4 * P), ("ys", 4 * P * K)]:
+        off = getattr(lay, name)
+        assert off % 256 == 0 and off >= end, name
+        end = off + size
+    assert lay.total_bytes >= end and nv.nvfp4_moe_w4a16_workspace_bytes(T, top_k, E, K, I) == lay.total_bytes
+    assert nv.nvfp4_moe_w4a16_workspace_bytes(T, top_k, E, 64 * 256 + 256, I) == 0   # K beyond 64 steps
+    assert nv.nvfp4_moe_w4a16_workspace_layout(T, top_k, E, K, 128, C.byref(lay)) == UNSUP   # I % 256
+
+    T, top_k, E, K, I = 4, 2, 4, 512, 256
+    gu, dn = _w(N=E * 2 * I, K=K), _w(N=E * K, K=I)
+    need = nv.nvfp4_moe_w4a16_workspace_bytes(T, top_k, E, K, I)
+    WS0 = 0x100000
+
+    def call(x=A16, T=T, ldx=K, ids=A16, w=A16, top_k=top_k, E=E, I=I, gu=gu, dn=dn, agu=A16, adn=A16, out=A16,
+             ldo=K, ws=WS0, ws_bytes=need):
+        return nv.nvfp4_moe_w4a16(x, T, ldx, ids, w, top_k, E, I, C.byref(gu) if gu is not None else None,
+                                  C.byref(dn) if dn is not None else None, agu, adn, out, ldo, ws, ws_bytes, None)
+
+    assert call(gu=None) == ARG
+    assert call(agu=None) == ARG
+    assert call(ids=None) == ARG
+    assert call(top_k=0) == ARG
+    assert call(dn=_w(N=E * K, K=512)) == SHAPE
+    assert call(gu=_w(N=E * 2 * I - 16, K=K)) == SHAPE
+    assert call(ldx=K - 8) == SHAPE
+    assert call(ldx=1 << 29) == UNSUP                # x's rows past 2^31 bytes
+    assert call(ldo=K + 4) == ALIGN
+    assert call(ws=WS0 + 16) == ALIGN
+    assert call(ws_bytes=need - 1) == WS
+    assert call(ws=None) == WS
+    assert call(T=0, x=None, ids=None, w=None, out=None, ws=None, ws_bytes=0) == OK

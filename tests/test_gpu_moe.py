@@ -111,7 +111,7 @@ class Banks:
                             self.o_alpha_gu, self.o_alpha_dn, tokens=tokens)
 
 
-def expected_align(ids, E):
+def expected_align(ids, E, rows=256):
     flat = ids.reshape(-1).astype(np.int64)
     valid = (flat >= 0) & (flat < E)
     idx = np.nonzero(valid)[0]
@@ -120,13 +120,13 @@ def expected_align(ids, E):
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     tiles = []
     for e in range(E):
-        for j in range(0, counts[e], 256):
-            tiles.append((e, offsets[e] + j, min(256, counts[e] - j), 0))
+        for j in range(0, counts[e], rows):
+            tiles.append((e, offsets[e] + j, min(rows, counts[e] - j), 0))
     return order, offsets, tiles
 
 
-def check_align(views, ids, E):
-    order, offsets, tiles = expected_align(ids, E)
+def check_align(views, ids, E, rows=256):
+    order, offsets, tiles = expected_align(ids, E, rows)
     n = len(order)
     got_sorted = views["sorted"].cpu().numpy()
     assert (got_sorted[:n] == order).all(), "sorted pairs differ from a stable sort by expert"
@@ -290,3 +290,105 @@ def test_moe_full_size_sampled(ops, orc):
     stats = check_out(bf16_host(out), res, tokens, flipped)
     assert h_amax.item() >= res["h_amax"] * (1 - 1e-5)
     print(f"flipped tokens {len(flipped)}/{len(tokens)}, code flips {ncf}, scale flips {nsf}, {stats}")
+
+
+# ------------------------------------------------------------ W4A16 layer
+# Stage-wise, as the GPU's z is an fp32 sum: h (bf16 by slot) within 2 bf16
+# ulp of the oracle's bf16(h), with the floor set by h's error scale and an
+# absolute floor of 2^-100 (an fp32 SiLU underflows to 0 for a gate below
+# about -87, where |h| < 2^-110; such an h moves no output by a measurable
+# amount); then the output against the oracle's down + route sum fed the
+# GPU's own h, to the linears' bar (2 bf16 ulp with the Sabs floor, rel-L2
+# <= 1e-3).
+H_ABS_FLOOR = 2.0 ** -100
+
+def banks16(ops, orc, gate_up, down, check_experts=None):
+    """Banks for the W4A16 layer: alpha_e = 1/g_e (no activation global)."""
+    return Banks(ops, orc, gate_up, down, 1.0, 1.0, check_experts=check_experts)
+
+
+def run16(ops, banks, x, ids, w, workspace=None):
+    import torch
+
+    T, top_k = ids.shape
+    if workspace is None:
+        workspace = torch.empty(max(1, ops.moe_w4a16_workspace_bytes(T, top_k, banks.E, banks.K, banks.I)),
+                                dtype=torch.uint8, device="cuda")
+    out = ops.moe_w4a16(bf16_dev(x), to_dev(ids), to_dev(w), banks.w_gu, banks.w_dn, banks.E, banks.alpha_gu,
+                        banks.alpha_dn, workspace=workspace)
+    torch.cuda.synchronize()
+    return out, workspace
+
+
+def check16(ops, orc, banks, x, ids, w, out, ws, tokens=None):
+    T, top_k = ids.shape
+    E, K, I = banks.E, banks.K, banks.I
+    views = ops.moe_w4a16_workspace_views(ws, T, top_k, E, K, I)
+    inv = check_align(views, ids, E, rows=16)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    args = (banks.o_gu[0], banks.o_gu[1], banks.o_dn[0], banks.o_dn[1], banks.o_alpha_gu, banks.o_alpha_dn)
+    res = orc.moe_w4a16(x, ids, w, *args, tokens=tokens)
+    hv = views["h"].cpu().numpy().view(np.uint16)
+    pairs = (tokens[:, None] * top_k + np.arange(top_k)[None, :]).reshape(-1)
+    slots = inv[pairs]
+    live = slots >= 0
+    h_gpu = np.zeros((len(pairs), I), np.uint16)
+    h_gpu[live] = hv[slots[live]]
+    hstats = gemm_check(h_gpu[live], res["h"][live], np.maximum(res["h_sabs"][live], 2.0 ** 13 * H_ABS_FLOOR))
+    fed = orc.moe_w4a16(x, ids, w, *args, tokens=tokens, h_in=h_gpu)
+    ostats = gemm_check(bf16_host(out)[tokens], fed["out"], fed["sabs"])
+    return hstats, ostats
+
+
+@pytest.fixture(scope="module")
+def full_banks16(ops, orc):
+    m = synth.MOE
+    d = synth.moe_inputs()
+    banks = banks16(ops, orc, d["gate_up"], d["down"], check_experts=[0, 1, m["E"] - 1])
+    return banks, d
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_moe_w4a16_decode(ops, orc, full_banks16, T):
+    # the MoE workload's banks (E=128, top-8, K=2048, I=768) at decode batch
+    # sizes: the first T tokens of its inputs and routing
+    banks, d = full_banks16
+    x, ids, w = d["x"][:T], d["ids"][:T], d["w"][:T]
+    out, ws = run16(ops, banks, x, ids, w)
+    hstats, ostats = check16(ops, orc, banks, x, ids, w, out, ws)
+    print(f"T={T}: h {hstats}, out {ostats}")
+
+
+def test_moe_w4a16_entries_skips_and_repeat(ops, orc):
+    # 8 experts, top-2, K=512, I=256, T=90: expert 0 draws most tokens (several
+    # 16-pair entries, the last ragged), expert 7 none, some ids skipped; a
+    # second call on the same workspace gives the same bits
+    E, top_k, K, I, T = 8, 2, 512, 256, 90
+    bias = np.zeros(E, np.float32)
+    bias[0], bias[7] = 2.5, -30.0
+    x, ids, w, _, _, _, gate_up, down = _small_case(303, T, E, top_k, K, I, bias)
+    ids = ids.copy()
+    ids[::9, 1] = -1
+    ids[4::13, 0] = E
+    banks = banks16(ops, orc, gate_up, down)
+    out1, ws = run16(ops, banks, x, ids, w)
+    counts = np.bincount(ids[(ids >= 0) & (ids < E)], minlength=E)
+    assert counts[0] > 48 and counts[7] == 0
+    check16(ops, orc, banks, x, ids, w, out1, ws)
+    out2, _ = run16(ops, banks, x, ids, w, workspace=ws)
+    assert (bf16_host(out1) == bf16_host(out2)).all(), "W4A16 MoE must be deterministic"
+
+
+def test_moe_w4a16_long_k_and_empty(ops, orc):
+    # K = 4096, I = 512 (16 and 2 steps per GEMM: two steps per wave on gate_up)
+    import torch
+
+    E, top_k, K, I, T = 4, 2, 4096, 512, 6
+    x, ids, w, _, _, _, gate_up, down = _small_case(404, T, E, top_k, K, I)
+    banks = banks16(ops, orc, gate_up, down)
+    out, ws = run16(ops, banks, x, ids, w)
+    check16(ops, orc, banks, x, ids, w, out, ws)
+    xe = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    ie = torch.empty((0, top_k), dtype=torch.int32, device="cuda")
+    we = torch.empty((0, top_k), dtype=torch.float32, device="cuda")
+    assert ops.moe_w4a16(xe, ie, we, banks.w_gu, banks.w_dn, E, banks.alpha_gu, banks.alpha_dn).shape == (0, K)
