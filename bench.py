@@ -325,6 +325,87 @@ def bench_moe(ops, torch, reps=10):
     return dict(T=T, E=E, top_k=top_k, K=K, I=I, layer_us=layer_us, tflops=flops / layer_us / 1e6)
 
 
+def bench_moe_decode(ops, torch, Ts=(1, 4, 16), reps=3):
+    """The same MoE layer at decode batch sizes through nvfp4_moe_w4a16 (bf16
+    x and h, align into entries of up to 16 pairs, grouped W4A16 gate_up with
+    the SiLU gate, grouped W4A16 down, route sum).  Cold banks: each call uses
+    the next of C prepared copies of both banks (over 2.2 GB in all) and the
+    next T tokens of the workload's inputs and routing, inside one HIP graph
+    per T.  Bytes per call: the gate_up and down banks of the experts the call
+    routes to (each read once: at most 16 pairs per expert here) plus x and
+    out; TB/s = bytes / time."""
+    from nvfp4_block_scaled_act_amd import synth
+
+    m = synth.MOE
+    E, top_k, K, I = m["E"], m["top_k"], m["K"], m["I"]
+    d = synth.moe_inputs()
+    banks, gws = [], []
+    for bank in (d["gate_up"], d["down"]):
+        rows, cols = bank.shape[1], bank.shape[2]
+        dev = dev_bf16(torch, bank.reshape(E * rows, cols))
+        codes = torch.empty((E * rows, cols // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((E * rows, cols // 16), dtype=torch.uint8, device="cuda")
+        gs = torch.empty(E, dtype=torch.float32, device="cuda")
+        for e in range(E):
+            sl = slice(e * rows, (e + 1) * rows)
+            ops.global_scale(dev[sl], out=gs[e:e + 1])
+            ops.quantize_act(dev[sl], gs[e:e + 1], codes=codes[sl], scales=scales[sl])
+        del dev
+        banks.append((codes, scales))
+        gws.append(gs)
+    expert_bytes = (2 * I * K + K * I) * 9 // 16
+    C = max(2, int(np.ceil(COLD_BYTES / (E * expert_bytes))))
+    copies = [(ops.prepare_weight(*banks[0]), ops.prepare_weight(*banks[1])) for _ in range(C)]
+    del banks
+    a_gu = torch.empty(E, dtype=torch.float32, device="cuda")
+    a_dn = torch.empty(E, dtype=torch.float32, device="cuda")
+    for e in range(E):
+        ops.alpha(gws[0][e:e + 1], out=a_gu[e:e + 1])
+        ops.alpha(gws[1][e:e + 1], out=a_dn[e:e + 1])
+    x = dev_bf16(torch, d["x"])
+    ids = torch.from_numpy(d["ids"]).cuda()
+    w = torch.from_numpy(d["w"]).cuda()
+    rows = []
+    for T in Ts:
+        n = 2 * C  # calls per graph replay: every copy twice, a new token window each call
+        ws = torch.empty(ops.moe_w4a16_workspace_bytes(T, top_k, E, K, I), dtype=torch.uint8, device="cuda")
+        out = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+        wins = [(i * T) % (m["T"] - T) for i in range(n)]
+        experts = [len(set(d["ids"][s:s + T].reshape(-1).tolist())) for s in wins]
+        nbytes = sum(ne * expert_bytes + 4 * T * K for ne in experts)
+
+        def call(i):
+            s = wins[i]
+            w_gu, w_dn = copies[i % C]
+            ops.moe_w4a16(x[s:s + T], ids[s:s + T], w[s:s + T], w_gu, w_dn, E, a_gu, a_dn, out=out, workspace=ws)
+
+        for i in range(2):
+            call(i)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(n):
+                call(i)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+        tb_s = nbytes / n / us / 1e6
+        rows.append(dict(T=T, us=round(us, 2), experts=round(sum(experts) / n, 1),
+                         mb=round(nbytes / n / 1e6, 2), tb_s=round(tb_s, 3)))
+        log(f"[moe_decode] T={T}: {us:.2f} us per layer, {sum(experts) / n:.1f} experts, "
+            f"{nbytes / n / 1e6:.1f} MB, {tb_s:.3f} TB/s")
+        del gr
+    del copies
+    torch.cuda.empty_cache()
+    return dict(copies=C, rows=rows)
+
+
 def bench_fused_sweep(ops, torch, reps=2):
     """The large fused-weight linear through the dispatch (nvfp4_linear) at
     every M of its sweep, over rotated weight copies (cold weights), and the
@@ -429,7 +510,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the W4A16 calls directly (counter runs)")
-    ap.add_argument("--only", choices=["all", "headline", "fused", "fused_sweep", "w4a4", "moe", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "headline", "fused", "fused_sweep", "w4a4", "moe", "moe_decode", "copy"],
+                    default="all",
                     help="run one part (for profiler runs); 'copy' times a plain 256 MiB device copy, the "
                          "reference for the HBM byte counters")
     args = ap.parse_args()
@@ -459,6 +541,9 @@ def main():
     if args.only == "moe":
         r5 = bench_moe(ops, torch, reps=args.steps)
         print(json.dumps({"moe": {k: round(v, 3) if isinstance(v, float) else v for k, v in r5.items()}}))
+        return
+    if args.only == "moe_decode":
+        print(json.dumps({"moe_decode": bench_moe_decode(ops, torch)}))
         return
     if args.only == "fused_sweep":
         print(json.dumps({"fused_large_sweep": bench_fused_sweep(ops, torch)}))
@@ -549,6 +634,13 @@ def main():
             "tflops": round(r5["tflops"], 2), "unit": "TFLOP/s", "layer_us": round(r5["layer_us"], 2),
             "flops": moe_flops(r5["T"], r5["top_k"], r5["K"], r5["I"]),
             "frac_of_fp16_mfma_peak": round(r5["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+        }
+        r6 = bench_moe_decode(ops, torch)
+        res["moe_decode"] = {
+            "workload": "NVFP4 MoE W4A16 (nvfp4_moe_w4a16), E=128, top-8, K=2048, I=768, T in {1,4,16}, cold banks "
+                        "(%d copies), whole layer: align, gate_up + SiLU gate, down + routing weight, route sum"
+                        % r6["copies"],
+            "unit": "TB/s of the routed experts' bank bytes", "per_T": r6["rows"],
         }
     if not args.no_cpu_baseline and args.only == "all":
         res["cpu_baseline"] = cpu_baseline()

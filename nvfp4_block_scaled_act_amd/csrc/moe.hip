@@ -145,6 +145,67 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __re
   }
 }
 
+// The three align steps in one workgroup, for at most kChunk pairs (decode
+// batches): the same results as count + scan + scatter (stable by pair within
+// an expert), tile table entries of up to tile_rows pairs.
+__global__ __launch_bounds__(kChunk) void moe_align_small_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                                 int32_t E, int32_t* __restrict__ offsets,
+                                                                 MoeTile* __restrict__ tiles, int32_t max_tiles,
+                                                                 int32_t tile_rows, int32_t* __restrict__ sorted,
+                                                                 int32_t* __restrict__ inv) {
+  extern __shared__ int32_t lds[];  // wave_count [16][E], then base [E]
+  __shared__ int32_t tmp[16];
+  int32_t* wave_count = lds;
+  int32_t* base = lds + 16 * E;
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  for (int i = int(threadIdx.x); i < 16 * E; i += kChunk) wave_count[i] = 0;
+  __syncthreads();
+  const int64_t p = threadIdx.x;
+  const int e = p < P ? expert_of(ids, p, E) : E;
+  uint64_t same = ~0ull;
+  for (int b = 0; (1 << b) <= E; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ball = __ballot(bit);
+    same &= bit ? ball : ~ball;
+  }
+  const uint64_t lower = same & ((1ull << lane) - 1ull);
+  if (e < E && lower == 0) wave_count[wave * E + e] = __popcll(same);
+  __syncthreads();
+  // per-expert totals, segment starts and tiles (thread = expert)
+  const int ex = int(threadIdx.x);
+  int32_t total = 0;
+  if (ex < E)
+    for (int w = 0; w < 16; ++w) total += wave_count[w * E + ex];
+  const int32_t ntile = (total + tile_rows - 1) / tile_rows;
+  int32_t pairs = 0, ntiles = 0;
+  const int32_t seg = block_exclusive_scan(total, tmp, pairs);
+  const int32_t tile0 = block_exclusive_scan(ntile, tmp, ntiles);
+  if (ex < E) {
+    base[ex] = seg;
+    offsets[ex] = seg;
+    for (int32_t j = 0; j < ntile; ++j) {
+      MoeTile t;
+      t.expert = ex;
+      t.slot0 = seg + tile_rows * j;
+      t.rows = min(tile_rows, total - tile_rows * j);
+      t.pad = 0;
+      tiles[tile0 + j] = t;
+    }
+  }
+  if (ex == 0) offsets[E] = pairs;
+  for (int32_t j = ntiles + ex; j < max_tiles; j += kChunk) tiles[j] = MoeTile{0, 0, 0, 0};
+  __syncthreads();
+  if (e < E) {
+    int32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_count[w * E + e];
+    const int32_t slot = base[e] + before + __popcll(lower);
+    sorted[slot] = int32_t(p);
+    inv[p] = slot;
+  } else if (p < P) {
+    inv[p] = -1;
+  }
+}
+
 // gate_up of one tile of pairs x 128 gate rows (block c, + the matching 128
 // up rows) of its expert, with the SiLU gate and NVFP4 quantization of h.
 // BMT = pair rows the workgroup computes (256, or 128 for a tile that fits).
@@ -445,12 +506,17 @@ hipError_t launch_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_t
   float* ys = reinterpret_cast<float*>(base + L.ys);
   const int64_t P = T * top_k;
   const uint32_t chunks = uint32_t(L.chunks);
-  hipLaunchKernelGGL(moe_count_kernel, dim3(chunks), dim3(kChunk), size_t(4 * E), stream, ids, P, int32_t(E), counts,
-                     nullptr);
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, int32_t(L.chunks), int32_t(E), offsets,
-                     tiles, int32_t(L.max_tiles), int32_t(kW4A16Rows));
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(chunks), dim3(kChunk), size_t(4 * 16 * E), stream, ids, P, int32_t(E),
-                     counts, sorted, inv);
+  if (P <= kChunk && 17 * 4 * E <= 65536) {
+    hipLaunchKernelGGL(moe_align_small_kernel, dim3(1), dim3(kChunk), size_t(4 * 17 * E), stream, ids, P, int32_t(E),
+                       offsets, tiles, int32_t(L.max_tiles), int32_t(kW4A16Rows), sorted, inv);
+  } else {
+    hipLaunchKernelGGL(moe_count_kernel, dim3(chunks), dim3(kChunk), size_t(4 * E), stream, ids, P, int32_t(E), counts,
+                       nullptr);
+    hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, int32_t(L.chunks), int32_t(E),
+                       offsets, tiles, int32_t(L.max_tiles), int32_t(kW4A16Rows));
+    hipLaunchKernelGGL(moe_scatter_kernel, dim3(chunks), dim3(kChunk), size_t(4 * 16 * E), stream, ids, P,
+                       int32_t(E), counts, sorted, inv);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // every live entry holds at least one pair

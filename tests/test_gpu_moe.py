@@ -379,6 +379,16 @@ def test_moe_w4a16_entries_skips_and_repeat(ops, orc):
     assert (bf16_host(out1) == bf16_host(out2)).all(), "W4A16 MoE must be deterministic"
 
 
+def test_moe_w4a16_many_pairs(ops, orc):
+    # 1200 pairs (more than one align chunk: the three-launch align), ragged
+    # entries of 16 over 8 experts; outputs checked on sampled tokens
+    E, top_k, K, I, T = 8, 2, 256, 256, 600
+    x, ids, w, _, _, _, gate_up, down = _small_case(505, T, E, top_k, K, I)
+    banks = banks16(ops, orc, gate_up, down)
+    out, ws = run16(ops, banks, x, ids, w)
+    check16(ops, orc, banks, x, ids, w, out, ws, tokens=[0, 1, 299, 300, 598, 599])
+
+
 def test_moe_w4a16_long_k_and_empty(ops, orc):
     # K = 4096, I = 512 (16 and 2 steps per GEMM: two steps per wave on gate_up)
     import torch
