@@ -325,7 +325,7 @@ def bench_moe(ops, torch, reps=10):
     return dict(T=T, E=E, top_k=top_k, K=K, I=I, layer_us=layer_us, tflops=flops / layer_us / 1e6)
 
 
-def bench_moe_decode(ops, torch, Ts=(1, 4, 16), reps=3):
+def bench_moe_decode(ops, torch, Ts=(1, 4, 16), cross_Ts=(16, 64, 256, 512, 1024, 2048), reps=3):
     """The same MoE layer at decode batch sizes through nvfp4_moe_w4a16 (bf16
     x and h, align into entries of up to 16 pairs, grouped W4A16 gate_up with
     the SiLU gate, grouped W4A16 down, route sum).  Cold banks: each call uses
@@ -333,7 +333,10 @@ def bench_moe_decode(ops, torch, Ts=(1, 4, 16), reps=3):
     next T tokens of the workload's inputs and routing, inside one HIP graph
     per T.  Bytes per call: the gate_up and down banks of the experts the call
     routes to (each read once: at most 16 pairs per expert here) plus x and
-    out; TB/s = bytes / time."""
+    out; TB/s = bytes / time.  For the layer's tokens-per-expert dispatch,
+    both layers (this one and nvfp4_moe_w4a4 with its static globals g1 =
+    2688/amax of the calibration batch and g2 from the layer's own h amax on
+    it) are also timed the same way at T in cross_Ts."""
     from nvfp4_block_scaled_act_amd import synth
 
     m = synth.MOE
@@ -365,10 +368,27 @@ def bench_moe_decode(ops, torch, Ts=(1, 4, 16), reps=3):
     x = dev_bf16(torch, d["x"])
     ids = torch.from_numpy(d["ids"]).cuda()
     w = torch.from_numpy(d["w"]).cuda()
-    rows = []
-    for T in Ts:
+    # the W4A4 layer's static globals and alphas
+    g1 = ops.global_scale(dev_bf16(torch, d["cal"]))
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    a_gu4 = torch.empty(E, dtype=torch.float32, device="cuda")
+    a_dn4 = torch.empty(E, dtype=torch.float32, device="cuda")
+    for e in range(E):
+        ops.alpha(gws[0][e:e + 1], g1, out=a_gu4[e:e + 1])
+        ops.alpha(gws[1][e:e + 1], one, out=a_dn4[e:e + 1])
+    h_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ops.moe_w4a4(dev_bf16(torch, d["cal"]), torch.from_numpy(d["cal_ids"]).cuda(),
+                 torch.from_numpy(d["cal_w"]).cuda(), *copies[0], E, g1, one, a_gu4, a_dn4, h_amax=h_amax)
+    g2 = (torch.full((1,), 2688.0, dtype=torch.float32, device="cuda") / h_amax).contiguous()
+    for e in range(E):
+        ops.alpha(gws[1][e:e + 1], g2, out=a_dn4[e:e + 1])
+
+    def timed(T, layer):
         n = 2 * C  # calls per graph replay: every copy twice, a new token window each call
-        ws = torch.empty(ops.moe_w4a16_workspace_bytes(T, top_k, E, K, I), dtype=torch.uint8, device="cuda")
+        if layer == "w4a16":
+            ws = torch.empty(ops.moe_w4a16_workspace_bytes(T, top_k, E, K, I), dtype=torch.uint8, device="cuda")
+        else:
+            ws = torch.empty(ops.moe_workspace_bytes(T, top_k, E, K, I), dtype=torch.uint8, device="cuda")
         out = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
         wins = [(i * T) % (m["T"] - T) for i in range(n)]
         experts = [len(set(d["ids"][s:s + T].reshape(-1).tolist())) for s in wins]
@@ -377,7 +397,12 @@ def bench_moe_decode(ops, torch, Ts=(1, 4, 16), reps=3):
         def call(i):
             s = wins[i]
             w_gu, w_dn = copies[i % C]
-            ops.moe_w4a16(x[s:s + T], ids[s:s + T], w[s:s + T], w_gu, w_dn, E, a_gu, a_dn, out=out, workspace=ws)
+            if layer == "w4a16":
+                ops.moe_w4a16(x[s:s + T], ids[s:s + T], w[s:s + T], w_gu, w_dn, E, a_gu, a_dn, out=out,
+                              workspace=ws)
+            else:
+                ops.moe_w4a4(x[s:s + T], ids[s:s + T], w[s:s + T], w_gu, w_dn, E, g1, g2, a_gu4, a_dn4, out=out,
+                             workspace=ws)
 
         for i in range(2):
             call(i)
@@ -394,16 +419,26 @@ def bench_moe_decode(ops, torch, Ts=(1, 4, 16), reps=3):
             gr.replay()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * n)
-        tb_s = nbytes / n / us / 1e6
-        rows.append(dict(T=T, us=round(us, 2), experts=round(sum(experts) / n, 1),
-                         mb=round(nbytes / n / 1e6, 2), tb_s=round(tb_s, 3)))
-        log(f"[moe_decode] T={T}: {us:.2f} us per layer, {sum(experts) / n:.1f} experts, "
-            f"{nbytes / n / 1e6:.1f} MB, {tb_s:.3f} TB/s")
         del gr
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+        return us, sum(experts) / n, nbytes / n
+
+    rows = []
+    for T in Ts:
+        us, ne, nb = timed(T, "w4a16")
+        rows.append(dict(T=T, us=round(us, 2), experts=round(ne, 1), mb=round(nb / 1e6, 2),
+                         tb_s=round(nb / us / 1e6, 3)))
+        log(f"[moe_decode] T={T}: {us:.2f} us per layer, {ne:.1f} experts, {nb / 1e6:.1f} MB, "
+            f"{nb / us / 1e6:.3f} TB/s")
+    cross = []
+    for T in cross_Ts:
+        u16, _, _ = timed(T, "w4a16")
+        u4, _, _ = timed(T, "w4a4")
+        cross.append(dict(T=T, tokens_per_expert=T * top_k / E, w4a16_us=round(u16, 2), w4a4_us=round(u4, 2)))
+        log(f"[moe_crossover] T={T} ({T * top_k / E:.1f} tokens per expert): W4A16 {u16:.2f} us, W4A4 {u4:.2f} us")
     del copies
     torch.cuda.empty_cache()
-    return dict(copies=C, rows=rows)
+    return dict(copies=C, rows=rows, crossover=cross)
 
 
 def bench_fused_sweep(ops, torch, reps=2):
@@ -641,6 +676,7 @@ def main():
                         "(%d copies), whole layer: align, gate_up + SiLU gate, down + routing weight, route sum"
                         % r6["copies"],
             "unit": "TB/s of the routed experts' bank bytes", "per_T": r6["rows"],
+            "crossover": r6["crossover"],
         }
     if not args.no_cpu_baseline and args.only == "all":
         res["cpu_baseline"] = cpu_baseline()

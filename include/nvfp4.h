@@ -363,6 +363,34 @@ nvfp4_status nvfp4_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_
                              int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Tokens-per-expert dispatch between the two MoE layers (FreeToken PR #736,
+ * Changes: W4A4 prefill from 4 tokens per expert on checkpoints whose experts
+ * carry static input scales, W4A16 below and for decode).
+ *   nvfp4_moe_route: pure; W4A4 iff has_act_globals && T*top_k > tpe * E,
+ *     else W4A16.  tpe (tokens per expert) defaults to 32, the measured
+ *     crossover on MI355X at E = 128, top-8, K = 2048, I = 768 (W4A16 208 us
+ *     against W4A4 213 us at T = 512, 359 against 233 at T = 1024); set it
+ *     with nvfp4_set_moe_route_tokens_per_expert (negative values give 0).
+ *   nvfp4_moe_dispatch_workspace_bytes: the workspace of the route taken.
+ *   nvfp4_moe: runs the route taken, reports it in *route_taken (may be
+ *     NULL).  g1 and g2 are both given (W4A4 possible) or both NULL (W4A16
+ *     only; INVALID_ARGUMENT if only one is).  The W4A4 route takes
+ *     alpha_*_w4a4 = 1/(g_e g1), 1/(g_e g2); the W4A16 route alpha_*_w4a16 =
+ *     1/g_e.  Other arguments and errors as the layer taken.  The two layers'
+ *     numerics differ (NVFP4 vs bf16 activations).
+ * ------------------------------------------------------------------------- */
+int nvfp4_moe_route(int64_t T, int64_t top_k, int64_t E, int has_act_globals);
+void nvfp4_set_moe_route_tokens_per_expert(int64_t tpe_max);
+int64_t nvfp4_get_moe_route_tokens_per_expert(void);
+size_t nvfp4_moe_dispatch_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I,
+                                          int has_act_globals);
+nvfp4_status nvfp4_moe(const void* x, int64_t T, int64_t ldx, const int32_t* topk_ids, const float* topk_w,
+                       int64_t top_k, int64_t E, int64_t I, const nvfp4_weight* gate_up, const nvfp4_weight* down,
+                       const float* g1, const float* g2, const float* alpha_gu_w4a4, const float* alpha_dn_w4a4,
+                       const float* alpha_gu_w4a16, const float* alpha_dn_w4a16, void* out, int64_t ldo, void* ws,
+                       size_t ws_bytes, int* route_taken, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * nvfp4_stream_read -- a measurement aid, not part of the NVFP4 method: reads
  * `bytes` of device memory once (one 16-byte nontemporal load per thread, the
  * way the W4A16 kernels read their weight units) and computes nothing from the

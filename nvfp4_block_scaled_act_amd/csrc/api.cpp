@@ -11,6 +11,7 @@ namespace {
 
 constexpr int64_t kInt32Max = 2147483647LL;
 std::atomic<int64_t> g_route_m_max{16};
+std::atomic<int64_t> g_moe_route_tpe_max{32};  // tokens per expert up to which the MoE stays W4A16
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
@@ -410,6 +411,39 @@ nvfp4_status nvfp4_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return NVFP4_ERR_ALIGNMENT;
   return hip_status(nvfp4::launch_moe_w4a16(x, T, ldx, topk_ids, topk_w, top_k, E, I, gate_up->data, down->data, K,
                                             alpha_gu, alpha_dn, out, ldo, ws, stream));
+}
+
+int nvfp4_moe_route(int64_t T, int64_t top_k, int64_t E, int has_act_globals) {
+  if (!has_act_globals || E < 1) return NVFP4_ROUTE_W4A16;
+  return T * top_k > g_moe_route_tpe_max.load() * E ? NVFP4_ROUTE_W4A4 : NVFP4_ROUTE_W4A16;
+}
+
+void nvfp4_set_moe_route_tokens_per_expert(int64_t tpe_max) {
+  g_moe_route_tpe_max.store(std::max<int64_t>(0, std::min<int64_t>(tpe_max, int64_t(1) << 31)));
+}
+
+int64_t nvfp4_get_moe_route_tokens_per_expert(void) { return g_moe_route_tpe_max.load(); }
+
+size_t nvfp4_moe_dispatch_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I,
+                                          int has_act_globals) {
+  return nvfp4_moe_route(T, top_k, E, has_act_globals) == NVFP4_ROUTE_W4A4
+             ? nvfp4_moe_workspace_bytes(T, top_k, E, K, I)
+             : nvfp4_moe_w4a16_workspace_bytes(T, top_k, E, K, I);
+}
+
+nvfp4_status nvfp4_moe(const void* x, int64_t T, int64_t ldx, const int32_t* topk_ids, const float* topk_w,
+                       int64_t top_k, int64_t E, int64_t I, const nvfp4_weight* gate_up, const nvfp4_weight* down,
+                       const float* g1, const float* g2, const float* alpha_gu_w4a4, const float* alpha_dn_w4a4,
+                       const float* alpha_gu_w4a16, const float* alpha_dn_w4a16, void* out, int64_t ldo, void* ws,
+                       size_t ws_bytes, int* route_taken, hipStream_t stream) {
+  if ((g1 == nullptr) != (g2 == nullptr)) return NVFP4_ERR_INVALID_ARGUMENT;  // both globals or neither
+  const int route = nvfp4_moe_route(T, top_k, E, g1 != nullptr);
+  if (route_taken) *route_taken = route;
+  if (route == NVFP4_ROUTE_W4A4)
+    return nvfp4_moe_w4a4(x, T, ldx, topk_ids, topk_w, top_k, E, I, gate_up, down, g1, g2, alpha_gu_w4a4,
+                          alpha_dn_w4a4, out, ldo, ws, ws_bytes, nullptr, stream);
+  return nvfp4_moe_w4a16(x, T, ldx, topk_ids, topk_w, top_k, E, I, gate_up, down, alpha_gu_w4a16, alpha_dn_w4a16,
+                         out, ldo, ws, ws_bytes, stream);
 }
 
 nvfp4_status nvfp4_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {

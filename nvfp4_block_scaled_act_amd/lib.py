@@ -65,6 +65,12 @@ _SIGS = {
     "nvfp4_linear_workspace_bytes": (SZ, [I64, I64, I64]),
     "nvfp4_linear": (I32, [P, I64, I64, C.POINTER(Weight), P, P, P, P, I64, P, SZ, C.POINTER(I32), P]),
     "nvfp4_stream_read": (I32, [P, SZ, P, P]),
+    "nvfp4_moe_route": (I32, [I64, I64, I64, I32]),
+    "nvfp4_set_moe_route_tokens_per_expert": (None, [I64]),
+    "nvfp4_get_moe_route_tokens_per_expert": (I64, []),
+    "nvfp4_moe_dispatch_workspace_bytes": (SZ, [I64, I64, I64, I64, I64, I32]),
+    "nvfp4_moe": (I32, [P, I64, I64, P, P, I64, I64, I64, C.POINTER(Weight), C.POINTER(Weight), P, P, P, P, P, P,
+                        P, I64, P, SZ, C.POINTER(I32), P]),
     "nvfp4_moe_w4a16_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
     "nvfp4_moe_w4a16_workspace_layout": (I32, [I64, I64, I64, I64, I64, C.POINTER(MoeW4A16Layout)]),
     "nvfp4_moe_w4a16": (I32, [P, I64, I64, P, P, I64, I64, I64, C.POINTER(Weight), C.POINTER(Weight), P, P, P,

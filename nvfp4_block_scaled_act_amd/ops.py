@@ -364,3 +364,59 @@ def moe_w4a16(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gat
                                        C.byref(gate_up.desc), C.byref(down.desc), _ptr(alpha_gu), _ptr(alpha_dn),
                                        _ptr(out), ldo, _ptr(ws), ws.numel(), _stream()))
     return out
+
+
+def moe_route(T: int, top_k: int, E: int, has_act_globals: bool) -> int:
+    return int(_L.load().nvfp4_moe_route(T, top_k, E, 1 if has_act_globals else 0))
+
+
+def set_moe_route_tokens_per_expert(tpe: int) -> None:
+    _L.load().nvfp4_set_moe_route_tokens_per_expert(int(tpe))
+
+
+def get_moe_route_tokens_per_expert() -> int:
+    return int(_L.load().nvfp4_get_moe_route_tokens_per_expert())
+
+
+def moe(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate_up: Weight, down: Weight,
+        num_experts: int, g1: torch.Tensor | None, g2: torch.Tensor | None, alpha_gu_w4a4: torch.Tensor | None,
+        alpha_dn_w4a4: torch.Tensor | None, alpha_gu_w4a16: torch.Tensor, alpha_dn_w4a16: torch.Tensor,
+        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, int]:
+    """Dispatched MoE layer (W4A4 above the tokens-per-expert threshold when
+    both static globals are given, else W4A16); returns (out, route taken)."""
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_w, torch.float32, "topk_w")
+    E = int(num_experts)
+    ldx = _rows(x, "x")
+    T, K = x.shape
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != T or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous [T, top_k] tensor")
+    if tuple(topk_w.shape) != tuple(topk_ids.shape) or not topk_w.is_contiguous():
+        raise ValueError("topk_w must be a contiguous tensor shaped like topk_ids")
+    top_k = topk_ids.shape[1]
+    I = down.K
+    for t, n in ((alpha_gu_w4a4, "alpha_gu_w4a4"), (alpha_dn_w4a4, "alpha_dn_w4a4"),
+                 (alpha_gu_w4a16, "alpha_gu_w4a16"), (alpha_dn_w4a16, "alpha_dn_w4a16")):
+        if t is not None:
+            _need(t, torch.float32, n)
+            if t.numel() < E or not t.is_contiguous():
+                raise ValueError(f"{n} must be a contiguous fp32 tensor of E values")
+    for t, n in ((g1, "g1"), (g2, "g2")):
+        if t is not None:
+            _scalar(t, n)
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out")
+    ldo = _rows(out, "out")
+    ws = workspace
+    if ws is None:
+        need = int(_L.load().nvfp4_moe_dispatch_workspace_bytes(T, top_k, E, K, I, 1 if g1 is not None else 0))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    route = C.c_int32(-1)
+    _L.check("nvfp4_moe",
+             _L.load().nvfp4_moe(_ptr(x), T, ldx, _ptr(topk_ids), _ptr(topk_w), top_k, E, I, C.byref(gate_up.desc),
+                                 C.byref(down.desc), _ptr(g1), _ptr(g2), _ptr(alpha_gu_w4a4), _ptr(alpha_dn_w4a4),
+                                 _ptr(alpha_gu_w4a16), _ptr(alpha_dn_w4a16), _ptr(out), ldo, _ptr(ws), ws.numel(),
+                                 C.byref(route), _stream()))
+    return out, int(route.value)

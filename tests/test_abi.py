@@ -279,3 +279,32 @@ def test_moe_w4a16_workspace_and_validation(nv):
     assert call(ws_bytes=need - 1) == WS
     assert call(ws=None) == WS
     assert call(T=0, x=None, ids=None, w=None, out=None, ws=None, ws_bytes=0) == OK
+
+
+def test_moe_route_and_dispatch_validation(nv):
+    assert nv.nvfp4_get_moe_route_tokens_per_expert() == 32
+    assert nv.nvfp4_moe_route(100000, 8, 128, 0) == 0   # no static globals: W4A16 only
+    assert nv.nvfp4_moe_route(512, 8, 128, 1) == 0      # 32 tokens per expert
+    assert nv.nvfp4_moe_route(513, 8, 128, 1) == 1
+    try:
+        nv.nvfp4_set_moe_route_tokens_per_expert(4)
+        assert nv.nvfp4_moe_route(64, 8, 128, 1) == 0 and nv.nvfp4_moe_route(65, 8, 128, 1) == 1
+        nv.nvfp4_set_moe_route_tokens_per_expert(-5)
+        assert nv.nvfp4_get_moe_route_tokens_per_expert() == 0
+        assert nv.nvfp4_moe_route(1, 1, 128, 1) == 1 and nv.nvfp4_moe_route(0, 8, 128, 1) == 0
+    finally:
+        nv.nvfp4_set_moe_route_tokens_per_expert(32)
+    for T, g in ((16, 1), (16, 0), (8192, 1)):
+        want = (nv.nvfp4_moe_workspace_bytes if nv.nvfp4_moe_route(T, 8, 128, g) else
+                nv.nvfp4_moe_w4a16_workspace_bytes)(T, 8, 128, 2048, 768)
+        assert nv.nvfp4_moe_dispatch_workspace_bytes(T, 8, 128, 2048, 768, g) == want > 0
+    E, K, I = 4, 512, 256
+    gu, dn = _w(N=E * 2 * I, K=K), _w(N=E * K, K=I)
+    route = C.c_int32(-1)
+    # one static global without the other
+    assert nv.nvfp4_moe(A16, 4, K, A16, A16, 2, E, I, C.byref(gu), C.byref(dn), A16, None, A16, A16, A16, A16,
+                        A16, K, 0x100000, 1 << 30, C.byref(route), None) == ARG
+    # the W4A16 route needs its alphas
+    assert nv.nvfp4_moe(A16, 4, K, A16, A16, 2, E, I, C.byref(gu), C.byref(dn), None, None, None, None, None, A16,
+                        A16, K, 0x100000, 1 << 30, C.byref(route), None) == ARG
+    assert route.value == 0

@@ -402,3 +402,32 @@ def test_moe_w4a16_long_k_and_empty(ops, orc):
     ie = torch.empty((0, top_k), dtype=torch.int32, device="cuda")
     we = torch.empty((0, top_k), dtype=torch.float32, device="cuda")
     assert ops.moe_w4a16(xe, ie, we, banks.w_gu, banks.w_dn, E, banks.alpha_gu, banks.alpha_dn).shape == (0, K)
+
+
+def test_moe_dispatch_routes(ops, orc):
+    # the dispatched layer runs exactly the layer it reports, on both routes
+    import torch
+
+    E, top_k, K, I, T = 4, 2, 256, 256, 40
+    x, ids, w, cal, cids, cw, gate_up, down = _small_case(606, T, E, top_k, K, I)
+    b4 = Banks(ops, orc, gate_up, down, orc.global_scale(cal), cal=(cal, cids, cw), check_experts=[0])
+    a_gu16 = torch.empty(E, dtype=torch.float32, device="cuda")
+    a_dn16 = torch.empty(E, dtype=torch.float32, device="cuda")
+    for e in range(E):  # 1/g_e from the W4A4 alphas' globals: alpha(g_e, 1)
+        a_gu16[e] = float(orc.alpha(orc.global_scale(gate_up[e]), np.float32(1.0)))
+        a_dn16[e] = float(orc.alpha(orc.global_scale(down[e]), np.float32(1.0)))
+    xd, idd, wd = bf16_dev(x), to_dev(ids), to_dev(w)
+    g1, g2 = f32_dev(b4.g1), f32_dev(b4.g2)
+    direct16 = ops.moe_w4a16(xd, idd, wd, b4.w_gu, b4.w_dn, E, a_gu16, a_dn16)
+    direct4 = ops.moe_w4a4(xd, idd, wd, b4.w_gu, b4.w_dn, E, g1, g2, b4.alpha_gu, b4.alpha_dn)
+    try:
+        for tpe, want in ((32, 0), (0, 1)):   # 40*2/4 = 20 tokens per expert
+            ops.set_moe_route_tokens_per_expert(tpe)
+            out, route = ops.moe(xd, idd, wd, b4.w_gu, b4.w_dn, E, g1, g2, b4.alpha_gu, b4.alpha_dn, a_gu16, a_dn16)
+            assert route == want
+            ref = direct16 if want == 0 else direct4
+            assert (bf16_host(out) == bf16_host(ref)).all()
+        out, route = ops.moe(xd, idd, wd, b4.w_gu, b4.w_dn, E, None, None, None, None, a_gu16, a_dn16)
+        assert route == 0 and (bf16_host(out) == bf16_host(direct16)).all()
+    finally:
+        ops.set_moe_route_tokens_per_expert(32)
