@@ -245,13 +245,35 @@ def bench_w4a4(ops, torch, reps=10):
         us = e1.elapsed_time(e2) / reps * 1e3
         sweep.append(dict(M=Ms, gemm_us=round(us, 2), tflops=round(2.0 * Ms * N * K / us / 1e6, 1)))
         log(f"[w4a4] M={Ms}: gemm {us:.1f} us = {2.0 * Ms * N * K / us / 1e6:.1f} TFLOP/s")
+    # the gated MLP's gate_up on the same weight read as [2I, K] (I = N/2):
+    # the GEMM plus the SiLU gate and NVFP4 quantization of h in its epilogue
+    I = N // 2
+    hc = torch.empty((M, I // 2), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((M, I // 16), dtype=torch.uint8, device="cuda")
+    h_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ops.gated_mlp_w4a4(ac, as_, w, al, torch.ones(1, dtype=torch.float32, device="cuda"), hc, hs, h_amax=h_amax)
+    g2 = (torch.full((1,), 2688.0, dtype=torch.float32, device="cuda") / h_amax).contiguous()
+    for _ in range(2):
+        ops.gated_mlp_w4a4(ac, as_, w, al, g2, hc, hs)
+    torch.cuda.synchronize()
+    e1.record()
+    for _ in range(reps):
+        ops.gated_mlp_w4a4(ac, as_, w, al, g2, hc, hs)
+    e2.record()
+    torch.cuda.synchronize()
+    gated_us = e1.elapsed_time(e2) / reps * 1e3
+    log(f"[w4a4] gated MLP gate_up M={M} 2I={N} K={K}: {gated_us:.1f} us = "
+        f"{2.0 * M * N * K / gated_us / 1e6:.1f} TFLOP/s (GEMM alone {sweep[-1]['gemm_us']:.1f} us)")
     flops = 2.0 * M * N * K
     qbytes = M * K * (2 + 0.5 + 1 / 16)
     log(f"[w4a4] M={M} N={N} K={K}: gemm {gemm_us:.1f} us = {flops / gemm_us / 1e6:.1f} TFLOP/s; "
         f"quantize {quant_us:.1f} us = {qbytes / quant_us / 1e3:.1f} GB/s; prepare {prepare_us:.1f} us")
     return dict(M=M, N=N, K=K, gemm_us=gemm_us, quant_us=quant_us, tflops=flops / gemm_us / 1e6,
                 linear_tflops=flops / (gemm_us + quant_us) / 1e6, quant_gbs=qbytes / quant_us / 1e3,
-                prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16, m_sweep=sweep)
+                prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16, m_sweep=sweep,
+                gated_mlp=dict(M=M, two_I=N, K=K, us=round(gated_us, 2),
+                               tflops=round(2.0 * M * N * K / gated_us / 1e6, 1),
+                               gemm_alone_us=sweep[-1]["gemm_us"]))
 
 
 def moe_flops(T, top_k, K, I):
@@ -654,6 +676,8 @@ def main():
             "linear_tflops_incl_quantize": round(r4["linear_tflops"], 2),
             "quantize_us": round(r4["quant_us"], 2), "quantize_gb_s": round(r4["quant_gbs"], 1),
             "m_sweep": r4["m_sweep"],
+            "gated_mlp": dict(r4["gated_mlp"], workload="nvfp4_gated_mlp_w4a4 on the same weight as gate_up [2I=8704, "
+                              "K=5120], M=8192: GEMM + SiLU gate + NVFP4 quantization of h [M, 4352]"),
             "roofline": {"bound": "mfma", "achieved": round(r4["tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(r4["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                          "traffic": load_traffic("w4a4_prefill_m8192",

@@ -363,6 +363,30 @@ nvfp4_status nvfp4_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_
                              int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * nvfp4_gated_mlp_w4a4 -- the first GEMM of a gated MLP on NVFP4 activations
+ * with the MoE gate_up epilogue (FreeToken PR #736, Changes: the gate_up GEMM
+ * applies the gated activation and quantizes its output to NVFP4, so the next
+ * GEMM's input needs no separate pass), for a dense batch:
+ *   z      = alpha * (dequant(A) @ dequant(W_gu).T)      [M, 2I], fp32 sums
+ *   h      = SiLU(z[:, 0:I]) * z[:, I:2I]                  fp32
+ *   h_codes, h_scales = nvfp4_quantize_act(h; g2)          [M, I/2], [M, I/16]
+ * Rows [0, I) of the weight are the gate, [I, 2I) the up projection; the
+ * outputs feed nvfp4_linear_w4a4 (the down projection) directly.
+ *   a_codes, a_scales  uint8 [M, K/2], [M, K/16] contiguous, 16-byte aligned
+ *   gate_up            prepared weight [2I, K]; I % 256 == 0
+ *   alpha              device fp32[1]: 1/(g_gu g_a); g2 device fp32[1]
+ *   h_codes, h_scales  uint8 [M, I/2] (16-byte aligned), [M, I/16], contiguous
+ *   h_amax             device fp32[1] or NULL: receives max |h| (calibration of g2)
+ * One launch (two with h_amax), no workspace, no host sync.  The h decisions
+ * are exact comparisons on the fp32 h (as in nvfp4_moe_w4a4).
+ * Errors: INVALID_ARGUMENT (nulls), INVALID_SHAPE (odd N, I % 16), UNSUPPORTED
+ * (I % 256, offsets past 2^32 bytes), ALIGNMENT, HIP.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_gated_mlp_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* gate_up,
+                                  const float* alpha, const float* g2, void* h_codes, void* h_scales, float* h_amax,
+                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Tokens-per-expert dispatch between the two MoE layers (FreeToken PR #736,
  * Changes: W4A4 prefill from 4 tokens per expert on checkpoints whose experts
  * carry static input scales, W4A16 below and for decode).

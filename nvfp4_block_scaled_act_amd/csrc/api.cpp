@@ -413,6 +413,29 @@ nvfp4_status nvfp4_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_
                                             alpha_gu, alpha_dn, out, ldo, ws, stream));
 }
 
+nvfp4_status nvfp4_gated_mlp_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* gate_up,
+                                  const float* alpha, const float* g2, void* h_codes, void* h_scales, float* h_amax,
+                                  hipStream_t stream) {
+  if (M < 0 || !alpha || !g2) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_weight(gate_up);
+  if (st != NVFP4_OK) return st;
+  const int64_t K = gate_up->K, I = gate_up->N / 2;
+  if (gate_up->N % 2 != 0 || I % 16 != 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (I % 256 != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (M == 0 || I == 0) return NVFP4_OK;  // empty batch: buffers may be null
+  if (!a_codes || !a_scales || !h_codes || !h_scales) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (M > kInt32Max) return NVFP4_ERR_INVALID_SHAPE;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(h_codes) ||
+      (reinterpret_cast<uintptr_t>(h_amax) & 3u))
+    return NVFP4_ERR_ALIGNMENT;
+  // grid rows of 256 activation rows; 32-bit byte offsets into the codes
+  if ((M + 255) / 256 * (I / 128) > kInt32Max || M * (K / 2) >= (int64_t(1) << 32) ||
+      M * (I / 2) >= (int64_t(1) << 32))
+    return NVFP4_ERR_UNSUPPORTED;
+  return hip_status(nvfp4::launch_gated_mlp_w4a4(a_codes, a_scales, M, gate_up->data, K, I, alpha, g2, h_codes,
+                                                 h_scales, h_amax, stream));
+}
+
 int nvfp4_moe_route(int64_t T, int64_t top_k, int64_t E, int has_act_globals) {
   if (!has_act_globals || E < 1) return NVFP4_ROUTE_W4A16;
   return T * top_k > g_moe_route_tpe_max.load() * E ? NVFP4_ROUTE_W4A4 : NVFP4_ROUTE_W4A16;

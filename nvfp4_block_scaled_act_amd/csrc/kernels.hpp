@@ -94,4 +94,11 @@ hipError_t launch_w4a16_grouped(bool gated, const void* a, int64_t lda, const in
                                 int64_t rows_per_expert, int64_t K, const float* alpha_e, const float* topk_w,
                                 void* out, int64_t ldo, hipStream_t stream);
 
+// Gated MLP gate_up on a dense NVFP4 batch: h = SiLU(z[:I]) * z[I:], z =
+// alpha * deq(A) . deq(W_gu)^T, quantized to NVFP4 under g2 ([M, I/2] codes,
+// [M, I/16] scales); h_amax (optional) receives max |h|.
+hipError_t launch_gated_mlp_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_gate_up,
+                                 int64_t K, int64_t I, const float* alpha, const float* g2, void* h_codes,
+                                 void* h_scales, float* h_amax, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -145,6 +145,8 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __re
   }
 }
 
+__global__ void set_u32_kernel_moe(uint32_t* p) { *p = 0u; }
+
 // The three align steps in one workgroup, for at most kChunk pairs (decode
 // batches): the same results as count + scan + scatter (stable by pair within
 // an expert), tile table entries of up to tile_rows pairs.
@@ -208,21 +210,21 @@ __global__ __launch_bounds__(kChunk) void moe_align_small_kernel(const int32_t* 
 
 // gate_up of one tile of pairs x 128 gate rows (block c, + the matching 128
 // up rows) of its expert, with the SiLU gate and NVFP4 quantization of h.
-// BMT = pair rows the workgroup computes (256, or 128 for a tile that fits).
-template <int BMT>
+// BMT = pair rows the workgroup computes (256, or 128 for a tile that fits);
+// row_of(i) = the activation row of the tile's row i (h is stored by slot).
+template <int BMT, class RowOf>
 __device__ __forceinline__ void gate_up_tile(_Float16* __restrict__ lds, const MoeTile& tile, int32_t c,
                                              const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-                                             int32_t K, int32_t top_k, const int32_t* __restrict__ sorted,
-                                             const uint8_t* __restrict__ wt, int32_t I, float alpha, float g2,
-                                             uint8_t* __restrict__ hc, uint8_t* __restrict__ hs,
-                                             uint32_t* __restrict__ h_amax) {
+                                             int32_t K, RowOf row_of, const uint8_t* __restrict__ wt, int32_t I,
+                                             float alpha, float g2, uint8_t* __restrict__ hc,
+                                             uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
   // LDS weight tiles 0..7: gate rows 128c..128c+127, 8..15: the up rows I + the same
   const int32_t gate_tile0 = tile.expert * (2 * I / 16) + 8 * c, up_tile0 = gate_tile0 + I / 16;
   gemm::AccT<BMT> acc;
   gemm::mainloop<false, BMT>(
-      acc, lds, xc, xs, [&](int i) { return int64_t(sorted[tile.slot0 + min(i, tile.rows - 1)] / top_k); }, wt,
+      acc, lds, xc, xs, row_of, wt,
       [&](int lt) { return int64_t(lt < 8 ? gate_tile0 + lt : up_tile0 + lt - 8); },
       // the wave's tiles 0, 1 are gate rows 64wn..64wn+63, tiles 2, 3 the up rows under them
       [&](int t) { return t < 2 ? 64 * wn + 32 * t : 128 + 64 * wn + 32 * (t - 2); }, K);
@@ -281,10 +283,30 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
   const MoeTile tile = tiles[ty];
   if (tile.rows == 0) return;
   const float alpha = alpha_gu[tile.expert], g2 = *g2_p;
+  auto row_of = [&](int i) { return int64_t(sorted[tile.slot0 + min(i, tile.rows - 1)] / top_k); };
   if (tile.rows <= gemm::BM / 2)
-    gate_up_tile<gemm::BM / 2>(lds, tile, c, xc, xs, K, top_k, sorted, wt, I, alpha, g2, hc, hs, h_amax);
+    gate_up_tile<gemm::BM / 2>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
   else
-    gate_up_tile<gemm::BM>(lds, tile, c, xc, xs, K, top_k, sorted, wt, I, alpha, g2, hc, hs, h_amax);
+    gate_up_tile<gemm::BM>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
+}
+
+// The same gate_up on a dense batch (a gated MLP's first GEMM): row tile ty
+// holds rows 256ty.. of the NVFP4 activations, h is stored by row.
+__global__ __launch_bounds__(gemm::kThreads) void gated_mlp_kernel(
+    const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int32_t K, int32_t M,
+    const uint8_t* __restrict__ wt, int32_t I, const float* __restrict__ alpha_p, const float* __restrict__ g2_p,
+    uint8_t* __restrict__ hc, uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
+  int32_t ty, c;
+  gemm::xcd_row_block(int32_t(blockIdx.x), I / 128, ty, c);
+  if (ty >= (M + gemm::BM - 1) / gemm::BM) return;
+  const MoeTile tile{0, ty * gemm::BM, min(gemm::BM, M - ty * gemm::BM), 0};
+  const float alpha = *alpha_p, g2 = *g2_p;
+  auto row_of = [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); };
+  if (tile.rows <= gemm::BM / 2)
+    gate_up_tile<gemm::BM / 2>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
+  else
+    gate_up_tile<gemm::BM>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
 }
 
 // down of one tile of pairs x 256 outputs (block nblk of K) of its expert,
@@ -528,6 +550,20 @@ hipError_t launch_moe_w4a16(const void* x, int64_t T, int64_t ldx, const int32_t
                              K, stream);
   if (err != hipSuccess) return err;
   return launch_route_sum(ys, inv, T, top_k, K, out, ldo, stream);
+}
+
+hipError_t launch_gated_mlp_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_gate_up,
+                                 int64_t K, int64_t I, const float* alpha, const float* g2, void* h_codes,
+                                 void* h_scales, float* h_amax, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  if (h_amax) hipLaunchKernelGGL(set_u32_kernel_moe, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(h_amax));
+  const int32_t tiles = int32_t((M + gemm::BM - 1) / gemm::BM);
+  hipLaunchKernelGGL(gated_mlp_kernel, dim3(uint32_t(gemm::xcd_rows_grid(tiles, int32_t(I / 128)))),
+                     dim3(gemm::kThreads), 0, stream, static_cast<const uint8_t*>(a_codes),
+                     static_cast<const uint8_t*>(a_scales), int32_t(K), int32_t(M),
+                     static_cast<const uint8_t*>(w_gate_up), int32_t(I), alpha, g2, static_cast<uint8_t*>(h_codes),
+                     static_cast<uint8_t*>(h_scales), reinterpret_cast<uint32_t*>(h_amax));
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

@@ -65,6 +65,7 @@ _SIGS = {
     "nvfp4_linear_workspace_bytes": (SZ, [I64, I64, I64]),
     "nvfp4_linear": (I32, [P, I64, I64, C.POINTER(Weight), P, P, P, P, I64, P, SZ, C.POINTER(I32), P]),
     "nvfp4_stream_read": (I32, [P, SZ, P, P]),
+    "nvfp4_gated_mlp_w4a4": (I32, [P, P, I64, C.POINTER(Weight), P, P, P, P, P, P]),
     "nvfp4_moe_route": (I32, [I64, I64, I64, I32]),
     "nvfp4_set_moe_route_tokens_per_expert": (None, [I64]),
     "nvfp4_get_moe_route_tokens_per_expert": (I64, []),

@@ -420,3 +420,34 @@ def moe(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate_up: 
                                  _ptr(alpha_gu_w4a16), _ptr(alpha_dn_w4a16), _ptr(out), ldo, _ptr(ws), ws.numel(),
                                  C.byref(route), _stream()))
     return out, int(route.value)
+
+
+def gated_mlp_w4a4(a_codes: torch.Tensor, a_scales: torch.Tensor, gate_up: Weight, alpha_: torch.Tensor,
+                   g2: torch.Tensor, h_codes: torch.Tensor | None = None, h_scales: torch.Tensor | None = None,
+                   h_amax: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """First GEMM of a gated MLP on NVFP4 activations: h = SiLU(z_gate) * z_up,
+    quantized to NVFP4 under g2; returns (h_codes [M, I/2], h_scales [M, I/16])."""
+    _need(a_codes, torch.uint8, "a_codes")
+    _need(a_scales, torch.uint8, "a_scales")
+    _scalar(alpha_, "alpha")
+    _scalar(g2, "g2")
+    M = a_codes.shape[0]
+    if a_codes.shape[1] * 2 != gate_up.K or tuple(a_scales.shape) != (M, gate_up.K // 16):
+        raise ValueError("activation codes/scales do not match the weight's K")
+    if not a_codes.is_contiguous() or not a_scales.is_contiguous():
+        raise ValueError("activation codes and scales must be contiguous")
+    I = gate_up.N // 2
+    if h_codes is None:
+        h_codes = torch.empty((M, I // 2), dtype=torch.uint8, device=a_codes.device)
+    if h_scales is None:
+        h_scales = torch.empty((M, I // 16), dtype=torch.uint8, device=a_codes.device)
+    if tuple(h_codes.shape) != (M, I // 2) or tuple(h_scales.shape) != (M, I // 16):
+        raise ValueError("h_codes / h_scales must be [M, I/2] / [M, I/16]")
+    if not h_codes.is_contiguous() or not h_scales.is_contiguous():
+        raise ValueError("h_codes and h_scales must be contiguous")
+    if h_amax is not None:
+        _scalar(h_amax, "h_amax")
+    _L.check("nvfp4_gated_mlp_w4a4",
+             _L.load().nvfp4_gated_mlp_w4a4(_ptr(a_codes), _ptr(a_scales), M, C.byref(gate_up.desc), _ptr(alpha_),
+                                            _ptr(g2), _ptr(h_codes), _ptr(h_scales), _ptr(h_amax), _stream()))
+    return h_codes, h_scales

@@ -308,3 +308,16 @@ def test_moe_route_and_dispatch_validation(nv):
     assert nv.nvfp4_moe(A16, 4, K, A16, A16, 2, E, I, C.byref(gu), C.byref(dn), None, None, None, None, None, A16,
                         A16, K, 0x100000, 1 << 30, C.byref(route), None) == ARG
     assert route.value == 0
+
+
+def test_gated_mlp_validation(nv):
+    M, K, I = 64, 512, 256
+    gu = _w(N=2 * I, K=K)
+    f = nv.nvfp4_gated_mlp_w4a4
+    assert f(A16, A16, M, C.byref(gu), None, A16, A16, A16, None, None) == ARG        # alpha
+    assert f(A16, A16, M, C.byref(gu), A16, None, A16, A16, None, None) == ARG        # g2
+    assert f(A16, A16, M, C.byref(_w(N=2 * I + 16, K=K)), A16, A16, A16, A16, None, None) == SHAPE  # odd N
+    assert f(A16, A16, M, C.byref(_w(N=2 * 128, K=K)), A16, A16, A16, A16, None, None) == UNSUP   # I % 256
+    assert f(A16, A16, M, C.byref(gu), A16, A16, A16 + 8, A16, None, None) == ALIGN   # h codes
+    assert f(A16, A16, M, C.byref(gu), A16, A16, None, A16, None, None) == ARG
+    assert f(None, None, 0, C.byref(gu), A16, A16, None, None, None, None) == OK        # empty batch

@@ -431,3 +431,30 @@ def test_moe_dispatch_routes(ops, orc):
         assert route == 0 and (bf16_host(out) == bf16_host(direct16)).all()
     finally:
         ops.set_moe_route_tokens_per_expert(32)
+
+
+# ------------------------------------------------------------ gated MLP
+@pytest.mark.parametrize("M,K,I", [(300, 512, 256), (1024, 2048, 768)])
+def test_gated_mlp_w4a4(ops, orc, M, K, I):
+    # the dense gated MLP = the MoE layer with one expert, one route of weight
+    # 1: h (NVFP4 under g2) against the oracle's with benign flips, then the
+    # down linear on the GPU's h against the layer's output
+    import torch
+
+    x, _, _, cal, _, _, gate_up, down = _small_case(707 + M, M, 1, 1, K, I, calib_rows=64)
+    ids = np.zeros((M, 1), np.int32)
+    w = np.ones((M, 1), np.float32)
+    cids = np.zeros((cal.shape[0], 1), np.int32)
+    cw = np.ones((cal.shape[0], 1), np.float32)
+    banks = Banks(ops, orc, gate_up, down, orc.global_scale(cal), cal=(cal, cids, cw))
+    xc, xs = ops.quantize_act(bf16_dev(x), f32_dev(banks.g1))
+    h_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    hc, hs = ops.gated_mlp_w4a4(xc, xs, banks.w_gu, banks.alpha_gu[0:1], f32_dev(banks.g2), h_amax=h_amax)
+    out = ops.linear_w4a4(hc, hs, banks.w_dn, banks.alpha_dn[0:1])
+    res = banks.oracle(orc, x, ids, w)
+    views = {"h_codes": hc, "h_scales": hs}
+    inv = np.arange(M)
+    flipped, ncf, nsf = check_h(views, inv, res, np.arange(M), 1, I)
+    stats = check_out(bf16_host(out), res, np.arange(M), flipped)
+    assert abs(h_amax.item() - res["h_amax"]) <= 1e-5 * res["h_amax"]
+    print(f"M={M}: flipped rows {len(flipped)}, code flips {ncf}, scale flips {nsf}, {stats}")
