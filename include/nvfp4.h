@@ -392,8 +392,8 @@ nvfp4_status nvfp4_gated_mlp_w4a4(const void* a_codes, const void* a_scales, int
  * carry static input scales, W4A16 below and for decode).
  *   nvfp4_moe_route: pure; W4A4 iff has_act_globals && T*top_k > tpe * E,
  *     else W4A16.  tpe (tokens per expert) defaults to 32, the measured
- *     crossover on MI355X at E = 128, top-8, K = 2048, I = 768 (W4A16 208 us
- *     against W4A4 213 us at T = 512, 359 against 233 at T = 1024); set it
+ *     crossover on MI355X at E = 128, top-8, K = 2048, I = 768 (W4A16 204 us
+ *     against W4A4 203 us at T = 512, 354 against 221 at T = 1024); set it
  *     with nvfp4_set_moe_route_tokens_per_expert (negative values give 0).
  *   nvfp4_moe_dispatch_workspace_bytes: the workspace of the route taken.
  *   nvfp4_moe: runs the route taken, reports it in *route_taken (may be

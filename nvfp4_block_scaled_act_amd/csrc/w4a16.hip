@@ -334,112 +334,6 @@ __global__ __launch_bounds__(1024) void w4a16_split_kernel(
   reduce_store(acc, red, wave, nwaves, lane, tile, M, N, alpha, out, ldo);
 }
 
-// ---------------------------------------------------------------- grouped
-// W4A16 on the experts of an MoE layer for decode-sized batches (the W4A16
-// side of the layer's tokens-per-expert dispatch, FreeToken PR #736,
-// Changes).  The align step cuts each expert's pairs into entries of up to 16
-// (MoeTile); one workgroup computes one 16-row output tile of one entry, its
-// waves taking interleaved 256-k steps, and the activation rows of a lane's
-// token column are gathered by slot (x by token for gate_up, h by slot for
-// down).  Lanes past the entry's pairs read nothing (out-of-range buffer
-// offsets) and their columns are not stored.
-//   GATED (gate_up): the workgroup computes gate tile t and up tile I/16 + t
-//     of the expert (each step's activation operands serve both) and stores
-//     h = bf16(SiLU(z_g) * z_u), z = alpha_e * acc, by slot;
-//   else (down): it stores the routing-weighted y = w * (alpha_e * acc) in
-//     fp32 by slot for the route sum.
-template <int PER, bool GATED>
-__global__ __launch_bounds__(512) void w4a16_grouped_kernel(
-    const uint16_t* __restrict__ a, int64_t lda, const int32_t* __restrict__ sorted, int32_t top_k,
-    const MoeTile* __restrict__ entries, int32_t out_tiles, const uint8_t* __restrict__ wt, int32_t rows_per_expert,
-    int32_t K, const float* __restrict__ alpha_e, const float* __restrict__ topk_w, void* __restrict__ out,
-    int64_t ldo) {
-  constexpr int R = GATED ? 2 : 1;
-  extern __shared__ float red[];  // [waves][R][64][4]
-  const int32_t entry = int32_t(blockIdx.x) / out_tiles, t = int32_t(blockIdx.x) - entry * out_tiles;
-  const MoeTile ent = entries[entry];
-  if (ent.rows <= 0) return;
-  const int lane = int(threadIdx.x & 63);
-  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  const int nwaves = int(blockDim.x >> 6);
-  const int q = lane >> 4;
-  const int32_t steps = K / 256;
-  const int32_t tiles_e = rows_per_expert / 16;
-  const int32_t wtile0 = ent.expert * tiles_e + t, wtile1 = wtile0 + tiles_e / 2;  // gate, up
-  // permuted activation loads: lane 4c + q loads what MFMA lane c + 16q needs
-  const int lrow = lane >> 2, lq = lane & 3;
-  const int src_byte = 4 * (4 * (lane & 15) + q);
-  int32_t arow = -1;
-  if (lrow < ent.rows) arow = GATED ? sorted[ent.slot0 + lrow] / top_k : ent.slot0 + lrow;
-  const __amdgpu_buffer_rsrc_t arsrc = act_rsrc(a);
-  const uint32_t aoff = arow >= 0 ? uint32_t(arow) * uint32_t(lda) * 2u + 32u * uint32_t(lq) : 0x80000000u;
-  auto unit_at = [&](int r, int32_t st) {
-    return load_unit(wt + (int64_t(r == 0 ? wtile0 : wtile1) * steps + min(st, steps - 1)) * kUnitBytes, lane);
-  };
-  auto b_at = [&](int32_t st) { return load_b_rows(arsrc, aoff, min(st, steps - 1)); };
-
-  f32x4_t acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  Unit w[2][R];
-  StepB b[2];
-  float alpha = alpha_e[ent.expert];
-#pragma unroll
-  for (int r = 0; r < R; ++r) w[0][r] = unit_at(r, wave);
-  b[0] = b_at(wave);
-  __builtin_amdgcn_sched_barrier(0);
-  settle(alpha);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (i + 1 < PER) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) w[(i + 1) & 1][r] = unit_at(r, wave + (i + 1) * nwaves);
-      b[(i + 1) & 1] = b_at(wave + (i + 1) * nwaves);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const bool live = wave + i * nwaves < steps;
-    const StepB& bs = b[i & 1];
-    uint4 b0[4], b1[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      b0[j] = to_mfma_lane(bs.v[j], src_byte);
-      b1[j] = to_mfma_lane(bs.v[4 + j], src_byte);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      mma_half(w[i & 1][r].c0, w[i & 1][r].sc, 0, b0, acc[r], live);
-      mma_half(w[i & 1][r].c1, w[i & 1][r].sc, 1, b1, acc[r], live);
-    }
-  }
-  // partial tiles added through LDS in wave order
-  if (nwaves > 1) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) *reinterpret_cast<f32x4_t*>(&red[((wave * R + r) * 64 + lane) * 4]) = acc[r];
-    __syncthreads();
-    if (wave != 0) return;
-    for (int w2 = 1; w2 < nwaves; ++w2)
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] += *reinterpret_cast<const f32x4_t*>(&red[((w2 * R + r) * 64 + lane) * 4]);
-  }
-  // lane (c, qq) holds rows 16t + 4qq + i of token column c
-  const int c = lane & 15, qq = lane >> 4;
-  if (c >= ent.rows) return;
-  const int32_t slot = ent.slot0 + c;
-  const int64_t at = int64_t(slot) * ldo + 16 * t + 4 * qq;
-  if (GATED) {
-    float h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = silu(alpha * acc[0][i]) * (alpha * acc[R - 1][i]);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + at) =
-        make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-  } else {
-    const float wr = topk_w[sorted[slot]];
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + at) =
-        make_float4(wr * (alpha * acc[0][0]), wr * (alpha * acc[0][1]), wr * (alpha * acc[0][2]),
-                    wr * (alpha * acc[0][3]));
-  }
-}
-
 // ------------------------------------------------------------------ shared
 // LDS holds two chunks of kc steps; a chunk is [kc steps][8 j][4 q][M c]
 // entries of 8 bf16 (only the M real token rows).
@@ -706,6 +600,225 @@ __global__ __launch_bounds__(1024) void w4a16_dot_kernel(
 #pragma unroll
     for (int m = 0; m < MT; ++m)
       if (m < M) out[int64_t(m) * ldo + row] = __builtin_bit_cast(uint16_t, (__bf16)(acc[m] * alpha));
+  }
+}
+
+// ---------------------------------------------------------------- grouped
+// W4A16 on the experts of an MoE layer for decode-sized batches (the W4A16
+// side of the layer's tokens-per-expert dispatch, FreeToken PR #736,
+// Changes).  The align step cuts each expert's pairs into entries of up to 16
+// (MoeTile); one workgroup computes one 16-row output tile of one entry, its
+// waves taking interleaved 256-k steps, and the activation rows of a lane's
+// token column are gathered by slot (x by token for gate_up, h by slot for
+// down).  Lanes past the entry's pairs read nothing (out-of-range buffer
+// offsets) and their columns are not stored.
+//   GATED (gate_up): the workgroup computes gate tile t and up tile I/16 + t
+//     of the expert (each step's activation operands serve both) and stores
+//     h = bf16(SiLU(z_g) * z_u), z = alpha_e * acc, by slot;
+//   else (down): it stores the routing-weighted y = w * (alpha_e * acc) in
+//     fp32 by slot for the route sum.
+// An entry of one or two pairs: the dot schedule's products on the VALU (each
+// lane loads 4 activations per token and step, the dot-product instruction
+// broadcasts them across the row; see the dot section), for the R tiles of
+// the workgroup at once.
+template <int PER, bool GATED, int MT>
+__device__ __forceinline__ void grouped_dot_body(const uint16_t* __restrict__ a, int64_t lda,
+                                                 const int32_t* __restrict__ sorted, int32_t top_k, const MoeTile& ent,
+                                                 int32_t t, const uint8_t* __restrict__ wt, int32_t rows_per_expert,
+                                                 int32_t K, const float* __restrict__ alpha_e,
+                                                 const float* __restrict__ topk_w, void* __restrict__ out, int64_t ldo,
+                                                 float* __restrict__ red) {
+  constexpr int R = GATED ? 2 : 1;
+  const int lane = int(threadIdx.x & 63);
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int nwaves = int(blockDim.x >> 6);
+  const int q = lane >> 4, n = lane & 15;
+  const int32_t steps = K / 256;
+  const int32_t tiles_e = rows_per_expert / 16;
+  const int32_t wtile[2] = {ent.expert * tiles_e + t, ent.expert * tiles_e + tiles_e / 2 + t};  // gate, up
+  const int koff = 64 * (n >> 2) + 16 * q + 8 * ((n >> 1) & 1) + 4 * (n & 1);
+  const uint16_t* arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int32_t slot = ent.slot0 + m;
+    arow[m] = a + int64_t(GATED ? sorted[slot] / top_k : slot) * lda + koff;
+  }
+  auto unit_at = [&](int r, int32_t st) {
+    return load_unit(wt + (int64_t(wtile[r]) * steps + min(st, steps - 1)) * kUnitBytes, lane);
+  };
+  auto act_at = [&](int32_t st, uint2 (&x)[MT]) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) x[m] = *reinterpret_cast<const uint2*>(arow[m] + 256 * int64_t(min(st, steps - 1)));
+  };
+  float alpha = alpha_e[ent.expert];
+  Unit w[2][R];
+  uint2 x[2][MT];
+  act_at(wave, x[0]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) w[0][r] = unit_at(r, wave);
+  if (PER > 1) {
+    act_at(wave + nwaves, x[1]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[1][r] = unit_at(r, wave + nwaves);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  settle(alpha);
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (wave + i * nwaves < steps) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) dot_step<MT>(w[i & 1][r], x[i & 1], acc[r]);
+    }
+    if (i + 2 < PER) {
+      act_at(wave + (i + 2) * nwaves, x[i & 1]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[i & 1][r] = unit_at(r, wave + (i + 2) * nwaves);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the row's 4 lanes (q), then the waves in order
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      acc[r][m] += __shfl_xor(acc[r][m], 16, 64);
+      acc[r][m] += __shfl_xor(acc[r][m], 32, 64);
+    }
+  if (nwaves > 1) {
+    if (q == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) red[((wave * R + r) * MT + m) * 16 + n] = acc[r][m];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        acc[r][m] = red[(r * MT + m) * 16 + n];
+        for (int k = 1; k < nwaves; ++k) acc[r][m] += red[((k * R + r) * MT + m) * 16 + n];
+      }
+  }
+  if (q != 0) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int32_t slot = ent.slot0 + m;
+    const int64_t at = int64_t(slot) * ldo + 16 * t + n;
+    if (GATED) {
+      const float h = silu(alpha * acc[0][m]) * (alpha * acc[R - 1][m]);
+      static_cast<uint16_t*>(out)[at] = __builtin_bit_cast(uint16_t, (__bf16)h);
+    } else {
+      static_cast<float*>(out)[at] = topk_w[sorted[slot]] * (alpha * acc[0][m]);
+    }
+  }
+}
+
+template <int PER, bool GATED>
+__global__ __launch_bounds__(512) void w4a16_grouped_kernel(
+    const uint16_t* __restrict__ a, int64_t lda, const int32_t* __restrict__ sorted, int32_t top_k,
+    const MoeTile* __restrict__ entries, int32_t out_tiles, const uint8_t* __restrict__ wt, int32_t rows_per_expert,
+    int32_t K, const float* __restrict__ alpha_e, const float* __restrict__ topk_w, void* __restrict__ out,
+    int64_t ldo) {
+  constexpr int R = GATED ? 2 : 1;
+  extern __shared__ float red[];  // [waves][R][64][4]
+  const int32_t entry = int32_t(blockIdx.x) / out_tiles, t = int32_t(blockIdx.x) - entry * out_tiles;
+  const MoeTile ent = entries[entry];
+  if (ent.rows <= 0) return;
+  if (ent.rows == 1) {
+    grouped_dot_body<PER, GATED, 1>(a, lda, sorted, top_k, ent, t, wt, rows_per_expert, K, alpha_e, topk_w, out, ldo,
+                                    red);
+    return;
+  }
+  if (ent.rows == 2) {
+    grouped_dot_body<PER, GATED, 2>(a, lda, sorted, top_k, ent, t, wt, rows_per_expert, K, alpha_e, topk_w, out, ldo,
+                                    red);
+    return;
+  }
+  const int lane = int(threadIdx.x & 63);
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int nwaves = int(blockDim.x >> 6);
+  const int q = lane >> 4;
+  const int32_t steps = K / 256;
+  const int32_t tiles_e = rows_per_expert / 16;
+  const int32_t wtile0 = ent.expert * tiles_e + t, wtile1 = wtile0 + tiles_e / 2;  // gate, up
+  // permuted activation loads: lane 4c + q loads what MFMA lane c + 16q needs
+  const int lrow = lane >> 2, lq = lane & 3;
+  const int src_byte = 4 * (4 * (lane & 15) + q);
+  int32_t arow = -1;
+  if (lrow < ent.rows) arow = GATED ? sorted[ent.slot0 + lrow] / top_k : ent.slot0 + lrow;
+  const __amdgpu_buffer_rsrc_t arsrc = act_rsrc(a);
+  const uint32_t aoff = arow >= 0 ? uint32_t(arow) * uint32_t(lda) * 2u + 32u * uint32_t(lq) : 0x80000000u;
+  auto unit_at = [&](int r, int32_t st) {
+    return load_unit(wt + (int64_t(r == 0 ? wtile0 : wtile1) * steps + min(st, steps - 1)) * kUnitBytes, lane);
+  };
+  auto b_at = [&](int32_t st) { return load_b_rows(arsrc, aoff, min(st, steps - 1)); };
+
+  f32x4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Unit w[2][R];
+  StepB b[2];
+  float alpha = alpha_e[ent.expert];
+#pragma unroll
+  for (int r = 0; r < R; ++r) w[0][r] = unit_at(r, wave);
+  b[0] = b_at(wave);
+  __builtin_amdgcn_sched_barrier(0);
+  settle(alpha);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (i + 1 < PER) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[(i + 1) & 1][r] = unit_at(r, wave + (i + 1) * nwaves);
+      b[(i + 1) & 1] = b_at(wave + (i + 1) * nwaves);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool live = wave + i * nwaves < steps;
+    const StepB& bs = b[i & 1];
+    uint4 b0[4], b1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b0[j] = to_mfma_lane(bs.v[j], src_byte);
+      b1[j] = to_mfma_lane(bs.v[4 + j], src_byte);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      mma_half(w[i & 1][r].c0, w[i & 1][r].sc, 0, b0, acc[r], live);
+      mma_half(w[i & 1][r].c1, w[i & 1][r].sc, 1, b1, acc[r], live);
+    }
+  }
+  // partial tiles added through LDS in wave order
+  if (nwaves > 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) *reinterpret_cast<f32x4_t*>(&red[((wave * R + r) * 64 + lane) * 4]) = acc[r];
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w2 = 1; w2 < nwaves; ++w2)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] += *reinterpret_cast<const f32x4_t*>(&red[((w2 * R + r) * 64 + lane) * 4]);
+  }
+  // lane (c, qq) holds rows 16t + 4qq + i of token column c
+  const int c = lane & 15, qq = lane >> 4;
+  if (c >= ent.rows) return;
+  const int32_t slot = ent.slot0 + c;
+  const int64_t at = int64_t(slot) * ldo + 16 * t + 4 * qq;
+  if (GATED) {
+    float h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = silu(alpha * acc[0][i]) * (alpha * acc[R - 1][i]);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + at) =
+        make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+  } else {
+    const float wr = topk_w[sorted[slot]];
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + at) =
+        make_float4(wr * (alpha * acc[0][0]), wr * (alpha * acc[0][1]), wr * (alpha * acc[0][2]),
+                    wr * (alpha * acc[0][3]));
   }
 }
 
