@@ -336,7 +336,11 @@ nvfp4_status nvfp4_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t
  * nvfp4_moe_w4a4 without g1, g2 and h_amax; ws >= nvfp4_moe_w4a16_workspace_bytes.
  * The align cuts each expert's pairs into entries of up to 16; both GEMMs run
  * one workgroup per (entry, 16-row tile of the expert's weight), so a call
- * reads the banks of the experts it routes to, each once per 16 of its pairs.
+ * reads the banks of the experts it routes to, each once per 16 of its pairs
+ * (an entry of one or two pairs on VALU dot products, a larger one on the
+ * MFMA).  A pair's fp32 sum order follows its entry's size, so a token's
+ * output bits may change (within fp32 rounding) with the number of other
+ * pairs routed to its experts; for given inputs the outputs are the same.
  * Five launches, no host sync; the outputs are the same bits on every call.
  * After the call the workspace holds, at the offsets
  * nvfp4_moe_w4a16_workspace_layout reports: sorted, offsets, inv (as for
