@@ -347,6 +347,76 @@ def bench_moe(ops, torch, reps=10):
     return dict(T=T, E=E, top_k=top_k, K=K, I=I, layer_us=layer_us, tflops=flops / layer_us / 1e6)
 
 
+def bench_w4a16_tactics(ops, torch, shapes=((11008, 4096), (4096, 11008), (14336, 4096), (4096, 14336),
+                                            (28672, 4096)), Ms=(1, 2, 4, 8, 16), reps=3):
+    """Cold check of the W4A16 default schedule on shapes outside the decode
+    sweep: every candidate (schedule, waves per tile, tiles per workgroup or
+    chunk) timed over graph replays of rotated weight copies (about 2.2 GB,
+    so each call reads its weight from HBM), the default against the best."""
+    import math
+
+    from nvfp4_block_scaled_act_amd import synth
+    from nvfp4_block_scaled_act_amd.lib import NVFP4Error
+
+    rows = []
+    for N, K in shapes:
+        steps = K // 256
+        wd = torch.from_numpy(synth.normal_bf16(1, N, K).view(np.int16)).cuda().view(torch.bfloat16)
+        g = ops.global_scale(wd)
+        c, s = ops.quantize_act(wd, g)
+        del wd
+        copies = [ops.prepare_weight(c, s) for _ in range(max(2, math.ceil(2.2e9 / (N * K * 9 // 16))))]
+        al = ops.alpha(g)
+        a = torch.from_numpy(synth.normal_bf16(2, 16, K).view(np.int16)).cuda().view(torch.bfloat16)
+        for M in Ms:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            cands = [(0, 0, 0)]
+            for ks in (2, 4, 6, 8, 12, 16):
+                per = -(-steps // min(ks, steps))
+                if per <= 8:
+                    cands.append((3, ks, 0))
+                    if -(-steps // per) <= 8:
+                        cands.append((3, ks, 2))
+                    if M <= 4:
+                        cands.append((4, ks, 0))
+            cands += [(2, 0, kc) for kc in (1, 2, 4) if M * min(kc, steps) <= 64]
+            res = []
+            for sch, ks, kc in cands:
+                def call(w, sch=sch, ks=ks, kc=kc):
+                    ops.linear_w4a16(a[:M], w, al, out=out, schedule=sch, ksplit=ks, chunk_steps=kc)
+                try:
+                    call(copies[0])
+                except NVFP4Error:
+                    continue  # not a valid candidate at this shape
+                torch.cuda.synchronize()
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    for w in copies:
+                        call(w)
+                gr.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    gr.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                res.append((e0.elapsed_time(e1) / reps / len(copies) * 1e3, sch, ks, kc))
+                del gr
+            best = min(res)
+            rows.append({"N": N, "K": K, "M": M, "default_us": round(res[0][0], 2), "best_us": round(best[0], 2),
+                         "best": {"schedule": best[1], "ksplit": best[2], "chunk_steps": best[3]},
+                         "default_over_best": round(res[0][0] / best[0], 3)})
+            print("[tactics] N=%d K=%d M=%d default %.2f us, best %.2f us %s" % (N, K, M, res[0][0], best[0],
+                  best[1:]), file=sys.stderr, flush=True)
+        del copies
+        torch.cuda.empty_cache()
+    return {"workload": "W4A16 default vs best candidate, cold, N x K in %s, M in %s" % (list(shapes), list(Ms)),
+            "geomean_default_over_best": round(float(np.exp(np.mean([np.log(r["default_over_best"]) for r in rows]))),
+                                               4),
+            "per_shape": rows}
+
+
 def bench_moe_decode(ops, torch, Ts=(1, 4, 16), cross_Ts=(16, 64, 256, 512, 1024, 2048), reps=3):
     """The same MoE layer at decode batch sizes through nvfp4_moe_w4a16 (bf16
     x and h, align into entries of up to 16 pairs, grouped W4A16 gate_up with
@@ -567,7 +637,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the W4A16 calls directly (counter runs)")
-    ap.add_argument("--only", choices=["all", "headline", "fused", "fused_sweep", "w4a4", "moe", "moe_decode", "copy"],
+    ap.add_argument("--only", choices=["all", "headline", "fused", "fused_sweep", "w4a4", "moe", "moe_decode", "w4a16_tactics", "copy"],
                     default="all",
                     help="run one part (for profiler runs); 'copy' times a plain 256 MiB device copy, the "
                          "reference for the HBM byte counters")
@@ -598,6 +668,9 @@ def main():
     if args.only == "moe":
         r5 = bench_moe(ops, torch, reps=args.steps)
         print(json.dumps({"moe": {k: round(v, 3) if isinstance(v, float) else v for k, v in r5.items()}}))
+        return
+    if args.only == "w4a16_tactics":
+        print(json.dumps({"w4a16_tactics": bench_w4a16_tactics(ops, torch)}))
         return
     if args.only == "moe_decode":
         print(json.dumps({"moe_decode": bench_moe_decode(ops, torch)}))

@@ -873,6 +873,9 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
     // weight at M = 1)
     int64_t ks = std::max<int64_t>({(8 * cus + tiles - 1) / tiles, (steps + kSplitMaxPer - 1) / kSplitMaxPer, 4});
     if (tiles <= 2 * cus) ks = std::max<int64_t>(ks, (steps + 1) / 2);
+    // long K (more than 32 steps): at most about 4 steps per wave (measured
+    // cold at K = 11008 and 14336: 5-8 % faster than 6-7 steps)
+    if (steps > 32) ks = std::max<int64_t>(ks, (steps + 3) / 4);
     c.schedule = 4;
     c.ksplit = int(std::min<int64_t>({ks, steps, 16}));
     return c;
@@ -887,7 +890,8 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
     // between one and two tiles per CU, two tiles per workgroup on 4 waves
     // (each step's activation operands serve both; measured 4-20 % faster at
     // 320 tiles, slower at 224 and within noise at 544)
-    const int64_t want = (8 * cus + tiles - 1) / tiles;
+    int64_t want = (8 * cus + tiles - 1) / tiles;
+    if (steps > 32) want = std::max<int64_t>(want, (steps + 3) / 4);  // long K: about 4 steps per wave
     c.ksplit = int(std::max<int64_t>(1, std::min<int64_t>({want, steps, 16})));
     const int64_t ks = std::min<int64_t>(c.ksplit, steps);
     c.schedule = (steps + ks - 1) / ks <= kSplitMaxPer ? 3 : 1;
@@ -895,6 +899,15 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
       W4A16Config two = c;
       two.chunk_steps = 2;
       two.ksplit = int(std::max<int64_t>(std::min<int64_t>(4, steps), (steps + kSplitMaxPer - 1) / kSplitMaxPer));
+      if (w4a16_config_valid(two, M, K)) c = two;
+    } else if (tiles > 2 * cus + cus / 2) {
+      // more than 2.5 tiles per CU: two tiles per workgroup on 8 waves
+      // (measured cold at N = 11008, 14336 and 28672, K = 4096: 15-37 %
+      // faster than one tile per workgroup; neutral at 2.1 tiles per CU)
+      W4A16Config two = c;
+      two.schedule = 3;
+      two.chunk_steps = 2;
+      two.ksplit = int(std::min<int64_t>(8, steps));
       if (w4a16_config_valid(two, M, K)) c = two;
     }
   }
