@@ -211,7 +211,7 @@ def bench_w4a4(ops, torch, reps=10):
     al = ops.alpha(gw, ga)
     ac, as_ = ops.quantize_act(ad, ga)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    ws = ops.w4a4_workspace()  # stream-K finish of the last round of tiles
+    ws = ops.w4a4_workspace()  # the workspace entry point (its stream-K finish is switched off)
     for _ in range(2):
         ops.quantize_act(ad, ga, ac, as_)
         ops.linear_w4a4(ac, as_, w, al, out=out, workspace=ws)

@@ -209,6 +209,9 @@ nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_
  * fp32 partial tiles in a fixed order (deterministic for a given shape and
  * device).  Results agree with nvfp4_linear_w4a4 to fp32 rounding (a
  * different summation order on the leftover tiles), not bit for bit.
+ * The stream-K finish is currently switched off (its cross-XCD exchange of
+ * partials was not always coherent): the call runs nvfp4_linear_w4a4's
+ * kernel and gives its bits, with the same workspace contract.
  *   ws, ws_bytes  device workspace of at least
  *                 nvfp4_linear_w4a4_workspace_bytes() bytes (for the device
  *                 current at the call), 256-byte aligned, ZERO-FILLED before

@@ -341,11 +341,22 @@ int64_t w4a4_workspace_bytes() {
   return cus * kPartialBytes + 4 * cus + 256;
 }
 
+// The stream-K finish is switched off: now and then a finishing workgroup
+// summed a partial that was not the one just published (two calls on the
+// same inputs gave different bits, each time right after another kernel had
+// overwritten the partial slots).  Its flags protocol never timed out, so the
+// read-modify-write atomics were coherent across XCDs, but the partial reads
+// after the agent-scope acquire were not always.  Until the exchange no
+// longer depends on that acquire, the workspace entry point runs the
+// one-launch kernel (same bits as the call without a workspace).
+constexpr bool kStreamKFinish = false;
+
 hipError_t launch_w4a4_sk(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
                           int64_t K, const float* alpha, void* out, int64_t ldo, void* ws, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   // (the stream-K stores use 32-bit byte offsets into out)
-  const SkPlan plan = M * ldo * 2 < (int64_t(1) << 31) ? sk_plan(M, N, K) : SkPlan{0, 0};
+  const SkPlan plan =
+      kStreamKFinish && M * ldo * 2 < (int64_t(1) << 31) ? sk_plan(M, N, K) : SkPlan{0, 0};
   if (plan.G == 0) return launch_w4a4(a_codes, a_scales, M, w_tiled, N, K, alpha, out, ldo, stream);
   const int64_t cus = device_cu_count();
   auto* partials = static_cast<float4*>(ws);
