@@ -151,6 +151,39 @@ nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t
                                   size_t dst_bytes, nvfp4_weight* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Interop with the 128x4-swizzled block-scale layout that checkpoints and
+ * NVIDIA's block-scaled GEMMs use (the FreeToken PR #737 page, Changes: the
+ * linears keep the checkpoint's codes with 128x4-swizzled scales, and the
+ * activation quant kernel can write that layout; FlashInfer PR #3597, API:
+ * weights prepared with the 128x4 scale-factor layout).  The pages name the
+ * layout without its index map; this library takes the public one: the
+ * [rows, K/16] scale matrix is padded with zeros to a multiple of 128 rows and
+ * 4 columns and stored as 512-byte blocks of 128 rows x 4 columns, row-major
+ * over the blocks; inside a block, scale (r, c) sits at byte
+ * 16 (r % 32) + 4 ((r / 32) % 4) + c % 4.
+ * nvfp4_swizzled_scales_bytes(rows, K) = roundup(rows, 128) * roundup(K/16, 4),
+ * 0 for an invalid shape (rows < 0, K <= 0, K % 16).
+ *
+ * nvfp4_quantize_act_swizzled: nvfp4_quantize_act with the scales written in
+ * that layout, padding included (zeros), into scales (>= scales_bytes =
+ * nvfp4_swizzled_scales_bytes(M, K) bytes; WORKSPACE if smaller).  Codes and
+ * scale values are those of nvfp4_quantize_act, bit for bit.  Other
+ * arguments and errors as nvfp4_quantize_act.
+ *
+ * nvfp4_prepare_weight_swizzled: nvfp4_prepare_weight from row-major codes
+ * [N, K/2] and swizzled scales (scales_bytes >= nvfp4_swizzled_scales_bytes(N,
+ * K), else WORKSPACE); the result is byte for byte the one nvfp4_prepare_weight
+ * makes from the same scales in row-major order.  Errors as
+ * nvfp4_prepare_weight.
+ * ------------------------------------------------------------------------- */
+size_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t K);
+nvfp4_status nvfp4_quantize_act_swizzled(const void* a, int64_t M, int64_t K, int64_t lda, const float* g,
+                                         void* codes, void* scales, size_t scales_bytes, hipStream_t stream);
+nvfp4_status nvfp4_prepare_weight_swizzled(const void* codes, const void* scales, size_t scales_bytes, int64_t N,
+                                           int64_t K, void* dst, size_t dst_bytes, nvfp4_weight* out,
+                                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * nvfp4_linear_w4a16 -- out = bf16((a @ dequant(W).T) * alpha), fp32
  * accumulation (FlashInfer PR #3597, Description), for decode-sized M <= 16
  * (FreeToken PR #737, Changes: small-batch kernels on the same weight).

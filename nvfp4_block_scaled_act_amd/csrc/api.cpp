@@ -122,6 +122,27 @@ nvfp4_status nvfp4_alpha(const float* g_w, const float* g_a, float* alpha_out, h
   return hip_status(nvfp4::launch_alpha(g_w, g_a, alpha_out, stream));
 }
 
+size_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t K) {
+  if (rows < 0 || K <= 0 || K % 16 != 0) return 0;
+  return size_t((rows + 127) / 128 * 128) * size_t((K / 16 + 3) / 4 * 4);
+}
+
+nvfp4_status nvfp4_quantize_act_swizzled(const void* a, int64_t M, int64_t K, int64_t lda, const float* g,
+                                         void* codes, void* scales, size_t scales_bytes, hipStream_t stream) {
+  if (M < 0 || K <= 0) return NVFP4_ERR_INVALID_SHAPE;
+  if (K % 16 != 0 || lda < K) return NVFP4_ERR_INVALID_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!g || !codes || !scales) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_bf16_input(a, M, K, lda);
+  if (st != NVFP4_OK) return st;
+  if (!aligned16(codes)) return NVFP4_ERR_ALIGNMENT;
+  const size_t need = nvfp4_swizzled_scales_bytes(M, K);
+  if (scales_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (need > size_t(kInt32Max)) return NVFP4_ERR_INVALID_SHAPE;
+  if ((M + 127) / 128 * 128 / 4 > 65535) return NVFP4_ERR_UNSUPPORTED;  // row mapping (grid.y)
+  return hip_status(nvfp4::launch_quantize(a, M, K, lda, g, codes, scales, stream, (K / 16 + 3) / 4 * 4));
+}
+
 size_t nvfp4_prepared_weight_bytes(int64_t N, int64_t K) {
   if (check_weight_shape(N, K) != NVFP4_OK) return 0;
   return size_t(nvfp4::tiled_weight_bytes(N, K));
@@ -138,6 +159,31 @@ nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t
   if (need > 0 && (!aligned16(dst) || (reinterpret_cast<uintptr_t>(codes) & 7u))) return NVFP4_ERR_ALIGNMENT;
   if (need > 0) {
     st = hip_status(nvfp4::launch_retile(codes, scales, N, K, dst, stream));
+    if (st != NVFP4_OK) return st;
+  }
+  nvfp4_weight w;
+  w.data = dst;
+  w.N = N;
+  w.K = K;
+  w.layout = NVFP4_LAYOUT_TILED;
+  w.reserved = 0;
+  *out = w;
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_prepare_weight_swizzled(const void* codes, const void* scales, size_t scales_bytes, int64_t N,
+                                           int64_t K, void* dst, size_t dst_bytes, nvfp4_weight* out,
+                                           hipStream_t stream) {
+  if (!out) return NVFP4_ERR_INVALID_ARGUMENT;
+  nvfp4_status st = check_weight_shape(N, K);
+  if (st != NVFP4_OK) return st;
+  const size_t need = size_t(nvfp4::tiled_weight_bytes(N, K));
+  if (need > 0 && (!codes || !scales || !dst)) return NVFP4_ERR_INVALID_ARGUMENT;
+  if (dst_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (need > 0 && scales_bytes < nvfp4_swizzled_scales_bytes(N, K)) return NVFP4_ERR_WORKSPACE;
+  if (need > 0 && (!aligned16(dst) || (reinterpret_cast<uintptr_t>(codes) & 7u))) return NVFP4_ERR_ALIGNMENT;
+  if (need > 0) {
+    st = hip_status(nvfp4::launch_retile(codes, scales, N, K, dst, stream, (K / 16 + 3) / 4 * 4));
     if (st != NVFP4_OK) return st;
   }
   nvfp4_weight w;

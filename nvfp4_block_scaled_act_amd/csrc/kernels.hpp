@@ -7,8 +7,10 @@
 
 namespace nvfp4 {
 
+// swz_cols > 0: scales in the 128x4-swizzled layout with swz_cols (K/16
+// rounded up to 4) scale columns, padding rows and columns written as zero.
 hipError_t launch_quantize(const void* a, int64_t M, int64_t K, int64_t lda, const float* g, void* codes,
-                           void* scales, hipStream_t stream);
+                           void* scales, hipStream_t stream, int64_t swz_cols = 0);
 hipError_t launch_global_scale(const void* x, int64_t rows, int64_t cols, int64_t ld, float* g_out,
                                hipStream_t stream);
 hipError_t launch_alpha(const float* g_w, const float* g_a, float* alpha, hipStream_t stream);
@@ -19,7 +21,15 @@ int device_cu_count();
 // Re-tiling of a canonical [N, K/2] + [N, K/16] weight into the tiled layout
 // both linears read (K % 256 == 0); tiled_weight_bytes is its size.
 int64_t tiled_weight_bytes(int64_t N, int64_t K);
-hipError_t launch_retile(const void* codes, const void* scales, int64_t N, int64_t K, void* dst, hipStream_t stream);
+hipError_t launch_retile(const void* codes, const void* scales, int64_t N, int64_t K, void* dst, hipStream_t stream,
+                         int64_t swz_cols = 0);
+// Byte offset of scale (row, col) in the 128x4-swizzled layout with cols_pad
+// (a multiple of 4) scale columns: 512-byte blocks of 128 rows x 4 columns,
+// row-major over the blocks; inside a block, row r and column c at
+// 16 (r % 32) + 4 ((r / 32) % 4) + c % 4.
+__host__ __device__ inline int64_t swizzled_scale_offset(int64_t row, int64_t col, int64_t cols_pad) {
+  return ((row >> 7) * (cols_pad >> 2) + (col >> 2)) * 512 + (row & 31) * 16 + ((row >> 5) & 3) * 4 + (col & 3);
+}
 
 // W4A16 skinny kernel: out[M, N] = bf16(alpha * a[M, K] @ dequant(W)^T), M <= 16.
 struct W4A16Config {

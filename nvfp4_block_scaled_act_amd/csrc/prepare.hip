@@ -24,7 +24,8 @@ namespace nvfp4 {
 namespace {
 
 __global__ __launch_bounds__(256) void retile_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                                     int32_t N, int32_t K, int64_t units, uint8_t* __restrict__ dst) {
+                                                     int32_t N, int32_t K, int64_t units, uint8_t* __restrict__ dst,
+                                                     int32_t swz_cols) {
   const int64_t gid = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // one wave per unit
   if (gid >= units) return;
   const int lane = int(threadIdx.x & 63);
@@ -40,7 +41,9 @@ __global__ __launch_bounds__(256) void retile_kernel(const uint8_t* __restrict__
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       c[p] = *reinterpret_cast<const uint2*>(crow + 32 * p + 8 * q);
-      sc |= uint32_t(srow[4 * p + q]) << (8 * p);
+      const uint8_t sb = swz_cols > 0 ? scales[swizzled_scale_offset(row, s * 16 + 4 * p + q, swz_cols)]
+                                      : srow[4 * p + q];
+      sc |= uint32_t(sb) << (8 * p);
     }
   }
   uint8_t* u = dst + gid * 2304;
@@ -53,12 +56,13 @@ __global__ __launch_bounds__(256) void retile_kernel(const uint8_t* __restrict__
 
 int64_t tiled_weight_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * (K / 256) * 2304; }
 
-hipError_t launch_retile(const void* codes, const void* scales, int64_t N, int64_t K, void* dst, hipStream_t stream) {
+hipError_t launch_retile(const void* codes, const void* scales, int64_t N, int64_t K, void* dst, hipStream_t stream,
+                         int64_t swz_cols) {
   const int64_t units = (N + 15) / 16 * (K / 256);
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL(retile_kernel, dim3(uint32_t((units + 3) / 4)), dim3(256), 0, stream,
                      static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales), int32_t(N), int32_t(K),
-                     units, static_cast<uint8_t*>(dst));
+                     units, static_cast<uint8_t*>(dst), int32_t(swz_cols));
   return hipGetLastError();
 }
 

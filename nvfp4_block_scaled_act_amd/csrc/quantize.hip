@@ -129,7 +129,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
                                                        int32_t rows, int32_t blocks_per_row,
                                                        const float* __restrict__ g_ptr,
                                                        uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales, int32_t swz_cols,
+                                                       int32_t rows_pad) {
   __shared__ ScaleTables T;
   const int32_t j = int32_t(blockIdx.x) * 64 + int32_t(threadIdx.x & 63);
   const int32_t row0 = (int32_t(blockIdx.y) * 4 + int32_t(threadIdx.x >> 6)) * kRowsPerWave;
@@ -152,7 +153,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     T.mid6[threadIdx.x] = sb == 0 ? 0.0f : 3.0f * (e4m3_pos_value(sb - 1) + val);
   }
   __syncthreads();
-  if (!active) return;
+  if (!active) {
+    // swizzled scales: the padding rows (up to a multiple of 128) and columns
+    // (up to a multiple of 4) are zero
+    if (swz_cols > 0 && j < swz_cols)
+      for (int r = 0; r < kRowsPerWave; ++r) {
+        const int32_t row = row0 + r;
+        if (row < rows_pad && (row >= rows || j >= blocks_per_row))
+          scales[swizzled_scale_offset(row, j, swz_cols)] = 0;
+      }
+    return;
+  }
   const int32_t half_k = blocks_per_row * 8;
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
@@ -162,7 +173,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     const int32_t row = row0 + r;
     if (row < rows) {
       *reinterpret_cast<uint2*>(codes + int64_t(row) * half_k + int64_t(j) * 8) = make_uint2(c0, c1);
-      scales[int64_t(row) * blocks_per_row + j] = uint8_t(s);
+      scales[swz_cols > 0 ? swizzled_scale_offset(row, j, swz_cols) : int64_t(row) * blocks_per_row + j] =
+          uint8_t(s);
+    } else if (swz_cols > 0 && row < rows_pad) {
+      scales[swizzled_scale_offset(row, j, swz_cols)] = 0;
     }
   }
 }
@@ -205,12 +219,14 @@ __global__ void alpha_kernel(const float* gw, const float* ga, float* alpha) {
 }  // namespace
 
 hipError_t launch_quantize(const void* a, int64_t M, int64_t K, int64_t lda, const float* g, void* codes,
-                           void* scales, hipStream_t stream) {
+                           void* scales, hipStream_t stream, int64_t swz_cols) {
   if (M == 0) return hipSuccess;
   const int32_t bpr = int32_t(K / 16);
-  dim3 grid((bpr + 63) / 64, uint32_t((M + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave)));
+  const int64_t rows = swz_cols > 0 ? (M + 127) / 128 * 128 : M;  // the grid covers the padding rows
+  dim3 grid((bpr + 63) / 64, uint32_t((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave)));
   hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a), lda,
-                     int32_t(M), bpr, g, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales));
+                     int32_t(M), bpr, g, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                     int32_t(swz_cols), int32_t(rows));
   return hipGetLastError();
 }
 

@@ -92,6 +92,46 @@ def quantize_act(a: torch.Tensor, g: torch.Tensor, codes: torch.Tensor | None = 
     return codes, scales
 
 
+def swizzled_scales_bytes(rows: int, K: int) -> int:
+    return int(_L.load().nvfp4_swizzled_scales_bytes(rows, K))
+
+
+def quantize_act_swizzled(a: torch.Tensor, g: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """quantize_act with the scales in the 128x4-swizzled layout (a flat
+    uint8 tensor of swizzled_scales_bytes(M, K) bytes, padding zeroed)."""
+    _need(a, torch.bfloat16, "a")
+    _scalar(g, "g")
+    lda = _rows(a, "a")
+    M, K = a.shape
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=a.device)
+    nb = swizzled_scales_bytes(M, K)
+    scales = torch.empty(max(nb, 1), dtype=torch.uint8, device=a.device)
+    _L.check("nvfp4_quantize_act_swizzled",
+             _L.load().nvfp4_quantize_act_swizzled(_ptr(a), M, K, lda, _ptr(g), _ptr(codes), _ptr(scales), nb,
+                                                   _stream()))
+    return codes, scales[:nb]
+
+
+def prepare_weight_swizzled(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None) -> Weight:
+    """prepare_weight from row-major codes [N, K/2] and 128x4-swizzled
+    scales (a flat uint8 tensor of swizzled_scales_bytes(N, K) bytes)."""
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if not codes.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("weight codes and scales must be contiguous")
+    N, half = codes.shape
+    K = 2 * half
+    nbytes = prepared_weight_bytes(N, K)
+    if out is None:
+        out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
+    _need(out, torch.uint8, "out")
+    desc = _L.Weight()
+    _L.check("nvfp4_prepare_weight_swizzled",
+             _L.load().nvfp4_prepare_weight_swizzled(_ptr(codes), _ptr(scales), scales.numel(), N, K, _ptr(out),
+                                                     out.numel(), C.byref(desc), _stream()))
+    return Weight(out, desc)
+
+
 def prepared_weight_bytes(N: int, K: int) -> int:
     return int(_L.load().nvfp4_prepared_weight_bytes(N, K))
 

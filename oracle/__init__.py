@@ -6,7 +6,10 @@ NVFP4 MoE expert layer (W4A4, and W4A16 for decode-sized batches).  Only the tes
 CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
 never loads it, and the two share no code.
 
-Functions whose parity is unpinned: none of the linear-path functions.  The MoE
+Functions whose parity is unpinned: none of the linear-path functions.  The
+128x4 scale swizzle (``swizzle_scales_128x4``) is parity unpinned against the
+pages, which name the layout without its index map: it follows the public
+layout, and its tests pin it to that layout's closed-form byte offset.  The MoE
 calibration of the second activation global (max |h| over a calibration batch)
 follows a reading, not a passage of the pages, and is parity unpinned as a
 choice of value (its arithmetic is the pinned global-scale formula).
@@ -281,3 +284,27 @@ def moe_w4a16(x_bf16, ids, rw, gu_codes, gu_scales, dn_codes, dn_scales, alpha_g
                         _ptr(res["h_ref"]), _ptr(res["h_sabs"]), _ptr(res["out"]), _ptr(res["ref"]),
                         _ptr(res["sabs"]))
     return res
+
+
+def swizzle_scales_128x4(scales: np.ndarray) -> np.ndarray:
+    """Block scales [rows, K/16] in the 128x4-swizzled layout that the FreeToken
+    PR #737 page (Changes) says checkpoints and the block-scaled GEMMs take.
+    The page names the layout without its index map, so this follows the
+    public one.  Pad with zeros to a multiple of 128 rows and 4 columns.  Split
+    the rows into (block, 4 groups of 32) and the columns into (block, 4).
+    Store block by block, and inside a block row r % 32 outermost, then the
+    group (r / 32) % 4, then the column.  Returns a flat uint8 array."""
+    rows, cols = scales.shape
+    rp, cp = -(-rows // 128) * 128, -(-cols // 4) * 4
+    pad = np.zeros((rp, cp), dtype=np.uint8)
+    pad[:rows, :cols] = scales
+    # axes: row block, row group of 32, row in group, column block, column in block
+    t = pad.reshape(rp // 128, 4, 32, cp // 4, 4)
+    return np.ascontiguousarray(t.transpose(0, 3, 2, 1, 4)).reshape(-1)
+
+
+def unswizzle_scales_128x4(buf: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """The inverse of swizzle_scales_128x4: the [rows, cols] scales back."""
+    rp, cp = -(-rows // 128) * 128, -(-cols // 4) * 4
+    t = np.asarray(buf, dtype=np.uint8)[:rp * cp].reshape(rp // 128, cp // 4, 32, 4, 4)
+    return np.ascontiguousarray(t.transpose(0, 3, 2, 1, 4)).reshape(rp, cp)[:rows, :cols]

@@ -321,3 +321,26 @@ def test_gated_mlp_validation(nv):
     assert f(A16, A16, M, C.byref(gu), A16, A16, A16 + 8, A16, None, None) == ALIGN   # h codes
     assert f(A16, A16, M, C.byref(gu), A16, A16, None, A16, None, None) == ARG
     assert f(None, None, 0, C.byref(gu), A16, A16, None, None, None, None) == OK        # empty batch
+
+
+def test_swizzled_scales_validation(nv):
+    # roundup(rows, 128) x roundup(K/16, 4) bytes
+    assert nv.nvfp4_swizzled_scales_bytes(300, 272) == 384 * 20
+    assert nv.nvfp4_swizzled_scales_bytes(128, 256) == 128 * 16
+    assert nv.nvfp4_swizzled_scales_bytes(0, 256) == 0
+    assert nv.nvfp4_swizzled_scales_bytes(128, 24) == 0      # K % 16
+    q = nv.nvfp4_quantize_act_swizzled
+    need = nv.nvfp4_swizzled_scales_bytes(300, 272)
+    assert q(A16, 300, 272, 272, A16, A16, A16, need - 1, None) == WS
+    assert q(A16, 300, 24, 24, A16, A16, A16, need, None) == SHAPE
+    assert q(A16, 300, 272, 272, None, A16, A16, need, None) == ARG
+    assert q(A16, 300, 272, 272, A16, A16 + 8, A16, need, None) == ALIGN
+    assert q(None, 0, 272, 272, A16, None, None, 0, None) == OK         # empty batch
+    d = L.Weight()
+    p = nv.nvfp4_prepare_weight_swizzled
+    wneed = nv.nvfp4_prepared_weight_bytes(128, 256)
+    sneed = nv.nvfp4_swizzled_scales_bytes(128, 256)
+    assert p(A16, A16, sneed - 1, 128, 256, A16, wneed, C.byref(d), None) == WS
+    assert p(A16, A16, sneed, 128, 256, A16, wneed - 1, C.byref(d), None) == WS
+    assert p(A16, A16, sneed, 128, 24, A16, wneed, C.byref(d), None) == SHAPE
+    assert p(A16, A16, sneed, 128, 256, A16, wneed, None, None) == ARG

@@ -138,3 +138,39 @@ def test_deterministic(ops):
     c1, s1 = ops.quantize_act(xd, g)
     c2, s2 = ops.quantize_act(xd, g)
     assert (u8_host(c1) == u8_host(c2)).all() and (u8_host(s1) == u8_host(s2)).all()
+
+
+# ------------------------------------------------------------------ 128x4-swizzled scales
+
+@pytest.mark.parametrize("M,K", [(300, 272), (1, 16), (128, 4096), (513, 1024)])
+def test_quantize_swizzled(ops, orc, M, K):
+    # codes as the row-major call, scales in the 128x4 layout with zero padding,
+    # bit for bit against the oracle's quantization and swizzle
+    import torch
+
+    a = synth.normal_bf16(41 + M, M, K)
+    g = orc.global_scale(a)
+    oc, os_ = orc.quantize(a, g)
+    ad, gd = bf16_dev(a), f32_dev(g)
+    torch.empty(1 << 24, dtype=torch.uint8, device="cuda").fill_(0xFF)  # leave non-zero bytes in the allocator
+    c, s = ops.quantize_act_swizzled(ad, gd)
+    assert (u8_host(c) == oc).all()
+    assert (u8_host(s) == orc.swizzle_scales_128x4(os_)).all()
+
+
+def test_prepare_weight_swizzled(ops, orc):
+    # the prepared weight from swizzled scales equals the one from row-major
+    # scales byte for byte (ragged N: the last 16-row tile and 128-row block)
+    import torch
+
+    N, K = 300, 512
+    W = synth.normal_bf16(43, N, K)
+    wd = bf16_dev(W)
+    gd = ops.global_scale(wd)
+    c, s = ops.quantize_act(wd, gd)
+    w_row = ops.prepare_weight(c, s)
+    sw = torch.from_numpy(orc.swizzle_scales_128x4(u8_host(s))).cuda()
+    w_swz = ops.prepare_weight_swizzled(c, sw)
+    assert (u8_host(w_swz.data) == u8_host(w_row.data)).all()
+    _, s2 = ops.quantize_act_swizzled(wd, gd)
+    assert (u8_host(ops.prepare_weight_swizzled(c, s2).data) == u8_host(w_row.data)).all()
