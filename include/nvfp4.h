@@ -177,6 +177,18 @@ nvfp4_status nvfp4_prepare_weight(const void* codes, const void* scales, int64_t
  * nvfp4_prepare_weight.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t K);
+
+/* nvfp4_fused_weight_global -- the one weight global of a fused weight (say
+ * q|k|v or gate|up stored as one [N, K] matrix) whose parts were quantized
+ * under their own globals: the largest per-part global, with the block
+ * scales unchanged (the FreeToken PR #737 page, Changes, which also warns at
+ * load time when the parts' globals differ by more than 5 %).  A host call on
+ * host memory, no launch.
+ *   g_parts  host fp32[n_parts], each finite and > 0
+ *   g_out    host fp32: max of g_parts
+ *   warn     host int32 or NULL: 1 when max > 1.05 * min (in double), else 0
+ * Errors: INVALID_ARGUMENT (null, n_parts <= 0, a global not finite or <= 0). */
+nvfp4_status nvfp4_fused_weight_global(const float* g_parts, int64_t n_parts, float* g_out, int32_t* warn);
 nvfp4_status nvfp4_quantize_act_swizzled(const void* a, int64_t M, int64_t K, int64_t lda, const float* g,
                                          void* codes, void* scales, size_t scales_bytes, hipStream_t stream);
 nvfp4_status nvfp4_prepare_weight_swizzled(const void* codes, const void* scales, size_t scales_bytes, int64_t N,

@@ -3,6 +3,7 @@
 #include "../../include/nvfp4.h"
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 
 #include "kernels.hpp"
@@ -120,6 +121,20 @@ nvfp4_status nvfp4_global_scale(const void* x, int64_t rows, int64_t cols, int64
 nvfp4_status nvfp4_alpha(const float* g_w, const float* g_a, float* alpha_out, hipStream_t stream) {
   if (!g_w || !alpha_out) return NVFP4_ERR_INVALID_ARGUMENT;
   return hip_status(nvfp4::launch_alpha(g_w, g_a, alpha_out, stream));
+}
+
+nvfp4_status nvfp4_fused_weight_global(const float* g_parts, int64_t n_parts, float* g_out, int32_t* warn) {
+  if (!g_parts || !g_out || n_parts <= 0) return NVFP4_ERR_INVALID_ARGUMENT;
+  float lo = g_parts[0], hi = g_parts[0];
+  for (int64_t i = 0; i < n_parts; ++i) {
+    const float g = g_parts[i];
+    if (!(g > 0.0f) || !std::isfinite(g)) return NVFP4_ERR_INVALID_ARGUMENT;
+    lo = std::min(lo, g);
+    hi = std::max(hi, g);
+  }
+  *g_out = hi;
+  if (warn) *warn = double(hi) > 1.05 * double(lo) ? 1 : 0;
+  return NVFP4_OK;
 }
 
 size_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t K) {

@@ -55,6 +55,7 @@ _SIGS = {
     "nvfp4_prepared_weight_bytes": (SZ, [I64, I64]),
     "nvfp4_prepare_weight": (I32, [P, P, I64, I64, P, SZ, C.POINTER(Weight), P]),
     "nvfp4_swizzled_scales_bytes": (SZ, [I64, I64]),
+    "nvfp4_fused_weight_global": (I32, [P, I64, P, P]),
     "nvfp4_quantize_act_swizzled": (I32, [P, I64, I64, I64, P, P, P, SZ, P]),
     "nvfp4_prepare_weight_swizzled": (I32, [P, P, SZ, I64, I64, P, SZ, C.POINTER(Weight), P]),
     "nvfp4_linear_w4a16": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, P]),

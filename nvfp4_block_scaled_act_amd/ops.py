@@ -92,6 +92,22 @@ def quantize_act(a: torch.Tensor, g: torch.Tensor, codes: torch.Tensor | None = 
     return codes, scales
 
 
+def fused_weight_global(g_parts) -> tuple[float, bool]:
+    """The global of a fused weight from its parts' globals (host floats):
+    the largest one, and whether the parts differ by more than 5 %."""
+    import warnings
+
+    arr = (C.c_float * len(g_parts))(*[float(g) for g in g_parts])
+    g, warn = C.c_float(0.0), C.c_int32(0)
+    _L.check("nvfp4_fused_weight_global",
+             _L.load().nvfp4_fused_weight_global(C.cast(arr, C.c_void_p), len(g_parts), C.cast(C.byref(g), C.c_void_p),
+                                                 C.cast(C.byref(warn), C.c_void_p)))
+    if warn.value:
+        warnings.warn("fused NVFP4 weight: the parts' globals differ by more than 5 %% (%s); the largest is used "
+                      "with the block scales unchanged" % list(g_parts))
+    return g.value, bool(warn.value)
+
+
 def swizzled_scales_bytes(rows: int, K: int) -> int:
     return int(_L.load().nvfp4_swizzled_scales_bytes(rows, K))
 

@@ -344,3 +344,41 @@ def test_swizzled_scales_validation(nv):
     assert p(A16, A16, sneed, 128, 256, A16, wneed - 1, C.byref(d), None) == WS
     assert p(A16, A16, sneed, 128, 24, A16, wneed, C.byref(d), None) == SHAPE
     assert p(A16, A16, sneed, 128, 256, A16, wneed, None, None) == ARG
+
+
+def test_fused_weight_global(nv):
+    # the largest per-part global; a warning when the parts differ by more than 5 %
+    f = nv.nvfp4_fused_weight_global
+
+    def call(gs):
+        arr = (C.c_float * len(gs))(*gs)
+        g, w = C.c_float(0.0), C.c_int32(-1)
+        st = f(C.cast(arr, C.c_void_p), len(gs), C.cast(C.byref(g), C.c_void_p), C.cast(C.byref(w), C.c_void_p))
+        return st, g.value, w.value
+
+    st, g, w = call([400.0, 410.0, 405.0])
+    assert (st, g, w) == (OK, 410.0, 0)
+    st, g, w = call([400.0, 430.0])       # 7.5 % apart
+    assert (st, g, w) == (OK, 430.0, 1)
+    st, g, w = call([400.0, 419.0])       # 4.75 % apart
+    assert (st, g, w) == (OK, 419.0, 0)
+    assert call([512.0])[:3] == (OK, 512.0, 0)
+    assert call([400.0, 0.0])[0] == ARG
+    assert call([400.0, float("inf")])[0] == ARG
+    assert call([400.0, float("nan")])[0] == ARG
+    g = C.c_float(0.0)
+    assert f(None, 1, C.cast(C.byref(g), C.c_void_p), None) == ARG
+    arr = (C.c_float * 1)(1.0)
+    assert f(C.cast(arr, C.c_void_p), 0, C.cast(C.byref(g), C.c_void_p), None) == ARG
+
+
+def test_fused_weight_global_binding_warns():
+    import warnings
+
+    from nvfp4_block_scaled_act_amd import ops
+
+    with warnings.catch_warnings(record=True) as rec:
+        warnings.simplefilter("always")
+        assert ops.fused_weight_global([300.0, 330.0]) == (330.0, True)
+        assert ops.fused_weight_global([300.0, 301.0]) == (301.0, False)
+    assert len(rec) == 1 and "5 %" in str(rec[0].message)
