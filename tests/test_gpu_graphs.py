@@ -1,8 +1,9 @@
 """HIP-graph capture of the compute calls: every replay must give the eager
 result bit for bit (all three paths have a fixed summation order), with eager
-work and host synchronizations between the replays.  The W4A4 stream-K path is
-the one with state across calls (its workspace flags, which each call must
-leave zeroed); the MoE layer clears its h amax inside a kernel, not with a
+work and host synchronizations between the replays.  The W4A4 workspace entry
+point is the one with state across calls (its workspace flags, which each call
+must leave zeroed; its stream-K finish is currently switched off, so it runs
+the one-launch kernel); the MoE layer clears its h amax inside a kernel, not with a
 memset, so it is capturable too.
 """
 import numpy as np
