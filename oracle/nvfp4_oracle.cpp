@@ -351,6 +351,31 @@ void orc_linear_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const int6
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// The pairs q = tt*top_k + r of the selected tokens (tt indexes `tokens`, or
+// is the token itself when `tokens` is null) routed to each expert, in pair
+// order.  A pair whose id lies outside [0, E) belongs to no expert: it is
+// skipped and adds nothing to its token's sum.
+std::vector<std::vector<int64_t>> pairs_by_expert(const int32_t* ids, const int64_t* tokens, int64_t n_tok,
+                                                  int64_t top_k, int64_t E) {
+  std::vector<std::vector<int64_t>> by(static_cast<size_t>(E));
+  for (int64_t tt = 0; tt < n_tok; ++tt) {
+    const int64_t t = tokens ? tokens[tt] : tt;
+    for (int64_t r = 0; r < top_k; ++r) {
+      const int64_t e = ids[t * top_k + r];
+      if (e >= 0 && e < E) by[size_t(e)].push_back(tt * top_k + r);
+    }
+  }
+  return by;
+}
+
+}  // namespace
+
+extern "C" {
+
 // NVFP4 MoE expert layer (W4A4 on both GEMMs) for selected tokens.
 //   x      : bf16 [T, K] hidden states
 //   ids, w : [T, top_k] expert ids (int32) and routing weights (fp32)
@@ -358,16 +383,20 @@ void orc_linear_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const int6
 //   down   : codes [E, K, I/2], scales [E, K, I/16]
 //   g1, g2 : static activation globals of the two GEMM inputs
 //   alpha_gu[e] = fp32(1/(g_gu[e]*g1)), alpha_dn[e] = fp32(1/(g_dn[e]*g2))
-// For each selected token t and route r (expert e):
+// For each selected token t and route r whose expert id e lies in [0, E)
+// (a route with any other id is skipped and adds nothing):
 //   z[j]   = alpha_gu[e] * <dequant(q(x_t; g1)), dequant(gate_up[e])[j]>, j < 2I (exact sum)
 //   h[i]   = SiLU(z[i]) * z[I + i]                                 (fp64, i < I)
 //   y[k]   = alpha_dn[e] * <dequant(q(h; g2)), dequant(down[e])[k]> (exact sum)
-//   out[t] = bf16_rne(sum_r w[t, r] * y_r)                          (fp64 sum)
+//   out[t] = bf16_rne(sum_r w[t, r] * y_r)       (fp64, routes added in order r = 0, 1, ...)
+// The work runs expert by expert, each expert's banks dequantized once; the
+// sums and their order are the ones written above.
 // Per (token, route) the oracle's own h codes/scales are returned
-// ([n_tok*top_k, I/2], [n_tok*top_k, I/16]) with, per h element, the relative
-// distance of |h|*g2/S to the nearest e2m1 rounding boundary, and per h block
-// the relative distance of amax*g2/6 to the nearest E4M3 boundary (margins
-// tell a benign rounding flip from a wrong code).  ref/sabs as for the linears.
+// ([n_tok*top_k, I/2], [n_tok*top_k, I/16]; zeros for a skipped pair) with,
+// per h element, the relative distance of |h|*g2/S to the nearest e2m1
+// rounding boundary, and per h block the relative distance of amax*g2/6 to
+// the nearest E4M3 boundary (margins tell a benign rounding flip from a
+// wrong code; infinite for a skipped pair).  ref/sabs as for the linears.
 // h_amax (optional, one double) receives max |h| over the computed pairs.
 void orc_moe_w4a4(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, const float* rw,
                   int64_t top_k, int64_t E, int64_t I,
@@ -378,26 +407,61 @@ void orc_moe_w4a4(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, c
                   uint8_t* h_codes, uint8_t* h_scales, double* h_code_margin, double* h_scale_margin,
                   double* h_amax, uint16_t* out, double* ref, double* sabs) {
   (void)T;
-  (void)E;
-  const int64_t twoI = 2 * I;
-  double amax_all = 0.0;
-#pragma omp parallel for schedule(dynamic, 1) reduction(max : amax_all)
+  const int64_t twoI = 2 * I, P = n_tok * top_k;
+  const double inf = std::numeric_limits<double>::infinity();
+
+  // Each selected token's hidden state quantized under g1, dequantized in 2^-10 units.
+  std::vector<int64_t> xa(size_t(n_tok * K));
+#pragma omp parallel for schedule(static)
   for (int64_t tt = 0; tt < n_tok; ++tt) {
     const int64_t t = tokens ? tokens[tt] : tt;
-    // Quantize the token's hidden state (g1) and dequantize it, in 2^-10 units.
     std::vector<uint8_t> xc(K / 2), xs(K / 16);
     orc_quantize_bf16(x + t * K, 1, K, K, g1, xc.data(), xs.data());
-    std::vector<int64_t> xa(K);
-    for (int64_t k = 0; k < K; ++k) xa[k] = dequant_units(xc.data(), xs.data(), k);
-    std::vector<double> acc(K, 0.0), acc_abs(K, 0.0);
-    for (int64_t r = 0; r < top_k; ++r) {
-      const int64_t e = ids[t * top_k + r];
-      const uint8_t* guc = gu_codes + e * twoI * (K / 2);
-      const uint8_t* gus = gu_scales + e * twoI * (K / 16);
+    for (int64_t k = 0; k < K; ++k) xa[size_t(tt * K + k)] = dequant_units(xc.data(), xs.data(), k);
+  }
+
+  // Skipped pairs: no h, infinite margins, nothing added.
+  for (int64_t p = 0; p < P; ++p) {
+    std::memset(h_codes + p * (I / 2), 0, size_t(I / 2));
+    std::memset(h_scales + p * (I / 16), 0, size_t(I / 16));
+    if (h_code_margin)
+      for (int64_t i = 0; i < I; ++i) h_code_margin[p * I + i] = inf;
+    if (h_scale_margin)
+      for (int64_t b = 0; b < I / 16; ++b) h_scale_margin[p * (I / 16) + b] = inf;
+  }
+
+  // y[p] = alpha_dn * exact down sum of pair p, ya[p] = the same of |products|.
+  std::vector<double> y(size_t(P * K), 0.0), ya(size_t(P * K), 0.0);
+  const std::vector<std::vector<int64_t>> by_expert = pairs_by_expert(ids, tokens, n_tok, top_k, E);
+  std::vector<int64_t> wgu, wdn;
+  double amax_all = 0.0;
+  for (int64_t e = 0; e < E; ++e) {
+    const std::vector<int64_t>& pe = by_expert[size_t(e)];
+    if (pe.empty()) continue;
+    // The expert's two banks, dequantized once (2^-10 units).
+    const uint8_t* guc = gu_codes + e * twoI * (K / 2);
+    const uint8_t* gus = gu_scales + e * twoI * (K / 16);
+    const uint8_t* dnc = dn_codes + e * K * (I / 2);
+    const uint8_t* dns = dn_scales + e * K * (I / 16);
+    wgu.resize(size_t(twoI * K));
+    wdn.resize(size_t(K * I));
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < twoI; ++j)
+      for (int64_t k = 0; k < K; ++k) wgu[size_t(j * K + k)] = dequant_units(guc + j * (K / 2), gus + j * (K / 16), k);
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+      for (int64_t i = 0; i < I; ++i) wdn[size_t(k * I + i)] = dequant_units(dnc + k * (I / 2), dns + k * (I / 16), i);
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(max : amax_all)
+    for (size_t q = 0; q < pe.size(); ++q) {
+      const int64_t p = pe[q], tt = p / top_k;
+      const int64_t* xr = &xa[size_t(tt * K)];
+      // gate_up, then the gated activation in fp64
       std::vector<double> z(twoI);
       for (int64_t j = 0; j < twoI; ++j) {
+        const int64_t* wr = &wgu[size_t(j * K)];
         int64_t s = 0;
-        for (int64_t k = 0; k < K; ++k) s += xa[k] * dequant_units(guc + j * (K / 2), gus + j * (K / 16), k);
+        for (int64_t k = 0; k < K; ++k) s += xr[k] * wr[k];
         z[j] = double(alpha_gu[e]) * std::ldexp(double(s), -20);
       }
       std::vector<double> h(I);
@@ -405,7 +469,7 @@ void orc_moe_w4a4(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, c
         h[i] = silu(z[i]) * z[I + i];
         amax_all = std::fmax(amax_all, std::fabs(h[i]));
       }
-      const int64_t p = tt * top_k + r;
+      // h quantized under g2, with its boundary margins
       uint8_t* hc = h_codes + p * (I / 2);
       uint8_t* hs = h_scales + p * (I / 16);
       orc_quantize_f64(h.data(), 1, I, I, g2, hc, hs);
@@ -418,26 +482,39 @@ void orc_moe_w4a4(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, c
           const int64_t idx = 16 * b + i;
           if (h_code_margin)
             h_code_margin[p * I + idx] =
-                (S == 0.0) ? std::numeric_limits<double>::infinity()
-                           : boundary_margin(std::fabs(h[idx]), double(g2), S, E2M1());
+                (S == 0.0) ? inf : boundary_margin(std::fabs(h[idx]), double(g2), S, E2M1());
         }
       }
-      // Down projection on the quantized h.
+      // down on the quantized h
       std::vector<int64_t> ha(I);
       for (int64_t i = 0; i < I; ++i) ha[i] = dequant_units(hc, hs, i);
-      const uint8_t* dnc = dn_codes + e * K * (I / 2);
-      const uint8_t* dns = dn_scales + e * K * (I / 16);
       for (int64_t k = 0; k < K; ++k) {
+        const int64_t* wr = &wdn[size_t(k * I)];
         int64_t s = 0, sa = 0;
         for (int64_t i = 0; i < I; ++i) {
-          const int64_t prod = ha[i] * dequant_units(dnc + k * (I / 2), dns + k * (I / 16), i);
+          const int64_t prod = ha[i] * wr[i];
           s += prod;
           sa += prod < 0 ? -prod : prod;
         }
-        const double y = double(alpha_dn[e]) * std::ldexp(double(s), -20);
-        const double ya = double(alpha_dn[e]) * std::ldexp(double(sa), -20);
-        acc[k] += double(rw[t * top_k + r]) * y;
-        acc_abs[k] += std::fabs(double(rw[t * top_k + r])) * ya;
+        y[size_t(p * K + k)] = double(alpha_dn[e]) * std::ldexp(double(s), -20);
+        ya[size_t(p * K + k)] = double(alpha_dn[e]) * std::ldexp(double(sa), -20);
+      }
+    }
+  }
+
+  // Each token's routes, added in order r = 0, 1, ... and rounded once.
+#pragma omp parallel for schedule(static)
+  for (int64_t tt = 0; tt < n_tok; ++tt) {
+    const int64_t t = tokens ? tokens[tt] : tt;
+    std::vector<double> acc(K, 0.0), acc_abs(K, 0.0);
+    for (int64_t r = 0; r < top_k; ++r) {
+      const int64_t e = ids[t * top_k + r];
+      if (e < 0 || e >= E) continue;
+      const int64_t p = tt * top_k + r;
+      const double wr = double(rw[t * top_k + r]);
+      for (int64_t k = 0; k < K; ++k) {
+        acc[k] += wr * y[size_t(p * K + k)];
+        acc_abs[k] += std::fabs(wr) * ya[size_t(p * K + k)];
       }
     }
     for (int64_t k = 0; k < K; ++k) {
@@ -457,7 +534,8 @@ void orc_moe_w4a4(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, c
 //   h[i]   = SiLU(z[i]) * z[I + i]                                     (fp64)
 //   hb[i]  = bf16_rne(h[i]), or h_in[pair][i] when h_in is given
 //   y[n]   = alpha_dn[e] * sum_i hb[i] * dequant(down[e])[n, i]        (fp64)
-//   out[t] = bf16_rne(sum_r w[t, r] * y_r)                             (fp64 sum)
+//   out[t] = bf16_rne(sum_r w[t, r] * y_r)       (fp64, routes added in order r = 0, 1, ...)
+// The work runs expert by expert, each expert's banks dequantized once.
 // Per pair q = tt*top_k + r (tt: index into tokens): h_bits[q] = bf16_rne(h),
 // h_ref[q] = h, and h_sabs[q] = |SiLU'(z_g)| |z_u| Sg + |SiLU(z_g)| Su, Sg
 // and Su being alpha_gu * sum |x w| of the two dot products (the scale of h's
@@ -470,31 +548,45 @@ void orc_moe_w4a16(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, 
                    const uint16_t* h_in, uint16_t* h_bits, double* h_ref, double* h_sabs,
                    uint16_t* out, double* ref, double* sabs) {
   (void)T;
-  const int64_t twoI = 2 * I;
+  const int64_t twoI = 2 * I, P = n_tok * top_k;
+  for (int64_t q = 0; q < P * I; ++q) {  // skipped pairs keep these zeros
+    if (h_bits) h_bits[q] = 0;
+    if (h_ref) h_ref[q] = 0.0;
+    if (h_sabs) h_sabs[q] = 0.0;
+  }
+  // s[p] = the down sum of pair p, sa[p] = the same of |products|.
+  std::vector<double> ys(size_t(P * K), 0.0), ysa(size_t(P * K), 0.0);
+  const std::vector<std::vector<int64_t>> by_expert = pairs_by_expert(ids, tokens, n_tok, top_k, E);
+  std::vector<double> wgu, wdn;
+  for (int64_t e = 0; e < E; ++e) {
+    const std::vector<int64_t>& pe = by_expert[size_t(e)];
+    if (pe.empty()) continue;
+    // The expert's two banks, dequantized once (exact in fp64).
+    const uint8_t* guc = gu_codes + e * twoI * (K / 2);
+    const uint8_t* gus = gu_scales + e * twoI * (K / 16);
+    const uint8_t* dnc = dn_codes + e * K * (I / 2);
+    const uint8_t* dns = dn_scales + e * K * (I / 16);
+    wgu.resize(size_t(twoI * K));
+    wdn.resize(size_t(K * I));
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < twoI; ++j)
+      for (int64_t k = 0; k < K; ++k) wgu[size_t(j * K + k)] = dequant(guc + j * (K / 2), gus + j * (K / 16), k);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < K; ++n)
+      for (int64_t i = 0; i < I; ++i) wdn[size_t(n * I + i)] = dequant(dnc + n * (I / 2), dns + n * (I / 16), i);
+
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t tt = 0; tt < n_tok; ++tt) {
-    const int64_t t = tokens ? tokens[tt] : tt;
-    std::vector<double> xv(K);
-    for (int64_t k = 0; k < K; ++k) xv[k] = bf16_to_double(x[t * K + k]);
-    std::vector<double> acc(K, 0.0), acc_abs(K, 0.0);
-    for (int64_t r = 0; r < top_k; ++r) {
-      const int64_t q = tt * top_k + r;
-      const int64_t e = ids[t * top_k + r];
-      if (e < 0 || e >= E) {
-        for (int64_t i = 0; i < I; ++i) {
-          if (h_bits) h_bits[q * I + i] = 0;
-          if (h_ref) h_ref[q * I + i] = 0.0;
-          if (h_sabs) h_sabs[q * I + i] = 0.0;
-        }
-        continue;
-      }
-      const uint8_t* guc = gu_codes + e * twoI * (K / 2);
-      const uint8_t* gus = gu_scales + e * twoI * (K / 16);
+    for (size_t qq = 0; qq < pe.size(); ++qq) {
+      const int64_t q = pe[qq], tt = q / top_k;
+      const int64_t t = tokens ? tokens[tt] : tt;
+      std::vector<double> xv(K);
+      for (int64_t k = 0; k < K; ++k) xv[k] = bf16_to_double(x[t * K + k]);
       std::vector<double> z(twoI), za(twoI);
       for (int64_t j = 0; j < twoI; ++j) {
+        const double* wr = &wgu[size_t(j * K)];
         double s = 0.0, sa = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-          const double p = xv[k] * dequant(guc + j * (K / 2), gus + j * (K / 16), k);  // exact product
+          const double p = xv[k] * wr[k];  // exact product
           s += p;
           sa += std::fabs(p);
         }
@@ -513,18 +605,33 @@ void orc_moe_w4a16(const uint16_t* x, int64_t T, int64_t K, const int32_t* ids, 
         if (h_sabs) h_sabs[q * I + i] = std::fabs(dsilu) * std::fabs(zu) * za[i] + std::fabs(silu(zg)) * za[I + i];
         hb[i] = bf16_to_double(h_in ? h_in[q * I + i] : bits);
       }
-      const uint8_t* dnc = dn_codes + e * K * (I / 2);
-      const uint8_t* dns = dn_scales + e * K * (I / 16);
       for (int64_t n = 0; n < K; ++n) {
+        const double* wr = &wdn[size_t(n * I)];
         double s = 0.0, sa = 0.0;
         for (int64_t i = 0; i < I; ++i) {
-          const double p = hb[i] * dequant(dnc + n * (I / 2), dns + n * (I / 16), i);  // exact product
+          const double p = hb[i] * wr[i];  // exact product
           s += p;
           sa += std::fabs(p);
         }
-        const double wr = double(rw[t * top_k + r]);
-        acc[n] += wr * (double(alpha_dn[e]) * s);
-        acc_abs[n] += std::fabs(wr) * double(alpha_dn[e]) * sa;
+        ys[size_t(q * K + n)] = s;
+        ysa[size_t(q * K + n)] = sa;
+      }
+    }
+  }
+
+  // Each token's routes, added in order r = 0, 1, ... and rounded once.
+#pragma omp parallel for schedule(static)
+  for (int64_t tt = 0; tt < n_tok; ++tt) {
+    const int64_t t = tokens ? tokens[tt] : tt;
+    std::vector<double> acc(K, 0.0), acc_abs(K, 0.0);
+    for (int64_t r = 0; r < top_k; ++r) {
+      const int64_t e = ids[t * top_k + r];
+      if (e < 0 || e >= E) continue;
+      const int64_t q = tt * top_k + r;
+      const double wr = double(rw[t * top_k + r]);
+      for (int64_t n = 0; n < K; ++n) {
+        acc[n] += wr * (double(alpha_dn[e]) * ys[size_t(q * K + n)]);
+        acc_abs[n] += std::fabs(wr) * double(alpha_dn[e]) * ysa[size_t(q * K + n)];
       }
     }
     for (int64_t n = 0; n < K; ++n) {

@@ -90,6 +90,30 @@ def test_token_selection(tiny_moe, orc):
     assert (sel["h_codes"][0:2] == full["h_codes"][8:10]).all()
 
 
+def test_skipped_ids(tiny_moe, orc):
+    # an id outside [0, E) adds nothing: the same sum as that route with
+    # weight 0, no h for the pair (zero codes and scales, infinite margins),
+    # and the other pairs' h unchanged
+    m = tiny_moe
+    rng = np.random.default_rng(8)
+    ids = np.stack([rng.permutation(m["E"])[:2] for _ in range(m["T"])]).astype(np.int32)
+    w = rng.uniform(0.05, 0.6, (m["T"], 2)).astype(np.float32)
+    args = (m["guc"], m["gus"], m["dnc"], m["dns"], m["g1"], m["g2"], m["agu"], m["adn"])
+    ids2 = ids.copy()
+    ids2[1, 0], ids2[3, 1] = -1, m["E"]
+    w0 = w.copy()
+    w0[1, 0] = w0[3, 1] = 0.0
+    skipped = orc.moe_w4a4(m["x"], ids2, w, *args)
+    zero_w = orc.moe_w4a4(m["x"], ids, w0, *args)
+    np.testing.assert_array_equal(skipped["ref"], zero_w["ref"])
+    np.testing.assert_array_equal(skipped["out"], zero_w["out"])
+    for p in (1 * 2 + 0, 3 * 2 + 1):
+        assert (skipped["h_codes"][p] == 0).all() and (skipped["h_scales"][p] == 0).all()
+        assert np.isinf(skipped["h_code_margin"][p]).all() and np.isinf(skipped["h_scale_margin"][p]).all()
+    kept = [p for p in range(2 * m["T"]) if p not in (2, 7)]
+    assert (skipped["h_codes"][kept] == zero_w["h_codes"][kept]).all()
+
+
 
 # ------------------------------------------------------------ W4A16 layer
 # The W4A16 layer keeps x and h in bf16 (no activation globals): with one
