@@ -211,10 +211,9 @@ def bench_w4a4(ops, torch, reps=10):
     al = ops.alpha(gw, ga)
     ac, as_ = ops.quantize_act(ad, ga)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    ws = ops.w4a4_workspace()  # the workspace entry point (its stream-K finish is switched off)
     for _ in range(2):
         ops.quantize_act(ad, ga, ac, as_)
-        ops.linear_w4a4(ac, as_, w, al, out=out, workspace=ws)
+        ops.linear_w4a4(ac, as_, w, al, out=out)
     torch.cuda.synchronize()
     # quantize -> GEMM pairs issued back to back (as consecutive prefill
     # layers would), one event before each call, one host sync at the end
@@ -223,7 +222,7 @@ def bench_w4a4(ops, torch, reps=10):
         ev[2 * i].record()
         ops.quantize_act(ad, ga, ac, as_)
         ev[2 * i + 1].record()
-        ops.linear_w4a4(ac, as_, w, al, out=out, workspace=ws)
+        ops.linear_w4a4(ac, as_, w, al, out=out)
     ev[2 * reps].record()
     torch.cuda.synchronize()
     tq = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps))
@@ -235,11 +234,11 @@ def bench_w4a4(ops, torch, reps=10):
     sweep = []
     for Ms in synth.W4A4_PREFILL["M"]:
         o = out[:Ms]
-        ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o, workspace=ws)
+        ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o)
         torch.cuda.synchronize()
         e1.record()
         for _ in range(reps):
-            ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o, workspace=ws)
+            ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o)
         e2.record()
         torch.cuda.synchronize()
         us = e1.elapsed_time(e2) / reps * 1e3

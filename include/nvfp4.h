@@ -87,6 +87,12 @@ const char* nvfp4_status_str(nvfp4_status s);
 /* Library version as an integer (major * 10000 + minor * 100 + patch). */
 int nvfp4_version(void);
 
+/* Hash of the sources this library was built from (16 hex digits of a
+ * sha256 over its source files and this header; "unknown" when built without
+ * it), so that a loader can refuse a library built from other sources.
+ * Static storage. */
+const char* nvfp4_build_source_hash(void);
+
 /* ---------------------------------------------------------------------------
  * nvfp4_quantize_act -- NVFP4 quantization of bf16 rows under a static global.
  * FreeToken PR #737, Changes (the activation quant kernel of the W4A4 route,
@@ -245,30 +251,6 @@ nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const 
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
                                const float* alpha, void* out, int64_t ldo, hipStream_t stream);
-
-/* Same product with a workspace, which lets the last round of 256 x 256
- * output tiles be finished stream-K style: when the tiles do not fill whole
- * rounds of one tile per compute unit, the 64-k steps of the leftover tiles
- * are dealt out evenly to all compute units and each leftover tile is
- * finished by the workgroup holding its last step, which adds the others'
- * fp32 partial tiles in a fixed order (deterministic for a given shape and
- * device).  Results agree with nvfp4_linear_w4a4 to fp32 rounding (a
- * different summation order on the leftover tiles), not bit for bit.
- * The stream-K finish is currently switched off (its cross-XCD exchange of
- * partials was not always coherent): the call runs nvfp4_linear_w4a4's
- * kernel and gives its bits, with the same workspace contract.
- *   ws, ws_bytes  device workspace of at least
- *                 nvfp4_linear_w4a4_workspace_bytes() bytes (for the device
- *                 current at the call), 256-byte aligned, ZERO-FILLED before
- *                 its first use; every call leaves it zero-filled again
- *                 (its flags are cleared by their consumers).  Calls that
- *                 overlap in time must not share a workspace.
- * Other arguments and errors as nvfp4_linear_w4a4, plus WORKSPACE (ws NULL or
- * too small) and ALIGNMENT (ws). */
-size_t nvfp4_linear_w4a4_workspace_bytes(void);
-nvfp4_status nvfp4_linear_w4a4_ws(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
-                                  const float* alpha, void* out, int64_t ldo, void* ws, size_t ws_bytes,
-                                  hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * M-threshold dispatch (FreeToken PR #737, Changes: W4A4 for prefill on

@@ -5,6 +5,7 @@ Usage: python -m nvfp4_block_scaled_act_amd.build
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -22,6 +23,22 @@ HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                "-Wno-unused-command-line-argument"]
 
 
+def source_hash() -> str:
+    """sha256 (first 16 hex digits) of every source the library is built
+    from: the csrc/ files in name order, then include/nvfp4.h.  The build
+    embeds it (nvfp4_build_source_hash) so that a loader can tell a library
+    built from other sources."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp", ".cpp", ".h")))
+    for f in files:
+        h.update(f.encode() + b"\0")
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(HERE, "..", "include", "nvfp4.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def _hipcc() -> str:
     for p in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
         if p and os.path.exists(p):
@@ -29,9 +46,10 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, src_hash: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, f'-DNVFP4_SOURCE_HASH="{src_hash}"', "-I", os.path.join(HERE, "..", "include"),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -41,8 +59,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    src_hash = source_hash()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, src_hash), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -70,6 +70,7 @@ nvfp4_status w4a16_checked(const void* a, int64_t M, int64_t lda, const nvfp4_we
   if (cfg_in && !nvfp4::w4a16_config_valid(*cfg_in, M, w->K)) return NVFP4_ERR_INVALID_ARGUMENT;
   if (w->N == 0) return NVFP4_OK;
   const nvfp4::W4A16Config cfg = cfg_in ? *cfg_in : nvfp4::w4a16_default_config(M, w->N, w->K);
+  if (!nvfp4::w4a16_config_valid(cfg, M, w->K)) return NVFP4_ERR_UNSUPPORTED;  // no schedule fits the shape
   return hip_status(nvfp4::launch_w4a16(a, M, lda, w->data, w->N, w->K, alpha, out, ldo, cfg, stream));
 }
 
@@ -93,6 +94,11 @@ const char* nvfp4_status_str(nvfp4_status s) {
 }
 
 int nvfp4_version(void) { return 100; }
+
+#ifndef NVFP4_SOURCE_HASH
+#define NVFP4_SOURCE_HASH "unknown"
+#endif
+const char* nvfp4_build_source_hash(void) { return NVFP4_SOURCE_HASH; }
 
 nvfp4_status nvfp4_quantize_act(const void* a, int64_t M, int64_t K, int64_t lda, const float* g, void* codes,
                                 void* scales, hipStream_t stream) {
@@ -230,8 +236,7 @@ nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const 
 namespace {
 
 nvfp4_status w4a4_checked(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
-                          const float* alpha, void* out, int64_t ldo, void* ws, size_t ws_bytes, bool with_ws,
-                          hipStream_t stream) {
+                          const float* alpha, void* out, int64_t ldo, hipStream_t stream) {
   if (M < 0 || !alpha) return NVFP4_ERR_INVALID_ARGUMENT;
   nvfp4_status st = check_weight(w);
   if (st != NVFP4_OK) return st;
@@ -242,14 +247,7 @@ nvfp4_status w4a4_checked(const void* a_codes, const void* a_scales, int64_t M, 
   if (!aligned16(a_codes) || !aligned16(a_scales)) return NVFP4_ERR_ALIGNMENT;
   // grid rows of 256 activation rows; 32-bit byte offsets into the codes
   if ((M + 255) / 256 > 65535 || M * (w->K / 2) >= (int64_t(1) << 32)) return NVFP4_ERR_UNSUPPORTED;
-  if (with_ws) {
-    if (!ws || ws_bytes < size_t(nvfp4::w4a4_workspace_bytes())) return NVFP4_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return NVFP4_ERR_ALIGNMENT;
-  }
   if (w->N == 0) return NVFP4_OK;
-  if (with_ws)
-    return hip_status(
-        nvfp4::launch_w4a4_sk(a_codes, a_scales, M, w->data, w->N, w->K, alpha, out, ldo, ws, stream));
   return hip_status(nvfp4::launch_w4a4(a_codes, a_scales, M, w->data, w->N, w->K, alpha, out, ldo, stream));
 }
 
@@ -257,15 +255,7 @@ nvfp4_status w4a4_checked(const void* a_codes, const void* a_scales, int64_t M, 
 
 nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
                                const float* alpha, void* out, int64_t ldo, hipStream_t stream) {
-  return w4a4_checked(a_codes, a_scales, M, w, alpha, out, ldo, nullptr, 0, false, stream);
-}
-
-size_t nvfp4_linear_w4a4_workspace_bytes(void) { return size_t(nvfp4::w4a4_workspace_bytes()); }
-
-nvfp4_status nvfp4_linear_w4a4_ws(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
-                                  const float* alpha, void* out, int64_t ldo, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
-  return w4a4_checked(a_codes, a_scales, M, w, alpha, out, ldo, ws, ws_bytes, true, stream);
+  return w4a4_checked(a_codes, a_scales, M, w, alpha, out, ldo, stream);
 }
 
 int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global) {

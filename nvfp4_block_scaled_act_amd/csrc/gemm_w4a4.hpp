@@ -321,9 +321,7 @@ __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ 
 // 4g .. 4g+3 of wave tile (t, u) (a float4); rows beyond M and columns beyond
 // N are not written.
 // Needs out and ldo*2 aligned to 16 bytes and n0 % 8 == 0 (else a direct store).
-// kCpol != 0: the global stores are buffer stores with that cache policy (the
-// output then spans less than 2 GiB).
-template <int BMT = BM, int kCpol = 0, typename Chunk>
+template <int BMT = BM, typename Chunk>
 __device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Chunk chunk, uint16_t* __restrict__ out,
                                                int64_t ldo, int32_t m0, int32_t M, int32_t n0, int32_t N) {
   constexpr int OP = BN + 8;  // bf16 per LDS output row
@@ -351,19 +349,7 @@ __device__ __forceinline__ void store_tile_lds(_Float16* __restrict__ lds, Chunk
     const uint4 v = *reinterpret_cast<const uint4*>(t16 + mloc * OP + 8 * piece);
     uint16_t* dst = out + int64_t(m) * ldo + n;
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    if (kCpol != 0) {
-      const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(out);
-      const int32_t off = int32_t((int64_t(m) * ldo + n) * 2);
-      if (n + 8 <= N) {
-        const u32x4_t vv = {v.x, v.y, v.z, v.w};
-        __builtin_amdgcn_raw_buffer_store_b128(vv, rsrc, off, 0, kCpol);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (n + i < N)
-            __builtin_amdgcn_raw_buffer_store_b16(uint16_t(w[i >> 1] >> (16 * (i & 1))), rsrc, off + 2 * i, 0, kCpol);
-      }
-    } else if (n + 8 <= N) {
+    if (n + 8 <= N) {
       *reinterpret_cast<uint4*>(dst) = v;
     } else {
 #pragma unroll

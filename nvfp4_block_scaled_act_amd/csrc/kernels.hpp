@@ -46,12 +46,6 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
 // W4A4 tiled GEMM: out[M, N] = bf16(alpha * dequant(A)[M, K] @ dequant(W)^T).
 hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
                        int64_t K, const float* alpha, void* out, int64_t ldo, hipStream_t stream);
-// Same with a stream-K finish of the last round (workspace of
-// w4a4_workspace_bytes() bytes, zero-filled before its first use, left
-// zero-filled; one launch at a time per workspace).
-int64_t w4a4_workspace_bytes();
-hipError_t launch_w4a4_sk(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
-                          int64_t K, const float* alpha, void* out, int64_t ldo, void* ws, hipStream_t stream);
 
 // Streaming-read diagnostic: reads `bytes` (a multiple of 16) once.
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);

@@ -876,9 +876,12 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
     // long K (more than 32 steps): at most about 4 steps per wave (measured
     // cold at K = 11008 and 14336: 5-8 % faster than 6-7 steps)
     if (steps > 32) ks = std::max<int64_t>(ks, (steps + 3) / 4);
-    c.schedule = 4;
-    c.ksplit = int(std::min<int64_t>({ks, steps, 16}));
-    return c;
+    W4A16Config dot = c;
+    dot.schedule = 4;
+    dot.ksplit = int(std::min<int64_t>({ks, steps, 16}));
+    // at most kSplitMaxPer steps per wave over at most 16 waves: above
+    // K = 16 * 8 * 256 the split schedules below take the call
+    if (w4a16_config_valid(dot, M, K)) return dot;
   }
   if (tiles >= int64_t(kSharedTiles) * cus * 3 / 2) {
     // shared: the largest chunk whose double buffer fits in 64 KiB of LDS

@@ -49,6 +49,7 @@ class MoeW4A16Layout(C.Structure):
 _SIGS = {
     "nvfp4_status_str": (C.c_char_p, [I32]),
     "nvfp4_version": (I32, []),
+    "nvfp4_build_source_hash": (C.c_char_p, []),
     "nvfp4_quantize_act": (I32, [P, I64, I64, I64, P, P, P, P]),
     "nvfp4_global_scale": (I32, [P, I64, I64, I64, P, P]),
     "nvfp4_alpha": (I32, [P, P, P, P]),
@@ -61,8 +62,6 @@ _SIGS = {
     "nvfp4_linear_w4a16": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, P]),
     "nvfp4_linear_w4a16_ex": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, I32, I32, I32, P]),
     "nvfp4_linear_w4a4": (I32, [P, P, I64, C.POINTER(Weight), P, P, I64, P]),
-    "nvfp4_linear_w4a4_workspace_bytes": (SZ, []),
-    "nvfp4_linear_w4a4_ws": (I32, [P, P, I64, C.POINTER(Weight), P, P, I64, P, SZ, P]),
     "nvfp4_route": (I32, [I64, I64, I64, I32]),
     "nvfp4_set_route_m_max": (None, [I64]),
     "nvfp4_get_route_m_max": (I64, []),
@@ -107,6 +106,13 @@ def load():
                 f = getattr(L, name)
                 f.restype = res
                 f.argtypes = args
+        from . import build as _build
+
+        want = _build.source_hash()
+        got = L.nvfp4_build_source_hash().decode() if hasattr(L, "nvfp4_build_source_hash") else "none"
+        if got != want:
+            raise RuntimeError(f"{LIB_PATH} was built from other sources (hash {got}, tree {want}): rebuild it "
+                               "with python -m nvfp4_block_scaled_act_amd.build")
         _lib = L
         return L
 

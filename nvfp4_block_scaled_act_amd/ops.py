@@ -212,15 +212,8 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None
     _L.check("nvfp4_stream_read", _L.load().nvfp4_stream_read(_ptr(src), n, _ptr(sink), _stream()))
 
 
-def w4a4_workspace(device=None) -> torch.Tensor:
-    """A zero-filled workspace for linear_w4a4(..., workspace=...) (stream-K
-    finish of the last round of tiles); every call leaves it zero-filled."""
-    n = int(_L.load().nvfp4_linear_w4a4_workspace_bytes())
-    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
-
-
 def linear_w4a4(a_codes: torch.Tensor, a_scales: torch.Tensor, w: Weight, alpha_: torch.Tensor,
-                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+                out: torch.Tensor | None = None) -> torch.Tensor:
     _need(a_codes, torch.uint8, "a_codes")
     _need(a_scales, torch.uint8, "a_scales")
     _scalar(alpha_, "alpha")
@@ -230,12 +223,6 @@ def linear_w4a4(a_codes: torch.Tensor, a_scales: torch.Tensor, w: Weight, alpha_
     if not a_codes.is_contiguous() or not a_scales.is_contiguous():
         raise ValueError("activation codes and scales must be contiguous")
     out, ldo = _out(out, M, w.N, a_codes.device)
-    if workspace is not None:
-        _need(workspace, torch.uint8, "workspace")
-        _L.check("nvfp4_linear_w4a4_ws",
-                 _L.load().nvfp4_linear_w4a4_ws(_ptr(a_codes), _ptr(a_scales), M, C.byref(w.desc), _ptr(alpha_),
-                                                _ptr(out), ldo, _ptr(workspace), workspace.numel(), _stream()))
-        return out
     _L.check("nvfp4_linear_w4a4",
              _L.load().nvfp4_linear_w4a4(_ptr(a_codes), _ptr(a_scales), M, C.byref(w.desc), _ptr(alpha_),
                                          _ptr(out), ldo, _stream()))

@@ -28,6 +28,20 @@ def test_exports_every_declared_function(nv):
         assert hasattr(nv, f)
 
 
+def test_built_from_this_tree(nv, monkeypatch):
+    # the library embeds the hash of the sources it was built from, and the
+    # loader refuses one whose hash is not the tree's
+    from nvfp4_block_scaled_act_amd import build as B
+
+    assert nv.nvfp4_build_source_hash().decode() == B.source_hash()
+    monkeypatch.setattr(B, "source_hash", lambda: "0" * 16)
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(RuntimeError, match="other sources"):
+        L.load()
+    monkeypatch.undo()
+    assert L.load() is not None
+
+
 def test_status_strings(nv):
     for code in range(7):
         assert nv.nvfp4_status_str(code)
@@ -110,18 +124,6 @@ def test_w4a16_validation(nv):
     assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 4, 3, None) == ARG  # 3 tiles per workgroup
     assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 10, 2, None) == ARG  # two tiles: 10 waves > 8
     assert g(A16, 1, 256 * 20, C.byref(wk), A16, A16, 64, 4, 2, 0, None) == ARG  # dot: 10 steps per wave > 8
-
-
-def test_w4a4_ws_validation(nv):
-    f = nv.nvfp4_linear_w4a4_ws
-    need = nv.nvfp4_linear_w4a4_workspace_bytes()
-    assert need >= 256 * 1024  # at least one 256 x 256 fp32 partial tile
-    w = _w()
-    assert f(A16, A16, 8, C.byref(w), A16, A16, 64, None, need, None) == WS          # no workspace
-    assert f(A16, A16, 8, C.byref(w), A16, A16, 64, A16, need - 1, None) == WS       # too small
-    assert f(A16, A16, 8, C.byref(w), A16, A16, 64, A16 + 16, need, None) == ALIGN   # not 256-aligned
-    assert f(A16, A16, 0, C.byref(w), A16, A16, 64, None, 0, None) == OK             # empty batch
-    assert f(A16, A16 + 4, 8, C.byref(w), A16, A16, 64, A16, need, None) == ALIGN
 
 
 def test_w4a4_validation(nv):

@@ -1,10 +1,7 @@
 """HIP-graph capture of the compute calls: every replay must give the eager
 result bit for bit (all three paths have a fixed summation order), with eager
-work and host synchronizations between the replays.  The W4A4 workspace entry
-point is the one with state across calls (its workspace flags, which each call
-must leave zeroed; its stream-K finish is currently switched off, so it runs
-the one-launch kernel); the MoE layer clears its h amax inside a kernel, not with a
-memset, so it is capturable too.
+work and host synchronizations between the replays.  The MoE layer clears its
+h amax inside a kernel, not with a memset, so it is capturable too.
 """
 import numpy as np
 import pytest
@@ -69,30 +66,20 @@ def test_graph_w4a16(ops):
     _replays_match(torch, gr, out, eager, lambda: torch.randn(1 << 20, device="cuda").sum())
 
 
-def test_graph_w4a4_streamk(ops):
+def test_graph_w4a4(ops):
     import torch
 
-    # 32 tiles of 256 x 256, each cut into pieces: every replay exchanges
-    # partials through the workspace, whose flags must come back to zero
-    N, K, M = 2048, 2048, 1024
-    w, gw = _weight(ops, 303, N, K)
-    ga = f32_dev(500.0)
-    ac, as_ = ops.quantize_act(bf16_dev(synth.normal_bf16(304, M, K)), ga)
-    al = ops.alpha(gw, ga)
-    ws = ops.w4a4_workspace()
-    eager = bf16_host(ops.linear_w4a4(ac, as_, w, al, workspace=ws))
-    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    gr = _capture(torch, lambda: ops.linear_w4a4(ac, as_, w, al, out=out, workspace=ws))
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-
-    def between():
-        # eager calls on the same workspace between replays, and NaN in every
-        # partial slot before each replay (a stale partial would show)
-        ops.linear_w4a4(ac, as_, w, al, workspace=ws)
-        ws[:cus * 256 * 1024].fill_(0xFF)
-
-    _replays_match(torch, gr, out, eager, between)
-    assert (ws[cus * 256 * 1024:cus * 256 * 1024 + 4 * cus + 4].cpu().numpy() == 0).all()
+    # 32 tiles of 256 x 256 (fewer than one per CU), then 9 x 34 = 306 tiles:
+    # a whole round on 256 CUs and 50 leftover tiles run as 128-row halves
+    for N, K, M, seed in ((2048, 2048, 1024, 303), (2304, 1024, 8704, 309)):
+        w, gw = _weight(ops, seed, N, K)
+        ga = f32_dev(500.0)
+        ac, as_ = ops.quantize_act(bf16_dev(synth.normal_bf16(seed + 1, M, K)), ga)
+        al = ops.alpha(gw, ga)
+        eager = bf16_host(ops.linear_w4a4(ac, as_, w, al))
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        gr = _capture(torch, lambda: ops.linear_w4a4(ac, as_, w, al, out=out))
+        _replays_match(torch, gr, out, eager, lambda: ops.linear_w4a4(ac, as_, w, al))
 
 
 def test_graph_moe(ops):

@@ -5,7 +5,7 @@ import pytest
 
 from nvfp4_block_scaled_act_amd import synth
 
-from helpers import bf16_dev, bf16_f64, bf16_host, f32_dev, gemm_check, u8_host
+from helpers import bf16_dev, bf16_host, f32_dev, gemm_check, schedules_for, u8_host
 
 pytestmark = pytest.mark.gpu
 
@@ -65,29 +65,6 @@ def test_w4a16_decode_sweep(ops, orc, shape_index):
         gemm_check(bf16_host(out), ref[:M], sabs[:M])
 
 
-SCHEDULES = ([(1, ks, 0) for ks in (1, 2, 3, 7, 16)] + [(2, 0, kc) for kc in (1, 2, 3, 4, 17)]
-             + [(3, ks, 0) for ks in (1, 3, 7, 16)] + [(3, ks, 2) for ks in (1, 3, 7, 8)]
-             + [(4, ks, 0) for ks in (1, 3, 7, 16)])
-
-
-def _valid(sch, M, K):
-    steps = K // 256
-    if sch[0] == 2:
-        return M * min(sch[2], steps) <= 64
-    if sch[0] == 3:  # chunk_steps 2: two tiles per workgroup, at most 8 waves
-        ks = min(sch[1], steps)
-        per = -(-steps // ks)
-        return per <= 8 and (sch[2] < 2 or -(-steps // per) <= 8)
-    if sch[0] == 4:  # dot: M <= 4, <= 8 steps per wave
-        ks = min(sch[1], steps)
-        return M <= 4 and -(-steps // ks) <= 8
-    return True
-
-
-def _schedules_for(M, K):
-    return [(0, 0, 0)] + [sch for sch in SCHEDULES if _valid(sch, M, K)]
-
-
 def test_w4a16_every_schedule(ops, orc):
     # ragged N (not a multiple of 16 or of a workgroup's 8 tiles), K with an odd
     # number of 256-k steps (17: uneven chunks), M between powers of two
@@ -97,7 +74,7 @@ def test_w4a16_every_schedule(ops, orc):
     q = Quantized(ops, orc, W)
     ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
     ad = bf16_dev(a)
-    for sch, ks, kc in _schedules_for(M, K):
+    for sch, ks, kc in schedules_for(M, K):
         out = ops.linear_w4a16(ad, q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=kc)
         gemm_check(bf16_host(out), ref, sabs)
     # every token count on a short K, including a chunk longer than K
@@ -132,6 +109,21 @@ def test_w4a16_long_k(ops, orc):
         for M in (1, 2, 3, 4):
             out = ops.linear_w4a16(ad[:M], q.w, q.alpha, schedule=sch, ksplit=ks, chunk_steps=r)
             gemm_check(bf16_host(out), ref[:M], sabs[:M])
+
+
+def test_w4a16_default_very_long_k(ops, orc):
+    # K = 256 * 129: more steps than the dot schedule's 16 waves x 8 steps, so
+    # the default takes a split schedule at every M (an invalid dot config
+    # there would fail the launch)
+    N, K = 40, 256 * 129
+    W = synth.normal_bf16(23, N, K)
+    a = synth.normal_bf16(24, 16, K)
+    q = Quantized(ops, orc, W)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    ad = bf16_dev(a)
+    for M in (1, 2, 3, 16):
+        out = ops.linear_w4a16(ad[:M], q.w, q.alpha)
+        gemm_check(bf16_host(out), ref[:M], sabs[:M])
 
 
 def test_w4a16_default_many_tiles(ops, orc):
@@ -215,8 +207,11 @@ def test_w4a16_deterministic(ops, orc):
 
 # ------------------------------------------------------------------ W4A4
 
-def _w4a4_case(ops, orc, W, a, cal, rows=None, cols=None, check_rows=None, ws=None):
-    q = Quantized(ops, orc, W, check_rows=check_rows)
+def _w4a4_case(ops, orc, W, a, cal, rows=None):
+    """Quantize W and a on the GPU (codes checked against the oracle), run the
+    W4A4 linear and check it against the oracle on all outputs (or on the
+    given rows, all columns)."""
+    q = Quantized(ops, orc, W)
     ga = orc.global_scale(cal)
     gad = ops.global_scale(bf16_dev(cal))
     assert gad.item() == ga
@@ -224,60 +219,77 @@ def _w4a4_case(ops, orc, W, a, cal, rows=None, cols=None, check_rows=None, ws=No
     ac, as_ = ops.quantize_act(ad, gad)
     al = ops.alpha(q.g_dev, gad)
     assert al.item() == orc.alpha(q.g, ga)
-    out = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=ws))
-    if ws is not None:
-        check_ws_clean(ops, ws)
-    oac, oas = orc.quantize(a if rows is None else a[rows], ga)
-    if rows is None:
-        assert (u8_host(ac) == oac).all() and (u8_host(as_) == oas).all()
-    else:
-        assert (u8_host(ac)[rows] == oac).all() and (u8_host(as_)[rows] == oas).all()
-    if cols is None:
-        wc, ws = q.codes, q.scales
-        sel_out = out if rows is None else out[rows]
-        ref, _, sabs = orc.linear_w4a4(oac, oas, wc, ws, orc.alpha(q.g, ga))
-    else:
-        wc, ws = orc.quantize(W[cols], q.g)
-        ref, _, sabs = orc.linear_w4a4(oac, oas, wc, ws, orc.alpha(q.g, ga))
-        sel_out = out[np.ix_(rows, cols)]
-    return gemm_check(sel_out, ref, sabs)
+    out = bf16_host(ops.linear_w4a4(ac, as_, q.w, al))
+    sel = slice(None) if rows is None else rows
+    oac, oas = orc.quantize(a[sel], ga)
+    assert (u8_host(ac)[sel] == oac).all() and (u8_host(as_)[sel] == oas).all()
+    ref, _, sabs = orc.linear_w4a4(oac, oas, q.codes, q.scales, orc.alpha(q.g, ga))
+    return gemm_check(out[sel], ref, sabs)
 
 
-def test_w4a4_prefill_m1024_full(ops, orc):
+@pytest.fixture(scope="module")
+def prefill(ops, orc):
+    """The W4A4 prefill workload (N=8704, K=5120, a of 8192 rows whose
+    prefixes are the smaller batches, 512-row calibration batch): the weight
+    and activations quantized on the GPU and checked against the oracle's
+    codes, and the oracle's output over all 8192 x 8704 outputs."""
     N, K = 8704, 5120
     W = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_W), N, K)
-    a = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), 1024, K)
+    a = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), 8192, K)
     cal = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_CAL), 512, K)
-    _w4a4_case(ops, orc, W, a, cal)
+    q = Quantized(ops, orc, W)
+    ga = orc.global_scale(cal)
+    gad = ops.global_scale(bf16_dev(cal))
+    assert gad.item() == ga
+    ac, as_ = ops.quantize_act(bf16_dev(a), gad)
+    oac, oas = orc.quantize(a, ga)
+    assert (u8_host(ac) == oac).all() and (u8_host(as_) == oas).all(), "activation quantization mismatch"
+    al = ops.alpha(q.g_dev, gad)
+    assert al.item() == orc.alpha(q.g, ga)
+    ref, _, sabs = orc.linear_w4a4(oac, oas, q.codes, q.scales, orc.alpha(q.g, ga))
+    return dict(q=q, ac=ac, as_=as_, al=al, ref=ref, sabs=sabs)
 
 
-@pytest.mark.parametrize("M", [4096, 8192])
-def test_w4a4_prefill_sampled(ops, orc, M):
-    N, K = 8704, 5120
-    W = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_W), N, K)
-    a = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), 8192, K)[:M]
-    cal = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_CAL), 512, K)
-    rng = np.random.default_rng(M)
-    rows = np.unique(np.concatenate([rng.integers(0, M, 96), [0, M - 1]]))
-    cols = np.unique(np.concatenate([rng.integers(0, N, 384), [0, N - 1]]))
-    _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols, check_rows=cols)
+@pytest.mark.parametrize("M", [1024, 4096, 8192])
+def test_w4a4_prefill_full(ops, prefill, M):
+    # every output of the W4A4 prefill linear at each batch size
+    p = prefill
+    out = bf16_host(ops.linear_w4a4(p["ac"][:M], p["as_"][:M], p["q"].w, p["al"]))
+    stats = gemm_check(out, p["ref"][:M], p["sabs"][:M])
+    print(f"M={M}: {stats}")
 
 
 def test_w4a4_split_final_round(ops, orc):
     # 17 x 16 tiles of 256 x 256 on 256 CUs: the 16 tiles of the final round
-    # run as 128-row halves (rows 3072.., cols 3328.. in the grouped tile
-    # order); checked in full there, and on sampled rows elsewhere
+    # run as 128-row halves; checked in full
     N, K, M = 4352, 1024, 4096
     W = synth.normal_bf16(81, N, K)
     a = synth.normal_bf16(82, M, K)
     cal = synth.normal_bf16(83, 64, K)
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([np.arange(3072, 4096), rng.integers(0, 3072, 64)]))
-    cols = np.unique(np.concatenate([np.arange(3328, 4352), rng.integers(0, 3328, 64)]))
-    _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols)
+    _w4a4_case(ops, orc, W, a, cal)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (130, 200, 512), (127, 129, 768), (300, 1000, 1024), (17, 8, 256)])
+def test_w4a4_whole_round_and_leftover(ops, orc):
+    # 9 x 34 = 306 tiles: a whole round, then 50 leftover tiles run as
+    # 128-row halves (on a 256-CU device); checked in full
+    N, K, M = 8704, 1024, 2304
+    W = synth.normal_bf16(84, N, K)
+    a = synth.normal_bf16(85, M, K)
+    cal = synth.normal_bf16(86, 64, K)
+    _w4a4_case(ops, orc, W, a, cal)
+
+
+def test_w4a4_few_tiles_long_k(ops, orc):
+    # 32 tiles over 80 steps of K, far fewer tiles than CUs; checked in full
+    N, K, M = 2048, 5120, 1024
+    W = synth.normal_bf16(87, N, K)
+    a = synth.normal_bf16(88, M, K)
+    cal = synth.normal_bf16(89, 64, K)
+    _w4a4_case(ops, orc, W, a, cal)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (130, 200, 512), (127, 129, 768), (300, 1000, 1024), (17, 8, 256),
+                                   (700, 520, 2048)])
 def test_w4a4_ragged(ops, orc, M, N, K):
     W = synth.normal_bf16(40 + N, N, K)
     a = synth.normal_bf16(50 + M, M, K)
@@ -297,106 +309,11 @@ def test_w4a4_deterministic(ops, orc):
         assert (bf16_host(ops.linear_w4a4(ac, as_, q.w, al)) == o1).all()
 
 
-# ------------------------------------------------------- W4A4, stream-K finish
-
-def poisoned_ws(ops, ws=None):
-    """A stream-K workspace whose partial slots hold NaN (flags zero), so a
-    finishing workgroup that read a stale copy of a partial instead of the
-    one just published would produce NaN, not a plausible sum."""
-    import torch
-
-    if ws is None:
-        ws = ops.w4a4_workspace()
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    ws[:cus * 256 * 1024].fill_(0xFF)
-    return ws
-
-
-def check_ws_clean(ops, ws):
-    """After a call the stream-K flags and the timed-out-wait count are zero."""
-    import torch
-
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tail = ws[cus * 256 * 1024:cus * 256 * 1024 + 4 * cus + 4].cpu().numpy()
-    assert (tail == 0).all(), "stream-K flags left set or a wait timed out"
-
-
-def test_w4a4_streamk_full_rounds(ops, orc):
-    # 9 x 34 = 306 tiles: a whole round, then 50 leftover tiles cut between
-    # the CUs (on a 256-CU device); checked in full
-    N, K, M = 8704, 1024, 2304
-    W = synth.normal_bf16(84, N, K)
-    a = synth.normal_bf16(85, M, K)
-    cal = synth.normal_bf16(86, 64, K)
-    _w4a4_case(ops, orc, W, a, cal, ws=poisoned_ws(ops))
-
-
-def test_w4a4_streamk_small_full(ops, orc):
-    # 32 tiles, each cut into 4 pieces of 20 steps; checked in full
-    N, K, M = 2048, 5120, 1024
-    W = synth.normal_bf16(87, N, K)
-    a = synth.normal_bf16(88, M, K)
-    cal = synth.normal_bf16(89, 64, K)
-    _w4a4_case(ops, orc, W, a, cal, ws=poisoned_ws(ops))
-
-
-def test_w4a4_streamk_m4096_sampled(ops, orc):
-    # 544 tiles: two whole rounds, then the 32 tiles of grouped positions
-    # 512.. (rows 3072.., cols 6656.. on a 256-CU device) split 8 ways
-    N, K, M = 8704, 5120, 4096
-    W = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_W), N, K)
-    a = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), 8192, K)[:M]
-    cal = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_CAL), 512, K)
-    rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([rng.integers(3072, M, 64), rng.integers(0, 3072, 32), [0, M - 1]]))
-    cols = np.unique(np.concatenate([rng.integers(6656, N, 256), rng.integers(0, 6656, 96), [0, N - 1]]))
-    _w4a4_case(ops, orc, W, a, cal, rows=rows, cols=cols, check_rows=cols, ws=poisoned_ws(ops))
-
-
-@pytest.mark.parametrize("M,N,K", [(1, 16, 256), (130, 200, 512), (300, 1000, 1024), (700, 520, 2048)])
-def test_w4a4_streamk_ragged(ops, orc, M, N, K):
-    # fewer tiles than CUs: each tile cut into up to 8 pieces of a few steps
-    W = synth.normal_bf16(40 + N, N, K)
-    a = synth.normal_bf16(50 + M, M, K)
-    cal = synth.normal_bf16(60 + M, 64, K)
-    _w4a4_case(ops, orc, W, a, cal, ws=poisoned_ws(ops))
-
-
-def test_w4a4_streamk_reuse_and_deterministic(ops, orc):
-    # one workspace across calls of different shapes: repeated calls give the
-    # same bits, and the stream-K result matches the workspace-free one to
-    # fp32 rounding
-    import torch
-
-    ws = ops.w4a4_workspace()
-    W = synth.normal_bf16(72, 1000, 2048)
-    q = Quantized(ops, orc, W)
-    g = f32_dev(400.0)
-    al = ops.alpha(q.g_dev, g)
-    for M in (300, 1024, 5, 300):
-        a = bf16_dev(synth.normal_bf16(73 + M, M, 2048))
-        ac, as_ = ops.quantize_act(a, g)
-        o1 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=poisoned_ws(ops, ws)))
-        check_ws_clean(ops, ws)
-        o2 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=poisoned_ws(ops, ws)))
-        if not (o1 == o2).all():
-            f1, f2 = bf16_f64(o1), bf16_f64(o2)
-            diff = np.nonzero(o1 != o2)
-            raise AssertionError(
-                f"M={M}: {len(diff[0])} outputs differ between two calls (rows {np.unique(diff[0])[:8]}, "
-                f"cols {np.unique(diff[1])[:8]}); non-finite: first {int((~np.isfinite(f1)).sum())}, "
-                f"second {int((~np.isfinite(f2)).sum())}; workspace tail after the second: "
-                f"{int(np.count_nonzero(ws[-(4 * torch.cuda.get_device_properties(0).multi_processor_count + 4):].cpu().numpy()))} "
-                f"nonzero bytes")
-        ref = bf16_f64(bf16_host(ops.linear_w4a4(ac, as_, q.w, al)))
-        got = bf16_f64(o1)
-        assert np.linalg.norm(got - ref) <= 1e-3 * np.linalg.norm(ref)
-
-
 # ------------------------------------------------------------------ dispatch
 
 def test_dispatch_routes_and_numerics(ops, orc):
-    # Large fused-weight shape scaled down in N (the routes do not depend on N).
+    # the routes at a smaller N (they do not depend on N), and a missing
+    # activation global
     N, K = 4096, 5120
     W = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_W), N, K)
     a = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_A), 256, K)
@@ -420,6 +337,81 @@ def test_dispatch_routes_and_numerics(ops, orc):
     # no activation global: always W4A16
     out, route = ops.linear(ad[:8], q.w, None, a16, None)
     assert route == 0
+
+
+@pytest.fixture(scope="module")
+def fused_large(ops, orc):
+    """The large fused-weight workload at its own shape: N=62080, K=5120 (one
+    global for the whole tensor), a of 8192 rows (the sweep's batches are its
+    prefixes), a 512-row calibration batch.  Weight and activation codes are
+    checked against the oracle's."""
+    import torch
+
+    N, K = synth.FUSED_LARGE["N"], synth.FUSED_LARGE["K"]
+    W = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_W), N, K)
+    a = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_A), 8192, K)
+    cal = synth.normal_bf16(synth.seed_for("fused_large", synth.ROLE_CAL), 512, K)
+    q = Quantized(ops, orc, W)
+    del W
+    ga = orc.global_scale(cal)
+    gad = ops.global_scale(bf16_dev(cal))
+    assert gad.item() == ga
+    ad = bf16_dev(a)
+    ac, as_ = ops.quantize_act(ad, gad)
+    oac, oas = orc.quantize(a, ga)
+    assert (u8_host(ac) == oac).all() and (u8_host(as_) == oas).all(), "activation quantization mismatch"
+    del ac, as_
+    torch.cuda.empty_cache()
+    return dict(q=q, a=a, ad=ad, ga=ga, gad=gad, oac=oac, oas=oas, a4=ops.alpha(q.g_dev, gad), N=N, K=K)
+
+
+def test_fused_large_w4a16_full(ops, orc, fused_large):
+    # the dispatched linear on the W4A16 route at M = 1, 8, 16: every output
+    f = fused_large
+    q = f["q"]
+    ref, _, sabs = orc.linear_w4a16(f["a"][:16], q.codes, q.scales, orc.alpha(q.g))
+    ops.set_route_m_max(16)
+    for M in (1, 8, 16):
+        out, route = ops.linear(f["ad"][:M], q.w, f["gad"], q.alpha, f["a4"])
+        assert route == 0
+        stats = gemm_check(bf16_host(out), ref[:M], sabs[:M])
+        print(f"M={M}: {stats}")
+
+
+def test_fused_large_w4a4_full(ops, orc, fused_large):
+    # the dispatched linear on the W4A4 route at M = 64, 256, 1024 (every
+    # output), and the W4A4 route called directly at M = 16 (the crossover)
+    f = fused_large
+    q = f["q"]
+    ref, _, sabs = orc.linear_w4a4(f["oac"][:1024], f["oas"][:1024], q.codes, q.scales, orc.alpha(q.g, f["ga"]))
+    ops.set_route_m_max(16)
+    for M in (64, 256, 1024):
+        out, route = ops.linear(f["ad"][:M], q.w, f["gad"], q.alpha, f["a4"])
+        assert route == 1
+        stats = gemm_check(bf16_host(out), ref[:M], sabs[:M])
+        print(f"M={M}: {stats}")
+    ac, as_ = ops.quantize_act(f["ad"][:16], f["gad"])
+    out = ops.linear_w4a4(ac, as_, q.w, f["a4"])
+    gemm_check(bf16_host(out), ref[:16], sabs[:16])
+
+
+def test_fused_large_w4a4_row_blocks(ops, orc, fused_large):
+    # M = 4096 and 8192 through the dispatched linear: every output of whole
+    # 256-row blocks (the first, one in the middle, and the last)
+    import torch
+
+    f = fused_large
+    q = f["q"]
+    ops.set_route_m_max(16)
+    for M in (4096, 8192):
+        out, route = ops.linear(f["ad"][:M], q.w, f["gad"], q.alpha, f["a4"])
+        assert route == 1
+        rows = np.concatenate([np.arange(0, 256), np.arange(M // 2, M // 2 + 256), np.arange(M - 256, M)])
+        ref, _, sabs = orc.linear_w4a4(f["oac"][rows], f["oas"][rows], q.codes, q.scales, orc.alpha(q.g, f["ga"]))
+        got = bf16_host(out[torch.from_numpy(rows).cuda()])
+        stats = gemm_check(got, ref, sabs)
+        print(f"M={M}: {stats}")
+        del out
 
 
 # ------------------------------------------------------ read diagnostic
