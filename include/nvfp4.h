@@ -284,6 +284,32 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
                           const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo, void* ws,
                           size_t ws_bytes, int* route_taken, hipStream_t stream);
 
+/* Size of the library's own scratch on each GPU, used by nvfp4_linear_noalloc
+ * for the W4A4 route's quantized activations: nvfp4_linear_workspace_bytes
+ * (M, N, K) must not exceed it (M = 8192 at K = 5120 needs 23.6 MB). */
+#define NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/* nvfp4_linear without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call allocates nothing and frees
+ * nothing.  On the W4A4 route the quantized activations go to a scratch
+ * array the library holds on each GPU (a device global of
+ * NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES, kept until the process ends);
+ * the W4A16 route needs none.  The caller still passes inputs and outputs.
+ *   Arguments, routes, numerics and errors as nvfp4_linear (the same kernels,
+ *   the same bits), plus WORKSPACE when nvfp4_linear_workspace_bytes(M, N, K)
+ *   exceeds NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES on the W4A4 route
+ *   (checked before any launch).
+ *   Every call on one GPU shares that GPU's scratch, so calls that overlap in
+ *   time on one GPU (on different streams) race and must not be issued; calls
+ *   on one stream are ordered and safe.  The first call on each device looks
+ *   up the scratch's device address (hipGetSymbolAddress, not a stream
+ *   operation); make that first call outside graph capture.  Nothing in the
+ *   scratch needs clearing: each call overwrites what it reads. */
+nvfp4_status nvfp4_linear_noalloc(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,
+                                  const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo,
+                                  int* route_taken, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * NVFP4 MoE expert layer, W4A4 on both GEMMs (FreeToken PR #736, Changes and
  * Results: both expert GEMMs take NVFP4 activations with static input scales,

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4.so")
 ARCH = os.environ.get("NVFP4_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["quantize.hip", "prepare.hip", "w4a16.hip", "w4a4.hip", "moe.hip", "stream.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "prepare.hip", "w4a16.hip", "w4a4.hip", "moe.hip", "stream.hip", "noalloc.hip", "api.cpp"]
 # Packed fp32 VALU ops are kept out of the generated code (-packed-fp32-ops).
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

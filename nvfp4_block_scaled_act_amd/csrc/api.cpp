@@ -278,9 +278,13 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return align_up(size_t(M) * size_t(K / 2), 256) + align_up(size_t(M) * size_t(K / 16), 256);
 }
 
-nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,
-                          const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo, void* ws,
-                          size_t ws_bytes, int* route_taken, hipStream_t stream) {
+namespace {
+
+// The dispatched linear; on the W4A4 route the quantized activations go to
+// ws (ws_bytes long) -- the caller's workspace or the library's scratch.
+nvfp4_status linear_impl(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,
+                         const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo, void* ws,
+                         size_t ws_bytes, bool use_scratch, int* route_taken, hipStream_t stream) {
   if (M < 0) return NVFP4_ERR_INVALID_ARGUMENT;
   nvfp4_status st = check_weight(w);
   if (st != NVFP4_OK) return st;
@@ -297,11 +301,16 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
     if ((st = check_bf16_input(a, M, w->K, lda)) != NVFP4_OK) return st;
     if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
     const size_t need = nvfp4_linear_workspace_bytes(M, w->N, w->K);
-    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
-    if (!aligned16(ws)) return NVFP4_ERR_ALIGNMENT;
     if (M * (w->K / 16) > kInt32Max || (M + 3) / 4 > 65535 || (M + 255) / 256 > 65535 ||
         M * (w->K / 2) >= (int64_t(1) << 32))
       return NVFP4_ERR_UNSUPPORTED;
+    if (use_scratch) {
+      if (need > nvfp4::scratch_capacity()) return NVFP4_ERR_WORKSPACE;  // beyond the scratch's fixed size
+      if ((st = hip_status(nvfp4::scratch_pointer(&ws))) != NVFP4_OK) return st;
+      ws_bytes = nvfp4::scratch_capacity();
+    }
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(ws)) return NVFP4_ERR_ALIGNMENT;
     uint8_t* codes = static_cast<uint8_t*>(ws);
     uint8_t* scales = codes + align_up(size_t(M) * size_t(w->K / 2), 256);
     st = hip_status(nvfp4::launch_quantize(a, M, w->K, lda, g_act, codes, scales, stream));
@@ -310,6 +319,22 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
   }
   if (st == NVFP4_OK && route_taken) *route_taken = route;
   return st;
+}
+
+}  // namespace
+
+nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,
+                          const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo, void* ws,
+                          size_t ws_bytes, int* route_taken, hipStream_t stream) {
+  return linear_impl(a, M, lda, w, g_act, alpha_w4a16, alpha_w4a4, out, ldo, ws, ws_bytes, false, route_taken,
+                     stream);
+}
+
+nvfp4_status nvfp4_linear_noalloc(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,
+                                  const float* alpha_w4a16, const float* alpha_w4a4, void* out, int64_t ldo,
+                                  int* route_taken, hipStream_t stream) {
+  return linear_impl(a, M, lda, w, g_act, alpha_w4a16, alpha_w4a4, out, ldo, nullptr, 0, true, route_taken,
+                     stream);
 }
 
 }  // extern "C"

@@ -47,6 +47,12 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
 hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
                        int64_t K, const float* alpha, void* out, int64_t ldo, hipStream_t stream);
 
+// Library-owned scratch of the allocation-free dispatched linear: its size,
+// and the device address of the current device's copy (looked up once per
+// device with hipGetSymbolAddress).
+size_t scratch_capacity();
+hipError_t scratch_pointer(void** out);
+
 // Streaming-read diagnostic: reads `bytes` (a multiple of 16) once.
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 

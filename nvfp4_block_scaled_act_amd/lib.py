@@ -67,6 +67,7 @@ _SIGS = {
     "nvfp4_get_route_m_max": (I64, []),
     "nvfp4_linear_workspace_bytes": (SZ, [I64, I64, I64]),
     "nvfp4_linear": (I32, [P, I64, I64, C.POINTER(Weight), P, P, P, P, I64, P, SZ, C.POINTER(I32), P]),
+    "nvfp4_linear_noalloc": (I32, [P, I64, I64, C.POINTER(Weight), P, P, P, P, I64, C.POINTER(I32), P]),
     "nvfp4_stream_read": (I32, [P, SZ, P, P]),
     "nvfp4_gated_mlp_w4a4": (I32, [P, P, I64, C.POINTER(Weight), P, P, P, P, P, P]),
     "nvfp4_moe_route": (I32, [I64, I64, I64, I32]),

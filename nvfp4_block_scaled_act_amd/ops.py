@@ -266,6 +266,28 @@ def linear(a: torch.Tensor, w: Weight, g_act: torch.Tensor | None, alpha_w4a16: 
     return out, int(r.value)
 
 
+NOALLOC_MAX_WORKSPACE_BYTES = 32 << 20  # NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES
+
+
+def linear_noalloc(a: torch.Tensor, w: Weight, g_act: torch.Tensor | None, alpha_w4a16: torch.Tensor,
+                   alpha_w4a4: torch.Tensor | None, out: torch.Tensor) -> int:
+    """The dispatched linear with no workspace and no allocation (the caller
+    passes the output; the W4A4 route's quantized activations go to the
+    library's scratch on the GPU).  Returns the route taken."""
+    _need(a, torch.bfloat16, "a")
+    _need(out, torch.bfloat16, "out")
+    lda = _rows(a, "a")
+    ldo = _rows(out, "out")
+    M = a.shape[0]
+    if tuple(out.shape) != (M, w.N):
+        raise ValueError(f"out must be [{M}, {w.N}], got {tuple(out.shape)}")
+    r = C.c_int(-1)
+    _L.check("nvfp4_linear_noalloc",
+             _L.load().nvfp4_linear_noalloc(_ptr(a), M, lda, C.byref(w.desc), _ptr(g_act), _ptr(alpha_w4a16),
+                                            _ptr(alpha_w4a4), _ptr(out), ldo, C.byref(r), _stream()))
+    return int(r.value)
+
+
 def moe_workspace_layout(T: int, top_k: int, E: int, K: int, I: int) -> dict:
     """Byte offsets of the MoE workspace's parts (and max_tiles, total_bytes)."""
     lay = _L.MoeLayout()

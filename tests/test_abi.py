@@ -178,6 +178,25 @@ def test_linear_dispatch_validation(nv):
     assert r.value == 0
 
 
+def test_linear_noalloc_validation(nv):
+    # the allocation-free dispatch validates as nvfp4_linear and rejects, before
+    # touching the device, a W4A4 call whose quantized activations would not
+    # fit its fixed scratch (32 MiB)
+    f = nv.nvfp4_linear_noalloc
+    w = _w(N=64, K=2048)
+    r = C.c_int(-1)
+    nv.nvfp4_set_route_m_max(16)
+    assert nv.nvfp4_linear_workspace_bytes(30000, 64, 2048) > (32 << 20)
+    assert f(A16, 30000, 2048, C.byref(w), A16, A16, A16, A16, 64, C.byref(r), None) == WS
+    assert f(A16, 32, 2048, C.byref(w), A16, A16, None, A16, 64, C.byref(r), None) == ARG    # no alpha_w4a4
+    assert f(A16, 32, 2048, C.byref(w), None, A16, None, A16, 64, C.byref(r), None) == UNSUP  # W4A16 beyond 16
+    assert f(A16 + 2, 32, 2048, C.byref(w), A16, A16, A16, A16, 64, C.byref(r), None) == ALIGN
+    assert f(A16, 32, 2048, C.byref(w), A16, A16, A16, A16, 10, C.byref(r), None) == SHAPE  # ldo < N
+    r.value = -1
+    assert f(None, 0, 2048, C.byref(w), A16, A16, A16, None, 64, C.byref(r), None) == OK   # empty batch
+    assert r.value == 0  # M = 0 <= M*: the W4A16 route, no launch
+
+
 def test_moe_workspace_layout(nv):
     T, top_k, E, K, I = 8192, 8, 128, 2048, 768
     lay = L.MoeLayout()
