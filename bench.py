@@ -80,6 +80,46 @@ def dev_bf16(torch, bits):
     return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
 
 
+def warm_gpu(torch, fn, ms=150.0, max_calls=10000):
+    """Run fn until at least `ms` of GPU time has passed.  The MI355X raises
+    its clock over the first tens of milliseconds of sustained load (a W4A4
+    GEMM at M = 8192 took 740 us in its first calls and 620 us after about 20
+    ms), so every timed leg first runs its own calls to the steady state."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    calls = 0
+    while calls < max_calls:
+        for _ in range(4):
+            fn()
+        calls += 4
+        e1.record()
+        e1.synchronize()
+        if e0.elapsed_time(e1) >= ms:
+            break
+
+
+def per_call_us(torch, fns, reps):
+    """Per-call times (us) of each function in `fns`, called in turn reps
+    times, each call between two HIP events, one host synchronization at the
+    end.  Returns one list of reps times per function."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(reps)]
+    for r in range(reps):
+        for i, fn in enumerate(fns):
+            ev[r][i][0].record()
+            fn()
+            ev[r][i][1].record()
+    torch.cuda.synchronize()
+    return [[ev[r][i][0].elapsed_time(ev[r][i][1]) * 1e3 for r in range(reps)] for i in range(len(fns))]
+
+
+def stats_us(ts):
+    """median, p10, p90 of per-call times (us)."""
+    a = np.asarray(ts, np.float64)
+    return dict(median=round(float(np.median(a)), 2), p10=round(float(np.percentile(a, 10)), 2),
+                p90=round(float(np.percentile(a, 90)), 2), n=int(a.size))
+
+
 def bench_w4a16(ops, torch, workload, shapes, Ms, steps, warmup, graphs=True):
     """Cold-weight W4A16 timing of every (shape, M); returns per-call rows and
     totals.  graphs=False launches the calls directly (for counter runs, which
@@ -138,6 +178,7 @@ def bench_w4a16(ops, torch, workload, shapes, Ms, steps, warmup, graphs=True):
     for _ in range(warmup):
         for e in entries:
             e["graph"]()
+    warm_gpu(torch, lambda: [e["graph"]() for e in entries], ms=150.0, max_calls=4 * max(1, warmup))
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in entries]
     per = np.zeros(len(entries))
@@ -190,7 +231,7 @@ def bench_w4a16(ops, torch, workload, shapes, Ms, steps, warmup, graphs=True):
                 weight_gb=sum(N * K * 9 / 16 * max(2, int(np.ceil(COLD_BYTES / (N * K * 9 / 16)))) for N, K in shapes) / 1e9)
 
 
-def bench_w4a4(ops, torch, reps=10):
+def bench_w4a4(ops, torch, reps=20):
     from nvfp4_block_scaled_act_amd import synth
 
     N, K = synth.W4A4_PREFILL["N"], synth.W4A4_PREFILL["K"]
@@ -201,49 +242,45 @@ def bench_w4a4(ops, torch, reps=10):
     wd, ad, cd = dev_bf16(torch, W), dev_bf16(torch, a), dev_bf16(torch, cal)
     gw, ga = ops.global_scale(wd), ops.global_scale(cd)
     codes, scales = ops.quantize_act(wd, gw)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
+    # the one-time prepare step, timed on its second call (the first touches
+    # a fresh output buffer) after a warm-up of the clocks
+    wbuf = torch.empty(ops.prepared_weight_bytes(N, K), dtype=torch.uint8, device="cuda")
+    warm_gpu(torch, lambda: ops.prepare_weight(codes, scales, out=wbuf), ms=30.0)
+    prepare_us = stats_us(per_call_us(torch, [lambda: ops.prepare_weight(codes, scales, out=wbuf)], 5)[0])["median"]
+    del wbuf
     w = ops.prepare_weight(codes, scales)
-    t1.record()
-    torch.cuda.synchronize()
-    prepare_us = t0.elapsed_time(t1) * 1e3
     al = ops.alpha(gw, ga)
     ac, as_ = ops.quantize_act(ad, ga)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    for _ in range(2):
+
+    def quant():
         ops.quantize_act(ad, ga, ac, as_)
+
+    def gemm():
         ops.linear_w4a4(ac, as_, w, al, out=out)
-    torch.cuda.synchronize()
+
     # quantize -> GEMM pairs issued back to back (as consecutive prefill
-    # layers would), one event before each call, one host sync at the end
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 1)]
-    for i in range(reps):
-        ev[2 * i].record()
-        ops.quantize_act(ad, ga, ac, as_)
-        ev[2 * i + 1].record()
-        ops.linear_w4a4(ac, as_, w, al, out=out)
-    ev[2 * reps].record()
-    torch.cuda.synchronize()
-    tq = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps))
-    tg = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(reps))
-    e1, e2 = ev[0], ev[1]
-    gemm_us = tg / reps * 1e3
-    quant_us = tq / reps * 1e3
+    # layers would), after a warm-up to steady clocks; each call between two
+    # HIP events; medians over the calls
+    warm_gpu(torch, lambda: (quant(), gemm()), ms=200.0)
+    tq, tg = per_call_us(torch, [quant, gemm], reps)
+    gemm_st, quant_st = stats_us(tg), stats_us(tq)
+    gemm_us, quant_us = gemm_st["median"], quant_st["median"]
     # the smaller prefill batches of the same workload (prefixes of a)
     sweep = []
     for Ms in synth.W4A4_PREFILL["M"]:
         o = out[:Ms]
-        ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o)
-        torch.cuda.synchronize()
-        e1.record()
-        for _ in range(reps):
+
+        def gm(Ms=Ms, o=o):
             ops.linear_w4a4(ac[:Ms], as_[:Ms], w, al, out=o)
-        e2.record()
-        torch.cuda.synchronize()
-        us = e1.elapsed_time(e2) / reps * 1e3
-        sweep.append(dict(M=Ms, gemm_us=round(us, 2), tflops=round(2.0 * Ms * N * K / us / 1e6, 1)))
-        log(f"[w4a4] M={Ms}: gemm {us:.1f} us = {2.0 * Ms * N * K / us / 1e6:.1f} TFLOP/s")
+
+        warm_gpu(torch, gm, ms=30.0)
+        st = stats_us(per_call_us(torch, [gm], reps)[0])
+        us = st["median"]
+        sweep.append(dict(M=Ms, gemm_us=round(us, 2), tflops=round(2.0 * Ms * N * K / us / 1e6, 1), p10_us=st["p10"],
+                          p90_us=st["p90"]))
+        log(f"[w4a4] M={Ms}: gemm {us:.1f} us = {2.0 * Ms * N * K / us / 1e6:.1f} TFLOP/s (p10 {st['p10']}, p90 "
+            f"{st['p90']})")
     # the gated MLP's gate_up on the same weight read as [2I, K] (I = N/2):
     # the GEMM plus the SiLU gate and NVFP4 quantization of h in its epilogue
     I = N // 2
@@ -252,15 +289,13 @@ def bench_w4a4(ops, torch, reps=10):
     h_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
     ops.gated_mlp_w4a4(ac, as_, w, al, torch.ones(1, dtype=torch.float32, device="cuda"), hc, hs, h_amax=h_amax)
     g2 = (torch.full((1,), 2688.0, dtype=torch.float32, device="cuda") / h_amax).contiguous()
-    for _ in range(2):
+
+    def gated():
         ops.gated_mlp_w4a4(ac, as_, w, al, g2, hc, hs)
-    torch.cuda.synchronize()
-    e1.record()
-    for _ in range(reps):
-        ops.gated_mlp_w4a4(ac, as_, w, al, g2, hc, hs)
-    e2.record()
-    torch.cuda.synchronize()
-    gated_us = e1.elapsed_time(e2) / reps * 1e3
+
+    warm_gpu(torch, gated, ms=60.0)
+    gated_st = stats_us(per_call_us(torch, [gated], reps)[0])
+    gated_us = gated_st["median"]
     log(f"[w4a4] gated MLP gate_up M={M} 2I={N} K={K}: {gated_us:.1f} us = "
         f"{2.0 * M * N * K / gated_us / 1e6:.1f} TFLOP/s (GEMM alone {sweep[-1]['gemm_us']:.1f} us)")
     flops = 2.0 * M * N * K
@@ -270,7 +305,9 @@ def bench_w4a4(ops, torch, reps=10):
     return dict(M=M, N=N, K=K, gemm_us=gemm_us, quant_us=quant_us, tflops=flops / gemm_us / 1e6,
                 linear_tflops=flops / (gemm_us + quant_us) / 1e6, quant_gbs=qbytes / quant_us / 1e3,
                 prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16, m_sweep=sweep,
-                gated_mlp=dict(M=M, two_I=N, K=K, us=round(gated_us, 2),
+                gemm_stats_us=gemm_st, quant_stats_us=quant_st,
+                gated_mlp=dict(M=M, two_I=N, K=K, us=round(gated_us, 2), p10_us=gated_st["p10"],
+                               p90_us=gated_st["p90"],
                                tflops=round(2.0 * M * N * K / gated_us / 1e6, 1),
                                gemm_alone_us=sweep[-1]["gemm_us"]))
 
@@ -281,7 +318,7 @@ def moe_flops(T, top_k, K, I):
     return 2.0 * T * top_k * 3 * K * I
 
 
-def bench_moe(ops, torch, reps=10):
+def bench_moe(ops, torch, reps=20):
     """The NVFP4 MoE layer (E=128, top-8, K=2048, I=768, T=8192): whole-layer
     time of nvfp4_moe_w4a4 (quantize x, align, gate_up, down, route sum) with
     HIP events.  Banks are quantized per expert on the GPU; g1 comes from the
@@ -330,20 +367,17 @@ def bench_moe(ops, torch, reps=10):
     out = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
     log(f"[moe] setup {time.perf_counter() - t_setup:.1f} s, g2 = {g2.item():.6g}")
-    for _ in range(2):
+    def layer():
         ops.moe_w4a4(x, ids, w, w_gu, w_dn, E, g1, g2, a_gu, a_dn, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        ops.moe_w4a4(x, ids, w, w_gu, w_dn, E, g1, g2, a_gu, a_dn, out=out, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    layer_us = e0.elapsed_time(e1) * 1e3 / reps
+
+    warm_gpu(torch, layer, ms=200.0)
+    st = stats_us(per_call_us(torch, [layer], reps)[0])
+    layer_us = st["median"]
     flops = moe_flops(T, top_k, K, I)
     log(f"[moe] T={T} E={E} top_k={top_k} K={K} I={I}: layer {layer_us:.1f} us = "
-        f"{flops / layer_us / 1e6:.1f} TFLOP/s")
-    return dict(T=T, E=E, top_k=top_k, K=K, I=I, layer_us=layer_us, tflops=flops / layer_us / 1e6)
+        f"{flops / layer_us / 1e6:.1f} TFLOP/s (p10 {st['p10']}, p90 {st['p90']})")
+    return dict(T=T, E=E, top_k=top_k, K=K, I=I, layer_us=layer_us, tflops=flops / layer_us / 1e6,
+                p10_us=st["p10"], p90_us=st["p90"])
 
 
 def bench_w4a16_tactics(ops, torch, shapes=((11008, 4096), (4096, 11008), (14336, 4096), (4096, 14336),
@@ -603,30 +637,80 @@ def bench_fused_sweep(ops, torch, reps=2):
     return rows
 
 
-def cpu_baseline(target_s=15.0):
-    """The oracle (as it stands) on a bounded sample of the headline workload:
-    the W4A16 call N=8704, K=5120, M=16 restricted to its first 512 weight
-    rows, repeated for about target_s seconds on the host cores."""
+def cpu_baseline(target_s=6.0):
+    """The oracle (as it stands) timed on the host cores on bounded samples of
+    each leg's workload, in the same units as the GPU figures:
+      * W4A16 (the headline's unit, `value`): the call N=8704, K=5120, M=16
+        restricted to its first 512 weight rows, repeated for about target_s;
+      * quantize: the W4A4 prefill activations (K=5120), 512 rows per pass;
+      * W4A4: the prefill GEMM (N=8704, K=5120) on 64 activation rows x 1024
+        weight rows per pass;
+      * MoE: the NVFP4 MoE layer (E=128, top-8, K=2048, I=768) on its first
+        256 tokens, once (bank quantization not timed)."""
     import oracle
     from nvfp4_block_scaled_act_amd import synth
 
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def loop(fn):
+        fn()  # load the library and touch the data outside the timed loop
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < target_s:
+            fn()
+            n += 1
+        return n, time.perf_counter() - t0
+
+    legs = {}
     K, M, rows_w = 5120, 16, 512
     W = synth.normal_bf16(synth.seed_for("w4a16_decode", synth.ROLE_W, 1), rows_w, K)
     a = synth.normal_bf16(synth.seed_for("w4a16_decode", synth.ROLE_A, 1), M, K)
     g = oracle.global_scale(W)
     c, s = oracle.quantize(W, g)
     al = oracle.alpha(g)
-    oracle.linear_w4a16(a, c[:8], s[:8], al)  # load the library outside the timed loop
+    n, dt = loop(lambda: oracle.linear_w4a16(a, c, s, al))
+    w16 = w4a16_bytes(M, rows_w, K) * n / dt / 1e12
+    legs["w4a16"] = dict(value=round(w16, 6), unit="TB/s", sample=f"N=512 rows of (8704, 5120), M=16, {n} passes "
+                         f"in {dt:.1f} s")
+    N4 = synth.W4A4_PREFILL["N"]
+    x = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_A), 512, K)
+    ga = np.float32(512.0)
+    n, dt = loop(lambda: oracle.quantize(x, ga))
+    legs["quantize"] = dict(value=round(512 * K * (2 + 0.5 + 1 / 16) * n / dt / 1e9, 3), unit="GB/s",
+                            sample=f"512 x {K} prefill activations, {n} passes in {dt:.1f} s")
+    Wp = synth.normal_bf16(synth.seed_for("w4a4_prefill", synth.ROLE_W), 1024, K)
+    gw = oracle.global_scale(Wp)
+    wc, ws = oracle.quantize(Wp, gw)
+    xc, xs = oracle.quantize(x[:64], ga)
+    a4 = oracle.alpha(gw, ga)
+    n, dt = loop(lambda: oracle.linear_w4a4(xc, xs, wc, ws, a4))
+    legs["w4a4"] = dict(value=round(2.0 * 64 * 1024 * K * n / dt / 1e9, 3), unit="GFLOP/s",
+                        sample=f"64 activation rows x 1024 weight rows of the ({N4}, {K}) prefill GEMM, {n} passes "
+                               f"in {dt:.1f} s")
+    d = synth.moe_inputs()
+    E, Km, I, top_k = d["E"], d["K"], d["I"], d["top_k"]
+    banks = []
+    for bank in (d["gate_up"], d["down"]):
+        codes = np.empty((E, bank.shape[1], bank.shape[2] // 2), np.uint8)
+        scales = np.empty((E, bank.shape[1], bank.shape[2] // 16), np.uint8)
+        gs = np.empty(E, np.float32)
+        for e in range(E):
+            gs[e] = oracle.global_scale(bank[e])
+            codes[e], scales[e] = oracle.quantize(bank[e], gs[e])
+        banks.append((codes, scales, gs))
+    g1 = oracle.global_scale(d["cal"])
+    g2 = np.float32(0.1)
+    agu = np.array([oracle.alpha(gg, g1) for gg in banks[0][2]], np.float32)
+    adn = np.array([oracle.alpha(gg, g2) for gg in banks[1][2]], np.float32)
+    nt = 256
     t0 = time.perf_counter()
-    passes = 0
-    while time.perf_counter() - t0 < target_s:
-        oracle.linear_w4a16(a, c, s, al)
-        passes += 1
+    oracle.moe_w4a4(d["x"], d["ids"], d["w"], banks[0][0], banks[0][1], banks[1][0], banks[1][1], g1, g2, agu, adn,
+                    tokens=np.arange(nt))
     dt = time.perf_counter() - t0
-    b = w4a16_bytes(M, rows_w, K) * passes
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=b / dt / 1e12, unit="TB/s", cores=cores, kind="oracle",
-                sample=f"W4A16 N=512 rows of (8704, 5120), M=16, {passes} passes in {dt:.1f} s")
+    legs["moe"] = dict(value=round(moe_flops(nt, top_k, Km, I) / dt / 1e9, 3), unit="GFLOP/s",
+                       sample=f"the MoE layer on its first {nt} tokens in {dt:.1f} s")
+    return dict(value=legs["w4a16"]["value"], unit="TB/s", cores=cores, kind="oracle",
+                sample=legs["w4a16"]["sample"] + "; the other legs under 'legs'", legs=legs)
 
 
 def main():
@@ -746,6 +830,8 @@ def main():
             "tflops": round(r4["tflops"], 2), "unit": "TFLOP/s", "gemm_us": round(r4["gemm_us"], 2),
             "frac_of_fp16_mfma_peak": round(r4["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
             "linear_tflops_incl_quantize": round(r4["linear_tflops"], 2),
+            "gemm_us_p10_p90": [r4["gemm_stats_us"]["p10"], r4["gemm_stats_us"]["p90"]],
+            "timing": "HIP events around each call of 20 quantize -> GEMM pairs after a 200 ms warm-up; medians",
             "quantize_us": round(r4["quant_us"], 2), "quantize_gb_s": round(r4["quant_gbs"], 1),
             "m_sweep": r4["m_sweep"],
             "gated_mlp": dict(r4["gated_mlp"], workload="nvfp4_gated_mlp_w4a4 on the same weight as gate_up [2I=8704, "
@@ -763,6 +849,7 @@ def main():
             "workload": "NVFP4 MoE W4A4, E=128, top-8, K=2048, I=768, T=8192 (whole layer: quantize, align, "
                         "gate_up + SiLU gate + NVFP4 quantize, down + routing weight + top-8 sum)",
             "tflops": round(r5["tflops"], 2), "unit": "TFLOP/s", "layer_us": round(r5["layer_us"], 2),
+            "layer_us_p10_p90": [r5["p10_us"], r5["p90_us"]],
             "flops": moe_flops(r5["T"], r5["top_k"], r5["K"], r5["I"]),
             "frac_of_fp16_mfma_peak": round(r5["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
         }

@@ -292,15 +292,23 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
 
 // The same gate_up on a dense batch (a gated MLP's first GEMM): row tile ty
 // holds rows 256ty.. of the NVFP4 activations, h is stored by row.
+// Workgroups [0, n_big) take (row tile, block) items by gemm::xcd_row_block;
+// when the items leave a last round at most half full, its items run as two
+// 128-row halves each: workgroup n_big + j takes half j % 2 of item
+// n_big + j / 2.
 __global__ __launch_bounds__(gemm::kThreads) void gated_mlp_kernel(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int32_t K, int32_t M,
     const uint8_t* __restrict__ wt, int32_t I, const float* __restrict__ alpha_p, const float* __restrict__ g2_p,
-    uint8_t* __restrict__ hc, uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
+    uint8_t* __restrict__ hc, uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax, int32_t n_big) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
+  const int32_t id = int32_t(blockIdx.x);
+  const bool half = id >= n_big;
   int32_t ty, c;
-  gemm::xcd_row_block(int32_t(blockIdx.x), I / 128, ty, c);
+  gemm::xcd_row_block(half ? n_big + (id - n_big) / 2 : id, I / 128, ty, c);
   if (ty >= (M + gemm::BM - 1) / gemm::BM) return;
-  const MoeTile tile{0, ty * gemm::BM, min(gemm::BM, M - ty * gemm::BM), 0};
+  const int32_t m0 = ty * gemm::BM + (half ? (gemm::BM / 2) * ((id - n_big) & 1) : 0);
+  if (m0 >= M) return;
+  const MoeTile tile{0, m0, min(half ? gemm::BM / 2 : gemm::BM, M - m0), 0};
   const float alpha = *alpha_p, g2 = *g2_p;
   auto row_of = [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); };
   if (tile.rows <= gemm::BM / 2)
@@ -558,11 +566,17 @@ hipError_t launch_gated_mlp_w4a4(const void* a_codes, const void* a_scales, int6
   if (M == 0) return hipSuccess;
   if (h_amax) hipLaunchKernelGGL(set_u32_kernel_moe, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(h_amax));
   const int32_t tiles = int32_t((M + gemm::BM - 1) / gemm::BM);
-  hipLaunchKernelGGL(gated_mlp_kernel, dim3(uint32_t(gemm::xcd_rows_grid(tiles, int32_t(I / 128)))),
-                     dim3(gemm::kThreads), 0, stream, static_cast<const uint8_t*>(a_codes),
-                     static_cast<const uint8_t*>(a_scales), int32_t(K), int32_t(M),
-                     static_cast<const uint8_t*>(w_gate_up), int32_t(I), alpha, g2, static_cast<uint8_t*>(h_codes),
-                     static_cast<uint8_t*>(h_scales), reinterpret_cast<uint32_t*>(h_amax));
+  // one workgroup fills a CU: the items run in rounds of one per CU; a last
+  // round at most half full runs as 128-row halves
+  const int64_t items = gemm::xcd_rows_grid(tiles, int32_t(I / 128));
+  const int64_t cus = device_cu_count();
+  const int64_t rest = items % cus;
+  const int64_t n_big = (items > cus && rest > 0 && 2 * rest <= cus) ? items - rest : items;
+  hipLaunchKernelGGL(gated_mlp_kernel, dim3(uint32_t(n_big + 2 * (items - n_big))), dim3(gemm::kThreads), 0, stream,
+                     static_cast<const uint8_t*>(a_codes), static_cast<const uint8_t*>(a_scales), int32_t(K),
+                     int32_t(M), static_cast<const uint8_t*>(w_gate_up), int32_t(I), alpha, g2,
+                     static_cast<uint8_t*>(h_codes), static_cast<uint8_t*>(h_scales),
+                     reinterpret_cast<uint32_t*>(h_amax), int32_t(n_big));
   return hipGetLastError();
 }
 

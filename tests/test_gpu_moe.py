@@ -423,11 +423,13 @@ def test_moe_dispatch_routes(ops, orc):
 
 
 # ------------------------------------------------------------ gated MLP
-@pytest.mark.parametrize("M,K,I", [(300, 512, 256), (1024, 2048, 768)])
+@pytest.mark.parametrize("M,K,I", [(300, 512, 256), (1024, 2048, 768), (4000, 512, 2304)])
 def test_gated_mlp_w4a4(ops, orc, M, K, I):
     # the dense gated MLP = the MoE layer with one expert, one route of weight
     # 1: h (NVFP4 under g2) against the oracle's with benign flips, then the
-    # down linear on the GPU's h against the layer's output
+    # down linear on the GPU's h against the layer's output.  (4000, 512,
+    # 2304): 16 row tiles x 18 blocks = 288 workgroup items on 256 CUs, so the
+    # last 32 run as 128-row halves, one of them on the ragged last 32 rows
     import torch
 
     x, _, _, cal, _, _, gate_up, down = _small_case(707 + M, M, 1, 1, K, I, calib_rows=64)
