@@ -2,7 +2,8 @@
 // (per-tensor global scale and alpha).
 //
 // What is computed (FlashInfer PR #3597, Description and API example; FreeToken
-// PR #737, Changes: "The activation quant kernel splits rows into blocks"):
+// PR #737, Changes, where the activation quantizer works on blocks of a row
+// rather than whole rows):
 //   for every 16 consecutive elements of a row:
 //     amax   = max |x|
 //     scale  = the E4M3 byte nearest to amax*g/6 (ties to even, saturating 448)
@@ -71,6 +72,16 @@ __device__ __forceinline__ uint32_t scale_byte_lut(float amax, float g, const Sc
 }
 
 // Codes and scale of one 16-element block (eight bf16 pairs in d).
+// SMALL_G: g has at most 8 significant bits (its low 16 mantissa bits are
+// zero).  Then x*g is exact in fp32 (8 + 8 bits), and x*g/S is either exactly
+// a value of at most 3 significant bits (a rounding threshold, or a code) or
+// at least about 2^-16 of itself away from every such value, since x*g - T*S
+// is then a nonzero multiple of the quantum of x*g.  w = x*fl(g/S) lies
+// within 2^-22 of x*g/S, so the convert of w rounds the right way except on
+// an exact tie: there w is snapped to its nearest 2-mantissa-bit value tn
+// when x*g == tn*S (both products exact), and the convert's ties-to-even
+// takes the even code.  No exact fallback is needed on this path.
+template <bool SMALL_G>
 __device__ __forceinline__ void quantize_block(const uint32_t (&d)[8], float g, const ScaleTables& T, uint32_t& c0,
                                                uint32_t& c1, uint32_t& s) {
   uint32_t mbits = 0;
@@ -88,17 +99,28 @@ __device__ __forceinline__ void quantize_block(const uint32_t (&d)[8], float g, 
   }
   c0 = 0;
   c1 = 0;
-  // near_threshold() for all 16 at once: (bits + 4) << 11 keeps the low 21
-  // bits plus 4, scaled to the top of the word; w is within 4 ulps of a value
-  // whose low 21 bits are zero iff that is below 9 << 11
   float w[16];
-  uint32_t dmin = 0xFFFFFFFFu;
+  bool near = false;
+  if (SMALL_G) {
+    const float S = T.val[s];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    w[i] = x[i] * G;
-    dmin = min(dmin, (__float_as_uint(w[i]) << 11) + (4u << 11));
+    for (int i = 0; i < 16; ++i) {
+      w[i] = x[i] * G;
+      const float tn = __uint_as_float((__float_as_uint(w[i]) + 0x100000u) & 0xFFE00000u);
+      w[i] = x[i] * g == tn * S ? tn : w[i];
+    }
+  } else {
+    // near_threshold() for all 16 at once: (bits + 4) << 11 keeps the low 21
+    // bits plus 4, scaled to the top of the word; w is within 4 ulps of a
+    // value whose low 21 bits are zero iff that is below 9 << 11
+    uint32_t dmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      w[i] = x[i] * G;
+      dmin = min(dmin, (__float_as_uint(w[i]) << 11) + (4u << 11));
+    }
+    near = dmin < (9u << 11);
   }
-  const bool near = dmin < (9u << 11);
   c0 = cvt_pair<0>(c0, w[0], w[1]);
   c0 = cvt_pair<1>(c0, w[2], w[3]);
   c0 = cvt_pair<2>(c0, w[4], w[5]);
@@ -108,7 +130,7 @@ __device__ __forceinline__ void quantize_block(const uint32_t (&d)[8], float g, 
   c1 = cvt_pair<2>(c1, w[12], w[13]);
   c1 = cvt_pair<3>(c1, w[14], w[15]);
 
-  if (near && s != 0) {
+  if (!SMALL_G && near && s != 0) {
     const float S = T.val[s];
     c0 = 0;
     c1 = 0;
@@ -165,11 +187,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     return;
   }
   const int32_t half_k = blocks_per_row * 8;
+  // g with at most 8 significant bits: the exact path of quantize_block<true>
+  const bool small_g = (__float_as_uint(g) & 0xFFFFu) == 0;
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     const uint32_t d[8] = {v[r][0].x, v[r][0].y, v[r][0].z, v[r][0].w, v[r][1].x, v[r][1].y, v[r][1].z, v[r][1].w};
     uint32_t c0, c1, s;
-    quantize_block(d, g, T, c0, c1, s);
+    if (small_g)
+      quantize_block<true>(d, g, T, c0, c1, s);
+    else
+      quantize_block<false>(d, g, T, c0, c1, s);
     const int32_t row = row0 + r;
     if (row < rows) {
       *reinterpret_cast<uint2*>(codes + int64_t(row) * half_k + int64_t(j) * 8) = make_uint2(c0, c1);

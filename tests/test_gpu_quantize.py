@@ -114,6 +114,34 @@ def test_exact_ties_and_near_ties(ops, orc):
         _assert_same(*_quant_both(ops, orc, x, g), f"ties at g={g!r}")
 
 
+def _tie_blocks_at(rng, nblocks, g):
+    """bf16 blocks whose |x|*g/S hit e2m1 midpoints (and codes) exactly under
+    the global g, with a block max that makes S the block's scale."""
+    thr = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.5, 1.0, 0.0]
+    blocks = []
+    while len(blocks) < nblocks:
+        sb = int(rng.integers(0x10, 0x78))
+        e, m = sb >> 3, sb & 7
+        S = (1 + m / 8) * 2.0 ** (e - 7)
+        vals = np.array([6.0 * S / g] + [t * S / g * rng.choice([-1, 1]) for t in rng.choice(thr, 15)], np.float32)
+        if (synth.bf16_to_f32(synth._bf16_bits(vals)) == vals).all():
+            blocks.append(vals)
+    return synth._bf16_bits(np.array(blocks, np.float32))
+
+
+@pytest.mark.parametrize("g", [512.0, 384.0, 96.0, 3.0, 0.75, 1.5 * 2 ** 20])
+def test_small_mantissa_global(ops, orc, g):
+    # a global of at most 8 significant bits takes the tie-snapping path (the
+    # prefill workload's g = 2688/5.25 = 512 is one): exact ties at every
+    # midpoint, and N(0,1) rows spread over 40 binades
+    rng = np.random.default_rng(int(g * 7) % 1000)
+    g = np.float32(g)
+    ties = _tie_blocks_at(rng, 4096, float(g)).reshape(256, 256)
+    _assert_same(*_quant_both(ops, orc, ties, g), f"ties at g={g}")
+    x = (rng.standard_normal((512, 1024)) * np.exp(rng.uniform(-14, 14, (512, 1)))).astype(np.float32) / g
+    _assert_same(*_quant_both(ops, orc, synth._bf16_bits(x), g), f"wide rows at g={g}")
+
+
 def test_special_values(ops, orc):
     rng = np.random.default_rng(7)
     x = rng.standard_normal((64, 512)).astype(np.float32)
