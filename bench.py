@@ -591,9 +591,10 @@ def bench_fused_sweep(ops, torch, reps=2):
     ga = ops.global_scale(dev_bf16(torch, cal))
     a16, a4 = ops.alpha(gw), ops.alpha(gw, ga)
     ws = torch.empty(ops.linear_workspace_bytes(max(Ms), N, K), dtype=torch.uint8, device="cuda")
-    qc = torch.empty((16, K // 2), dtype=torch.uint8, device="cuda")
-    qs = torch.empty((16, K // 16), dtype=torch.uint8, device="cuda")
-    ops.set_route_m_max(16)
+    qc = torch.empty((128, K // 2), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((128, K // 16), dtype=torch.uint8, device="cuda")
+
+    warm_gpu(torch, lambda: [ops.linear_w4a16(ad[:16], w, a16) for w in copies[:8]], ms=100.0)
 
     def timed(fn):
         for w in copies[:2]:
@@ -622,19 +623,27 @@ def bench_fused_sweep(ops, torch, reps=2):
             r["tb_s"] = round(w4a16_bytes(M, N, K) / us / 1e6, 3)
         else:
             r["tflops"] = round(2.0 * M * N * K / us / 1e6, 1)
-        if M <= 16:
-            def forced(w):
-                ops.quantize_act(ad[:M], ga, codes=qc[:M], scales=qs[:M])
-                ops.linear_w4a4(qc[:M], qs[:M], w, a4, out=out)
-
-            r["w4a4_forced_us"] = round(timed(forced), 2)
         rows.append(r)
-        extra = f", W4A4 forced {r['w4a4_forced_us']:.1f} us" if M <= 16 else ""
         rate = f"{r['tb_s']:.3f} TB/s" if "tb_s" in r else f"{r['tflops']:.1f} TFLOP/s"
-        log(f"[fused_sweep] N={N} K={K} M={M:5d}: {r['route']} {us:9.2f} us ({rate}){extra}")
+        log(f"[fused_sweep] N={N} K={K} M={M:5d}: {r['route']} {us:9.2f} us ({rate})")
+    # both routes forced around the crossover: W4A16 (its kernels take M <= 64)
+    # and W4A4 (quantize + GEMM)
+    cross = []
+    for M in (8, 16, 24, 32, 40, 48, 56, 64, 96, 128):
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def forced4(w, M=M, out=out):
+            ops.quantize_act(ad[:M], ga, codes=qc[:M], scales=qs[:M])
+            ops.linear_w4a4(qc[:M], qs[:M], w, a4, out=out)
+
+        c = dict(M=M, w4a4_us=round(timed(forced4), 2))
+        if M <= 64:
+            c["w4a16_us"] = round(timed(lambda w, M=M, out=out: ops.linear_w4a16(ad[:M], w, a16, out=out)), 2)
+        cross.append(c)
+        log(f"[fused_sweep] crossover M={M}: W4A16 {c.get('w4a16_us', float('nan')):.1f} us, W4A4 {c['w4a4_us']:.1f} us")
     del copies
     torch.cuda.empty_cache()
-    return rows
+    return dict(per_m=rows, crossover=cross, route_m_max=ops.get_route_m_max())
 
 
 def cpu_baseline(target_s=6.0):
@@ -820,10 +829,11 @@ def main():
         res["fused_large_decode"] = {
             "workload": "W4A16 N=62080 K=5120 M in {1,8,16}, cold", "tb_s": round(gbs3 / 1e3, 4),
             "frac_of_hbm_peak": round(gbs3 / HBM_PEAK_GBS, 4), "kernel": "w4a16_shared_kernel", "per_m": r3["rows"]}
+        fs = bench_fused_sweep(ops, torch)
         res["fused_large_sweep"] = {
             "workload": "dispatched linear N=62080 K=5120 at every M of the sweep (route reported), cold weights; "
-                        "W4A4 forced at M <= 16 for the crossover",
-            "route_m_max": 16, "per_m": bench_fused_sweep(ops, torch)}
+                        "both routes forced at M = 8..128 for the crossover",
+            "route_m_max": fs["route_m_max"], "per_m": fs["per_m"], "crossover": fs["crossover"]}
         r4 = bench_w4a4(ops, torch)
         res["w4a4_prefill"] = {
             "workload": "W4A4 M=8192 N=8704 K=5120, NVFP4 activations (static global, 512-row calibration)",

@@ -59,7 +59,7 @@ typedef enum nvfp4_status {
   NVFP4_ERR_INVALID_ARGUMENT = 1, /* null pointer where one is required, negative size */
   NVFP4_ERR_INVALID_SHAPE = 2,    /* K % 16 != 0, lda < K, ldo < N, size overflow */
   NVFP4_ERR_ALIGNMENT = 3,        /* misaligned base pointer or stride */
-  NVFP4_ERR_UNSUPPORTED = 4,      /* valid NVFP4 but outside this build's kernels (K % 256, M > 16 on W4A16) */
+  NVFP4_ERR_UNSUPPORTED = 4,      /* valid NVFP4 but outside this build's kernels (K % 256, M > 64 on W4A16) */
   NVFP4_ERR_WORKSPACE = 5,        /* workspace missing or too small */
   NVFP4_ERR_HIP = 6               /* a kernel launch failed */
 } nvfp4_status;
@@ -203,15 +203,18 @@ nvfp4_status nvfp4_prepare_weight_swizzled(const void* codes, const void* scales
 
 /* ---------------------------------------------------------------------------
  * nvfp4_linear_w4a16 -- out = bf16((a @ dequant(W).T) * alpha), fp32
- * accumulation (FlashInfer PR #3597, Description), for decode-sized M <= 16
- * (FreeToken PR #737, Changes: small-batch kernels on the same weight).
+ * accumulation (FlashInfer PR #3597, Description), for decode-sized M <= 64
+ * (FreeToken PR #737, Changes: small-batch kernels on the same weight; its
+ * Results keep a W4A16 tier to about 48 tokens).  Up to 16 tokens several
+ * schedules; 17..64 tokens the shared schedule with up to four 16-token
+ * groups on each dequantized weight fragment.
  *   a      bf16 [M, K], lda >= K
  *   w      prepared weight descriptor (host pointer)
  *   alpha  device fp32[1] (1/g_w)
  *   out    bf16 [M, N], ldo >= N
  * One launch, no workspace.  Deterministic: the fp32 sum order depends only
  * on (M, N, K).
- * Errors: as above; UNSUPPORTED for M > 16, or when a's last row ends 2^31 -
+ * Errors: as above; UNSUPPORTED for M > 64, or when a's last row ends 2^31 -
  * 4096 bytes or more past its first element ((M-1)*lda*2 + 2*K; the kernels
  * address the activations with 32-bit offsets).
  * ------------------------------------------------------------------------- */
@@ -224,7 +227,8 @@ nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvf
  *                  waves split K into contiguous runs of 256-k steps
  *   schedule 2     shared: one workgroup per 8 tiles over all of K, the
  *                  activations streamed through LDS in chunks of chunk_steps
- *                  256-k steps; needs M * min(chunk_steps, K/256) <= 64
+ *                  256-k steps; needs M * min(chunk_steps, K/256) <= 64;
+ *                  the only schedule for M > 16 (INVALID_ARGUMENT otherwise)
  *   schedule 3     split with interleaved steps (wave w takes steps w,
  *                  w + waves, ...); needs ceil(K/256 / ksplit) <= 8.  Here
  *                  chunk_steps is the tiles per workgroup: 0 or 1, or 2
@@ -257,9 +261,10 @@ nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_
  * checkpoints with static activation scales, W4A16 kernels for batches up to
  * a threshold T, 8 or 16 there).
  *   nvfp4_route: pure; W4A4 iff has_act_global && M > M*; else W4A16.
- *   nvfp4_set_route_m_max / get: M* (default 16; values above 16 are clamped
- *   to 16, the W4A16 kernel's limit, and a missing activation global with
- *   M > 16 is UNSUPPORTED).
+ *   nvfp4_set_route_m_max / get: M* (default 64, where the W4A16 kernels
+ *   still beat quantize + W4A4 on the large fused weight N = 62080, K = 5120
+ *   on MI355X; values above 64 are clamped to 64, the W4A16 kernels' limit,
+ *   and a missing activation global with M > 64 is UNSUPPORTED).
  * ------------------------------------------------------------------------- */
 int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global);
 void nvfp4_set_route_m_max(int64_t m_max);

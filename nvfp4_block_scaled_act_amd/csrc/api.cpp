@@ -11,7 +11,7 @@
 namespace {
 
 constexpr int64_t kInt32Max = 2147483647LL;
-std::atomic<int64_t> g_route_m_max{16};
+std::atomic<int64_t> g_route_m_max{64};  // measured crossover, N = 62080, K = 5120
 std::atomic<int64_t> g_moe_route_tpe_max{32};  // tokens per expert up to which the MoE stays W4A16
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -65,7 +65,7 @@ nvfp4_status w4a16_checked(const void* a, int64_t M, int64_t lda, const nvfp4_we
   if (M == 0) return NVFP4_OK;  // empty batch: a and out may be null
   if ((st = check_bf16_input(a, M, w->K, lda)) != NVFP4_OK) return st;
   if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
-  if (M > 16) return NVFP4_ERR_UNSUPPORTED;
+  if (M > nvfp4::kW4A16MaxM) return NVFP4_ERR_UNSUPPORTED;
   if ((M - 1) * lda * 2 + 2 * w->K > (int64_t(1) << 31) - 4096) return NVFP4_ERR_UNSUPPORTED;  // 32-bit offsets
   if (cfg_in && !nvfp4::w4a16_config_valid(*cfg_in, M, w->K)) return NVFP4_ERR_INVALID_ARGUMENT;
   if (w->N == 0) return NVFP4_OK;
@@ -266,7 +266,7 @@ int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global) {
 
 void nvfp4_set_route_m_max(int64_t m_max) {
   if (m_max < 0) m_max = 0;
-  if (m_max > 16) m_max = 16;
+  if (m_max > nvfp4::kW4A16MaxM) m_max = nvfp4::kW4A16MaxM;
   g_route_m_max.store(m_max);
 }
 
@@ -294,7 +294,7 @@ nvfp4_status linear_impl(const void* a, int64_t M, int64_t lda, const nvfp4_weig
     return NVFP4_OK;
   }
   if (route == NVFP4_ROUTE_W4A16) {
-    if (M > 16) return NVFP4_ERR_UNSUPPORTED;
+    if (M > nvfp4::kW4A16MaxM) return NVFP4_ERR_UNSUPPORTED;
     st = w4a16_checked(a, M, lda, w, alpha_w4a16, out, ldo, nullptr, stream);
   } else {
     if (!alpha_w4a4) return NVFP4_ERR_INVALID_ARGUMENT;

@@ -31,7 +31,9 @@ __host__ __device__ inline int64_t swizzled_scale_offset(int64_t row, int64_t co
   return ((row >> 7) * (cols_pad >> 2) + (col >> 2)) * 512 + (row & 31) * 16 + ((row >> 5) & 3) * 4 + (col & 3);
 }
 
-// W4A16 skinny kernel: out[M, N] = bf16(alpha * a[M, K] @ dequant(W)^T), M <= 16.
+// W4A16 skinny kernel: out[M, N] = bf16(alpha * a[M, K] @ dequant(W)^T), M <=
+// kW4A16MaxM (schedules 1, 3 and 4 take M <= 16; schedule 2 up to 64).
+constexpr int64_t kW4A16MaxM = 64;
 struct W4A16Config {
   int schedule;     // 1 = split (one tile per workgroup, K split over its waves), 2 = shared (8 tiles, all of K),
                     // 3 = split with interleaved steps, 4 = dot (split on the VALU, M <= 4)

@@ -1,4 +1,4 @@
-// W4A16 NVFP4 linear for decode-sized M (M <= 16) on gfx950.
+// W4A16 NVFP4 linear for decode-sized M (M <= 64) on gfx950.
 //
 // Computes out[m, n] = bf16(alpha * sum_k a[m, k] * e2m1(c[n, k]) * E4M3(s[n, k/16]))
 // with fp32 accumulation (FlashInfer PR #3597, Description: out = (a @
@@ -355,6 +355,23 @@ __device__ __forceinline__ void stage_load(const uint16_t* __restrict__ a, int64
   }
 }
 
+// Lane (c, qq) of token group mg holds out[16 mg + c][16 * tile + 4qq + i].
+__device__ __forceinline__ void store_tile_rows(const f32x4_t& acc, float alpha, int lane, int32_t tile, int32_t row0,
+                                                int32_t M, int32_t N, uint16_t* __restrict__ out, int64_t ldo) {
+  const int c = lane & 15, qq = lane >> 4;
+  if (row0 + c >= M) return;
+  uint16_t* orow = out + int64_t(row0 + c) * ldo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t n = 16 * tile + 4 * qq + i;
+    if (n < N) orow[n] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] * alpha));
+  }
+}
+
+// MG token groups of 16 (M <= 16 MG): the codes of each MFMA operand are
+// dequantized once and multiply the activation operands of every group, so
+// the dequant work per weight does not grow with M.
+template <int MG>
 __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __restrict__ a, int64_t lda, int32_t M,
                                                            const uint8_t* __restrict__ wt, int32_t N, int32_t K,
                                                            int32_t kc, const float* __restrict__ alpha_p,
@@ -369,7 +386,11 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
   const int32_t chunk_entries = kc * 32 * M;
   const int32_t tile = int32_t(blockIdx.x) * kSharedTiles + wave;
   const bool has_tile = tile < tiles;
-  const int lds_lane = (lane >> 4) * M + min(lane & 15, M - 1);
+  // token row 16 mg + (lane % 16) of k sub-block lane / 16 (rows past M repeat
+  // row M - 1; their outputs are not stored)
+  int lds_lane[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg) lds_lane[mg] = (lane >> 4) * M + min(16 * mg + (lane & 15), M - 1);
   const uint8_t* wtile = wt + int64_t(has_tile ? tile : 0) * steps * kUnitBytes;
 
   // The weight units of the next kSharedDepth steps are in flight while a
@@ -391,7 +412,9 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
     if (dst[i] >= 0) act[dst[i]] = v[i];
   __syncthreads();
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg) acc[mg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // step gs of chunk ch = gs / kc.  At a chunk's first step the chunk staged
   // during the previous one is written to its LDS buffer (every wave is past
   // the chunk before it, which used that buffer) and the next chunk's loads
@@ -409,10 +432,28 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
     const uint4* lds_step = act + (ch & 1) * chunk_entries + s * 32 * M;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      uint4 bb[4];
+      if (MG == 1) {
+        uint4 bb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bb[i] = lds_step[(4 * half + i) * 4 * M + lds_lane];
-      mma_half(half == 0 ? cur.c0 : cur.c1, cur.sc, half, bb, acc);
+        for (int i = 0; i < 4; ++i) bb[i] = lds_step[(4 * half + i) * 4 * M + lds_lane[0]];
+        mma_half(half == 0 ? cur.c0 : cur.c1, cur.sc, half, bb, acc[0]);
+      } else {
+        const uint4 codes = half == 0 ? cur.c0 : cur.c1;
+        const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
+        const float S0 = half == 0 ? e4m3_to_f32<0>(cur.sc) : e4m3_to_f32<2>(cur.sc);
+        const float S1 = half == 0 ? e4m3_to_f32<1>(cur.sc) : e4m3_to_f32<3>(cur.sc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t av[4];
+          dequant8_bf16(cw[i], i < 2 ? S0 : S1, av);
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
+#pragma unroll
+          for (int mg = 0; mg < MG; ++mg) {
+            const bf16x8_t B = __builtin_bit_cast(bf16x8_t, lds_step[(4 * half + i) * 4 * M + lds_lane[mg]]);
+            acc[mg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[mg], 0, 0, 0);
+          }
+        }
+      }
     }
   };
   for (int32_t gs = 0; gs < steps; gs += 4) {
@@ -429,7 +470,10 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
     w3 = unit_at(gs + 7);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (has_tile) store_tile(acc, alpha, lane, tile, M, N, out, ldo);
+  if (has_tile) {
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) store_tile_rows(acc[mg], alpha, lane, tile, 16 * mg, M, N, out, ldo);
+  }
 }
 
 // --------------------------------------------------------------------- dot
@@ -865,6 +909,13 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
   W4A16Config c;
   c.ksplit = 0;
   c.chunk_steps = 0;
+  if (M > 16) {
+    // more than one token group: only the shared schedule (16 M-row MFMA
+    // columns per group, the weight dequantized once for all groups)
+    c.schedule = 2;
+    c.chunk_steps = int(std::max<int64_t>(1, std::min<int64_t>(steps, 64 / M)));
+    return c;
+  }
   if (M <= 2 || (M == 3 && tiles * steps >= 20 * cus && tiles < int64_t(kSharedTiles) * cus * 3 / 2)) {
     // dot: waves per tile so the launch gives every CU about 8 waves (at
     // least 4 per workgroup), and at most 2 steps per wave while there are at
@@ -918,6 +969,7 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
 }
 
 bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K) {
+  if (M > kW4A16MaxM || (M > 16 && c.schedule != 2)) return false;
   if (c.schedule == 1) return c.ksplit >= 1 && c.ksplit <= 16;
   if (c.schedule == 3) {
     // chunk_steps: tiles per workgroup (0 or 1: one; 2: two, at most 8 waves)
@@ -951,8 +1003,15 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
     const int64_t kc = std::min<int64_t>(cfg.chunk_steps, steps);
     const size_t lds = 2 * size_t(M) * size_t(kc) * 32 * 16;
     const int64_t groups = (tiles + kSharedTiles - 1) / kSharedTiles;
-    hipLaunchKernelGGL(w4a16_shared_kernel, dim3(uint32_t(groups)), dim3(64 * kSharedTiles), lds, stream, A, lda,
-                       int32_t(M), WT, int32_t(N), int32_t(K), int32_t(kc), alpha, O, ldo);
+    const dim3 grid{uint32_t(groups)}, block{uint32_t(64 * kSharedTiles)};
+#define NVFP4_SHARED_LAUNCH(MG)                                                                                  \
+  hipLaunchKernelGGL((w4a16_shared_kernel<MG>), grid, block, lds, stream, A, lda, int32_t(M), WT, int32_t(N),    \
+                     int32_t(K), int32_t(kc), alpha, O, ldo)
+    if (M <= 16) NVFP4_SHARED_LAUNCH(1);
+    else if (M <= 32) NVFP4_SHARED_LAUNCH(2);
+    else if (M <= 48) NVFP4_SHARED_LAUNCH(3);
+    else NVFP4_SHARED_LAUNCH(4);
+#undef NVFP4_SHARED_LAUNCH
     return hipGetLastError();
   }
   if (cfg.schedule == 4) {

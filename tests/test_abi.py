@@ -94,7 +94,7 @@ def test_prepare_weight_validation(nv):
 def test_w4a16_validation(nv):
     f = nv.nvfp4_linear_w4a16
     w = _w()
-    assert f(A16, 17, 256, C.byref(w), A16, A16, 64, None) == UNSUP    # M > 16
+    assert f(A16, 65, 256, C.byref(w), A16, A16, 64, None) == UNSUP    # M > 64
     assert f(A16, 16, 1 << 27, C.byref(w), A16, A16, 64, None) == UNSUP  # offsets past 2^31 bytes
     assert f(A16, 4, 256, C.byref(w), None, A16, 64, None) == ARG      # alpha
     assert f(A16, 4, 256, C.byref(w), A16, A16, 63, None) == SHAPE     # ldo < N
@@ -142,6 +142,17 @@ def test_w4a4_validation(nv):
     assert f(A16, A16, 8, C.byref(wmis), A16, A16, 64, None) == ALIGN
 
 
+def test_route_default_threshold():
+    # a fresh process sees the documented default M* = 64 (the measured
+    # crossover on the large fused weight)
+    import sys
+
+    code = "from nvfp4_block_scaled_act_amd import lib; print(lib.load().nvfp4_get_route_m_max())"
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
+                         cwd=L.HERE + "/..").stdout
+    assert out.strip() == "64"
+
+
 def test_route_is_a_pure_threshold(nv):
     nv.nvfp4_set_route_m_max(16)
     assert nv.nvfp4_get_route_m_max() == 16
@@ -151,8 +162,8 @@ def test_route_is_a_pure_threshold(nv):
             assert nv.nvfp4_route(M, 8704, 5120, has_g) == want
     nv.nvfp4_set_route_m_max(4)
     assert nv.nvfp4_route(5, 1, 256, 1) == 1 and nv.nvfp4_route(4, 1, 256, 1) == 0
-    nv.nvfp4_set_route_m_max(100)          # clamped to the W4A16 kernel's limit
-    assert nv.nvfp4_get_route_m_max() == 16
+    nv.nvfp4_set_route_m_max(100)          # clamped to the W4A16 kernels' limit
+    assert nv.nvfp4_get_route_m_max() == 64
     nv.nvfp4_set_route_m_max(-3)
     assert nv.nvfp4_get_route_m_max() == 0
     nv.nvfp4_set_route_m_max(16)
@@ -168,8 +179,8 @@ def test_linear_dispatch_validation(nv):
     need = nv.nvfp4_linear_workspace_bytes(32, 64, 256)
     assert need >= 32 * 128 + 32 * 16
     assert f(A16, 32, 256, C.byref(w), A16, A16, A16, A16, 64, A16, need - 1, C.byref(r), None) == WS
-    # W4A16 route beyond its limit when no activation global is given
-    assert f(A16, 32, 256, C.byref(w), None, A16, None, A16, 64, None, 0, C.byref(r), None) == UNSUP
+    # W4A16 route beyond its limit (64) when no activation global is given
+    assert f(A16, 65, 256, C.byref(w), None, A16, None, A16, 64, None, 0, C.byref(r), None) == UNSUP
     # W4A4 route needs alpha_w4a4
     assert f(A16, 32, 256, C.byref(w), A16, A16, None, A16, 64, A16, need, C.byref(r), None) == ARG
     # empty batch, either route
@@ -189,7 +200,7 @@ def test_linear_noalloc_validation(nv):
     assert nv.nvfp4_linear_workspace_bytes(30000, 64, 2048) > (32 << 20)
     assert f(A16, 30000, 2048, C.byref(w), A16, A16, A16, A16, 64, C.byref(r), None) == WS
     assert f(A16, 32, 2048, C.byref(w), A16, A16, None, A16, 64, C.byref(r), None) == ARG    # no alpha_w4a4
-    assert f(A16, 32, 2048, C.byref(w), None, A16, None, A16, 64, C.byref(r), None) == UNSUP  # W4A16 beyond 16
+    assert f(A16, 65, 2048, C.byref(w), None, A16, None, A16, 64, C.byref(r), None) == UNSUP  # W4A16 beyond 64
     assert f(A16 + 2, 32, 2048, C.byref(w), A16, A16, A16, A16, 64, C.byref(r), None) == ALIGN
     assert f(A16, 32, 2048, C.byref(w), A16, A16, A16, A16, 10, C.byref(r), None) == SHAPE  # ldo < N
     r.value = -1

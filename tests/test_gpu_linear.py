@@ -111,6 +111,33 @@ def test_w4a16_long_k(ops, orc):
             gemm_check(bf16_host(out), ref[:M], sabs[:M])
 
 
+def test_w4a16_many_tokens(ops, orc):
+    # 17..64 tokens: the shared schedule with up to four 16-token groups on
+    # one dequantized weight, on a ragged N and an odd number of K steps, at
+    # the default chunk and at explicit chunks
+    N, K = 1000, 4352
+    W = synth.normal_bf16(25, N, K)
+    a = synth.normal_bf16(26, 64, K)
+    q = Quantized(ops, orc, W)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    ad = bf16_dev(a)
+    for M in (17, 24, 31, 32, 33, 47, 48, 49, 63, 64):
+        out = ops.linear_w4a16(ad[:M], q.w, q.alpha)
+        gemm_check(bf16_host(out), ref[:M], sabs[:M])
+        for kc in (1, 64 // M):
+            out = ops.linear_w4a16(ad[:M], q.w, q.alpha, schedule=2, chunk_steps=kc)
+            gemm_check(bf16_host(out), ref[:M], sabs[:M])
+    # long K: 72 steps in chunks of one step
+    N2, K2 = 200, 256 * 72
+    W2 = synth.normal_bf16(27, N2, K2)
+    a2 = synth.normal_bf16(28, 64, K2)
+    q2 = Quantized(ops, orc, W2)
+    ref2, _, sabs2 = orc.linear_w4a16(a2, q2.codes, q2.scales, orc.alpha(q2.g))
+    a2d = bf16_dev(a2)
+    for M in (20, 64):
+        gemm_check(bf16_host(ops.linear_w4a16(a2d[:M], q2.w, q2.alpha)), ref2[:M], sabs2[:M])
+
+
 def test_w4a16_default_very_long_k(ops, orc):
     # K = 256 * 129: more steps than the dot schedule's 16 waves x 8 steps, so
     # the default takes a split schedule at every M (an invalid dot config
@@ -191,7 +218,10 @@ def test_w4a16_empty_and_limits(ops, orc):
     out = ops.linear_w4a16(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), q.w, q.alpha)
     assert out.shape == (0, 64)
     with pytest.raises(ValueError):
-        ops.linear_w4a16(torch.zeros((17, 256), dtype=torch.bfloat16, device="cuda"), q.w, q.alpha)
+        ops.linear_w4a16(torch.zeros((65, 256), dtype=torch.bfloat16, device="cuda"), q.w, q.alpha)
+    with pytest.raises(ValueError):  # above 16 tokens only the shared schedule
+        ops.linear_w4a16(torch.zeros((17, 256), dtype=torch.bfloat16, device="cuda"), q.w, q.alpha, schedule=1,
+                         ksplit=1)
 
 
 def test_w4a16_deterministic(ops, orc):
@@ -337,6 +367,18 @@ def test_dispatch_routes_and_numerics(ops, orc):
     # no activation global: always W4A16
     out, route = ops.linear(ad[:8], q.w, None, a16, None)
     assert route == 0
+    # the default threshold M* = 64: W4A16 up to 64 tokens, W4A4 above
+    ops.set_route_m_max(64)
+    for M in (17, 40, 64, 65, 100):
+        out, route = ops.linear(ad[:M], q.w, gad, a16, a4)
+        assert route == (1 if M > 64 else 0)
+        if route == 0:
+            ref, _, sabs = orc.linear_w4a16(a[:M], q.codes, q.scales, orc.alpha(q.g))
+        else:
+            oac, oas = orc.quantize(a[:M], ga)
+            ref, _, sabs = orc.linear_w4a4(oac, oas, q.codes, q.scales, orc.alpha(q.g, ga))
+        gemm_check(bf16_host(out), ref, sabs)
+    ops.set_route_m_max(16)
 
 
 @pytest.fixture(scope="module")
@@ -366,14 +408,20 @@ def fused_large(ops, orc):
 
 
 def test_fused_large_w4a16_full(ops, orc, fused_large):
-    # the dispatched linear on the W4A16 route at M = 1, 8, 16: every output
+    # the dispatched linear on the W4A16 route at M = 1, 8, 16, and the W4A16
+    # kernels at M = 24, 32, 64: every output
     f = fused_large
     q = f["q"]
-    ref, _, sabs = orc.linear_w4a16(f["a"][:16], q.codes, q.scales, orc.alpha(q.g))
+    ref, _, sabs = orc.linear_w4a16(f["a"][:64], q.codes, q.scales, orc.alpha(q.g))
     ops.set_route_m_max(16)
     for M in (1, 8, 16):
         out, route = ops.linear(f["ad"][:M], q.w, f["gad"], q.alpha, f["a4"])
         assert route == 0
+        stats = gemm_check(bf16_host(out), ref[:M], sabs[:M])
+        print(f"M={M}: {stats}")
+    # the W4A16 kernels above 16 tokens (the crossover region), called directly
+    for M in (24, 32, 64):
+        out = ops.linear_w4a16(f["ad"][:M], q.w, q.alpha)
         stats = gemm_check(bf16_host(out), ref[:M], sabs[:M])
         print(f"M={M}: {stats}")
 
