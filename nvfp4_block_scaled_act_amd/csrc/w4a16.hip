@@ -194,23 +194,25 @@ __device__ __forceinline__ void reduce_store(f32x4_t acc, float* red, int wave, 
 // activation steps at a time and share them in the L1 cache.
 constexpr int kSplitMaxPer = 8;
 
-// R tiles per workgroup (R = 2 where a CU would otherwise hold two or more
-// one-tile workgroups): each step's activation operands are loaded (and
-// permuted) once and serve the R tiles' weight units.
+// Up to R tiles per workgroup (R = 2 where a CU would otherwise hold two or
+// more one-tile workgroups; R = 3 with one workgroup per CU holding 2 or 3
+// tiles): each step's activation operands are loaded (and permuted) once and
+// serve the workgroup's `count` tiles' weight units.
 template <int R>
 __device__ __forceinline__ void reduce_store_tiles(const f32x4_t (&acc)[R], float* red, int wave, int nwaves, int lane,
-                                                   int32_t tile0, int32_t tiles, int32_t M, int32_t N, float alpha,
-                                                   uint16_t* __restrict__ out, int64_t ldo) {
+                                                   int32_t tile0, int32_t count, int32_t tiles, int32_t M, int32_t N,
+                                                   float alpha, uint16_t* __restrict__ out, int64_t ldo) {
   if (nwaves == 1) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (tile0 + r < tiles) store_tile(acc[r], alpha, lane, tile0 + r, M, N, out, ldo);
+      if (r < count && tile0 + r < tiles) store_tile(acc[r], alpha, lane, tile0 + r, M, N, out, ldo);
     return;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) *reinterpret_cast<f32x4_t*>(&red[((wave * R + r) * 64 + lane) * 4]) = acc[r];
   __syncthreads();
-  if (wave >= R || tile0 + wave >= tiles) return;  // nwaves >= 2 >= R: wave r adds up tile r
+  // nwaves >= R: wave r adds up tile r
+  if (wave >= count || tile0 + wave >= tiles) return;
   f32x4_t sum = *reinterpret_cast<const f32x4_t*>(&red[(wave * 64 + lane) * 4]);
   for (int w = 1; w < nwaves; ++w) sum += *reinterpret_cast<const f32x4_t*>(&red[((w * R + wave) * 64 + lane) * 4]);
   store_tile(sum, alpha, lane, tile0 + wave, M, N, out, ldo);
@@ -219,14 +221,18 @@ __device__ __forceinline__ void reduce_store_tiles(const f32x4_t (&acc)[R], floa
 template <int PER, bool INTERLEAVE, bool PERM, int R>
 __global__ __launch_bounds__(R == 1 ? 1024 : 512) void w4a16_split_fixed_kernel(
     const uint16_t* __restrict__ a, int64_t lda, int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
-    int32_t steps_per_wave, const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo) {
+    int32_t steps_per_wave, const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo,
+    int32_t full) {
   extern __shared__ float red[];  // [waves][R][64][4]
   const int lane = int(threadIdx.x & 63);
   const int wave = int(threadIdx.x >> 6);
   const int nwaves = int(blockDim.x >> 6);
   const int q = lane >> 4;
   const int32_t tiles = (N + 15) / 16;
-  const int32_t tile0 = int32_t(blockIdx.x) * R;
+  // workgroups [0, full) hold R consecutive tiles, the rest R - 1
+  const int32_t wg = int32_t(blockIdx.x);
+  const int32_t tile0 = wg * (R - 1) + min(wg, full);
+  const int32_t count = R - 1 + (wg < full ? 1 : 0);
   const int32_t steps = K / 256;
   const int32_t s0 = INTERLEAVE ? wave : wave * steps_per_wave;
   const int32_t ds = INTERLEAVE ? nwaves : 1;
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void w4a16_split_fixed_kernel(
   const uint32_t aoff = act_off(lda, M, lrow, lq);
   // tiles past the last re-read the last tile; their results are not stored
   auto unit_at = [&](int r, int32_t st) {
-    const int32_t t = min(tile0 + r, tiles - 1);
+    const int32_t t = min(tile0 + min(r, count - 1), tiles - 1);
     return load_unit(wt + (int64_t(t) * steps + min(st, steps - 1)) * kUnitBytes, lane);
   };
   auto b_at = [&](int32_t st) { return load_b_rows(arsrc, aoff, min(st, steps - 1)); };
@@ -278,12 +284,14 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void w4a16_split_fixed_kernel(
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        mma_half(w[i & 1][r].c0, w[i & 1][r].sc, 0, b0, acc[r], live);
-        mma_half(w[i & 1][r].c1, w[i & 1][r].sc, 1, b1, acc[r], live);
+        if (R < 3 || r < count) {  // (uniform) a two-tile workgroup of R = 3 skips its third
+          mma_half(w[i & 1][r].c0, w[i & 1][r].sc, 0, b0, acc[r], live);
+          mma_half(w[i & 1][r].c1, w[i & 1][r].sc, 1, b1, acc[r], live);
+        }
       }
     }
   }
-  reduce_store_tiles<R>(acc, red, wave, nwaves, lane, tile0, tiles, M, N, alpha, out, ldo);
+  reduce_store_tiles<R>(acc, red, wave, nwaves, lane, tile0, count, tiles, M, N, alpha, out, ldo);
 }
 
 // Each wave runs steps [s0, s1) of one tile.  Step s+1's weight unit and
@@ -949,7 +957,17 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
     c.ksplit = int(std::max<int64_t>(1, std::min<int64_t>({want, steps, 16})));
     const int64_t ks = std::min<int64_t>(c.ksplit, steps);
     c.schedule = (steps + ks - 1) / ks <= kSplitMaxPer ? 3 : 1;
-    if (c.schedule == 3 && tiles > cus && tiles <= 2 * cus) {
+    W4A16Config three = c;
+    three.schedule = 3;
+    three.chunk_steps = 3;
+    three.ksplit = int(std::max<int64_t>(4, (steps + kSplitMaxPer - 1) / kSplitMaxPer));
+    if (tiles > 2 * cus && tiles <= 3 * cus && w4a16_config_valid(three, M, K)) {
+      // between 2 and 3 tiles per CU: one workgroup per CU holding 2 or 3
+      // tiles, each step's activation operands serving all of them (measured
+      // cold: 8704 x 5120 at M = 4/8/16 from 10.3/11.2/14.0 to 8.6/9.6/10.3
+      // us; 11008 x 4096 7-14 % faster)
+      c = three;
+    } else if (c.schedule == 3 && tiles > cus && tiles <= 2 * cus) {
       W4A16Config two = c;
       two.chunk_steps = 2;
       two.ksplit = int(std::max<int64_t>(std::min<int64_t>(4, steps), (steps + kSplitMaxPer - 1) / kSplitMaxPer));
@@ -974,9 +992,10 @@ bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K) {
   if (c.schedule == 3) {
     // chunk_steps: tiles per workgroup (0 or 1: one; 2: two, at most 8 waves)
     const int64_t steps = K / 256;
-    if (c.ksplit < 1 || c.ksplit > 16 || c.chunk_steps < 0 || c.chunk_steps > 2) return false;
+    if (c.ksplit < 1 || c.ksplit > 16 || c.chunk_steps < 0 || c.chunk_steps > 3) return false;
     const SplitShape sh = split_shape(c.ksplit, steps);
-    return sh.per <= kSplitMaxPer && (c.chunk_steps < 2 || sh.waves <= 8);
+    // two tiles: at most 8 waves; 2-3 tiles: 3 to 8 waves (wave r adds up tile r)
+    return sh.per <= kSplitMaxPer && (c.chunk_steps < 2 || sh.waves <= 8) && (c.chunk_steps < 3 || sh.waves >= 3);
   }
   if (c.schedule == 4) {
     if (M > kDotMaxM || c.ksplit < 1 || c.ksplit > 16) return false;
@@ -1045,17 +1064,26 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
   const int64_t ks = std::min<int64_t>(cfg.ksplit, steps);
   const int64_t per = (steps + ks - 1) / ks;
   const int waves = int((steps + per - 1) / per);
-  const int R = cfg.schedule == 3 && cfg.chunk_steps == 2 ? 2 : 1;  // tiles per workgroup
+  // tiles per workgroup: 1, 2, or (chunk_steps 3) 2 to 3 on about one
+  // workgroup per CU: G workgroups, the first `full` of them with 3 tiles
+  const int R = cfg.schedule == 3 && cfg.chunk_steps >= 2 ? cfg.chunk_steps : 1;
+  int64_t G = (tiles + R - 1) / R, full = G;
+  if (R == 3) {
+    G = std::max<int64_t>(std::min<int64_t>(cu_count(), tiles / 2), (tiles + 2) / 3);
+    full = std::max<int64_t>(0, tiles - 2 * G);
+  }
   const size_t lds = waves > 1 ? size_t(waves) * R * 64 * 4 * sizeof(float) : 0;
-  const dim3 grid{uint32_t((tiles + R - 1) / R)}, block{uint32_t(64 * waves)};
+  const dim3 grid{uint32_t(G)}, block{uint32_t(64 * waves)};
   // permuted activation loads once several token rows share a load group
   const bool perm = M > 4;
 #define NVFP4_SPLIT_LAUNCH(P, IL, PM, RR)                                                                       \
   hipLaunchKernelGGL((w4a16_split_fixed_kernel<P, IL, PM, RR>), grid, block, lds, stream, A, lda, int32_t(M),   \
-                     WT, int32_t(N), int32_t(K), int32_t(per), alpha, O, ldo)
+                     WT, int32_t(N), int32_t(K), int32_t(per), alpha, O, ldo, int32_t(full))
 #define NVFP4_SPLIT_FIXED(P)                                                                                    \
   case P:                                                                                                       \
-    if (cfg.schedule == 3 && R == 2) {                                                                          \
+    if (cfg.schedule == 3 && R == 3) {                                                                          \
+      if (perm) NVFP4_SPLIT_LAUNCH(P, true, true, 3); else NVFP4_SPLIT_LAUNCH(P, true, false, 3);               \
+    } else if (cfg.schedule == 3 && R == 2) {                                                                   \
       if (perm) NVFP4_SPLIT_LAUNCH(P, true, true, 2); else NVFP4_SPLIT_LAUNCH(P, true, false, 2);               \
     } else if (cfg.schedule == 3) {                                                                             \
       if (perm) NVFP4_SPLIT_LAUNCH(P, true, true, 1); else NVFP4_SPLIT_LAUNCH(P, true, false, 1);               \

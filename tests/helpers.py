@@ -75,6 +75,7 @@ def f32_dev(v) -> "torch.Tensor":
 # the default (0, 0, 0); schedules_for keeps the ones valid at (M, K).
 SCHEDULES = ([(1, ks, 0) for ks in (1, 2, 3, 7, 16)] + [(2, 0, kc) for kc in (1, 2, 3, 4, 17)]
              + [(3, ks, 0) for ks in (1, 3, 7, 16)] + [(3, ks, 2) for ks in (1, 3, 7, 8)]
+             + [(3, ks, 3) for ks in (3, 5, 8)]
              + [(4, ks, 0) for ks in (1, 3, 7, 16)])
 
 
@@ -82,10 +83,11 @@ def _schedule_valid(sch, M, K):
     steps = K // 256
     if sch[0] == 2:
         return M * min(sch[2], steps) <= 64
-    if sch[0] == 3:  # chunk_steps 2: two tiles per workgroup, at most 8 waves
+    if sch[0] == 3:  # chunk_steps 2: two tiles per workgroup, at most 8 waves; 3: 2-3 tiles, 3-8 waves
         ks = min(sch[1], steps)
         per = -(-steps // ks)
-        return per <= 8 and (sch[2] < 2 or -(-steps // per) <= 8)
+        waves = -(-steps // per)
+        return per <= 8 and (sch[2] < 2 or waves <= 8) and (sch[2] < 3 or waves >= 3)
     if sch[0] == 4:  # dot: M <= 4, <= 8 steps per wave
         ks = min(sch[1], steps)
         return M <= 4 and -(-steps // ks) <= 8

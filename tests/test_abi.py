@@ -121,7 +121,10 @@ def test_w4a16_validation(nv):
     assert g(A16, 4, 256 * 8, C.byref(wl), A16, A16, 64, 3, 0, 0, None) == ARG   # burst: ksplit 0
     wk = _w(N=64, K=256 * 20)
     assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 2, 0, None) == ARG  # burst: 10 steps per wave > 8
-    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 4, 3, None) == ARG  # 3 tiles per workgroup
+    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 4, 4, None) == ARG  # 4 tiles per workgroup
+    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 2, 3, None) == ARG  # 2-3 tiles: 10 steps per wave
+    w2 = _w(N=64, K=256 * 2)
+    assert g(A16, 4, 256 * 2, C.byref(w2), A16, A16, 64, 3, 4, 3, None) == ARG  # 2-3 tiles on 2 waves (< 3)
     assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 10, 2, None) == ARG  # two tiles: 10 waves > 8
     assert g(A16, 1, 256 * 20, C.byref(wk), A16, A16, 64, 4, 2, 0, None) == ARG  # dot: 10 steps per wave > 8
 
