@@ -450,6 +450,66 @@ def bench_w4a16_tactics(ops, torch, shapes=((11008, 4096), (4096, 11008), (14336
             "per_shape": rows}
 
 
+def bench_w4a16_cache_policy(ops, torch, reps=5):
+    """Cache-policy bits of the W4A16 loads measured in a sequence, as a decode
+    step runs them: per step one decode linear (the dot schedule) on a cold
+    weight copy, then a kernel on a buffer that stays cache-resident across
+    steps (8 MB, inside the L2s; 64 MB, inside the last-level cache only).
+    Per policy: the linear alone, the buffer kernel alone, and the sequence,
+    whose excess over the linear is what the linear costs the kernel after it."""
+    import math
+
+    from nvfp4_block_scaled_act_amd import synth
+
+    rows = []
+    policies = {0: "weights nontemporal, activations default (default)", 1: "weights default",
+                2: "weights and activations nontemporal"}
+    for N, K, ks in ((8704, 5120, 4), (3584, 5120, 10)):
+        wd = dev_bf16(torch, synth.normal_bf16(1, N, K))
+        g = ops.global_scale(wd)
+        c, s = ops.quantize_act(wd, g)
+        del wd
+        C = max(2, math.ceil(COLD_BYTES / (N * K * 9 / 16)))
+        copies = [ops.prepare_weight(c, s) for _ in range(C)]
+        al = ops.alpha(g)
+        a = dev_bf16(torch, synth.normal_bf16(2, 2, K))
+        for hot_mb in (8, 64):
+            hot = torch.ones(hot_mb << 18, dtype=torch.float32, device="cuda")
+            for M in (1, 2):
+                out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+                for cp, name in policies.items():
+                    def lin(w, cp=cp):
+                        ops.linear_w4a16(a[:M], w, al, out=out, schedule=4, ksplit=ks, cache_policy=cp)
+
+                    for w in copies[:2]:
+                        lin(w)
+                    torch.cuda.synchronize()
+                    graphs = {}
+                    for key, fn in (("linear", lambda: [lin(w) for w in copies]),
+                                    ("sequence", lambda: [(lin(w), hot.mul_(1.0)) for w in copies]),
+                                    ("buffer", lambda: [hot.mul_(1.0) for _ in copies])):
+                        gr = torch.cuda.CUDAGraph()
+                        with torch.cuda.graph(gr):
+                            fn()
+                        graphs[key] = gr
+                    warm_gpu(torch, lambda: (graphs["linear"].replay(), graphs["sequence"].replay()), ms=50.0)
+                    t = {}
+                    for key, gr in graphs.items():
+                        ts = per_call_us(torch, [gr.replay], reps)[0]
+                        t[key] = float(np.median(ts)) / C
+                    row = dict(N=N, K=K, M=M, buffer_mb=hot_mb, cache_policy=cp, policy=name,
+                               linear_us=round(t["linear"], 2), buffer_alone_us=round(t["buffer"], 2),
+                               sequence_us=round(t["sequence"], 2),
+                               buffer_in_sequence_us=round(t["sequence"] - t["linear"], 2))
+                    rows.append(row)
+                    log(f"[cache_policy] N={N} M={M} buffer {hot_mb} MB, {name}: linear {row['linear_us']} us, "
+                        f"buffer kernel alone {row['buffer_alone_us']} us, in sequence {row['buffer_in_sequence_us']} us")
+                    del graphs
+        del copies
+        torch.cuda.empty_cache()
+    return rows
+
+
 def bench_moe_decode(ops, torch, Ts=(1, 4, 16), cross_Ts=(16, 64, 256, 512, 1024, 2048), reps=3):
     """The same MoE layer at decode batch sizes through nvfp4_moe_w4a16 (bf16
     x and h, align into entries of up to 16 pairs, grouped W4A16 gate_up with
@@ -729,7 +789,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the W4A16 calls directly (counter runs)")
-    ap.add_argument("--only", choices=["all", "headline", "fused", "fused_sweep", "w4a4", "moe", "moe_decode", "w4a16_tactics", "copy"],
+    ap.add_argument("--only", choices=["all", "headline", "fused", "fused_sweep", "w4a4", "moe", "moe_decode", "w4a16_tactics",
+                                       "w4a16_cache_policy", "copy"],
                     default="all",
                     help="run one part (for profiler runs); 'copy' times a plain 256 MiB device copy, the "
                          "reference for the HBM byte counters")
@@ -760,6 +821,9 @@ def main():
     if args.only == "moe":
         r5 = bench_moe(ops, torch, reps=args.steps)
         print(json.dumps({"moe": {k: round(v, 3) if isinstance(v, float) else v for k, v in r5.items()}}))
+        return
+    if args.only == "w4a16_cache_policy":
+        print(json.dumps({"w4a16_cache_policy": bench_w4a16_cache_policy(ops, torch)}))
         return
     if args.only == "w4a16_tactics":
         print(json.dumps({"w4a16_tactics": bench_w4a16_tactics(ops, torch)}))

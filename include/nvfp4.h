@@ -237,11 +237,19 @@ nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvf
  *   schedule 4     dot: schedule 3's work split with the products on the
  *                  VALU (bf16 dot products, activations broadcast across
  *                  lanes); needs M <= 4 and ceil(K/256 / ksplit) <= 8
+ * cache_policy (schedule 4 only; 0 elsewhere, INVALID_ARGUMENT otherwise):
+ *                  0 the default: weight loads nontemporal (streamed without
+ *                  keeping them in the caches), activation loads default;
+ *                  1 weight loads default; 2 activation loads nontemporal
+ *                  too.  Same results; a tactic measured in a sequence of
+ *                  kernels (FreeToken PR #737, Changes, notes that a cache
+ *                  hint on the weights can help a linear alone and hurt the
+ *                  kernels after it).
  * Other values return INVALID_ARGUMENT.  The result bits depend on (M, N, K)
  * and the schedule. */
 nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w,
                                    const float* alpha, void* out, int64_t ldo, int schedule, int ksplit,
-                                   int chunk_steps, hipStream_t stream);
+                                   int chunk_steps, int cache_policy, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * nvfp4_linear_w4a4 -- out = bf16((dequant(A) @ dequant(W).T) * alpha) on

@@ -224,12 +224,14 @@ nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvf
 
 nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w,
                                    const float* alpha, void* out, int64_t ldo, int schedule, int ksplit,
-                                   int chunk_steps, hipStream_t stream) {
-  if (schedule == 0) return w4a16_checked(a, M, lda, w, alpha, out, ldo, nullptr, stream);
+                                   int chunk_steps, int cache_policy, hipStream_t stream) {
+  if (schedule == 0 && cache_policy == 0) return w4a16_checked(a, M, lda, w, alpha, out, ldo, nullptr, stream);
+  if (schedule == 0) return NVFP4_ERR_INVALID_ARGUMENT;
   nvfp4::W4A16Config cfg;
   cfg.schedule = schedule;
   cfg.ksplit = ksplit;
   cfg.chunk_steps = chunk_steps;
+  cfg.cache_policy = cache_policy;
   return w4a16_checked(a, M, lda, w, alpha, out, ldo, &cfg, stream);
 }
 

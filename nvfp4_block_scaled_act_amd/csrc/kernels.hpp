@@ -39,6 +39,8 @@ struct W4A16Config {
                     // 3 = split with interleaved steps, 4 = dot (split on the VALU, M <= 4)
   int ksplit;       // split, dot: waves per tile, 1..16
   int chunk_steps;  // shared: 256-k steps per LDS activation chunk
+  int cache_policy = 0;  // dot only: 0 weights nontemporal, activations default (the default);
+                         // 1 weights default; 2 activations nontemporal too
 };
 W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K);
 bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K);

@@ -52,6 +52,8 @@ namespace {
 constexpr int kUnitBytes = 2304;
 constexpr int kSharedTiles = 8;
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 struct Unit {
   uint4 c0, c1;
   uint32_t sc;
@@ -62,6 +64,16 @@ __device__ __forceinline__ Unit load_unit(const uint8_t* __restrict__ u, int lan
   x.c0 = ld16_nt(u + 16 * lane);
   x.c1 = ld16_nt(u + 1024 + 16 * lane);
   x.sc = ld4_nt(u + 2048 + 4 * lane);
+  return x;
+}
+
+// The same without the nontemporal hint (a cache-policy tactic, measured
+// against the default: it slows the linear and the kernels after it).
+__device__ __forceinline__ Unit load_unit_cached(const uint8_t* __restrict__ u, int lane) {
+  Unit x;
+  x.c0 = ld16(u + 16 * lane);
+  x.c1 = ld16(u + 1024 + 16 * lane);
+  x.sc = *reinterpret_cast<const uint32_t*>(u + 2048 + 4 * lane);
   return x;
 }
 
@@ -586,7 +598,7 @@ __device__ __forceinline__ void dot_step(const Unit& u, const uint2 (&x)[MT], fl
 // Wave w takes steps w, w + waves, ... (PER of them; the ones past K are
 // skipped) of the workgroup's tile, with the units and activations of two
 // steps in flight while one is computed.
-template <int PER, int MT>
+template <int PER, int MT, int CP>
 __global__ __launch_bounds__(1024) void w4a16_dot_kernel(
     const uint16_t* __restrict__ a, int64_t lda, int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
     const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo) {
@@ -599,10 +611,23 @@ __global__ __launch_bounds__(1024) void w4a16_dot_kernel(
   const uint16_t* arow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) arow[m] = a + int64_t(min(m, M - 1)) * lda + koff;
-  auto unit_at = [&](int32_t st) { return load_unit(wtile + int64_t(min(st, steps - 1)) * kUnitBytes, lane); };
+  // CP: the cache policy of the loads (0 the default; 1 weights without the
+  // nontemporal hint; 2 activations with it)
+  auto unit_at = [&](int32_t st) {
+    const uint8_t* u = wtile + int64_t(min(st, steps - 1)) * kUnitBytes;
+    return CP == 1 ? load_unit_cached(u, lane) : load_unit(u, lane);
+  };
   auto act_at = [&](int32_t st, uint2 (&x)[MT]) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) x[m] = *reinterpret_cast<const uint2*>(arow[m] + 256 * int64_t(min(st, steps - 1)));
+    for (int m = 0; m < MT; ++m) {
+      const uint16_t* p = arow[m] + 256 * int64_t(min(st, steps - 1));
+      if (CP == 2) {
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        x[m] = make_uint2(v.x, v.y);
+      } else {
+        x[m] = *reinterpret_cast<const uint2*>(p);
+      }
+    }
   };
 
   float alpha = *alpha_p;
@@ -988,6 +1013,7 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
 
 bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K) {
   if (M > kW4A16MaxM || (M > 16 && c.schedule != 2)) return false;
+  if (c.cache_policy < 0 || c.cache_policy > 2 || (c.cache_policy != 0 && c.schedule != 4)) return false;
   if (c.schedule == 1) return c.ksplit >= 1 && c.ksplit <= 16;
   if (c.schedule == 3) {
     // chunk_steps: tiles per workgroup (0 or 1: one; 2: two, at most 8 waves)
@@ -1037,13 +1063,17 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
     const SplitShape sh = split_shape(cfg.ksplit, steps);
     const size_t lds = size_t(sh.waves) * kDotMaxM * 16 * sizeof(float);
     const dim3 grid{uint32_t(tiles)}, block{uint32_t(64 * sh.waves)};
-#define NVFP4_DOT_LAUNCH(P, MT)                                                                                  \
-  hipLaunchKernelGGL((w4a16_dot_kernel<P, MT>), grid, block, lds, stream, A, lda, int32_t(M), WT, int32_t(N),    \
+#define NVFP4_DOT_LAUNCH(P, MT, CP)                                                                              \
+  hipLaunchKernelGGL((w4a16_dot_kernel<P, MT, CP>), grid, block, lds, stream, A, lda, int32_t(M), WT, int32_t(N),\
                      int32_t(K), alpha, O, ldo)
+#define NVFP4_DOT_M(P, CP)                                                                                       \
+    if (M == 1) NVFP4_DOT_LAUNCH(P, 1, CP); else if (M == 2) NVFP4_DOT_LAUNCH(P, 2, CP);                         \
+    else if (M == 3) NVFP4_DOT_LAUNCH(P, 3, CP); else NVFP4_DOT_LAUNCH(P, 4, CP);
 #define NVFP4_DOT(P)                                                                                             \
   case P:                                                                                                        \
-    if (M == 1) NVFP4_DOT_LAUNCH(P, 1); else if (M == 2) NVFP4_DOT_LAUNCH(P, 2);                                 \
-    else if (M == 3) NVFP4_DOT_LAUNCH(P, 3); else NVFP4_DOT_LAUNCH(P, 4);                                        \
+    if (cfg.cache_policy == 1) { NVFP4_DOT_M(P, 1) }                                                             \
+    else if (cfg.cache_policy == 2) { NVFP4_DOT_M(P, 2) }                                                        \
+    else { NVFP4_DOT_M(P, 0) }                                                                                   \
     return hipGetLastError();
     switch (sh.per) {
       NVFP4_DOT(1)
@@ -1058,6 +1088,7 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
         return hipErrorInvalidValue;
     }
 #undef NVFP4_DOT
+#undef NVFP4_DOT_M
 #undef NVFP4_DOT_LAUNCH
   }
   // contiguous runs of steps per wave; no wave is left without a step

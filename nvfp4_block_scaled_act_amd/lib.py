@@ -60,7 +60,7 @@ _SIGS = {
     "nvfp4_quantize_act_swizzled": (I32, [P, I64, I64, I64, P, P, P, SZ, P]),
     "nvfp4_prepare_weight_swizzled": (I32, [P, P, SZ, I64, I64, P, SZ, C.POINTER(Weight), P]),
     "nvfp4_linear_w4a16": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, P]),
-    "nvfp4_linear_w4a16_ex": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, I32, I32, I32, P]),
+    "nvfp4_linear_w4a16_ex": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, I32, I32, I32, I32, P]),
     "nvfp4_linear_w4a4": (I32, [P, P, I64, C.POINTER(Weight), P, P, I64, P]),
     "nvfp4_route": (I32, [I64, I64, I64, I32]),
     "nvfp4_set_route_m_max": (None, [I64]),

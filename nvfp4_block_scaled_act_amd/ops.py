@@ -182,12 +182,13 @@ def _out(out, M, N, device):
 
 
 def linear_w4a16(a: torch.Tensor, w: Weight, alpha_: torch.Tensor, out: torch.Tensor | None = None,
-                 schedule: int = 0, ksplit: int = 0, chunk_steps: int = 0) -> torch.Tensor:
+                 schedule: int = 0, ksplit: int = 0, chunk_steps: int = 0, cache_policy: int = 0) -> torch.Tensor:
     """W4A16 linear; schedule 0 picks the default schedule for (M, N, K)
     (1 = split with ksplit waves per tile, 2 = shared with LDS chunks of
-    chunk_steps steps, 3 = split with interleaved steps and chunk_steps (1 or
-    2) tiles per workgroup, 4 = dot: split on
-    the VALU, M <= 4)."""
+    chunk_steps steps, 3 = split with interleaved steps and chunk_steps (1,
+    2, or 3 = two to three) tiles per workgroup, 4 = dot: split on the VALU,
+    M <= 4).  cache_policy (dot only): 0 default, 1 weight loads without the
+    nontemporal hint, 2 activation loads with it."""
     _need(a, torch.bfloat16, "a")
     _scalar(alpha_, "alpha")
     lda = _rows(a, "a")
@@ -197,7 +198,7 @@ def linear_w4a16(a: torch.Tensor, w: Weight, alpha_: torch.Tensor, out: torch.Te
     out, ldo = _out(out, M, w.N, a.device)
     _L.check("nvfp4_linear_w4a16_ex",
              _L.load().nvfp4_linear_w4a16_ex(_ptr(a), M, lda, C.byref(w.desc), _ptr(alpha_), _ptr(out), ldo,
-                                             schedule, ksplit, chunk_steps, _stream()))
+                                             schedule, ksplit, chunk_steps, cache_policy, _stream()))
     return out
 
 

@@ -108,25 +108,28 @@ def test_w4a16_validation(nv):
     wz = _w(N=0)
     assert f(A16, 4, 256, C.byref(wz), A16, A16, 1, None) == OK         # N = 0
     g = nv.nvfp4_linear_w4a16_ex
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 5, 1, 1, None) == ARG    # schedule 5
-    assert g(A16, 5, 256, C.byref(w), A16, A16, 64, 4, 1, 0, None) == ARG    # dot: M > 4
-    assert g(A16, 2, 256, C.byref(w), A16, A16, 64, 4, 0, 0, None) == ARG    # dot: ksplit 0
-    assert g(A16, 2, 256, C.byref(w), A16, A16, 64, 4, 17, 0, None) == ARG   # dot: ksplit 17
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 0, 0, None) == ARG    # split: ksplit 0
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 17, 0, None) == ARG   # split: ksplit 17
-    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 2, 0, 0, None) == ARG    # shared: chunk 0
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 5, 1, 1, 0, None) == ARG    # schedule 5
+    assert g(A16, 5, 256, C.byref(w), A16, A16, 64, 4, 1, 0, 0, None) == ARG    # dot: M > 4
+    assert g(A16, 2, 256, C.byref(w), A16, A16, 64, 4, 0, 0, 0, None) == ARG    # dot: ksplit 0
+    assert g(A16, 2, 256, C.byref(w), A16, A16, 64, 4, 17, 0, 0, None) == ARG   # dot: ksplit 17
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 0, 0, 0, None) == ARG    # split: ksplit 0
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 1, 17, 0, 0, None) == ARG   # split: ksplit 17
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 2, 0, 0, 0, None) == ARG    # shared: chunk 0
     wl = _w(N=64, K=256 * 8)
-    assert g(A16, 16, 256 * 8, C.byref(wl), A16, A16, 64, 2, 0, 5, None) == ARG  # 16 x 5 > 64
-    assert g(A16, 0, 256, C.byref(w), A16, A16, 64, 2, 0, 5, None) == OK     # empty
-    assert g(A16, 4, 256 * 8, C.byref(wl), A16, A16, 64, 3, 0, 0, None) == ARG   # burst: ksplit 0
+    assert g(A16, 16, 256 * 8, C.byref(wl), A16, A16, 64, 2, 0, 5, 0, None) == ARG  # 16 x 5 > 64
+    assert g(A16, 0, 256, C.byref(w), A16, A16, 64, 2, 0, 5, 0, None) == OK     # empty
+    assert g(A16, 4, 256 * 8, C.byref(wl), A16, A16, 64, 3, 0, 0, 0, None) == ARG   # burst: ksplit 0
     wk = _w(N=64, K=256 * 20)
-    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 2, 0, None) == ARG  # burst: 10 steps per wave > 8
-    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 4, 4, None) == ARG  # 4 tiles per workgroup
-    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 2, 3, None) == ARG  # 2-3 tiles: 10 steps per wave
+    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 2, 0, 0, None) == ARG  # burst: 10 steps per wave > 8
+    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 4, 4, 0, None) == ARG  # 4 tiles per workgroup
+    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 2, 3, 0, None) == ARG  # 2-3 tiles: 10 steps per wave
     w2 = _w(N=64, K=256 * 2)
-    assert g(A16, 4, 256 * 2, C.byref(w2), A16, A16, 64, 3, 4, 3, None) == ARG  # 2-3 tiles on 2 waves (< 3)
-    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 10, 2, None) == ARG  # two tiles: 10 waves > 8
-    assert g(A16, 1, 256 * 20, C.byref(wk), A16, A16, 64, 4, 2, 0, None) == ARG  # dot: 10 steps per wave > 8
+    assert g(A16, 4, 256 * 2, C.byref(w2), A16, A16, 64, 3, 4, 3, 0, None) == ARG  # 2-3 tiles on 2 waves (< 3)
+    assert g(A16, 4, 256 * 20, C.byref(wk), A16, A16, 64, 3, 10, 2, 0, None) == ARG  # two tiles: 10 waves > 8
+    assert g(A16, 1, 256 * 20, C.byref(wk), A16, A16, 64, 4, 2, 0, 0, None) == ARG  # dot: 10 steps per wave > 8
+    assert g(A16, 1, 256, C.byref(w), A16, A16, 64, 4, 1, 0, 3, None) == ARG     # cache policy 3
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 3, 1, 0, 1, None) == ARG     # cache policy off the dot schedule
+    assert g(A16, 4, 256, C.byref(w), A16, A16, 64, 0, 0, 0, 2, None) == ARG     # ... or with the default
 
 
 def test_w4a4_validation(nv):

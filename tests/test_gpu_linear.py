@@ -91,6 +91,23 @@ def test_w4a16_every_schedule(ops, orc):
             gemm_check(bf16_host(out), ref2[:M], sabs2[:M])
 
 
+def test_w4a16_cache_policies(ops, orc):
+    # the dot schedule's cache-policy tactic changes load hints only: the
+    # same bits as the default policy, within the bar of the oracle
+    N, K = 1000, 4352
+    W = synth.normal_bf16(21, N, K)
+    a = synth.normal_bf16(22, 4, K)
+    q = Quantized(ops, orc, W)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    ad = bf16_dev(a)
+    for M in (1, 2, 4):
+        base = bf16_host(ops.linear_w4a16(ad[:M], q.w, q.alpha, schedule=4, ksplit=7))
+        gemm_check(base, ref[:M], sabs[:M])
+        for cp in (1, 2):
+            got = bf16_host(ops.linear_w4a16(ad[:M], q.w, q.alpha, schedule=4, ksplit=7, cache_policy=cp))
+            assert (got == base).all(), (M, cp)
+
+
 def test_w4a16_long_k(ops, orc):
     # K/256 = 72 steps: long runs per wave, many LDS chunks
     N, K = 200, 256 * 72
