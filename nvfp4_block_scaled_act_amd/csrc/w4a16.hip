@@ -602,7 +602,7 @@ template <int PER, int MT, int CP>
 __global__ __launch_bounds__(1024) void w4a16_dot_kernel(
     const uint16_t* __restrict__ a, int64_t lda, int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
     const float* __restrict__ alpha_p, uint16_t* __restrict__ out, int64_t ldo) {
-  extern __shared__ float dot_red[];  // [waves][MT][16]
+  extern __shared__ float dot_red[];  // [16][MT][16]: a slot per possible wave
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6), nwaves = int(blockDim.x >> 6);
   const int q = lane >> 4, n = lane & 15;
   const int32_t tile = int32_t(blockIdx.x), steps = K / 256;
@@ -666,10 +666,19 @@ __global__ __launch_bounds__(1024) void w4a16_dot_kernel(
     }
     __syncthreads();
     if (wave != 0) return;
+    // in wave order, from every slot read at once (the ones past nwaves are
+    // read and dropped)
+    float v[16][MT];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) v[k][m] = dot_red[(k * MT + m) * 16 + n];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      acc[m] = dot_red[m * 16 + n];
-      for (int k = 1; k < nwaves; ++k) acc[m] += dot_red[(k * MT + m) * 16 + n];
+      acc[m] = v[0][m];
+#pragma unroll
+      for (int k = 1; k < 16; ++k)
+        if (k < nwaves) acc[m] += v[k][m];
     }
   }
   const int32_t row = 16 * tile + n;
@@ -1061,7 +1070,7 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
   }
   if (cfg.schedule == 4) {
     const SplitShape sh = split_shape(cfg.ksplit, steps);
-    const size_t lds = size_t(sh.waves) * kDotMaxM * 16 * sizeof(float);
+    const size_t lds = size_t(16) * kDotMaxM * 16 * sizeof(float);
     const dim3 grid{uint32_t(tiles)}, block{uint32_t(64 * sh.waves)};
 #define NVFP4_DOT_LAUNCH(P, MT, CP)                                                                              \
   hipLaunchKernelGGL((w4a16_dot_kernel<P, MT, CP>), grid, block, lds, stream, A, lda, int32_t(M), WT, int32_t(N),\
