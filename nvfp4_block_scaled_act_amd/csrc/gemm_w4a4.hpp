@@ -15,8 +15,12 @@
 // (fp16, row-major, double-buffered): the weight tile from the tiled weight
 // (the step's 64 k of a 16-row tile are groups 4b..4b+3 of its unit, 8 code
 // bytes and one scale byte per (row, group)), the activation tile from the
-// canonical [rows, K/2] codes and [rows, K/16] scales.  The next step's loads
-// are in flight while the MFMAs of the current one run; one barrier per step.
+// canonical [rows, K/2] codes and [rows, K/16] scales.  The loads come in
+// pairs of steps (128 k): a weight item's 16 code bytes of both steps and its
+// unit's 4 scale bytes, an activation piece's 16 code bytes per step and its
+// row's 8 scale bytes of the pair, so every code load is a dwordx4 and no load
+// is narrower than a dword pair.  A pair is loaded two steps before its first
+// step is dequantized; one barrier per step.
 // Waves are laid out 2 (weight rows) x 4 (activation rows); each owns 128 x
 // BMT/4 outputs as 4 x BMT/128 MFMA tiles of 32 x 32 (the 32x32x16 shape runs at about
 // 1.6 times the rate of 16x16x32 on gfx950).  Register i of lane l in tile
@@ -105,12 +109,13 @@ struct AccT {
 };
 using Acc = AccT<BM>;
 
-// Staged (not yet dequantized) operand bytes of one step for this thread.
+// Staged (not yet dequantized) operand bytes of a pair of steps (2p, 2p+1)
+// for this thread.
 struct Stage {
-  uint2 w[2];      // weight: two (row, group) items of 16 codes
-  uint32_t ws[2];  // their scale bytes
-  uint4 a;         // activation: 32 codes of row tid/2, k 32*(tid&1) .. +32
-  uint32_t as;     // its two scale bytes (low 16 bits)
+  uint4 w[2];      // weight items j: 16 codes of step 2p (x, y) and of step 2p+1 (z, w)
+  uint32_t ws[2];  // their unit's scale bytes (steps 0..3 of the unit, byte b = step b)
+  uint4 a[2];      // activation: 32 codes of row tid/2, k 32*(tid&1) .. +32, of step 2p+h
+  uint2 as;        // the row's 8 scale bytes of the pair (x: step 2p, y: step 2p+1)
 };
 
 // The operands are read with buffer loads: a descriptor (scalar registers)
@@ -131,7 +136,7 @@ struct StageOffsets {
   uint32_t w[2];   // item's unit row start (relative to the descriptor) + 16*l
   uint32_t ws[2];  // the same + 2048 + 4*l (scale bytes)
   uint32_t a;      // activation codes of row tid/2, k 32*(tid&1)
-  uint32_t as;     // its scale bytes
+  uint32_t as;     // its scale bytes (the row's)
 };
 
 template <typename WTile, typename ARow>
@@ -149,7 +154,7 @@ __device__ __forceinline__ StageOffsets stage_offsets(WTile wtile, ARow a_row, i
   }
   const uint32_t arow = uint32_t(a_row(tid >> 1)), half = uint32_t(tid & 1);
   o.a = arow * uint32_t(K / 2) + 16u * half;
-  o.as = arow * uint32_t(K / 16) + 2u * half;
+  o.as = arow * uint32_t(K / 16);
   return o;
 }
 
@@ -157,38 +162,44 @@ struct StageSrc {
   __amdgpu_buffer_rsrc_t w, a, as;
 };
 
-__device__ __forceinline__ Stage load_stage(const StageSrc& src, const StageOffsets& o, int32_t step) {
-  const int b = step & 3;
-  // uniform parts: the step's unit within a tile row and its place in the unit
-  const int32_t wu = (step >> 2) * kUnitBytes;
-  const int32_t wc = wu + 1024 * (b >> 1) + 8 * (b & 1);
+// Loads of pair p: the unit of the pair's steps is p / 2 and its code chunk
+// (steps 4(p/2) + 2c, + 1) is c = p % 2.
+__device__ __forceinline__ Stage load_pair(const StageSrc& src, const StageOffsets& o, int32_t p) {
+  const int32_t wu = (p >> 1) * kUnitBytes;
+  const int32_t wc = wu + 1024 * (p & 1);
   Stage s;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.w, o.w[j], wc, 0);
-    s.w[j] = make_uint2(v[0], v[1]);
-    s.ws[j] = __builtin_amdgcn_raw_buffer_load_b8(src.w, o.ws[j], wu + b, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(src.w, o.w[j], wc, 0);
+    s.w[j] = make_uint4(v[0], v[1], v[2], v[3]);
+    s.ws[j] = __builtin_amdgcn_raw_buffer_load_b32(src.w, o.ws[j], wu, 0);
   }
-  const auto a = __builtin_amdgcn_raw_buffer_load_b128(src.a, o.a, step * (BK / 2), 0);
-  s.a = make_uint4(a[0], a[1], a[2], a[3]);
-  s.as = __builtin_amdgcn_raw_buffer_load_b16(src.as, o.as, step * (BK / 16), 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(src.a, o.a, p * BK + h * (BK / 2), 0);
+    s.a[h] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  const auto sv = __builtin_amdgcn_raw_buffer_load_b64(src.as, o.as, p * (2 * BK / 16), 0);
+  s.as = make_uint2(sv[0], sv[1]);
   return s;
 }
 
-// Dequantizes part `part` (0..3) of a staged step into LDS: parts 0 and 1 are
-// the thread's two weight items, parts 2 and 3 the two 16-k groups of its
-// activation piece.  Split in four so the work interleaves with the MFMAs.
+// Dequantizes part `part` (0..3) of step h (0, 1) of a staged pair with code
+// chunk c into LDS: parts 0 and 1 are the thread's two weight items, parts 2
+// and 3 the two 16-k groups of its activation piece.  Split in four so the
+// work interleaves with the MFMAs.
 template <int BMT>
-__device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* __restrict__ wbuf,
+__device__ __forceinline__ void store_part(const Stage& s, int c, int h, int part, _Float16* __restrict__ wbuf,
                                            _Float16* __restrict__ abuf) {
   const int tid = int(threadIdx.x);
   uint32_t v0[4], v1[4];
   if (part < 2) {
     const int i = tid + kThreads * part;
     const int lt = i >> 6, l = i & 63, r = l & 15, q = l >> 4;
-    const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(s.ws[part], 0));
-    dequant8_f16(s.w[part].x, S2, v0);
-    dequant8_f16(s.w[part].y, S2, v1);
+    // the step's scale byte: step 2c + h of the unit
+    const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(s.ws[part] >> (8 * (2 * c + h)), 0));
+    dequant8_f16(h == 0 ? s.w[part].x : s.w[part].z, S2, v0);
+    dequant8_f16(h == 0 ? s.w[part].y : s.w[part].w, S2, v1);
     uint4* d = reinterpret_cast<uint4*>(wbuf + (16 * lt + r) * PITCH + 16 * q);
     d[0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
     d[1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
@@ -198,9 +209,12 @@ __device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* _
     // narrow tiles stage fewer activation rows: waves BMT/32.. have none (a
     // wave-uniform test, so it is a scalar branch)
     if (BMT < BM && __builtin_amdgcn_readfirstlane(tid >> 6) >= BMT / 32) return;
-    const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(s.as >> (8 * g), 0));
-    dequant8_f16(g == 0 ? s.a.x : s.a.z, S2, v0);
-    dequant8_f16(g == 0 ? s.a.y : s.a.w, S2, v1);
+    // group 2 half + g of the step: byte 2 half + g of the step's scale dword
+    const uint32_t sb = (h == 0 ? s.as.x : s.as.y) >> (8 * (2 * half + g));
+    const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(sb, 0));
+    const uint4& ca = s.a[h];
+    dequant8_f16(g == 0 ? ca.x : ca.z, S2, v0);
+    dequant8_f16(g == 0 ? ca.y : ca.w, S2, v1);
     uint4* d = reinterpret_cast<uint4*>(abuf + row * PITCH + 32 * half + 16 * g);
     d[0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
     d[1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
@@ -208,14 +222,15 @@ __device__ __forceinline__ void store_part(const Stage& s, int part, _Float16* _
 }
 
 // acc += W tile x A tile over one step (four 16-k MFMA blocks); after block
-// kk, part kk of the next step's staged operands is dequantized into the other
-// LDS buffer, so the VALU work runs under the MFMAs.  (After the last step the
-// staged set is a re-read of it and lands in a buffer nobody reads.)
+// kk, part kk of the next step (step nh of the staged pair `next`, code chunk
+// nc) is dequantized into the other LDS buffer, so the VALU work runs under the
+// MFMAs.  (After the last step the staged pair is a re-read of the last one
+// and lands in a buffer nobody reads.)
 // wave_row0(t) = first LDS weight row of the wave's 32-row tile t.
 template <bool kSwap, int BMT, typename WaveRow0>
 __device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restrict__ wbuf, const _Float16* __restrict__ abuf,
-                                         WaveRow0 wave_row0, int wm, int lane, const Stage& next,
-                                         _Float16* __restrict__ wnext, _Float16* __restrict__ anext) {
+                                         WaveRow0 wave_row0, int wm, int lane, const Stage& next, int nc,
+                                         int nh, _Float16* __restrict__ wnext, _Float16* __restrict__ anext) {
   const int r = lane & 31, h = lane >> 5;
   // operands of block kk + 1 are read from LDS while the MFMAs of block kk run
   constexpr int U = BMT / 128;
@@ -239,7 +254,7 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restr
       for (int u = 0; u < U; ++u)
         acc.v[t][u] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_f16(B[cur][u], A[cur][t], acc.v[t][u], 0, 0, 0)
                             : __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][t], B[cur][u], acc.v[t][u], 0, 0, 0);
-    store_part<BMT>(next, kk, wnext, anext);
+    store_part<BMT>(next, nc, nh, kk, wnext, anext);
     // One MFMA, then a few VALU instructions of the staged dequant (and the
     // next block's LDS reads): the wave keeps its MFMA pipe busy while its own
     // VALU work issues in the MFMAs' shadow, instead of issuing the MFMAs
@@ -255,8 +270,8 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restr
   }
 }
 
-// The K loop of one workgroup tile over the 64-k steps [s_begin, s_end)
-// (default: all of K).
+// The K loop of one workgroup tile over all of K (K % 256 == 0, so the number
+// of 64-k steps is a multiple of 4 and the number of pairs is even).
 //   a_row(i)    global activation row of tile row i (0..255): always a valid row
 //               (rows BMT..255 are loaded but not used by a narrow tile)
 //   wtile(lt)   tile index in the tiled weight of LDS weight tile lt (0..15): always valid
@@ -264,11 +279,10 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restr
 template <bool kSwap = false, int BMT = BM, typename ARow, typename WTile, typename WaveRow0>
 __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ lds, const uint8_t* __restrict__ a_codes,
                                          const uint8_t* __restrict__ a_scales, ARow a_row,
-                                         const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K,
-                                         int32_t s_begin = 0, int32_t s_end = -1) {
+                                         const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K) {
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wm = wave >> 1;
-  const int32_t steps = s_end < 0 ? K / BK : s_end, steps256 = K / 256;  // steps: one past the last step
+  const int32_t pairs = K / (2 * BK), steps256 = K / 256;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -284,34 +298,39 @@ __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ 
   // tile at lds + 2 * BN * PITCH + b * BMT * PITCH (offsets, so that the
   // compiler keeps every access in the LDS address space)
   _Float16* const abase = lds + 2 * BN * PITCH;
-
-  // Step s+1's operands are staged in registers during step s-1 and
-  // dequantized into LDS during step s: the loads have a whole step to land.
-  // The two staging sets alternate by name (the loop runs two steps per
-  // iteration), so no staged register is copied while its load is in flight,
-  // and every step issues the same loads (past the last step they re-read it,
-  // unused): the compiler's wait counts then stay exact around the loop rather
-  // than draining the memory pipeline once per step.
-  Stage sa = load_stage(src, so, s_begin);
-#pragma unroll
-  for (int part = 0; part < 4; ++part) store_part<BMT>(sa, part, lds, abase);
-  sa = load_stage(src, so, min(s_begin + 1, steps - 1));
-  __syncthreads();
   _Float16* const w0 = lds;
   _Float16* const w1 = lds + BN * PITCH;
   _Float16* const a0 = abase;
   _Float16* const a1 = abase + BMT * PITCH;
-  for (int32_t s = s_begin;; s += 2) {
-    // step s from buffer 0; step s+1 (in sa) goes to buffer 1
-    const Stage sb = load_stage(src, so, min(s + 2, steps - 1));
-    mma_step<kSwap, BMT>(acc, w0, a0, wave_row0, wm, lane, sa, w1, a1);
+
+  // Pairs alternate between the staging sets X and Y by name (the loop runs
+  // two pairs per iteration), so no staged register is copied while its load
+  // is in flight, and every iteration issues the same loads (past the last
+  // pair they re-read it, unused): the compiler's wait counts then stay exact
+  // around the loop.  A pair is loaded during the step two before the one
+  // that dequantizes its first step, so its loads have two steps to land.
+  // The loop has one exit, at its end (a mid-loop exit made the register
+  // allocator move the accumulators through memory).
+  Stage X = load_pair(src, so, 0);
+  Stage Y = load_pair(src, so, min(1, pairs - 1));
+#pragma unroll
+  for (int part = 0; part < 4; ++part) store_part<BMT>(X, 0, 0, part, w0, a0);
+  __syncthreads();
+  for (int32_t p = 0; p < pairs; p += 2) {
+    // step 2p (buffer 0); step 2p+1, the second of X, -> buffer 1
+    mma_step<kSwap, BMT>(acc, w0, a0, wave_row0, wm, lane, X, p & 1, 1, w1, a1);
     __syncthreads();
-    if (s + 1 >= steps) break;
-    // step s+1 from buffer 1; step s+2 (in sb) goes to buffer 0
-    sa = load_stage(src, so, min(s + 3, steps - 1));
-    mma_step<kSwap, BMT>(acc, w1, a1, wave_row0, wm, lane, sb, w0, a0);
+    // step 2p+1 (buffer 1); step 2p+2, the first of Y, -> buffer 0; X <- pair p+2
+    X = load_pair(src, so, min(p + 2, pairs - 1));
+    mma_step<kSwap, BMT>(acc, w1, a1, wave_row0, wm, lane, Y, (p + 1) & 1, 0, w0, a0);
     __syncthreads();
-    if (s + 2 >= steps) break;
+    // step 2p+2 (buffer 0); step 2p+3, the second of Y, -> buffer 1
+    mma_step<kSwap, BMT>(acc, w0, a0, wave_row0, wm, lane, Y, (p + 1) & 1, 1, w1, a1);
+    __syncthreads();
+    // step 2p+3 (buffer 1); step 2p+4, the first of X, -> buffer 0; Y <- pair p+3
+    Y = load_pair(src, so, min(p + 3, pairs - 1));
+    mma_step<kSwap, BMT>(acc, w1, a1, wave_row0, wm, lane, X, p & 1, 0, w0, a0);
+    __syncthreads();
   }
 }
 
