@@ -50,6 +50,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def trace_summary(root):
+    """Markdown table of dispatch durations per (kernel, grid, block) from the
+    rocprofv3 kernel traces under root: dispatches, median, p10, p90 and mean
+    in us, heaviest first."""
+    import csv
+    import glob
+
+    rows = {}
+    for path in sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"].replace("nvfp4::(anonymous namespace)::", "").replace("void ", "")
+                name = name.split("(")[0]
+                grid = r.get("Grid_Size_X") or r.get("Grid_Size", "?")
+                block = r.get("Workgroup_Size_X") or r.get("Workgroup_Size", "?")
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                rows.setdefault((name, grid, block), []).append(us)
+    out = ["| kernel | grid x block (threads) | dispatches | median us | p10 us | p90 us | mean us |",
+           "|---|---|---|---|---|---|---|"]
+    for (name, grid, block), ts in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(ts)
+        out.append(f"| {name} | {grid} x {block} | {a.size} | {np.median(a):.2f} | {np.percentile(a, 10):.2f} | "
+                   f"{np.percentile(a, 90):.2f} | {a.mean():.2f} |")
+    return "\n".join(out)
+
+
 def w4a16_bytes(M, N, K):
     return N * K // 2 + N * K // 16 + 2 * M * K + 2 * M * N + 4
 
@@ -794,7 +820,13 @@ def main():
                     default="all",
                     help="run one part (for profiler runs); 'copy' times a plain 256 MiB device copy, the "
                          "reference for the HBM byte counters")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print per-(kernel, grid) median, p10 and p90 dispatch durations from the rocprofv3 "
+                         "kernel traces (*kernel_trace.csv) under DIR and exit (no GPU use)")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the NVFP4 linear here has no multi-GPU path (got --gpus {args.gpus})",
               file=sys.stderr)
