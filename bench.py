@@ -924,7 +924,9 @@ def main():
         gbs3 = r3["bytes"] / (r3["kernel_ms"] * 1e-3) / 1e9
         res["fused_large_decode"] = {
             "workload": "W4A16 N=62080 K=5120 M in {1,8,16}, cold", "tb_s": round(gbs3 / 1e3, 4),
-            "frac_of_hbm_peak": round(gbs3 / HBM_PEAK_GBS, 4), "kernel": "w4a16_shared_kernel", "per_m": r3["rows"]}
+            "frac_of_hbm_peak": round(gbs3 / HBM_PEAK_GBS, 4),
+            "kernel": "w4a16_dot_kernel (M = 1), w4a16_split_fixed_kernel (M = 8), w4a16_shared_kernel (M = 16)",
+            "per_m": r3["rows"]}
         fs = bench_fused_sweep(ops, torch)
         res["fused_large_sweep"] = {
             "workload": "dispatched linear N=62080 K=5120 at every M of the sweep (route reported), cold weights; "
