@@ -378,6 +378,25 @@ def test_moe_w4a16_many_pairs(ops, orc):
     check16(ops, orc, banks, x, ids, w, out, ws, tokens=[0, 1, 299, 300, 598, 599])
 
 
+def test_moe_align_large_count_table(ops, orc):
+    # E = 1024 experts, top-8, T = 2100: 16800 pairs in 17 align chunks, so
+    # the [chunks, E] count table (17408 entries) is larger than the scan's LDS
+    # staging and the scan walks it in global memory.  The align of both
+    # layers against a stable sort, W4A16 outputs on sampled tokens, and the
+    # W4A4 layer's align on the same inputs; a second W4A16 call gives the
+    # same bits.
+    E, top_k, K, I, T = 1024, 8, 256, 256, 2100
+    x, ids, w, _, _, _, gate_up, down = _small_case(606, T, E, top_k, K, I)
+    assert -(-T * top_k // 1024) * E > 16384
+    banks = banks16(ops, orc, gate_up, down, check_experts=[0, 511, E - 1])
+    out1, ws = run16(ops, banks, x, ids, w)
+    check16(ops, orc, banks, x, ids, w, out1, ws, tokens=[0, 1, 1049, 2098, 2099])
+    out2, _ = run16(ops, banks, x, ids, w, workspace=ws)
+    assert (bf16_host(out1) == bf16_host(out2)).all(), "W4A16 MoE must be deterministic"
+    _, ws4 = banks.run(ops, x, ids, w)
+    check_align(ops.moe_workspace_views(ws4, T, top_k, E, K, I), ids, E)
+
+
 def test_moe_w4a16_long_k_and_empty(ops, orc):
     # K = 4096, I = 512 (16 and 2 steps per GEMM: two steps per wave on gate_up)
     import torch
