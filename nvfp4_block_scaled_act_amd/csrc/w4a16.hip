@@ -31,10 +31,11 @@
 //    read the same activation steps at a time.  With more than 4 token rows
 //    the activation loads are issued in a cache-line-friendly lane order and
 //    moved to their MFMA lanes by a cross-lane permute.
-//  * shared -- for weights with many row tiles: a workgroup owns 8 tiles (one
-//    per wave) over all of K and streams the activations through LDS in
-//    double-buffered chunks of `kc` steps, so each chunk is read from L2 once
-//    per 8 tiles and from LDS by every wave.
+//  * shared -- for weights with many row tiles: a workgroup owns 8 tiles (16
+//    on weights of at least 1.5 x 8 tiles per CU; one per wave) over all of K
+//    and streams the activations through LDS in double-buffered chunks of `kc`
+//    steps, so each chunk is read from L2 once per 8 or 16 tiles and from LDS
+//    by every wave.
 //  * dot -- up to 4 tokens, the split schedule's work split on the VALU
 //    instead of the MFMA: each lane loads 4 activations per token and step
 //    (no duplicates), the dot-product instruction broadcasts them across the
@@ -358,12 +359,13 @@ __global__ __launch_bounds__(1024) void w4a16_split_kernel(
 // LDS holds two chunks of kc steps; a chunk is [kc steps][8 j][4 q][M c]
 // entries of 8 bf16 (only the M real token rows).
 __device__ __forceinline__ void stage_load(const uint16_t* __restrict__ a, int64_t lda, int32_t M, int32_t s_begin,
-                                           int32_t ns, int32_t tid, uint4 (&v)[4], int32_t (&dst)[4]) {
+                                           int32_t ns, int32_t tid, int32_t nthreads, uint4 (&v)[4],
+                                           int32_t (&dst)[4]) {
   const int32_t per_row = ns * 32;  // 16-byte pieces per token row in the chunk
   const int32_t total = per_row * M;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int32_t e = tid + i * kSharedTiles * 64;
+    const int32_t e = tid + i * nthreads;
     dst[i] = -1;
     if (e < total) {
       const int32_t c = e / per_row, kk = e - c * per_row;
@@ -390,9 +392,10 @@ __device__ __forceinline__ void store_tile_rows(const f32x4_t& acc, float alpha,
 
 // MG token groups of 16 (M <= 16 MG): the codes of each MFMA operand are
 // dequantized once and multiply the activation operands of every group, so
-// the dequant work per weight does not grow with M.
-template <int MG>
-__global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __restrict__ a, int64_t lda, int32_t M,
+// the dequant work per weight does not grow with M.  TPW tiles (one per wave)
+// per workgroup share each staged activation chunk.
+template <int MG, int TPW>
+__global__ __launch_bounds__(TPW * 64) void w4a16_shared_kernel(const uint16_t* __restrict__ a, int64_t lda, int32_t M,
                                                            const uint8_t* __restrict__ wt, int32_t N, int32_t K,
                                                            int32_t kc, const float* __restrict__ alpha_p,
                                                            uint16_t* __restrict__ out, int64_t ldo) {
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
   const int32_t steps = K / 256;
   const int32_t nch = (steps + kc - 1) / kc;
   const int32_t chunk_entries = kc * 32 * M;
-  const int32_t tile = int32_t(blockIdx.x) * kSharedTiles + wave;
+  const int32_t tile = int32_t(blockIdx.x) * TPW + wave;
   const bool has_tile = tile < tiles;
   // token row 16 mg + (lane % 16) of k sub-block lane / 16 (rows past M repeat
   // row M - 1; their outputs are not stored)
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
   uint4 v[4];
   int32_t dst[4];
   float alpha = *alpha_p;
-  stage_load(a, lda, M, 0, min(kc, steps), tid, v, dst);
+  stage_load(a, lda, M, 0, min(kc, steps), tid, TPW * 64, v, dst);
   Unit w0 = unit_at(0), w1 = unit_at(1), w2 = unit_at(2), w3 = unit_at(3);
   __builtin_amdgcn_sched_barrier(0);
   settle(alpha);
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(512) void w4a16_shared_kernel(const uint16_t* __res
         if (dst[i] >= 0) nbuf[dst[i]] = v[i];
       __syncthreads();
     }
-    if (s == 0 && ch + 1 < nch) stage_load(a, lda, M, gs + kc, min(kc, steps - gs - kc), tid, v, dst);
+    if (s == 0 && ch + 1 < nch) stage_load(a, lda, M, gs + kc, min(kc, steps - gs - kc), tid, TPW * 64, v, dst);
     const uint4* lds_step = act + (ch & 1) * chunk_entries + s * 32 * M;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -1063,11 +1066,22 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
   if (cfg.schedule == 2) {
     const int64_t kc = std::min<int64_t>(cfg.chunk_steps, steps);
     const size_t lds = 2 * size_t(M) * size_t(kc) * 32 * 16;
-    const int64_t groups = (tiles + kSharedTiles - 1) / kSharedTiles;
-    const dim3 grid{uint32_t(groups)}, block{uint32_t(64 * kSharedTiles)};
+    // 16 tiles per workgroup on weights of at least 1.5 x 8 tiles per CU
+    // (measured cold at N = 62080, K = 5120: M = 16/32/64 46.2/64.6/100.1 ->
+    // 41.9/57.1/80.7 us against 8 tiles); 8 below, where 16 would leave CUs idle
+    const bool wide = tiles >= int64_t(kSharedTiles) * cu_count() * 3 / 2;
+    const int tpw = wide ? 2 * kSharedTiles : kSharedTiles;
+    const int64_t groups = (tiles + tpw - 1) / tpw;
+    const dim3 grid{uint32_t(groups)}, block{uint32_t(64 * tpw)};
 #define NVFP4_SHARED_LAUNCH(MG)                                                                                  \
-  hipLaunchKernelGGL((w4a16_shared_kernel<MG>), grid, block, lds, stream, A, lda, int32_t(M), WT, int32_t(N),    \
-                     int32_t(K), int32_t(kc), alpha, O, ldo)
+  do {                                                                                                           \
+    if (wide)                                                                                                    \
+      hipLaunchKernelGGL((w4a16_shared_kernel<MG, 2 * kSharedTiles>), grid, block, lds, stream, A, lda,          \
+                         int32_t(M), WT, int32_t(N), int32_t(K), int32_t(kc), alpha, O, ldo);                    \
+    else                                                                                                         \
+      hipLaunchKernelGGL((w4a16_shared_kernel<MG, kSharedTiles>), grid, block, lds, stream, A, lda, int32_t(M),  \
+                         WT, int32_t(N), int32_t(K), int32_t(kc), alpha, O, ldo);                                \
+  } while (0)
     if (M <= 16) NVFP4_SHARED_LAUNCH(1);
     else if (M <= 32) NVFP4_SHARED_LAUNCH(2);
     else if (M <= 48) NVFP4_SHARED_LAUNCH(3);
