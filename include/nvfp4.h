@@ -410,15 +410,23 @@ nvfp4_status nvfp4_moe_w4a4(const void* x, int64_t T, int64_t ldx, const int32_t
  * MFMA).  A pair's fp32 sum order follows its entry's size, so a token's
  * output bits may change (within fp32 rounding) with the number of other
  * pairs routed to its experts; for given inputs the outputs are the same.
- * Five launches, no host sync; the outputs are the same bits on every call.
- * After the call the workspace holds, at the offsets
+ * Up to five launches, no host sync; the outputs are the same bits on every
+ * call.  After the call the workspace holds, at the offsets
  * nvfp4_moe_w4a16_workspace_layout reports: sorted, offsets, inv (as for
  * nvfp4_moe_w4a4), tiles (entries of up to 16 slots) and h (bf16 [T*top_k, I]
  * by slot).
+ * Few pairs (T*top_k <= NVFP4_MOE_W4A16_DIRECT_PAIRS, top_k <= 16, I <= 2048):
+ * every pair is its own entry and the layer runs in two launches without the
+ * align -- gate_up per pair, storing h at the pair index t*top_k + r (a
+ * skipped pair's row is not written), then down and the route sum together,
+ * one wave per route adding the token's routes in the order r = 0, 1, ... in
+ * fp32.  sorted, offsets, tiles and inv are then not written.
  * Needs K % 256 == 0, I % 256 == 0, K and I <= 16384, 1 <= E <= 1024,
  * T*top_k < 2^31, h below 2^31 bytes and x's last row ending below 2^31 bytes.
  * Errors as nvfp4_moe_w4a4.
  * ------------------------------------------------------------------------- */
+#define NVFP4_MOE_W4A16_DIRECT_PAIRS 64
+
 typedef struct nvfp4_moe_w4a16_layout {
   int64_t counts, offsets, tiles, sorted, inv;  /* as nvfp4_moe_layout */
   int64_t h;                                    /* bf16 [T*top_k, I] by slot */

@@ -8,6 +8,8 @@
 
 #include "kernels.hpp"
 
+static_assert(nvfp4::kMoeDirectPairs == NVFP4_MOE_W4A16_DIRECT_PAIRS, "direct-path threshold out of sync");
+
 namespace {
 
 constexpr int64_t kInt32Max = 2147483647LL;

@@ -108,6 +108,15 @@ hipError_t launch_w4a16_grouped(bool gated, const void* a, int64_t lda, const in
                                 int64_t rows_per_expert, int64_t K, const float* alpha_e, const float* topk_w,
                                 void* out, int64_t ldo, hipStream_t stream);
 
+// The W4A16 MoE layer for at most kMoeDirectPairs pairs (top_k <= 16, I and
+// K/256 steps <= 8 x 8 and 8): gate_up per pair into bf16 h at the pair
+// index (no align), then down and the fixed-order route sum in one launch.
+constexpr int64_t kMoeDirectPairs = 64;  // NVFP4_MOE_W4A16_DIRECT_PAIRS (checked in api.cpp)
+hipError_t launch_w4a16_moe_direct(const void* x, int64_t ldx, const int32_t* ids, int64_t T, int64_t top_k,
+                                   int64_t E, int64_t I, const void* w_gate_up, const void* w_down, int64_t K,
+                                   const float* alpha_gu, const float* alpha_dn, const float* topk_w, void* h,
+                                   void* out, int64_t ldo, hipStream_t stream);
+
 // Gated MLP gate_up on a dense NVFP4 batch: h = SiLU(z[:I]) * z[I:], z =
 // alpha * deq(A) . deq(W_gu)^T, quantized to NVFP4 under g2 ([M, I/2] codes,
 // [M, I/16] scales); h_amax (optional) receives max |h|.

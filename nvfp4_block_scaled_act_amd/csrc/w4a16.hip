@@ -710,7 +710,7 @@ __global__ __launch_bounds__(1024) void w4a16_dot_kernel(
 // lane loads 4 activations per token and step, the dot-product instruction
 // broadcasts them across the row; see the dot section), for the R tiles of
 // the workgroup at once.
-template <int PER, bool GATED, int MT>
+template <int PER, bool GATED, int MT, bool DIRECT = false>
 __device__ __forceinline__ void grouped_dot_body(const uint16_t* __restrict__ a, int64_t lda,
                                                  const int32_t* __restrict__ sorted, int32_t top_k, const MoeTile& ent,
                                                  int32_t t, const uint8_t* __restrict__ wt, int32_t rows_per_expert,
@@ -730,7 +730,8 @@ __device__ __forceinline__ void grouped_dot_body(const uint16_t* __restrict__ a,
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int32_t slot = ent.slot0 + m;
-    arow[m] = a + int64_t(GATED ? sorted[slot] / top_k : slot) * lda + koff;
+    // DIRECT: each pair is its own entry, its slot the pair index itself
+    arow[m] = a + int64_t(GATED ? (DIRECT ? slot : sorted[slot]) / top_k : slot) * lda + koff;
   }
   auto unit_at = [&](int r, int32_t st) {
     return load_unit(wt + (int64_t(wtile[r]) * steps + min(st, steps - 1)) * kUnitBytes, lane);
@@ -909,6 +910,89 @@ __global__ __launch_bounds__(512) void w4a16_grouped_kernel(
         make_float4(wr * (alpha * acc[0][0]), wr * (alpha * acc[0][1]), wr * (alpha * acc[0][2]),
                     wr * (alpha * acc[0][3]));
   }
+}
+
+// ------------------------------------------------------- direct (decode)
+// The W4A16 MoE layer when every pair can be its own entry (few pairs): no
+// align.  gate_up: one workgroup per (pair, 16-row gate tile) on the dot
+// products of a one-pair entry, reading the pair's expert from the routing
+// ids and storing h at the pair index.  Skipped pairs (ids outside [0, E))
+// store nothing.
+template <int PER>
+__global__ __launch_bounds__(512) void w4a16_direct_gate_up_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int32_t top_k, int32_t E,
+    int32_t out_tiles, const uint8_t* __restrict__ wt, int32_t rows_per_expert, int32_t K,
+    const float* __restrict__ alpha_e, uint16_t* __restrict__ h, int64_t ldh) {
+  extern __shared__ float red[];  // [waves][2][1][16]
+  const int32_t p = int32_t(blockIdx.x) / out_tiles, t = int32_t(blockIdx.x) - p * out_tiles;
+  const int32_t e = ids[p];
+  if (e < 0 || e >= E) return;
+  MoeTile ent;
+  ent.expert = e;
+  ent.slot0 = p;
+  ent.rows = 1;
+  ent.pad = 0;
+  grouped_dot_body<PER, true, 1, true>(x, ldx, nullptr, top_k, ent, t, wt, rows_per_expert, K, alpha_e, nullptr, h,
+                                       ldh, red);
+}
+
+// down and the route sum in one launch: workgroup (token t, 16-row output
+// tile) has one wave per route r.  Wave r computes y_r = w[t, r] *
+// (alpha_dn[e] * (h[t*top_k + r] . W_dn[e] rows)) over I with the dot
+// products of the dot schedule (PER = I/256 steps, two in flight); wave 0 then
+// adds the token's routes in the order r = 0, 1, ... in fp32 (skipped routes
+// add nothing) and rounds once to bf16 -- the route sum of the grouped path.
+template <int PER>
+__global__ __launch_bounds__(1024) void w4a16_direct_down_sum_kernel(
+    const uint16_t* __restrict__ h, const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
+    int32_t top_k, int32_t E, const uint8_t* __restrict__ wt, int32_t K, int32_t I,
+    const float* __restrict__ alpha_e, uint16_t* __restrict__ out, int64_t ldo) {
+  __shared__ float ys[16][16];  // [route][output row of the tile]
+  __shared__ int32_t live_r[16];
+  const int lane = int(threadIdx.x & 63);
+  const int r = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int q = lane >> 4, n = lane & 15;
+  const int32_t tiles_e = K / 16;  // output tiles of one expert's down bank
+  const int32_t t = int32_t(blockIdx.x) / tiles_e, tile = int32_t(blockIdx.x) - t * tiles_e;
+  const int32_t p = t * top_k + r;
+  const int32_t e = ids[p];
+  const bool live = e >= 0 && e < E;  // uniform per wave
+  float y = 0.0f;
+  if (live) {
+    const uint8_t* wtile = wt + (int64_t(e) * tiles_e + tile) * PER * kUnitBytes;
+    const int koff = 64 * (n >> 2) + 16 * q + 8 * ((n >> 1) & 1) + 4 * (n & 1);
+    const uint16_t* arow = h + int64_t(p) * I + koff;
+    const float alpha = alpha_e[e];
+    Unit w[2];
+    uint2 xa[2][1];
+    w[0] = load_unit(wtile, lane);
+    xa[0][0] = *reinterpret_cast<const uint2*>(arow);
+    if (PER > 1) {
+      w[1] = load_unit(wtile + kUnitBytes, lane);
+      xa[1][0] = *reinterpret_cast<const uint2*>(arow + 256);
+    }
+    float acc[1] = {0.0f};
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      dot_step<1>(w[i & 1], xa[i & 1], acc);
+      if (i + 2 < PER) {
+        w[i & 1] = load_unit(wtile + (i + 2) * kUnitBytes, lane);
+        xa[i & 1][0] = *reinterpret_cast<const uint2*>(arow + 256 * (i + 2));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    acc[0] += __shfl_xor(acc[0], 16, 64);
+    acc[0] += __shfl_xor(acc[0], 32, 64);
+    y = topk_w[p] * (alpha * acc[0]);
+  }
+  if (lane == 0) live_r[r] = live ? 1 : 0;
+  if (q == 0) ys[r][n] = y;
+  __syncthreads();
+  if (r != 0 || q != 0) return;
+  float sum = 0.0f;
+  for (int rr = 0; rr < top_k; ++rr)
+    if (live_r[rr]) sum += ys[rr][n];
+  out[int64_t(t) * ldo + 16 * tile + n] = __builtin_bit_cast(uint16_t, (__bf16)sum);
 }
 
 std::atomic<int> g_cu_count[64];
@@ -1207,6 +1291,68 @@ hipError_t launch_w4a16_grouped(bool gated, const void* a, int64_t lda, const in
       return hipErrorInvalidValue;
   }
 #undef NVFP4_GROUPED
+}
+
+hipError_t launch_w4a16_moe_direct(const void* x, int64_t ldx, const int32_t* ids, int64_t T, int64_t top_k,
+                                   int64_t E, int64_t I, const void* w_gate_up, const void* w_down, int64_t K,
+                                   const float* alpha_gu, const float* alpha_dn, const float* topk_w, void* h,
+                                   void* out, int64_t ldo, hipStream_t stream) {
+  const int64_t P = T * top_k;
+  if (P == 0) return hipSuccess;
+  const auto* X = static_cast<const uint16_t*>(x);
+  auto* H = static_cast<uint16_t*>(h);
+  // gate_up: K/256 steps over up to 8 waves, as the grouped kernels
+  {
+    const int64_t steps = K / 256;
+    const int64_t waves = std::min<int64_t>(steps, 8);
+    const int64_t per = (steps + waves - 1) / waves;
+    const size_t lds = size_t(waves) * 2 * 16 * sizeof(float);
+    const dim3 grid{uint32_t(P * (I / 16))}, block{uint32_t(64 * waves)};
+    const auto* WT = static_cast<const uint8_t*>(w_gate_up);
+#define NVFP4_DIRECT_GU(PP)                                                                                    \
+  case PP:                                                                                                     \
+    hipLaunchKernelGGL((w4a16_direct_gate_up_kernel<PP>), grid, block, lds, stream, X, ldx, ids, int32_t(top_k), \
+                       int32_t(E), int32_t(I / 16), WT, int32_t(2 * I), int32_t(K), alpha_gu, H, I);           \
+    break;
+    switch (per) {
+      NVFP4_DIRECT_GU(1)
+      NVFP4_DIRECT_GU(2)
+      NVFP4_DIRECT_GU(3)
+      NVFP4_DIRECT_GU(4)
+      NVFP4_DIRECT_GU(5)
+      NVFP4_DIRECT_GU(6)
+      NVFP4_DIRECT_GU(7)
+      NVFP4_DIRECT_GU(8)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef NVFP4_DIRECT_GU
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  // down + route sum: one wave per route, I/256 steps each
+  const dim3 grid{uint32_t(T * (K / 16))}, block{uint32_t(64 * top_k)};
+  const auto* WD = static_cast<const uint8_t*>(w_down);
+  auto* O = static_cast<uint16_t*>(out);
+#define NVFP4_DIRECT_DN(PP)                                                                                    \
+  case PP:                                                                                                     \
+    hipLaunchKernelGGL((w4a16_direct_down_sum_kernel<PP>), grid, block, 0, stream, H, ids, topk_w,             \
+                       int32_t(top_k), int32_t(E), WD, int32_t(K), int32_t(I), alpha_dn, O, ldo);              \
+    break;
+  switch (I / 256) {
+    NVFP4_DIRECT_DN(1)
+    NVFP4_DIRECT_DN(2)
+    NVFP4_DIRECT_DN(3)
+    NVFP4_DIRECT_DN(4)
+    NVFP4_DIRECT_DN(5)
+    NVFP4_DIRECT_DN(6)
+    NVFP4_DIRECT_DN(7)
+    NVFP4_DIRECT_DN(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef NVFP4_DIRECT_DN
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

@@ -268,6 +268,7 @@ def linear(a: torch.Tensor, w: Weight, g_act: torch.Tensor | None, alpha_w4a16: 
 
 
 NOALLOC_MAX_WORKSPACE_BYTES = 32 << 20  # NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES
+MOE_W4A16_DIRECT_PAIRS = 64  # NVFP4_MOE_W4A16_DIRECT_PAIRS
 
 
 def linear_noalloc(a: torch.Tensor, w: Weight, g_act: torch.Tensor | None, alpha_w4a16: torch.Tensor,

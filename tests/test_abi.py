@@ -420,3 +420,15 @@ def test_fused_weight_global_binding_warns():
         assert ops.fused_weight_global([300.0, 330.0]) == (330.0, True)
         assert ops.fused_weight_global([300.0, 301.0]) == (301.0, False)
     assert len(rec) == 1 and "5 %" in str(rec[0].message)
+
+
+def test_moe_w4a16_direct_pairs_constant():
+    # the binding's copy of the direct-path threshold matches the header
+    import os
+    import re
+
+    hdr = open(os.path.join(os.path.dirname(L.__file__), "..", "include", "nvfp4.h")).read()
+    m = re.search(r"#define NVFP4_MOE_W4A16_DIRECT_PAIRS (\d+)", hdr)
+    from nvfp4_block_scaled_act_amd import ops
+
+    assert m and int(m.group(1)) == ops.MOE_W4A16_DIRECT_PAIRS

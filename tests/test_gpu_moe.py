@@ -313,7 +313,12 @@ def check16(ops, orc, banks, x, ids, w, out, ws, tokens=None):
     T, top_k = ids.shape
     E, K, I = banks.E, banks.K, banks.I
     views = ops.moe_w4a16_workspace_views(ws, T, top_k, E, K, I)
-    inv = check_align(views, ids, E, rows=16)
+    if T * top_k <= ops.MOE_W4A16_DIRECT_PAIRS and top_k <= 16 and I <= 2048:
+        # the direct path: no align, h at the pair index (skipped pairs unwritten)
+        valid = ((ids >= 0) & (ids < E)).reshape(-1)
+        inv = np.where(valid, np.arange(T * top_k), -1)
+    else:
+        inv = check_align(views, ids, E, rows=16)
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     args = (banks.o_gu[0], banks.o_gu[1], banks.o_dn[0], banks.o_dn[1], banks.o_alpha_gu, banks.o_alpha_dn)
     res = orc.moe_w4a16(x, ids, w, *args, tokens=tokens)
@@ -337,7 +342,7 @@ def full_banks16(ops, orc):
     return banks, d
 
 
-@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("T", [1, 4, 8, 16])
 def test_moe_w4a16_decode(ops, orc, full_banks16, T):
     # the MoE workload's banks (E=128, top-8, K=2048, I=768) at decode batch
     # sizes: the first T tokens of its inputs and routing
@@ -366,6 +371,26 @@ def test_moe_w4a16_entries_skips_and_repeat(ops, orc):
     check16(ops, orc, banks, x, ids, w, out1, ws)
     out2, _ = run16(ops, banks, x, ids, w, workspace=ws)
     assert (bf16_host(out1) == bf16_host(out2)).all(), "W4A16 MoE must be deterministic"
+
+
+def test_moe_w4a16_direct_skips_and_repeat(ops, orc):
+    # few pairs (the direct path: no align, down and the route sum in one
+    # launch): top-3 over 8 experts, T = 7 (21 pairs), ids outside [0, E)
+    # skipped, a token with every route skipped; a second call on the same
+    # workspace gives the same bits
+    E, top_k, K, I, T = 8, 3, 512, 256, 7
+    x, ids, w, _, _, _, gate_up, down = _small_case(707, T, E, top_k, K, I)
+    ids = ids.copy()
+    ids[1, 0] = -1
+    ids[4, 2] = E
+    ids[6, :] = -1
+    assert T * top_k <= ops.MOE_W4A16_DIRECT_PAIRS
+    banks = banks16(ops, orc, gate_up, down)
+    out1, ws = run16(ops, banks, x, ids, w)
+    check16(ops, orc, banks, x, ids, w, out1, ws)
+    out2, _ = run16(ops, banks, x, ids, w, workspace=ws)
+    assert (bf16_host(out1) == bf16_host(out2)).all(), "W4A16 MoE must be deterministic"
+    assert (bf16_host(out1)[6] == 0).all(), "a token with every route skipped is zero"
 
 
 def test_moe_w4a16_many_pairs(ops, orc):
