@@ -184,6 +184,25 @@ def test_w4a16_default_many_tiles(ops, orc):
             gemm_check(bf16_host(out), ref[:M], sabs[:M])
 
 
+def test_w4a16_shared_wide_ragged(ops, orc):
+    # 3073 tiles (at least 1.5 x 8 tiles per CU on 256 CUs): the shared schedule
+    # runs 16 tiles per workgroup, the last workgroup holding one partial tile
+    # (N = 3072 * 16 + 8); M = 16 (one token group) and 40 (three), default and
+    # explicit chunks; M = 5 and 8 take the two-tile split there
+    N, K = 3072 * 16 + 8, 512
+    W = synth.normal_bf16(29, N, K)
+    a = synth.normal_bf16(30, 40, K)
+    q = Quantized(ops, orc, W)
+    ref, _, sabs = orc.linear_w4a16(a, q.codes, q.scales, orc.alpha(q.g))
+    ad = bf16_dev(a)
+    for M in (5, 8, 16, 40):
+        out = ops.linear_w4a16(ad[:M], q.w, q.alpha)
+        gemm_check(bf16_host(out), ref[:M], sabs[:M])
+    for M, kc in ((16, 1), (16, 2), (40, 1)):
+        out = ops.linear_w4a16(ad[:M], q.w, q.alpha, schedule=2, chunk_steps=kc)
+        gemm_check(bf16_host(out), ref[:M], sabs[:M])
+
+
 def test_prepared_layout(ops, orc):
     """The tiled weight follows the documented unit layout byte for byte."""
     N, K = 40, 512
