@@ -221,16 +221,48 @@ __device__ __forceinline__ void store_part(const Stage& s, int c, int h, int par
   }
 }
 
+// MFMAs of the last 16-k block of a step that are issued after the barrier
+// that ends the step, right after the next step's first LDS reads: every
+// wave leaves the barrier at once and waits for those reads, and the held
+// MFMAs keep the matrix pipe busy meanwhile.  Their operands are registers,
+// and each accumulator still receives its products in k order, so the
+// results are the same bits.  Holding the last weight tile (2 MFMAs per wave
+// at 256 activation rows) took the GEMM at N = 8704, K = 5120 from 108.5 to
+// 103.4 us (M = 1024) and from 591 to 577 us (M = 8192); holding two was no
+// better.
+constexpr int kHoldT = 1;  // wave 32-row weight tiles t = 4 - kHoldT .. 3 are held
+
+template <int BMT>
+struct HeldT {
+  f16x8_t a[kHoldT];
+  f16x8_t b[BMT / 128];
+};
+
+template <bool kSwap, int BMT>
+__device__ __forceinline__ void issue_held(AccT<BMT>& acc, const HeldT<BMT>& held) {
+#pragma unroll
+  for (int i = 0; i < kHoldT; ++i)
+#pragma unroll
+    for (int u = 0; u < BMT / 128; ++u) {
+      const int t = 4 - kHoldT + i;
+      acc.v[t][u] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_f16(held.b[u], held.a[i], acc.v[t][u], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_f16(held.a[i], held.b[u], acc.v[t][u], 0, 0, 0);
+    }
+}
+
 // acc += W tile x A tile over one step (four 16-k MFMA blocks); after block
 // kk, part kk of the next step (step nh of the staged pair `next`, code chunk
 // nc) is dequantized into the other LDS buffer, so the VALU work runs under the
 // MFMAs.  (After the last step the staged pair is a re-read of the last one
-// and lands in a buffer nobody reads.)
+// and lands in a buffer nobody reads.)  The held MFMAs of the previous step
+// are issued first (zero operands before the first step add nothing), and
+// this step's are left in `held`.
 // wave_row0(t) = first LDS weight row of the wave's 32-row tile t.
 template <bool kSwap, int BMT, typename WaveRow0>
-__device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restrict__ wbuf, const _Float16* __restrict__ abuf,
-                                         WaveRow0 wave_row0, int wm, int lane, const Stage& next, int nc,
-                                         int nh, _Float16* __restrict__ wnext, _Float16* __restrict__ anext) {
+__device__ __forceinline__ void mma_step(AccT<BMT>& acc, HeldT<BMT>& held, const _Float16* __restrict__ wbuf,
+                                         const _Float16* __restrict__ abuf, WaveRow0 wave_row0, int wm, int lane,
+                                         const Stage& next, int nc, int nh, _Float16* __restrict__ wnext,
+                                         _Float16* __restrict__ anext) {
   const int r = lane & 31, h = lane >> 5;
   // operands of block kk + 1 are read from LDS while the MFMAs of block kk run
   constexpr int U = BMT / 128;
@@ -244,23 +276,29 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restr
       A[slot][t] = *reinterpret_cast<const f16x8_t*>(wbuf + (wave_row0(t) + r) * PITCH + 16 * kk + 8 * h);
   };
   read(0, 0);
+  issue_held<kSwap, BMT>(acc, held);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
     const int cur = kk & 1;
-    if (kk + 1 < BK / 16) read(kk + 1, cur ^ 1);
+    const bool last = kk + 1 == BK / 16;
+    if (!last) read(kk + 1, cur ^ 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        if (last && t >= 4 - kHoldT) continue;
         acc.v[t][u] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_f16(B[cur][u], A[cur][t], acc.v[t][u], 0, 0, 0)
                             : __builtin_amdgcn_mfma_f32_32x32x16_f16(A[cur][t], B[cur][u], acc.v[t][u], 0, 0, 0);
+      }
     store_part<BMT>(next, nc, nh, kk, wnext, anext);
     // One MFMA, then a few VALU instructions of the staged dequant (and the
     // next block's LDS reads): the wave keeps its MFMA pipe busy while its own
     // VALU work issues in the MFMAs' shadow, instead of issuing the MFMAs
     // back to back and the VALU work after them.
+    constexpr int kLastMfma = (4 - kHoldT) * U;
 #pragma unroll
-    for (int i = 0; i < 4 * U; ++i) {
+    for (int i = 0; i < (last ? kLastMfma : 4 * U); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
@@ -268,6 +306,10 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, const _Float16* __restr
     __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // LDS write
     __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int i = 0; i < kHoldT; ++i) held.a[i] = A[1][4 - kHoldT + i];
+#pragma unroll
+  for (int u = 0; u < U; ++u) held.b[u] = B[1][u];
 }
 
 // The K loop of one workgroup tile over all of K (K % 256 == 0, so the number
@@ -289,6 +331,11 @@ __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ 
     for (int u = 0; u < BMT / 128; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc.v[t][u][i] = 0.f;
+  HeldT<BMT> held;
+#pragma unroll
+  for (int i = 0; i < kHoldT; ++i) held.a[i] = f16x8_t{};
+#pragma unroll
+  for (int u = 0; u < BMT / 128; ++u) held.b[u] = f16x8_t{};
   const StageOffsets so = stage_offsets(wtile, a_row, steps256, K);
   StageSrc src;
   src.w = buffer_rsrc(wt + wtile(0) * steps256 * kUnitBytes);
@@ -318,20 +365,21 @@ __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ 
   __syncthreads();
   for (int32_t p = 0; p < pairs; p += 2) {
     // step 2p (buffer 0); step 2p+1, the second of X, -> buffer 1
-    mma_step<kSwap, BMT>(acc, w0, a0, wave_row0, wm, lane, X, p & 1, 1, w1, a1);
+    mma_step<kSwap, BMT>(acc, held, w0, a0, wave_row0, wm, lane, X, p & 1, 1, w1, a1);
     __syncthreads();
     // step 2p+1 (buffer 1); step 2p+2, the first of Y, -> buffer 0; X <- pair p+2
     X = load_pair(src, so, min(p + 2, pairs - 1));
-    mma_step<kSwap, BMT>(acc, w1, a1, wave_row0, wm, lane, Y, (p + 1) & 1, 0, w0, a0);
+    mma_step<kSwap, BMT>(acc, held, w1, a1, wave_row0, wm, lane, Y, (p + 1) & 1, 0, w0, a0);
     __syncthreads();
     // step 2p+2 (buffer 0); step 2p+3, the second of Y, -> buffer 1
-    mma_step<kSwap, BMT>(acc, w0, a0, wave_row0, wm, lane, Y, (p + 1) & 1, 1, w1, a1);
+    mma_step<kSwap, BMT>(acc, held, w0, a0, wave_row0, wm, lane, Y, (p + 1) & 1, 1, w1, a1);
     __syncthreads();
     // step 2p+3 (buffer 1); step 2p+4, the first of X, -> buffer 0; Y <- pair p+3
     Y = load_pair(src, so, min(p + 3, pairs - 1));
-    mma_step<kSwap, BMT>(acc, w1, a1, wave_row0, wm, lane, X, p & 1, 0, w0, a0);
+    mma_step<kSwap, BMT>(acc, held, w1, a1, wave_row0, wm, lane, X, p & 1, 0, w0, a0);
     __syncthreads();
   }
+  issue_held<kSwap, BMT>(acc, held);
 }
 
 // Writes the bf16 tile out[m][n] (activation row m, weight row n) of the
