@@ -225,9 +225,11 @@ nvfp4_status nvfp4_linear_w4a16(const void* a, int64_t M, int64_t lda, const nvf
  *   schedule 0     the default for (M, N, K); the other arguments are ignored
  *   schedule 1     split: one workgroup per 16-row tile whose ksplit (1..16)
  *                  waves split K into contiguous runs of 256-k steps
- *   schedule 2     shared: one workgroup per 8 tiles over all of K, the
- *                  activations streamed through LDS in chunks of chunk_steps
- *                  256-k steps; needs M * min(chunk_steps, K/256) <= 64;
+ *   schedule 2     shared: one workgroup per 8 tiles (16 on weights of at
+ *                  least 12 tiles per CU) over all of K, the activations
+ *                  streamed through LDS in chunks of chunk_steps 256-k steps;
+ *                  needs R * min(chunk_steps, K/256) <= 64 with R = M
+ *                  up to 16 tokens and 16 * ceil(M/16) above;
  *                  the only schedule for M > 16 (INVALID_ARGUMENT otherwise)
  *   schedule 3     split with interleaved steps (wave w takes steps w,
  *                  w + waves, ...); needs ceil(K/256 / ksplit) <= 8.  Here

@@ -356,25 +356,60 @@ __global__ __launch_bounds__(1024) void w4a16_split_kernel(
 }
 
 // ------------------------------------------------------------------ shared
-// LDS holds two chunks of kc steps; a chunk is [kc steps][8 j][4 q][M c]
-// entries of 8 bf16 (only the M real token rows).
-__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ a, int64_t lda, int32_t M, int32_t s_begin,
-                                           int32_t ns, int32_t tid, int32_t nthreads, uint4 (&v)[4],
-                                           int32_t (&dst)[4]) {
-  const int32_t per_row = ns * 32;  // 16-byte pieces per token row in the chunk
-  const int32_t total = per_row * M;
+// LDS holds two chunks of kc steps; a chunk is [kc steps][8 j][4 q][MP c]
+// entries of 8 bf16: the M real token rows, with MP = M for one token group
+// and M padded to the kernel's 16 MG rows above, so that the distance between
+// the (j, q) blocks is a constant and the LDS reads of a step take immediate
+// offsets.
+//
+// Thread e of the workgroup stages entry e (and e + threads, ...) of the
+// chunk's real rows in token-row-fastest order, so the LDS writes of a wave
+// are runs of M consecutive entries.  (With one token row per run of
+// neighbouring threads their entries lay M apart and the writes of a wave all
+// fell in one bank: about half of the kernel's LDS cycles were bank
+// conflicts, and N = 62080, K = 5120 took 80/69/59 us at M = 64/48/32
+// against 76/63/54 us without them.)  The global loads then take 16 bytes
+// from each of up to 64 token rows per instruction; they hit L2.  Where an
+// entry goes and what it loads is the same for every chunk, so it is computed
+// once per thread (with the padded rows, about a sixth fewer VALU
+// instructions at M = 64 and 2-6 % less time at M = 16 and 32).
+struct SharedStage {
+  int32_t dst[4];  // LDS entry in a chunk (kc * 32 * MP when the thread has none)
+  int32_t src[4];  // token row c | (k offset in the chunk << 8)
+};
+
+__device__ __forceinline__ SharedStage shared_stage(int32_t M, int32_t MP, int32_t kc, int32_t tid, int32_t nthreads) {
+  SharedStage st;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int32_t e = tid + i * nthreads;
-    dst[i] = -1;
-    if (e < total) {
-      const int32_t c = e / per_row, kk = e - c * per_row;
-      const int32_t s = kk >> 5, r5 = kk & 31;                   // step in the chunk, piece in the step
-      const int32_t p = r5 >> 3, q = (r5 >> 1) & 3, h = r5 & 1;  // k = 64p + 16q + 8h
-      v[i] = ld16(a + int64_t(c) * lda + int64_t(s_begin + s) * 256 + 8 * r5);
-      dst[i] = ((s * 8 + 2 * p + h) * 4 + q) * M + c;
+    st.dst[i] = kc * 32 * MP;
+    st.src[i] = 0;
+    if (e < kc * 32 * M) {
+      const int32_t rest = e / M, c = e - rest * M;  // rest = (s * 8 + j) * 4 + q
+      const int32_t q = rest & 3, j = (rest >> 2) & 7, s = rest >> 5;
+      st.dst[i] = rest * MP + c;
+      // MFMA j = 2p + h of a step multiplies k = 64p + 16q + 8h + (0..7)
+      st.src[i] = c | ((s * 256 + 64 * (j >> 1) + 16 * q + 8 * (j & 1)) << 8);
     }
   }
+  return st;
+}
+
+// Loads of the chunk that starts at step s_begin and has ns steps.
+__device__ __forceinline__ void shared_load(const uint16_t* __restrict__ a, int64_t lda, const SharedStage& st,
+                                            int32_t MP, int32_t s_begin, int32_t ns, uint4 (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (st.dst[i] < ns * 32 * MP)
+      v[i] = ld16(a + int64_t(st.src[i] & 255) * lda + int64_t(s_begin) * 256 + (st.src[i] >> 8));
+}
+
+__device__ __forceinline__ void shared_store(uint4* __restrict__ buf, const SharedStage& st, int32_t MP, int32_t ns,
+                                             const uint4 (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (st.dst[i] < ns * 32 * MP) buf[st.dst[i]] = v[i];
 }
 
 // Lane (c, qq) of token group mg holds out[16 mg + c][16 * tile + 4qq + i].
@@ -399,21 +434,22 @@ __global__ __launch_bounds__(TPW * 64) void w4a16_shared_kernel(const uint16_t* 
                                                            const uint8_t* __restrict__ wt, int32_t N, int32_t K,
                                                            int32_t kc, const float* __restrict__ alpha_p,
                                                            uint16_t* __restrict__ out, int64_t ldo) {
-  extern __shared__ uint4 act[];  // two chunks of kc * 32 * M entries
+  const int32_t MP = MG == 1 ? M : 16 * MG;  // LDS token rows per (step, j, q): a constant above one group
+  extern __shared__ uint4 act[];  // two chunks of kc * 32 * MP entries
   const int lane = int(threadIdx.x & 63);
   const int wave = int(threadIdx.x >> 6);
   const int32_t tid = int32_t(threadIdx.x);
   const int32_t tiles = (N + 15) / 16;
   const int32_t steps = K / 256;
   const int32_t nch = (steps + kc - 1) / kc;
-  const int32_t chunk_entries = kc * 32 * M;
+  const int32_t chunk_entries = kc * 32 * MP;
   const int32_t tile = int32_t(blockIdx.x) * TPW + wave;
   const bool has_tile = tile < tiles;
   // token row 16 mg + (lane % 16) of k sub-block lane / 16 (rows past M repeat
   // row M - 1; their outputs are not stored)
   int lds_lane[MG];
 #pragma unroll
-  for (int mg = 0; mg < MG; ++mg) lds_lane[mg] = (lane >> 4) * M + min(16 * mg + (lane & 15), M - 1);
+  for (int mg = 0; mg < MG; ++mg) lds_lane[mg] = (lane >> 4) * MP + min(16 * mg + (lane & 15), M - 1);
   const uint8_t* wtile = wt + int64_t(has_tile ? tile : 0) * steps * kUnitBytes;
 
   // The weight units of the next kSharedDepth steps are in flight while a
@@ -424,15 +460,14 @@ __global__ __launch_bounds__(TPW * 64) void w4a16_shared_kernel(const uint16_t* 
   // outstanding (that would wait for it, and for everything older).
   auto unit_at = [&](int32_t st) { return load_unit(wtile + int64_t(min(st, steps - 1)) * kUnitBytes, lane); };
   uint4 v[4];
-  int32_t dst[4];
+  const SharedStage st = shared_stage(M, MP, kc, tid, TPW * 64);
   float alpha = *alpha_p;
-  stage_load(a, lda, M, 0, min(kc, steps), tid, TPW * 64, v, dst);
+  int32_t staged_ns = min(kc, steps);  // steps of the chunk in v
+  shared_load(a, lda, st, MP, 0, staged_ns, v);
   Unit w0 = unit_at(0), w1 = unit_at(1), w2 = unit_at(2), w3 = unit_at(3);
   __builtin_amdgcn_sched_barrier(0);
   settle(alpha);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (dst[i] >= 0) act[dst[i]] = v[i];
+  shared_store(act, st, MP, staged_ns, v);
   __syncthreads();
 
   f32x4_t acc[MG];
@@ -445,20 +480,20 @@ __global__ __launch_bounds__(TPW * 64) void w4a16_shared_kernel(const uint16_t* 
   auto step = [&](int32_t gs, const Unit& cur) {
     const int32_t ch = gs / kc, s = gs - ch * kc;
     if (s == 0 && ch > 0) {
-      uint4* nbuf = act + (ch & 1) * chunk_entries;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (dst[i] >= 0) nbuf[dst[i]] = v[i];
+      shared_store(act + (ch & 1) * chunk_entries, st, MP, staged_ns, v);
       __syncthreads();
     }
-    if (s == 0 && ch + 1 < nch) stage_load(a, lda, M, gs + kc, min(kc, steps - gs - kc), tid, TPW * 64, v, dst);
-    const uint4* lds_step = act + (ch & 1) * chunk_entries + s * 32 * M;
+    if (s == 0 && ch + 1 < nch) {
+      staged_ns = min(kc, steps - gs - kc);
+      shared_load(a, lda, st, MP, gs + kc, staged_ns, v);
+    }
+    const uint4* lds_step = act + (ch & 1) * chunk_entries + s * 32 * MP;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       if (MG == 1) {
         uint4 bb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bb[i] = lds_step[(4 * half + i) * 4 * M + lds_lane[0]];
+        for (int i = 0; i < 4; ++i) bb[i] = lds_step[(4 * half + i) * 4 * MP + lds_lane[0]];
         mma_half(half == 0 ? cur.c0 : cur.c1, cur.sc, half, bb, acc[0]);
       } else {
         const uint4 codes = half == 0 ? cur.c0 : cur.c1;
@@ -472,7 +507,7 @@ __global__ __launch_bounds__(TPW * 64) void w4a16_shared_kernel(const uint16_t* 
           const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
 #pragma unroll
           for (int mg = 0; mg < MG; ++mg) {
-            const bf16x8_t B = __builtin_bit_cast(bf16x8_t, lds_step[(4 * half + i) * 4 * M + lds_lane[mg]]);
+            const bf16x8_t B = __builtin_bit_cast(bf16x8_t, lds_step[(4 * half + i) * 4 * MP + lds_lane[mg]]);
             acc[mg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[mg], 0, 0, 0);
           }
         }
@@ -1023,6 +1058,10 @@ namespace {
 struct SplitShape {
   int64_t per, waves;
 };
+// LDS token rows of the shared schedule: M for one token group, else M
+// padded to its 16-row token groups.
+int64_t shared_rows(int64_t M) { return M <= 16 ? std::max<int64_t>(1, M) : 16 * ((M + 15) / 16); }
+
 SplitShape split_shape(int64_t ksplit, int64_t steps) {
   const int64_t ks = std::min<int64_t>(ksplit, steps);
   const int64_t per = (steps + ks - 1) / ks;
@@ -1042,7 +1081,7 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
     // more than one token group: only the shared schedule (16 M-row MFMA
     // columns per group, the weight dequantized once for all groups)
     c.schedule = 2;
-    c.chunk_steps = int(std::max<int64_t>(1, std::min<int64_t>(steps, 64 / M)));
+    c.chunk_steps = int(std::max<int64_t>(1, std::min<int64_t>(steps, 64 / shared_rows(M))));
     return c;
   }
   if (M <= 2 || (M == 3 && tiles * steps >= 20 * cus && tiles < int64_t(kSharedTiles) * cus * 3 / 2)) {
@@ -1066,7 +1105,7 @@ W4A16Config w4a16_default_config(int64_t M, int64_t N, int64_t K) {
   if (tiles >= int64_t(kSharedTiles) * cus * 3 / 2) {
     // shared: the largest chunk whose double buffer fits in 64 KiB of LDS
     c.schedule = 2;
-    c.chunk_steps = int(std::max<int64_t>(1, std::min<int64_t>(steps, 64 / std::max<int64_t>(1, M))));
+    c.chunk_steps = int(std::max<int64_t>(1, std::min<int64_t>(steps, 64 / shared_rows(M))));
     // up to 8 tokens: two tiles per workgroup on 4 waves instead (measured
     // cold at N = 62080, K = 5120: M = 4 37.1 -> 34.8 us, M = 8 37.3 -> 37.0)
     W4A16Config two = c;
@@ -1133,8 +1172,8 @@ bool w4a16_config_valid(const W4A16Config& c, int64_t M, int64_t K) {
   if (c.schedule == 2) {
     if (c.chunk_steps < 1) return false;
     const int64_t kc = std::min<int64_t>(c.chunk_steps, K / 256);
-    const int64_t per_chunk = std::max<int64_t>(1, M) * kc * 32;  // 16-byte entries
-    return 2 * per_chunk * 16 <= 64 * 1024 && per_chunk <= 4 * kSharedTiles * 64;  // LDS, staging registers
+    // 16-byte entries: LDS (rows padded to the token groups), staging registers (real rows)
+    return 2 * shared_rows(M) * kc * 32 * 16 <= 64 * 1024 && std::max<int64_t>(1, M) * kc * 32 <= 4 * kSharedTiles * 64;
   }
   return false;
 }
@@ -1149,7 +1188,7 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
   auto* O = static_cast<uint16_t*>(out);
   if (cfg.schedule == 2) {
     const int64_t kc = std::min<int64_t>(cfg.chunk_steps, steps);
-    const size_t lds = 2 * size_t(M) * size_t(kc) * 32 * 16;
+    const size_t lds = 2 * size_t(shared_rows(M)) * size_t(kc) * 32 * 16;
     // 16 tiles per workgroup on weights of at least 1.5 x 8 tiles per CU
     // (measured cold at N = 62080, K = 5120: M = 16/32/64 46.2/64.6/100.1 ->
     // 41.9/57.1/80.7 us against 8 tiles); 8 below, where 16 would leave CUs idle

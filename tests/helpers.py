@@ -81,8 +81,9 @@ SCHEDULES = ([(1, ks, 0) for ks in (1, 2, 3, 7, 16)] + [(2, 0, kc) for kc in (1,
 
 def _schedule_valid(sch, M, K):
     steps = K // 256
-    if sch[0] == 2:
-        return M * min(sch[2], steps) <= 64
+    if sch[0] == 2:  # LDS rows: M for one token group, else M padded to 16-row groups
+        rows = M if M <= 16 else 16 * -(-M // 16)
+        return rows * min(sch[2], steps) <= 64
     if sch[0] == 3:  # chunk_steps 2: two tiles per workgroup, at most 8 waves; 3: 2-3 tiles, 3-8 waves
         ks = min(sch[1], steps)
         per = -(-steps // ks)
