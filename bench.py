@@ -292,6 +292,19 @@ def bench_w4a4(ops, torch, reps=20):
     tq, tg = per_call_us(torch, [quant, gemm], reps)
     gemm_st, quant_st = stats_us(tg), stats_us(tq)
     gemm_us, quant_us = gemm_st["median"], quant_st["median"]
+    # the quantizer on cold inputs: the pairs above re-read one input, which
+    # the GEMM between two calls leaves in the 256 MB last-level cache; here
+    # each call takes the next of 6 copies (504 MB), so it reads from HBM
+    cold = [ad.clone() for _ in range(6)]
+    turn = [0]
+
+    def quant_cold():
+        ops.quantize_act(cold[turn[0] % len(cold)], ga, ac, as_)
+        turn[0] += 1
+
+    warm_gpu(torch, quant_cold, ms=30.0)
+    quant_cold_st = stats_us(per_call_us(torch, [quant_cold], 3 * reps)[0])
+    del cold
     # the smaller prefill batches of the same workload (prefixes of a)
     sweep = []
     for Ms in synth.W4A4_PREFILL["M"]:
@@ -327,8 +340,10 @@ def bench_w4a4(ops, torch, reps=20):
     flops = 2.0 * M * N * K
     qbytes = M * K * (2 + 0.5 + 1 / 16)
     log(f"[w4a4] M={M} N={N} K={K}: gemm {gemm_us:.1f} us = {flops / gemm_us / 1e6:.1f} TFLOP/s; "
-        f"quantize {quant_us:.1f} us = {qbytes / quant_us / 1e3:.1f} GB/s; prepare {prepare_us:.1f} us")
+        f"quantize {quant_us:.1f} us = {qbytes / quant_us / 1e3:.1f} GB/s (cold input {quant_cold_st['median']:.1f} us = "
+        f"{qbytes / quant_cold_st['median'] / 1e3:.1f} GB/s); prepare {prepare_us:.1f} us")
     return dict(M=M, N=N, K=K, gemm_us=gemm_us, quant_us=quant_us, tflops=flops / gemm_us / 1e6,
+                quant_cold_us=quant_cold_st["median"], quant_cold_gbs=qbytes / quant_cold_st["median"] / 1e3,
                 linear_tflops=flops / (gemm_us + quant_us) / 1e6, quant_gbs=qbytes / quant_us / 1e3,
                 prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16, m_sweep=sweep,
                 gemm_stats_us=gemm_st, quant_stats_us=quant_st,
@@ -941,6 +956,9 @@ def main():
             "gemm_us_p10_p90": [r4["gemm_stats_us"]["p10"], r4["gemm_stats_us"]["p90"]],
             "timing": "HIP events around each call of 20 quantize -> GEMM pairs after a 200 ms warm-up; medians",
             "quantize_us": round(r4["quant_us"], 2), "quantize_gb_s": round(r4["quant_gbs"], 1),
+            "quantize_cold_us": round(r4["quant_cold_us"], 2), "quantize_cold_gb_s": round(r4["quant_cold_gbs"], 1),
+            "quantize_timing": "quantize_us: the pairs above (its input re-read from the last-level cache); "
+                               "quantize_cold_us: each call on the next of 6 input copies (504 MB), read from HBM",
             "m_sweep": r4["m_sweep"],
             "gated_mlp": dict(r4["gated_mlp"], workload="nvfp4_gated_mlp_w4a4 on the same weight as gate_up [2I=8704, "
                               "K=5120], M=8192: GEMM + SiLU gate + NVFP4 quantization of h [M, 4352]"),

@@ -24,8 +24,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// 16-byte loads.  The nontemporal form streams data that is read once (weights,
-// activations being quantized) without keeping it in the caches.
+// 16-byte loads.  The nontemporal form streams data that is read once (the
+// weights of the decode linears) without keeping it in the caches.
 __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
