@@ -349,6 +349,11 @@ __device__ __forceinline__ void down_tile(_Float16* __restrict__ lds, const MoeT
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
   const int32_t wtile0 = tile.expert * (K / 16) + nblk * 16;
+  // the tile row's pair index, loaded before the main loop so that only the
+  // routing weight's load is left for the epilogue (two dependent loads there
+  // cost about 5 us per layer at T = 8192)
+  int32_t pr = 0;
+  if (threadIdx.x < BMT) pr = sorted[tile.slot0 + min(int(threadIdx.x), tile.rows - 1)];
   gemm::AccT<BMT> acc;
   gemm::mainloop<true, BMT>(
       acc, lds, hc, hs, [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); }, wt,
@@ -356,10 +361,7 @@ __device__ __forceinline__ void down_tile(_Float16* __restrict__ lds, const MoeT
 
   // the tile's routing-weight scales, through LDS (free after the main loop)
   float* s_scale = reinterpret_cast<float*>(lds);
-  if (threadIdx.x < BMT) {
-    const int m = int(threadIdx.x);
-    s_scale[m] = alpha * topk_w[sorted[tile.slot0 + min(m, tile.rows - 1)]];
-  }
+  if (threadIdx.x < BMT) s_scale[threadIdx.x] = alpha * topk_w[pr];
   __syncthreads();
   const int32_t n = nblk * 256 + 128 * wn + (lane & 31);
 #pragma unroll
