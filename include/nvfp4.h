@@ -262,9 +262,33 @@ nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const 
  *   w                  prepared weight descriptor
  *   alpha              device fp32[1]
  *   out                bf16 [M, N], ldo >= N
+ * One launch over all of K, no workspace.
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
                                const float* alpha, void* out, int64_t ldo, hipStream_t stream);
+
+/* nvfp4_linear_w4a4 with a workspace for a split of K across workgroups
+ * (split-K).  A small batch on a weight of a few thousand rows has few
+ * 256 x 256 output tiles (N = 8704 has 34 column tiles), and one workgroup per
+ * tile leaves most CUs idle while each works through all of K.  When the
+ * tiles fill at most half the CUs, K is split into S ranges of whole 256-k
+ * units (S <= 16, at least two units each); tile x range workgroups store
+ * fp32 partial tiles in ws, and a second launch adds the ranges' partials in
+ * range order (fixed fp32 order: deterministic), scales by alpha and rounds
+ * once to bf16.  The sum order differs from the one-launch call's, so the
+ * bits can differ from nvfp4_linear_w4a4's (both meet the same bar).
+ *   nvfp4_linear_w4a4_workspace_bytes: S * M * N * 4 bytes (256-byte
+ *   aligned) when the shape splits on the current device, else 0 (then ws
+ *   may be NULL and the call is nvfp4_linear_w4a4's one launch).  S keeps the
+ *   partials within 48 MiB and, with nvfp4_linear's quantized activations,
+ *   within NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES.
+ *   ws, ws_bytes  device workspace, 16-byte aligned, >= the bytes above
+ * Errors: as nvfp4_linear_w4a4, plus WORKSPACE (ws missing or too small) and
+ * ALIGNMENT (ws). */
+size_t nvfp4_linear_w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+nvfp4_status nvfp4_linear_w4a4_ws(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
+                                  const float* alpha, void* out, int64_t ldo, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * M-threshold dispatch (FreeToken PR #737, Changes: W4A4 for prefill on
@@ -280,8 +304,10 @@ int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global);
 void nvfp4_set_route_m_max(int64_t m_max);
 int64_t nvfp4_get_route_m_max(void);
 
-/* Workspace nvfp4_linear needs: M*K/2 + M*K/16 bytes (256-byte aligned parts)
- * for the quantized activations of the W4A4 route; the W4A16 route uses none. */
+/* Workspace nvfp4_linear needs on the W4A4 route: M*K/2 + M*K/16 bytes
+ * (256-byte aligned parts) for the quantized activations, then
+ * nvfp4_linear_w4a4_workspace_bytes(M, N, K) for the split-K partials (the
+ * W4A4 route runs nvfp4_linear_w4a4_ws's kernels); the W4A16 route uses none. */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------------
@@ -300,15 +326,17 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
                           size_t ws_bytes, int* route_taken, hipStream_t stream);
 
 /* Size of the library's own scratch on each GPU, used by nvfp4_linear_noalloc
- * for the W4A4 route's quantized activations: nvfp4_linear_workspace_bytes
- * (M, N, K) must not exceed it (M = 8192 at K = 5120 needs 23.6 MB). */
-#define NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)32 << 20)
+ * for the W4A4 route's quantized activations and split-K partials:
+ * nvfp4_linear_workspace_bytes(M, N, K) must not exceed it (M = 8192 at
+ * K = 5120 needs 23.6 MB; the split-K partials are sized to fit beside the
+ * activations). */
+#define NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)64 << 20)
 
 /* nvfp4_linear without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  The call allocates nothing and frees
- * nothing.  On the W4A4 route the quantized activations go to a scratch
- * array the library holds on each GPU (a device global of
+ * nothing.  On the W4A4 route the quantized activations (and the split-K
+ * partials) go to a scratch array the library holds on each GPU (a device global of
  * NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES, kept until the process ends);
  * the W4A16 route needs none.  The caller still passes inputs and outputs.
  *   Arguments, routes, numerics and errors as nvfp4_linear (the same kernels,

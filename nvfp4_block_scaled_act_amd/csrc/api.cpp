@@ -9,6 +9,7 @@
 #include "kernels.hpp"
 
 static_assert(nvfp4::kMoeDirectPairs == NVFP4_MOE_W4A16_DIRECT_PAIRS, "direct-path threshold out of sync");
+static_assert(nvfp4::kLinearScratchBytes == NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES, "scratch size out of sync");
 
 namespace {
 
@@ -239,8 +240,10 @@ nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const 
 
 namespace {
 
+// partials: fp32 room for the split-K ranges (nvfp4::w4a4_partials_bytes), or
+// null for one launch over all of K.
 nvfp4_status w4a4_checked(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
-                          const float* alpha, void* out, int64_t ldo, hipStream_t stream) {
+                          const float* alpha, void* out, int64_t ldo, float* partials, hipStream_t stream) {
   if (M < 0 || !alpha) return NVFP4_ERR_INVALID_ARGUMENT;
   nvfp4_status st = check_weight(w);
   if (st != NVFP4_OK) return st;
@@ -252,14 +255,34 @@ nvfp4_status w4a4_checked(const void* a_codes, const void* a_scales, int64_t M, 
   // grid rows of 256 activation rows; 32-bit byte offsets into the codes
   if ((M + 255) / 256 > 65535 || M * (w->K / 2) >= (int64_t(1) << 32)) return NVFP4_ERR_UNSUPPORTED;
   if (w->N == 0) return NVFP4_OK;
-  return hip_status(nvfp4::launch_w4a4(a_codes, a_scales, M, w->data, w->N, w->K, alpha, out, ldo, stream));
+  return hip_status(
+      nvfp4::launch_w4a4(a_codes, a_scales, M, w->data, w->N, w->K, alpha, out, ldo, partials, stream));
 }
 
 }  // namespace
 
 nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
                                const float* alpha, void* out, int64_t ldo, hipStream_t stream) {
-  return w4a4_checked(a_codes, a_scales, M, w, alpha, out, ldo, stream);
+  return w4a4_checked(a_codes, a_scales, M, w, alpha, out, ldo, nullptr, stream);
+}
+
+size_t nvfp4_linear_w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return nvfp4::w4a4_partials_bytes(M, N, K);
+}
+
+nvfp4_status nvfp4_linear_w4a4_ws(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
+                                  const float* alpha, void* out, int64_t ldo, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  nvfp4_status st = check_weight(w);
+  if (st != NVFP4_OK) return st;
+  const size_t need = M > 0 ? nvfp4_linear_w4a4_workspace_bytes(M, w->N, w->K) : 0;
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(ws)) return NVFP4_ERR_ALIGNMENT;
+  }
+  return w4a4_checked(a_codes, a_scales, M, w, alpha, out, ldo, need > 0 ? static_cast<float*>(ws) : nullptr,
+                      stream);
 }
 
 int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global) {
@@ -277,9 +300,8 @@ void nvfp4_set_route_m_max(int64_t m_max) {
 int64_t nvfp4_get_route_m_max(void) { return g_route_m_max.load(); }
 
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)N;
   if (M <= 0 || K <= 0) return 0;
-  return align_up(size_t(M) * size_t(K / 2), 256) + align_up(size_t(M) * size_t(K / 16), 256);
+  return nvfp4::linear_act_bytes(M, K) + (N > 0 ? nvfp4::w4a4_partials_bytes(M, N, K) : 0);
 }
 
 namespace {
@@ -317,9 +339,14 @@ nvfp4_status linear_impl(const void* a, int64_t M, int64_t lda, const nvfp4_weig
     if (!aligned16(ws)) return NVFP4_ERR_ALIGNMENT;
     uint8_t* codes = static_cast<uint8_t*>(ws);
     uint8_t* scales = codes + align_up(size_t(M) * size_t(w->K / 2), 256);
+    // split-K partials after the activations, when the shape takes them
+    float* partials = nvfp4::w4a4_partials_bytes(M, w->N, w->K) > 0
+                          ? reinterpret_cast<float*>(codes + nvfp4::linear_act_bytes(M, w->K))
+                          : nullptr;
     st = hip_status(nvfp4::launch_quantize(a, M, w->K, lda, g_act, codes, scales, stream));
     if (st == NVFP4_OK)
-      st = hip_status(nvfp4::launch_w4a4(codes, scales, M, w->data, w->N, w->K, alpha_w4a4, out, ldo, stream));
+      st = hip_status(
+          nvfp4::launch_w4a4(codes, scales, M, w->data, w->N, w->K, alpha_w4a4, out, ldo, partials, stream));
   }
   if (st == NVFP4_OK && route_taken) *route_taken = route;
   return st;

@@ -312,8 +312,9 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, HeldT<BMT>& held, const
   for (int u = 0; u < U; ++u) held.b[u] = B[1][u];
 }
 
-// The K loop of one workgroup tile over all of K (K % 256 == 0, so the number
-// of 64-k steps is a multiple of 4 and the number of pairs is even).
+// The K loop of one workgroup tile over the 128-k pairs [p_begin, p_begin +
+// p_count) of K (K % 256 == 0; p_begin and p_count even, so the range is
+// whole 256-k units; by default all of K).
 //   a_row(i)    global activation row of tile row i (0..255): always a valid row
 //               (rows BMT..255 are loaded but not used by a narrow tile)
 //   wtile(lt)   tile index in the tiled weight of LDS weight tile lt (0..15): always valid
@@ -321,10 +322,11 @@ __device__ __forceinline__ void mma_step(AccT<BMT>& acc, HeldT<BMT>& held, const
 template <bool kSwap = false, int BMT = BM, typename ARow, typename WTile, typename WaveRow0>
 __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ lds, const uint8_t* __restrict__ a_codes,
                                          const uint8_t* __restrict__ a_scales, ARow a_row,
-                                         const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K) {
+                                         const uint8_t* __restrict__ wt, WTile wtile, WaveRow0 wave_row0, int32_t K,
+                                         int32_t p_begin = 0, int32_t p_count = -1) {
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int wm = wave >> 1;
-  const int32_t pairs = K / (2 * BK), steps256 = K / 256;
+  const int32_t pairs = p_count < 0 ? K / (2 * BK) : p_count, steps256 = K / 256;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -358,8 +360,8 @@ __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ 
   // that dequantizes its first step, so its loads have two steps to land.
   // The loop has one exit, at its end (a mid-loop exit made the register
   // allocator move the accumulators through memory).
-  Stage X = load_pair(src, so, 0);
-  Stage Y = load_pair(src, so, min(1, pairs - 1));
+  Stage X = load_pair(src, so, p_begin);
+  Stage Y = load_pair(src, so, p_begin + min(1, pairs - 1));
 #pragma unroll
   for (int part = 0; part < 4; ++part) store_part<BMT>(X, 0, 0, part, w0, a0);
   __syncthreads();
@@ -368,14 +370,14 @@ __device__ __forceinline__ void mainloop(AccT<BMT>& acc, _Float16* __restrict__ 
     mma_step<kSwap, BMT>(acc, held, w0, a0, wave_row0, wm, lane, X, p & 1, 1, w1, a1);
     __syncthreads();
     // step 2p+1 (buffer 1); step 2p+2, the first of Y, -> buffer 0; X <- pair p+2
-    X = load_pair(src, so, min(p + 2, pairs - 1));
+    X = load_pair(src, so, p_begin + min(p + 2, pairs - 1));
     mma_step<kSwap, BMT>(acc, held, w1, a1, wave_row0, wm, lane, Y, (p + 1) & 1, 0, w0, a0);
     __syncthreads();
     // step 2p+2 (buffer 0); step 2p+3, the second of Y, -> buffer 1
     mma_step<kSwap, BMT>(acc, held, w0, a0, wave_row0, wm, lane, Y, (p + 1) & 1, 1, w1, a1);
     __syncthreads();
     // step 2p+3 (buffer 1); step 2p+4, the first of X, -> buffer 0; Y <- pair p+3
-    Y = load_pair(src, so, min(p + 3, pairs - 1));
+    Y = load_pair(src, so, p_begin + min(p + 3, pairs - 1));
     mma_step<kSwap, BMT>(acc, held, w1, a1, wave_row0, wm, lane, X, p & 1, 0, w0, a0);
     __syncthreads();
   }

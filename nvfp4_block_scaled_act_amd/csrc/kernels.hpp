@@ -48,8 +48,28 @@ hipError_t launch_w4a16(const void* a, int64_t M, int64_t lda, const void* w_til
                         const float* alpha, void* out, int64_t ldo, const W4A16Config& cfg, hipStream_t stream);
 
 // W4A4 tiled GEMM: out[M, N] = bf16(alpha * dequant(A)[M, K] @ dequant(W)^T).
+// With partials (fp32, w4a4_partials_bytes(M, N, K) long) and
+// w4a4_splits(M, N, K) > 1, K is split across workgroups into that many
+// ranges of whole 256-k units whose fp32 partial tiles a second launch adds
+// in range order; without, one launch over all of K.
 hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
-                       int64_t K, const float* alpha, void* out, int64_t ldo, hipStream_t stream);
+                       int64_t K, const float* alpha, void* out, int64_t ldo, float* partials, hipStream_t stream);
+int w4a4_splits(int64_t M, int64_t N, int64_t K);
+size_t w4a4_partials_bytes(int64_t M, int64_t N, int64_t K);
+
+// Bytes of the dispatched linear's quantized activations (codes, then scales,
+// each part 256-byte aligned); its split-K partials follow them.
+inline size_t linear_act_bytes(int64_t M, int64_t K) {
+  const size_t codes = (size_t(M) * size_t(K / 2) + 255) / 256 * 256;
+  const size_t scales = (size_t(M) * size_t(K / 16) + 255) / 256 * 256;
+  return codes + scales;
+}
+
+// The allocation-free linear's scratch size (NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES,
+// checked in api.cpp): the split decision keeps activations + partials within it,
+// so that every entry point takes the same decision for a shape.
+constexpr size_t kLinearScratchBytes = size_t(64) << 20;
+constexpr size_t kSplitKMaxBytes = size_t(48) << 20;  // fp32 partials of one split-K call, at most
 
 // Library-owned scratch of the allocation-free dispatched linear: its size,
 // and the device address of the current device's copy (looked up once per

@@ -9,7 +9,16 @@
 //
 // One workgroup fills a CU (LDS), so the tiles run in rounds of one per CU.
 // When the last round would be at most half full, its tiles are split into
-// two 128-row halves each, which take about half as long.
+// two 128-row halves each, which take about half as long; a batch of at most
+// 128 rows runs on 128-row tiles throughout.
+//
+// Few tiles (a small batch on a weight of a few thousand rows: N = 8704 has
+// 34 column tiles, so 34 of 256 CUs would work through all of K) split K
+// across workgroups when the caller provides room for fp32 partials: tile x
+// range workgroups each run the main loop over their range of whole 256-k
+// units and store an fp32 partial tile; a second launch adds the ranges'
+// partials in range order (a fixed fp32 sum order), scales by alpha and
+// rounds once to bf16.
 #include "gemm_w4a4.hpp"
 #include "kernels.hpp"
 
@@ -81,13 +90,14 @@ __device__ __forceinline__ void w4a4_tile(_Float16* __restrict__ lds, const uint
 }
 
 // Workgroups [0, grid_big) run the first n_big tiles of the grouped order as
-// 256-row tiles (XCD-aware); the rest run the remaining tiles as 128-row halves.
+// 256-row tiles (XCD-aware); the rest run the remaining tiles as 128-row
+// halves, `halves` workgroups per tile (2, or 1 when M <= 128).
 __global__ __launch_bounds__(gemm::kThreads) void w4a4_kernel(const uint8_t* __restrict__ ac,
                                                               const uint8_t* __restrict__ as, int32_t M,
                                                               const uint8_t* __restrict__ wt, int32_t N, int32_t K,
                                                               const float* __restrict__ alpha_p,
                                                               uint16_t* __restrict__ out, int64_t ldo, int vec_store,
-                                                              int32_t n_big, int32_t grid_big) {
+                                                              int32_t n_big, int32_t grid_big, int32_t halves) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
   const int32_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
   const float alpha = *alpha_p;
@@ -98,31 +108,177 @@ __global__ __launch_bounds__(gemm::kThreads) void w4a4_kernel(const uint8_t* __r
     w4a4_tile<gemm::BM>(lds, ac, as, M, wt, N, K, alpha, out, ldo, vec_store, nblk, mblk * gemm::BM);
   } else {
     const int32_t j = id - grid_big;
-    gemm::grouped_tile(n_big + j / 2, nt, mt, nblk, mblk);
-    const int32_t m0 = mblk * gemm::BM + (gemm::BM / 2) * (j & 1);
+    gemm::grouped_tile(n_big + j / halves, nt, mt, nblk, mblk);
+    const int32_t m0 = mblk * gemm::BM + (gemm::BM / 2) * (j % halves);
     if (m0 >= M) return;
     w4a4_tile<gemm::BM / 2>(lds, ac, as, M, wt, N, K, alpha, out, ldo, vec_store, nblk, m0);
   }
 }
 
+// ---------------------------------------------------------------- split K
+// fp32 partial of tile (nblk, m0) over the 256-k units [u0, u1): stored
+// unscaled at part[m][n] (row-major [M, N]).  The operands run swapped in the
+// MFMA, so register i of lane l in wave tile (t, u) holds weight row 16 tb +
+// 128 wn + 32 t + l % 32 for activation row m0 + (BMT/4) wm + 32 u + 8 (i/4)
+// + 4 (l/32) + i % 4, and each store instruction writes whole 128-byte rows
+// pieces.
+template <int BMT>
+__device__ __forceinline__ void w4a4_partial_tile(_Float16* __restrict__ lds, const uint8_t* __restrict__ ac,
+                                                  const uint8_t* __restrict__ as, int32_t M,
+                                                  const uint8_t* __restrict__ wt, int32_t N, int32_t K,
+                                                  float* __restrict__ part, int32_t nblk, int32_t m0, int32_t u0,
+                                                  int32_t u1) {
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1, h = lane >> 5;
+  const int32_t tb = nblk * (gemm::BN / 16);
+  const int32_t tiles = (N + 15) / 16;
+  gemm::AccT<BMT> acc;
+  gemm::mainloop<true, BMT>(
+      acc, lds, ac, as, [&](int i) { return int64_t(min(m0 + i, M - 1)); }, wt,
+      [&](int lt) { return int64_t(min(tb + lt, tiles - 1)); }, [&](int t) { return 128 * wn + 32 * t; }, K,
+      2 * u0, 2 * (u1 - u0));
+  const int32_t n = 16 * tb + 128 * wn + (lane & 31);
+#pragma unroll
+  for (int u = 0; u < BMT / 128; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int32_t m = m0 + wm * (BMT / 4) + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (m >= M) continue;
+      float* row = part + int64_t(m) * N;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (n + 32 * t < N) row[n + 32 * t] = acc.v[t][u][i];
+    }
+}
+
+// Workgroup id -> (tile L = id % tiles, range s = id / tiles); tiles of 128
+// rows when M <= 128 (narrow), else the 256-row tiles of the grouped order.
+__global__ __launch_bounds__(gemm::kThreads) void w4a4_splitk_kernel(const uint8_t* __restrict__ ac,
+                                                                     const uint8_t* __restrict__ as, int32_t M,
+                                                                     const uint8_t* __restrict__ wt, int32_t N,
+                                                                     int32_t K, float* __restrict__ partials,
+                                                                     int32_t splits, int32_t tiles, int narrow) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
+  const int32_t id = int32_t(blockIdx.x);
+  const int32_t L = id % tiles, s = id / tiles;
+  const int32_t units = K / 256;
+  const int32_t u0 = int32_t(int64_t(s) * units / splits), u1 = int32_t(int64_t(s + 1) * units / splits);
+  float* part = partials + int64_t(s) * M * N;
+  if (narrow) {
+    w4a4_partial_tile<gemm::BM / 2>(lds, ac, as, M, wt, N, K, part, L, 0, u0, u1);
+  } else {
+    const int32_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
+    int32_t nblk, mblk;
+    gemm::grouped_tile(L, nt, mt, nblk, mblk);
+    w4a4_partial_tile<gemm::BM>(lds, ac, as, M, wt, N, K, part, nblk, mblk * gemm::BM, u0, u1);
+  }
+}
+
+// out[m][n] = bf16(alpha * (part_0 + part_1 + ... + part_{splits-1})[m][n]),
+// added in range order in fp32; four outputs of one row per thread.
+__global__ __launch_bounds__(256) void w4a4_splitk_reduce_kernel(const float* __restrict__ partials, int32_t splits,
+                                                                 int32_t M, int32_t N,
+                                                                 const float* __restrict__ alpha_p,
+                                                                 uint16_t* __restrict__ out, int64_t ldo) {
+  const int32_t nq = (N + 3) / 4;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(M) * nq) return;
+  const int32_t m = int32_t(i / nq), n = int32_t(i - int64_t(m) * nq) * 4;
+  const float alpha = *alpha_p;
+  const int64_t plane = int64_t(M) * N;
+  const float* p = partials + int64_t(m) * N + n;
+  uint16_t* o = out + int64_t(m) * ldo + n;
+  if (N % 4 == 0) {  // whole 16-byte pieces (each row starts 16-byte aligned)
+    float4 a = *reinterpret_cast<const float4*>(p);
+    for (int32_t s = 1; s < splits; ++s) {
+      const float4 b = *reinterpret_cast<const float4*>(p + s * plane);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    const uint2 v = make_uint2(pack_bf16x2(a.x * alpha, a.y * alpha), pack_bf16x2(a.z * alpha, a.w * alpha));
+    if ((reinterpret_cast<uintptr_t>(o) & 7) == 0) {
+      *reinterpret_cast<uint2*>(o) = v;
+    } else {
+      o[0] = uint16_t(v.x);
+      o[1] = uint16_t(v.x >> 16);
+      o[2] = uint16_t(v.y);
+      o[3] = uint16_t(v.y >> 16);
+    }
+    return;
+  }
+  for (int e = 0; e < 4 && n + e < N; ++e) {
+    float a = p[e];
+    for (int32_t s = 1; s < splits; ++s) a += p[s * plane + e];
+    o[e] = __builtin_bit_cast(uint16_t, (__bf16)(a * alpha));
+  }
+}
+
 }  // namespace
 
+int w4a4_splits(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K < 256) return 1;
+  const int64_t units = K / 256;
+  const int64_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
+  const int64_t tiles = M <= gemm::BM / 2 ? nt : nt * mt;
+  const int64_t cus = device_cu_count();
+  // only when the tiles fill at most half the CUs; at least two units per range
+  if (units < 4 || 2 * tiles > cus) return 1;
+  int64_t s = std::min<int64_t>({cus / tiles, units / 2, 16});
+  // the partials stay within kSplitKMaxBytes and, with the dispatched
+  // linear's quantized activations, within its allocation-free scratch
+  const int64_t act = int64_t(linear_act_bytes(M, K));
+  const int64_t budget = std::min<int64_t>(int64_t(kSplitKMaxBytes), int64_t(kLinearScratchBytes) - act - 256);
+  const int64_t plane = M * N * 4;
+  s = std::min<int64_t>(s, budget > 0 ? budget / plane : 0);
+  return s >= 2 ? int(s) : 1;
+}
+
+size_t w4a4_partials_bytes(int64_t M, int64_t N, int64_t K) {
+  const int s = w4a4_splits(M, N, K);
+  return s > 1 ? (size_t(s) * size_t(M) * size_t(N) * 4 + 255) / 256 * 256 : 0;
+}
+
 hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, const void* w_tiled, int64_t N,
-                       int64_t K, const float* alpha, void* out, int64_t ldo, hipStream_t stream) {
+                       int64_t K, const float* alpha, void* out, int64_t ldo, float* partials, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int64_t total = ((N + gemm::BN - 1) / gemm::BN) * ((M + gemm::BM - 1) / gemm::BM);
+  const auto* AC = static_cast<const uint8_t*>(a_codes);
+  const auto* AS = static_cast<const uint8_t*>(a_scales);
+  const auto* WT = static_cast<const uint8_t*>(w_tiled);
+  auto* O = static_cast<uint16_t*>(out);
+  const int64_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
+  const int splits = partials ? w4a4_splits(M, N, K) : 1;
+  if (splits > 1) {
+    const bool narrow = M <= gemm::BM / 2;
+    const int64_t tiles = narrow ? nt : nt * mt;
+    hipLaunchKernelGGL(w4a4_splitk_kernel, dim3(uint32_t(tiles * splits)), dim3(gemm::kThreads), 0, stream, AC, AS,
+                       int32_t(M), WT, int32_t(N), int32_t(K), partials, splits, int32_t(tiles), narrow ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = M * ((N + 3) / 4);
+    hipLaunchKernelGGL(w4a4_splitk_reduce_kernel, dim3(uint32_t((threads + 255) / 256)), dim3(256), 0, stream,
+                       partials, splits, int32_t(M), int32_t(N), alpha, O, ldo);
+    return hipGetLastError();
+  }
+  const int64_t total = nt * mt;
   const int64_t cus = device_cu_count();
   const int64_t rest = total % cus;
-  // split the last round into halves when it is at most half full
-  const int64_t n_big = (total > cus && rest > 0 && 2 * rest <= cus) ? total - rest : total;
-  const int64_t grid_big = gemm::xcd_grid(int32_t(n_big));
-  const int64_t grid = grid_big + 2 * (total - n_big);
+  int64_t n_big, halves = 2;
+  if (M <= gemm::BM / 2) {
+    n_big = 0;  // one 128-row tile per column block
+    halves = 1;
+  } else {
+    // split the last round into halves when it is at most half full
+    n_big = (total > cus && rest > 0 && 2 * rest <= cus) ? total - rest : total;
+  }
+  const int64_t grid_big = n_big > 0 ? gemm::xcd_grid(int32_t(n_big)) : 0;
+  const int64_t grid = grid_big + halves * (total - n_big);
   // whole 16-byte output pieces when the rows are 16-byte aligned
   const int vec_store = (reinterpret_cast<uintptr_t>(out) % 16 == 0 && (ldo * 2) % 16 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(w4a4_kernel, dim3(uint32_t(grid)), dim3(gemm::kThreads), 0, stream,
-                     static_cast<const uint8_t*>(a_codes), static_cast<const uint8_t*>(a_scales), int32_t(M),
-                     static_cast<const uint8_t*>(w_tiled), int32_t(N), int32_t(K), alpha, static_cast<uint16_t*>(out),
-                     ldo, vec_store, int32_t(n_big), int32_t(grid_big));
+  hipLaunchKernelGGL(w4a4_kernel, dim3(uint32_t(grid)), dim3(gemm::kThreads), 0, stream, AC, AS, int32_t(M), WT,
+                     int32_t(N), int32_t(K), alpha, O, ldo, vec_store, int32_t(n_big), int32_t(grid_big),
+                     int32_t(halves));
   return hipGetLastError();
 }
 

@@ -62,6 +62,8 @@ _SIGS = {
     "nvfp4_linear_w4a16": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, P]),
     "nvfp4_linear_w4a16_ex": (I32, [P, I64, I64, C.POINTER(Weight), P, P, I64, I32, I32, I32, I32, P]),
     "nvfp4_linear_w4a4": (I32, [P, P, I64, C.POINTER(Weight), P, P, I64, P]),
+    "nvfp4_linear_w4a4_ws": (I32, [P, P, I64, C.POINTER(Weight), P, P, I64, P, SZ, P]),
+    "nvfp4_linear_w4a4_workspace_bytes": (SZ, [I64, I64, I64]),
     "nvfp4_route": (I32, [I64, I64, I64, I32]),
     "nvfp4_set_route_m_max": (None, [I64]),
     "nvfp4_get_route_m_max": (I64, []),

@@ -213,8 +213,17 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None
     _L.check("nvfp4_stream_read", _L.load().nvfp4_stream_read(_ptr(src), n, _ptr(sink), _stream()))
 
 
+def linear_w4a4_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Bytes of fp32 split-K partials linear_w4a4 takes with a workspace (0:
+    the shape runs one launch over all of K)."""
+    return int(_L.load().nvfp4_linear_w4a4_workspace_bytes(M, N, K))
+
+
 def linear_w4a4(a_codes: torch.Tensor, a_scales: torch.Tensor, w: Weight, alpha_: torch.Tensor,
-                out: torch.Tensor | None = None) -> torch.Tensor:
+                out: torch.Tensor | None = None, workspace: torch.Tensor | bool | None = None) -> torch.Tensor:
+    """W4A4 linear.  workspace: None -> one launch over K (nvfp4_linear_w4a4);
+    a uint8 device tensor, or True to allocate one -> nvfp4_linear_w4a4_ws
+    (split-K where the shape takes it)."""
     _need(a_codes, torch.uint8, "a_codes")
     _need(a_scales, torch.uint8, "a_scales")
     _scalar(alpha_, "alpha")
@@ -224,9 +233,18 @@ def linear_w4a4(a_codes: torch.Tensor, a_scales: torch.Tensor, w: Weight, alpha_
     if not a_codes.is_contiguous() or not a_scales.is_contiguous():
         raise ValueError("activation codes and scales must be contiguous")
     out, ldo = _out(out, M, w.N, a_codes.device)
-    _L.check("nvfp4_linear_w4a4",
-             _L.load().nvfp4_linear_w4a4(_ptr(a_codes), _ptr(a_scales), M, C.byref(w.desc), _ptr(alpha_),
-                                         _ptr(out), ldo, _stream()))
+    if workspace is None:
+        _L.check("nvfp4_linear_w4a4",
+                 _L.load().nvfp4_linear_w4a4(_ptr(a_codes), _ptr(a_scales), M, C.byref(w.desc), _ptr(alpha_),
+                                             _ptr(out), ldo, _stream()))
+        return out
+    if workspace is True:
+        need = linear_w4a4_workspace_bytes(M, w.N, w.K)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a_codes.device)
+    _need(workspace, torch.uint8, "workspace")
+    _L.check("nvfp4_linear_w4a4_ws",
+             _L.load().nvfp4_linear_w4a4_ws(_ptr(a_codes), _ptr(a_scales), M, C.byref(w.desc), _ptr(alpha_),
+                                            _ptr(out), ldo, _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 
@@ -267,7 +285,7 @@ def linear(a: torch.Tensor, w: Weight, g_act: torch.Tensor | None, alpha_w4a16: 
     return out, int(r.value)
 
 
-NOALLOC_MAX_WORKSPACE_BYTES = 32 << 20  # NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES
+NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20  # NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES
 MOE_W4A16_DIRECT_PAIRS = 64  # NVFP4_MOE_W4A16_DIRECT_PAIRS
 
 

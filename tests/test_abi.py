@@ -198,13 +198,13 @@ def test_linear_dispatch_validation(nv):
 def test_linear_noalloc_validation(nv):
     # the allocation-free dispatch validates as nvfp4_linear and rejects, before
     # touching the device, a W4A4 call whose quantized activations would not
-    # fit its fixed scratch (32 MiB)
+    # fit its fixed scratch (64 MiB)
     f = nv.nvfp4_linear_noalloc
     w = _w(N=64, K=2048)
     r = C.c_int(-1)
     nv.nvfp4_set_route_m_max(16)
-    assert nv.nvfp4_linear_workspace_bytes(30000, 64, 2048) > (32 << 20)
-    assert f(A16, 30000, 2048, C.byref(w), A16, A16, A16, A16, 64, C.byref(r), None) == WS
+    assert nv.nvfp4_linear_workspace_bytes(60000, 64, 2048) > (64 << 20)
+    assert f(A16, 60000, 2048, C.byref(w), A16, A16, A16, A16, 64, C.byref(r), None) == WS
     assert f(A16, 32, 2048, C.byref(w), A16, A16, None, A16, 64, C.byref(r), None) == ARG    # no alpha_w4a4
     assert f(A16, 65, 2048, C.byref(w), None, A16, None, A16, 64, C.byref(r), None) == UNSUP  # W4A16 beyond 64
     assert f(A16 + 2, 32, 2048, C.byref(w), A16, A16, A16, A16, 64, C.byref(r), None) == ALIGN

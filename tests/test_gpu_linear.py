@@ -375,6 +375,83 @@ def test_w4a4_deterministic(ops, orc):
         assert (bf16_host(ops.linear_w4a4(ac, as_, q.w, al)) == o1).all()
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 512, 2048), (17, 1002, 4352), (128, 3000, 2048), (200, 1000, 1024),
+                                   (300, 520, 5120)])
+def test_w4a4_split_k(ops, orc, M, N, K):
+    # few output tiles (on a 256-CU device): K split across workgroups, fp32
+    # partials added in range order by a second launch.  Checked in full
+    # against the oracle; the workspace is poisoned with NaN bytes, so an
+    # element a partial tile does not write shows up; repeated calls give the
+    # same bits
+    import torch
+
+    need = ops.linear_w4a4_workspace_bytes(M, N, K)
+    assert need > 0, "the shape should split K"
+    W = synth.normal_bf16(120 + N, N, K)
+    a = synth.normal_bf16(130 + M, M, K)
+    cal = synth.normal_bf16(140 + M, 64, K)
+    q = Quantized(ops, orc, W)
+    ga = orc.global_scale(cal)
+    gad = ops.global_scale(bf16_dev(cal))
+    ac, as_ = ops.quantize_act(bf16_dev(a), gad)
+    al = ops.alpha(q.g_dev, gad)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=ws))
+    oac, oas = orc.quantize(a, ga)
+    ref, _, sabs = orc.linear_w4a4(oac, oas, q.codes, q.scales, orc.alpha(q.g, ga))
+    print(gemm_check(out, ref, sabs))
+    for _ in range(2):
+        ws.fill_(0xFF)
+        assert (bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=ws)) == out).all()
+    # one launch over all of K (no workspace) meets the same bar
+    gemm_check(bf16_host(ops.linear_w4a4(ac, as_, q.w, al)), ref, sabs)
+
+
+def test_w4a4_split_k_not_taken(ops, orc):
+    # fewer than four 256-k units, or tiles for more than half the CUs: one
+    # launch, and the workspace call needs no workspace
+    assert ops.linear_w4a4_workspace_bytes(16, 1000, 768) == 0
+    assert ops.linear_w4a4_workspace_bytes(1024, 8704, 5120) == 0
+    M, N, K = 16, 1000, 768
+    W = synth.normal_bf16(150, N, K)
+    q = Quantized(ops, orc, W)
+    a = bf16_dev(synth.normal_bf16(151, M, K))
+    g = f32_dev(400.0)
+    ac, as_ = ops.quantize_act(a, g)
+    al = ops.alpha(q.g_dev, g)
+    o1 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al))
+    o2 = bf16_host(ops.linear_w4a4(ac, as_, q.w, al, workspace=True))
+    assert (o1 == o2).all()
+
+
+def test_w4a4_split_k_entry_points_agree(ops, orc):
+    # the dispatched linear's W4A4 route, its allocation-free form and
+    # linear_w4a4 with a workspace run the same split-K kernels: same bits
+    import torch
+
+    N, K, M = 3000, 2048, 100
+    assert ops.linear_w4a4_workspace_bytes(M, N, K) > 0
+    W = synth.normal_bf16(160, N, K)
+    a = synth.normal_bf16(161, M, K)
+    cal = synth.normal_bf16(162, 64, K)
+    q = Quantized(ops, orc, W)
+    gad = ops.global_scale(bf16_dev(cal))
+    a4 = ops.alpha(q.g_dev, gad)
+    ad = bf16_dev(a)
+    ops.set_route_m_max(64)
+    try:
+        out_lin, route = ops.linear(ad, q.w, gad, q.alpha, a4)
+        assert route == 1
+        out_na = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        assert ops.linear_noalloc(ad, q.w, gad, q.alpha, a4, out_na) == 1
+    finally:
+        ops.set_route_m_max(16)
+    ac, as_ = ops.quantize_act(ad, gad)
+    out_ws = ops.linear_w4a4(ac, as_, q.w, a4, workspace=True)
+    assert (bf16_host(out_lin) == bf16_host(out_ws)).all()
+    assert (bf16_host(out_na) == bf16_host(out_ws)).all()
+
+
 # ------------------------------------------------------------------ dispatch
 
 def test_dispatch_routes_and_numerics(ops, orc):

@@ -62,8 +62,8 @@ def test_noalloc_matches_workspace_call(ops, orc):
 def test_noalloc_rejects_beyond_scratch(ops):
     import torch
 
-    # K = 2048 needs 1152 bytes per row: 30000 rows exceed the 32 MiB scratch
-    N, K, M = 64, 2048, 30000
+    # K = 2048 needs 1152 bytes per row: 60000 rows exceed the 64 MiB scratch
+    N, K, M = 64, 2048, 60000
     assert ops.linear_workspace_bytes(M, N, K) > ops.NOALLOC_MAX_WORKSPACE_BYTES
     c = torch.zeros((N, K // 2), dtype=torch.uint8, device="cuda")
     s = torch.zeros((N, K // 16), dtype=torch.uint8, device="cuda")
