@@ -320,6 +320,40 @@ def bench_w4a4(ops, torch, reps=20):
                           p90_us=st["p90"]))
         log(f"[w4a4] M={Ms}: gemm {us:.1f} us = {2.0 * Ms * N * K / us / 1e6:.1f} TFLOP/s (p10 {st['p10']}, p90 "
             f"{st['p90']})")
+    # small batches (prefixes of a) on cold copies of the same weight: one
+    # launch over all of K (nvfp4_linear_w4a4) against K split across
+    # workgroups (nvfp4_linear_w4a4_ws, the dispatched linear's W4A4 kernels)
+    small = []
+    copies = [ops.prepare_weight(codes, scales) for _ in range(max(2, int(np.ceil(COLD_BYTES / (N * K * 9 / 16)))))]
+
+    def cold_us(fn):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for wc in copies:
+                fn(wc)
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / len(copies))
+        return float(np.median(ts))
+
+    for Ms in (16, 64, 128, 256, 512):
+        o = out[:Ms]
+        need = ops.linear_w4a4_workspace_bytes(Ms, N, K)
+        wsp = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        one = cold_us(lambda wc, Ms=Ms, o=o: ops.linear_w4a4(ac[:Ms], as_[:Ms], wc, al, out=o))
+        spl = cold_us(lambda wc, Ms=Ms, o=o, wsp=wsp: ops.linear_w4a4(ac[:Ms], as_[:Ms], wc, al, out=o, workspace=wsp))
+        small.append(dict(M=Ms, one_launch_us=round(one, 2), split_k_us=round(spl, 2), partial_mb=round(need / 1e6, 1),
+                          split_k_tflops=round(2.0 * Ms * N * K / spl / 1e6, 1)))
+        log(f"[w4a4] M={Ms} (cold weight): one launch {one:.1f} us, split-K {spl:.1f} us ({need / 1e6:.1f} MB partials)")
+    del copies
     # the gated MLP's gate_up on the same weight read as [2I, K] (I = N/2):
     # the GEMM plus the SiLU gate and NVFP4 quantization of h in its epilogue
     I = N // 2
@@ -345,7 +379,7 @@ def bench_w4a4(ops, torch, reps=20):
     return dict(M=M, N=N, K=K, gemm_us=gemm_us, quant_us=quant_us, tflops=flops / gemm_us / 1e6,
                 quant_cold_us=quant_cold_st["median"], quant_cold_gbs=qbytes / quant_cold_st["median"] / 1e3,
                 linear_tflops=flops / (gemm_us + quant_us) / 1e6, quant_gbs=qbytes / quant_us / 1e3,
-                prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16, m_sweep=sweep,
+                prepare_us=prepare_us, prepare_bytes=2 * N * K * 9 // 16, m_sweep=sweep, small_m=small,
                 gemm_stats_us=gemm_st, quant_stats_us=quant_st,
                 gated_mlp=dict(M=M, two_I=N, K=K, us=round(gated_us, 2), p10_us=gated_st["p10"],
                                p90_us=gated_st["p90"],
@@ -960,6 +994,9 @@ def main():
             "quantize_timing": "quantize_us: the pairs above (its input re-read from the last-level cache); "
                                "quantize_cold_us: each call on the next of 6 input copies (504 MB), read from HBM",
             "m_sweep": r4["m_sweep"],
+            "small_m": r4["small_m"],
+            "small_m_timing": "cold weight copies in HIP graphs; one_launch: nvfp4_linear_w4a4, split_k: "
+                              "nvfp4_linear_w4a4_ws (the dispatched linear's W4A4 kernels)",
             "gated_mlp": dict(r4["gated_mlp"], workload="nvfp4_gated_mlp_w4a4 on the same weight as gate_up [2I=8704, "
                               "K=5120], M=8192: GEMM + SiLU gate + NVFP4 quantization of h [M, 4352]"),
             "roofline": {"bound": "mfma", "achieved": round(r4["tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,

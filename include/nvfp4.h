@@ -307,7 +307,12 @@ int64_t nvfp4_get_route_m_max(void);
 /* Workspace nvfp4_linear needs on the W4A4 route: M*K/2 + M*K/16 bytes
  * (256-byte aligned parts) for the quantized activations, then
  * nvfp4_linear_w4a4_workspace_bytes(M, N, K) for the split-K partials (the
- * W4A4 route runs nvfp4_linear_w4a4_ws's kernels); the W4A16 route uses none. */
+ * W4A4 route runs nvfp4_linear_w4a4_ws's kernels); the W4A16 route uses none.
+ * The partials make the total larger for some small M than for a large one
+ * (N = 8704, K = 5120: 42.7 MB at M = 256, 23.6 MB at M = 8192).  A workspace
+ * that holds the activations but not the partials runs the one-launch kernel
+ * instead (nvfp4_linear_w4a4's bits); only less than the activations is a
+ * WORKSPACE error. */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------------
@@ -318,7 +323,9 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   alpha_w4a16   device fp32[1], 1/g_w
  *   alpha_w4a4    device fp32[1], 1/(g_w g_act) (may be NULL when g_act is)
  *   ws, ws_bytes  device workspace, >= nvfp4_linear_workspace_bytes(M, N, K)
- *                 on the W4A4 route (may be NULL on the W4A16 route)
+ *                 on the W4A4 route for the split-K kernels, at least the
+ *                 activations' part for the one-launch kernel (may be NULL
+ *                 on the W4A16 route)
  *   route_taken   host int out (NVFP4_ROUTE_*), may be NULL
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_weight* w, const float* g_act,
@@ -339,8 +346,9 @@ nvfp4_status nvfp4_linear(const void* a, int64_t M, int64_t lda, const nvfp4_wei
  * partials) go to a scratch array the library holds on each GPU (a device global of
  * NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES, kept until the process ends);
  * the W4A16 route needs none.  The caller still passes inputs and outputs.
- *   Arguments, routes, numerics and errors as nvfp4_linear (the same kernels,
- *   the same bits), plus WORKSPACE when nvfp4_linear_workspace_bytes(M, N, K)
+ *   Arguments, routes, numerics and errors as nvfp4_linear with a workspace
+ *   of nvfp4_linear_workspace_bytes(M, N, K) (the same kernels, the same
+ *   bits), plus WORKSPACE when nvfp4_linear_workspace_bytes(M, N, K)
  *   exceeds NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_BYTES on the W4A4 route
  *   (checked before any launch).
  *   Every call on one GPU shares that GPU's scratch, so calls that overlap in

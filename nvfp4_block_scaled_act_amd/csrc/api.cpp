@@ -326,6 +326,7 @@ nvfp4_status linear_impl(const void* a, int64_t M, int64_t lda, const nvfp4_weig
     if (!alpha_w4a4) return NVFP4_ERR_INVALID_ARGUMENT;
     if ((st = check_bf16_input(a, M, w->K, lda)) != NVFP4_OK) return st;
     if ((st = check_out(out, M, w->N, ldo)) != NVFP4_OK) return st;
+    const size_t need_act = nvfp4::linear_act_bytes(M, w->K);
     const size_t need = nvfp4_linear_workspace_bytes(M, w->N, w->K);
     if (M * (w->K / 16) > kInt32Max || (M + 3) / 4 > 65535 || (M + 255) / 256 > 65535 ||
         M * (w->K / 2) >= (int64_t(1) << 32))
@@ -335,14 +336,13 @@ nvfp4_status linear_impl(const void* a, int64_t M, int64_t lda, const nvfp4_weig
       if ((st = hip_status(nvfp4::scratch_pointer(&ws))) != NVFP4_OK) return st;
       ws_bytes = nvfp4::scratch_capacity();
     }
-    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!ws || ws_bytes < need_act) return NVFP4_ERR_WORKSPACE;
     if (!aligned16(ws)) return NVFP4_ERR_ALIGNMENT;
     uint8_t* codes = static_cast<uint8_t*>(ws);
     uint8_t* scales = codes + align_up(size_t(M) * size_t(w->K / 2), 256);
-    // split-K partials after the activations, when the shape takes them
-    float* partials = nvfp4::w4a4_partials_bytes(M, w->N, w->K) > 0
-                          ? reinterpret_cast<float*>(codes + nvfp4::linear_act_bytes(M, w->K))
-                          : nullptr;
+    // split-K partials after the activations, when the shape takes them and
+    // the workspace holds them (else one launch over all of K)
+    float* partials = need > need_act && ws_bytes >= need ? reinterpret_cast<float*>(codes + need_act) : nullptr;
     st = hip_status(nvfp4::launch_quantize(a, M, w->K, lda, g_act, codes, scales, stream));
     if (st == NVFP4_OK)
       st = hip_status(

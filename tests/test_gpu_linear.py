@@ -450,6 +450,16 @@ def test_w4a4_split_k_entry_points_agree(ops, orc):
     out_ws = ops.linear_w4a4(ac, as_, q.w, a4, workspace=True)
     assert (bf16_host(out_lin) == bf16_host(out_ws)).all()
     assert (bf16_host(out_na) == bf16_host(out_ws)).all()
+    # a workspace with room for the activations only: the one-launch kernel
+    act_bytes = ops.linear_workspace_bytes(M, N, K) - ops.linear_w4a4_workspace_bytes(M, N, K)
+    small = torch.empty(act_bytes, dtype=torch.uint8, device="cuda")
+    ops.set_route_m_max(64)
+    try:
+        out_small, route = ops.linear(ad, q.w, gad, q.alpha, a4, workspace=small)
+    finally:
+        ops.set_route_m_max(16)
+    assert route == 1
+    assert (bf16_host(out_small) == bf16_host(ops.linear_w4a4(ac, as_, q.w, a4))).all()
 
 
 # ------------------------------------------------------------------ dispatch
