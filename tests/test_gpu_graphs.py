@@ -82,6 +82,40 @@ def test_graph_w4a4(ops):
         _replays_match(torch, gr, out, eager, lambda: ops.linear_w4a4(ac, as_, w, al))
 
 
+def test_graph_w4a4_split_k(ops):
+    import torch
+
+    # few tiles: K split across workgroups, two launches per call (partial
+    # tiles, then their fixed-order sum).  Captured with a caller workspace,
+    # through the dispatched linear, and through the allocation-free form,
+    # whose scratch eager calls on other inputs overwrite between replays
+    M, N, K = 100, 3000, 2048
+    assert ops.linear_w4a4_workspace_bytes(M, N, K) > 0
+    w, gw = _weight(ops, 311, N, K)
+    ga = f32_dev(500.0)
+    a = bf16_dev(synth.normal_bf16(312, M, K))
+    other = bf16_dev(synth.normal_bf16(313, M, K))
+    ac, as_ = ops.quantize_act(a, ga)
+    al, a16 = ops.alpha(gw, ga), ops.alpha(gw)
+    ws = torch.empty(ops.linear_w4a4_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    eager = bf16_host(ops.linear_w4a4(ac, as_, w, al, workspace=ws))
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gr = _capture(torch, lambda: ops.linear_w4a4(ac, as_, w, al, out=out, workspace=ws))
+    _replays_match(torch, gr, out, eager, lambda: ops.linear_w4a4(ac, as_, w, al, workspace=True))
+    ops.set_route_m_max(64)
+    try:
+        lws = torch.empty(ops.linear_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+        lin, route = ops.linear(a, w, ga, a16, al, workspace=lws)
+        assert route == 1 and (bf16_host(lin) == eager).all()
+        gr = _capture(torch, lambda: ops.linear(a, w, ga, a16, al, out=out, workspace=lws))
+        _replays_match(torch, gr, out, eager, lambda: ops.linear(other, w, ga, a16, al))
+        scratch_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        gr = _capture(torch, lambda: ops.linear_noalloc(a, w, ga, a16, al, out))
+        _replays_match(torch, gr, out, eager, lambda: ops.linear_noalloc(other, w, ga, a16, al, scratch_out))
+    finally:
+        ops.set_route_m_max(16)
+
+
 def test_graph_moe(ops):
     import torch
 
