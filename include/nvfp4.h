@@ -295,10 +295,12 @@ nvfp4_status nvfp4_linear_w4a4_ws(const void* a_codes, const void* a_scales, int
  * checkpoints with static activation scales, W4A16 kernels for batches up to
  * a threshold T, 8 or 16 there).
  *   nvfp4_route: pure; W4A4 iff has_act_global && M > M*; else W4A16.
- *   nvfp4_set_route_m_max / get: M* (default 64, where the W4A16 kernels
- *   still beat quantize + W4A4 on the large fused weight N = 62080, K = 5120
- *   on MI355X; values above 64 are clamped to 64, the W4A16 kernels' limit,
- *   and a missing activation global with M > 64 is UNSUPPORTED).
+ *   nvfp4_set_route_m_max / get: M* (default 16: from 17 rows on, quantize
+ *   + W4A4 beats the W4A16 kernels on the large fused weight N = 62080,
+ *   K = 5120 on MI355X, and on N = 3584, 8704 and 43008 (K = 5120); on
+ *   N = 14336 and 28672 W4A16 stays ahead up to about 24 and 56 rows.
+ *   Values above 64 are clamped to 64, the W4A16 kernels' limit, and a
+ *   missing activation global with M > 64 is UNSUPPORTED).
  * ------------------------------------------------------------------------- */
 int nvfp4_route(int64_t M, int64_t N, int64_t K, int has_act_global);
 void nvfp4_set_route_m_max(int64_t m_max);

@@ -14,7 +14,8 @@ static_assert(nvfp4::kLinearScratchBytes == NVFP4_LINEAR_NOALLOC_MAX_WORKSPACE_B
 namespace {
 
 constexpr int64_t kInt32Max = 2147483647LL;
-std::atomic<int64_t> g_route_m_max{64};  // measured crossover, N = 62080, K = 5120
+constexpr int64_t kW4a4MaxK = int64_t(1) << 24;  // the W4A4 kernels' 32-bit weight offsets
+std::atomic<int64_t> g_route_m_max{16};  // measured crossover, N = 62080, K = 5120 (and most weights)
 std::atomic<int64_t> g_moe_route_tpe_max{32};  // tokens per expert up to which the MoE stays W4A16
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -254,6 +255,8 @@ nvfp4_status w4a4_checked(const void* a_codes, const void* a_scales, int64_t M, 
   if (!aligned16(a_codes) || !aligned16(a_scales)) return NVFP4_ERR_ALIGNMENT;
   // grid rows of 256 activation rows; 32-bit byte offsets into the codes
   if ((M + 255) / 256 > 65535 || M * (w->K / 2) >= (int64_t(1) << 32)) return NVFP4_ERR_UNSUPPORTED;
+  // 32-bit byte offsets within a workgroup's 16 weight tiles (17 K/256 units)
+  if (w->K > kW4a4MaxK) return NVFP4_ERR_UNSUPPORTED;
   if (w->N == 0) return NVFP4_OK;
   return hip_status(
       nvfp4::launch_w4a4(a_codes, a_scales, M, w->data, w->N, w->K, alpha, out, ldo, partials, stream));
@@ -329,7 +332,7 @@ nvfp4_status linear_impl(const void* a, int64_t M, int64_t lda, const nvfp4_weig
     const size_t need_act = nvfp4::linear_act_bytes(M, w->K);
     const size_t need = nvfp4_linear_workspace_bytes(M, w->N, w->K);
     if (M * (w->K / 16) > kInt32Max || (M + 3) / 4 > 65535 || (M + 255) / 256 > 65535 ||
-        M * (w->K / 2) >= (int64_t(1) << 32))
+        M * (w->K / 2) >= (int64_t(1) << 32) || w->K > kW4a4MaxK)
       return NVFP4_ERR_UNSUPPORTED;
     if (use_scratch) {
       if (need > nvfp4::scratch_capacity()) return NVFP4_ERR_WORKSPACE;  // beyond the scratch's fixed size
@@ -382,6 +385,8 @@ nvfp4_status moe_shape(int64_t T, int64_t top_k, int64_t E, int64_t K, int64_t I
   // 32-bit byte offsets into the quantized x and h
   if (T * (K / 2) >= (int64_t(1) << 32) || T * top_k * (I / 2) >= (int64_t(1) << 32)) return NVFP4_ERR_UNSUPPORTED;
   if (E * 2 * I > kInt32Max - 15 || E * K > kInt32Max - 15) return NVFP4_ERR_UNSUPPORTED;
+  // 32-bit byte offsets within one expert's prepared gate_up and down weights
+  if (2 * I * (K / 256) * 2304 >= (int64_t(1) << 32)) return NVFP4_ERR_UNSUPPORTED;
   return NVFP4_OK;
 }
 
@@ -539,6 +544,8 @@ nvfp4_status nvfp4_gated_mlp_w4a4(const void* a_codes, const void* a_scales, int
   if ((M + 255) / 256 * (I / 128) > kInt32Max || M * (K / 2) >= (int64_t(1) << 32) ||
       M * (I / 2) >= (int64_t(1) << 32))
     return NVFP4_ERR_UNSUPPORTED;
+  // 32-bit byte offsets within the prepared gate_up weight
+  if (2 * I * (K / 256) * 2304 >= (int64_t(1) << 32)) return NVFP4_ERR_UNSUPPORTED;
   return hip_status(nvfp4::launch_gated_mlp_w4a4(a_codes, a_scales, M, gate_up->data, K, I, alpha, g2, h_codes,
                                                  h_scales, h_amax, stream));
 }

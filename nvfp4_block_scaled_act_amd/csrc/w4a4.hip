@@ -9,8 +9,13 @@
 //
 // One workgroup fills a CU (LDS), so the tiles run in rounds of one per CU.
 // When the last round would be at most half full, its tiles are split into
-// two 128-row halves each, which take about half as long; a batch of at most
-// 128 rows runs on 128-row tiles throughout.
+// two 128-row halves each, which take about half as long.
+//
+// A batch of at most 128 rows runs on its own kernel (skinny::kernel): each
+// wave dequantizes its weight rows straight into MFMA operand registers and
+// only the activation tile goes through LDS, so the weight stream, not the
+// LDS staging of a mostly empty 256 x 256 tile, sets the pace (N = 62080,
+// K = 5120: 81 -> 37 us at M <= 32, 88 -> 54 us at M = 64).
 //
 // Few tiles (a small batch on a weight of a few thousand rows: N = 8704 has
 // 34 column tiles, so 34 of 256 CUs would work through all of K) split K
@@ -90,14 +95,14 @@ __device__ __forceinline__ void w4a4_tile(_Float16* __restrict__ lds, const uint
 }
 
 // Workgroups [0, grid_big) run the first n_big tiles of the grouped order as
-// 256-row tiles (XCD-aware); the rest run the remaining tiles as 128-row
-// halves, `halves` workgroups per tile (2, or 1 when M <= 128).
+// 256-row tiles (XCD-aware); the rest run the remaining tiles as two 128-row
+// halves each.
 __global__ __launch_bounds__(gemm::kThreads) void w4a4_kernel(const uint8_t* __restrict__ ac,
                                                               const uint8_t* __restrict__ as, int32_t M,
                                                               const uint8_t* __restrict__ wt, int32_t N, int32_t K,
                                                               const float* __restrict__ alpha_p,
                                                               uint16_t* __restrict__ out, int64_t ldo, int vec_store,
-                                                              int32_t n_big, int32_t grid_big, int32_t halves) {
+                                                              int32_t n_big, int32_t grid_big) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
   const int32_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
   const float alpha = *alpha_p;
@@ -108,8 +113,8 @@ __global__ __launch_bounds__(gemm::kThreads) void w4a4_kernel(const uint8_t* __r
     w4a4_tile<gemm::BM>(lds, ac, as, M, wt, N, K, alpha, out, ldo, vec_store, nblk, mblk * gemm::BM);
   } else {
     const int32_t j = id - grid_big;
-    gemm::grouped_tile(n_big + j / halves, nt, mt, nblk, mblk);
-    const int32_t m0 = mblk * gemm::BM + (gemm::BM / 2) * (j % halves);
+    gemm::grouped_tile(n_big + j / 2, nt, mt, nblk, mblk);
+    const int32_t m0 = mblk * gemm::BM + (gemm::BM / 2) * (j % 2);
     if (m0 >= M) return;
     w4a4_tile<gemm::BM / 2>(lds, ac, as, M, wt, N, K, alpha, out, ldo, vec_store, nblk, m0);
   }
@@ -151,27 +156,23 @@ __device__ __forceinline__ void w4a4_partial_tile(_Float16* __restrict__ lds, co
     }
 }
 
-// Workgroup id -> (tile L = id % tiles, range s = id / tiles); tiles of 128
-// rows when M <= 128 (narrow), else the 256-row tiles of the grouped order.
+// Workgroup id -> (tile L = id % tiles of the grouped order, range s = id /
+// tiles).
 __global__ __launch_bounds__(gemm::kThreads) void w4a4_splitk_kernel(const uint8_t* __restrict__ ac,
                                                                      const uint8_t* __restrict__ as, int32_t M,
                                                                      const uint8_t* __restrict__ wt, int32_t N,
                                                                      int32_t K, float* __restrict__ partials,
-                                                                     int32_t splits, int32_t tiles, int narrow) {
+                                                                     int32_t splits, int32_t tiles) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[gemm::kLdsHalves];
   const int32_t id = int32_t(blockIdx.x);
   const int32_t L = id % tiles, s = id / tiles;
   const int32_t units = K / 256;
   const int32_t u0 = int32_t(int64_t(s) * units / splits), u1 = int32_t(int64_t(s + 1) * units / splits);
   float* part = partials + int64_t(s) * M * N;
-  if (narrow) {
-    w4a4_partial_tile<gemm::BM / 2>(lds, ac, as, M, wt, N, K, part, L, 0, u0, u1);
-  } else {
-    const int32_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
-    int32_t nblk, mblk;
-    gemm::grouped_tile(L, nt, mt, nblk, mblk);
-    w4a4_partial_tile<gemm::BM>(lds, ac, as, M, wt, N, K, part, nblk, mblk * gemm::BM, u0, u1);
-  }
+  const int32_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
+  int32_t nblk, mblk;
+  gemm::grouped_tile(L, nt, mt, nblk, mblk);
+  w4a4_partial_tile<gemm::BM>(lds, ac, as, M, wt, N, K, part, nblk, mblk * gemm::BM, u0, u1);
 }
 
 // out[m][n] = bf16(alpha * (part_0 + part_1 + ... + part_{splits-1})[m][n]),
@@ -215,13 +216,331 @@ __global__ __launch_bounds__(256) void w4a4_splitk_reduce_kernel(const float* __
   }
 }
 
+// ---------------------------------------------------------------- few rows
+// A batch of at most 128 rows (M <= 32 G, G = 1, 2 or 4 groups of 32 rows).
+// The 256 x 256 tile main loop would run its tiles mostly empty here and
+// stage every weight tile through LDS for a handful of rows; instead each
+// wave dequantizes its own weight rows straight into MFMA operand registers
+// and only the small activation tile goes through LDS, shared by the
+// workgroup's waves.  A workgroup is 8 waves x one tile of 32 weight rows =
+// 256 rows, over all M rows (or a range of whole 256-k units: split K); two
+// waves per SIMD, so one wave's dequant issues under the other's MFMAs.
+//
+// MFMA operand order.  32x32x16 fp16: lane (r, h) (r = lane % 32, h = lane /
+// 32) supplies 8 consecutive k-slots 8h..8h+7 of row r.  The contraction does
+// not care which k a slot holds as long as both operands agree, so the 16
+// MFMAs j = 2J + e (J = 0..7, e = 0, 1) of a 256-k unit give slot 8h + x the
+// k = 16 (2J + h) + 8e + x: a lane takes the groups of its parity h.  In the
+// tiled weight those are the groups 4p + q with q = h and q = h + 2 of lane
+// slots r' + 16h and r' + 16(h + 2) (r' = r % 16): four 16-byte code loads
+// and two scale dwords per lane and unit, all whole, and every lane uses all
+// it loads.  The activation tile sits in LDS in plain k order (fp16, one
+// padded row per activation row), so the B operand is one 16-byte read.
+// Every value is exact in fp16 and every product in fp32, as in the main loop.
+//
+// Pipeline per 256-k step (one barrier): the weights of D steps live in
+// registers, and after a step's MFMAs the next step's activation tile is
+// dequantized into the other LDS buffer (see the kernel's ring).
+namespace skinny {
+
+constexpr int kWaves = 8;               // two waves per SIMD: one's dequant runs under the other's MFMAs
+constexpr int kThreads = 64 * kWaves;
+constexpr int TW = 1;                    // 32-row weight tiles per wave
+constexpr int kRows = 32 * TW * kWaves;  // weight rows per workgroup
+constexpr int kMaxM = 32 * 4;            // activation rows: up to four groups of 32
+constexpr int PITCH = 256 + 8;           // fp16 per LDS activation row (the pad staggers rows across banks)
+
+template <int G>
+constexpr int lds_halves() {
+  return 2 * 32 * G * PITCH;
+}
+
+struct WTileRegs {  // one lane's bytes of a 32-row tile's 256-k unit
+  uint4 q[4];       // q = h groups p = 0,1 | p = 2,3; q = h + 2 groups p = 0,1 | p = 2,3
+  uint32_t sc[2];   // scale bytes of the q = h groups (byte p), of the q = h + 2 groups
+};
+struct WRegs {
+  WTileRegs t[TW];
+};
+
+// Activation pieces (32 codes of one row: 256 G per step) per thread; with
+// fewer pieces than threads the waves past them stage none (a wave-uniform
+// test).
+template <int G>
+constexpr int pieces_per_thread() {
+  return (256 * G + kThreads - 1) / kThreads;
+}
+
+template <int G>
+struct ARegs {      // a thread's activation pieces of one 256-k step
+  uint4 c[pieces_per_thread<G>()];     // 32 codes: groups 2 pc, 2 pc + 1 of the step
+  uint32_t s[pieces_per_thread<G>()];  // the dword holding their two scale bytes
+};
+
+struct Offsets {
+  uint32_t w[TW];   // weight codes of lane slot r' + 16 h (relative to the descriptor)
+  uint32_t ws[TW];  // its scale bytes
+};
+
+template <int G>
+struct AOffsets {
+  uint32_t c[pieces_per_thread<G>()], s[pieces_per_thread<G>()];
+  int32_t lds[pieces_per_thread<G>()];    // fp16 offset of the piece in an LDS buffer
+  int32_t shift[pieces_per_thread<G>()];  // bit offset of the piece's two scale bytes in the dword
+};
+
+template <int G>
+__device__ __forceinline__ bool has_piece(int i) {
+  return 256 * G >= kThreads * (i + 1) || __builtin_amdgcn_readfirstlane(int(threadIdx.x)) + kThreads * i < 256 * G;
+}
+
+__device__ __forceinline__ WRegs load_w(__amdgpu_buffer_rsrc_t rsrc, const Offsets& o, int32_t unit) {
+  const int32_t so = unit * gemm::kUnitBytes;
+  WRegs w;
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    // lane slot r' + 16 (h + 2) is 32 slots on: 512 code bytes, 128 scale bytes
+    const uint32_t offs[4] = {o.w[t], o.w[t] + 1024u, o.w[t] + 512u, o.w[t] + 1536u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, offs[i], so, 0);
+      w.t[t].q[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    w.t[t].sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, o.ws[t], so, 0);
+    w.t[t].sc[1] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, o.ws[t] + 128u, so, 0);
+  }
+  return w;
+}
+
+template <int G>
+__device__ __forceinline__ ARegs<G> load_a(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                           const AOffsets<G>& o, int32_t unit) {
+  ARegs<G> a;
+#pragma unroll
+  for (int i = 0; i < pieces_per_thread<G>(); ++i) {
+    if (!has_piece<G>(i)) {
+      a.c[i] = make_uint4(0, 0, 0, 0);
+      a.s[i] = 0;
+      continue;
+    }
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, o.c[i], unit * 128, 0);
+    a.c[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    a.s[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.s[i], unit * 16, 0);
+  }
+  return a;
+}
+
+// Dequantizes the thread's pieces into LDS buffer buf (fp16, k order).
+template <int G>
+__device__ __forceinline__ void store_a(const ARegs<G>& a, const AOffsets<G>& o, _Float16* __restrict__ buf) {
+#pragma unroll
+  for (int i = 0; i < pieces_per_thread<G>(); ++i) {
+    if (!has_piece<G>(i)) continue;
+    const uint32_t sb = a.s[i] >> o.shift[i];
+    const uint32_t S0 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(sb, 0));
+    const uint32_t S1 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(sb, 1));
+    uint32_t v[4][4];
+    dequant8_f16(a.c[i].x, S0, v[0]);
+    dequant8_f16(a.c[i].y, S0, v[1]);
+    dequant8_f16(a.c[i].z, S1, v[2]);
+    dequant8_f16(a.c[i].w, S1, v[3]);
+    uint4* d = reinterpret_cast<uint4*>(buf + o.lds[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = make_uint4(v[j][0], v[j][1], v[j][2], v[j][3]);
+  }
+}
+
+// acc[t][g] += weight tile t x activation rows 32g.. over one 256-k step.
+// Register i of lane l in acc[t][g] holds activation row 32g + 8(i/4) +
+// 4(l/32) + i%4 and weight row 32t + l%32 of the wave's 64 (the activations
+// are the MFMA's first operand, so a register's 32 lanes are 32 consecutive
+// outputs of one activation row).  Software-pipelined by one MFMA block:
+// the LDS reads and the weight dequant of block j + 1 are issued while the
+// MFMAs of block j run, so neither the LDS latency nor the VALU work sits
+// between two blocks' MFMAs.
+template <int G>
+__device__ __forceinline__ void read_b(f16x8_t (&B)[G], const _Float16* __restrict__ brow, int j) {
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    B[g] = *reinterpret_cast<const f16x8_t*>(brow + 32 * g * PITCH + 32 * (j >> 1) + 8 * (j & 1));
+}
+
+// Weight operand of block j = 2J + e for tile t: codes of group 2J + h, half e.
+__device__ __forceinline__ f16x8_t weight_a(const WTileRegs& w, int j) {
+  const int J = j >> 1, e = j & 1;
+  const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(w.sc[J & 1] >> (8 * (J >> 1)), 0));
+  const uint4& q = w.q[(J & 1) * 2 + (J >> 2)];
+  const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+  uint32_t a[4];
+  dequant8_f16(qw[((J >> 1) & 1) * 2 + e], S2, a);
+  return __builtin_bit_cast(f16x8_t, make_uint4(a[0], a[1], a[2], a[3]));
+}
+
+template <int G>
+__device__ __forceinline__ void step(f32x16_t (&acc)[TW][G], const WRegs& w, const _Float16* __restrict__ abuf,
+                                     int lane) {
+  const _Float16* brow = abuf + (lane & 31) * PITCH + 16 * (lane >> 5);
+  f16x8_t B[2][G], A[2][TW];
+  read_b<G>(B[0], brow, 0);
+#pragma unroll
+  for (int t = 0; t < TW; ++t) A[0][t] = weight_a(w.t[t], 0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int cur = j & 1;
+    if (j < 15) read_b<G>(B[cur ^ 1], brow, j + 1);
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        acc[t][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(B[cur][g], A[cur][t], acc[t][g], 0, 0, 0);
+    if (j < 15) {
+#pragma unroll
+      for (int t = 0; t < TW; ++t) A[cur ^ 1][t] = weight_a(w.t[t], j + 1);
+    }
+  }
+}
+
+// Workgroup id -> (row block blk = id % nblocks, K range s = id / nblocks).
+// splits == 1: out[m][n] = bf16(alpha * acc); else the unscaled fp32 partial
+// of range s at partials + s * M * N, row-major [M, N].
+// D = steps of weights (and activation codes) held in registers: as deep as
+// the register file allows at G groups of 32 rows.
+template <int G, int D = (G == 4 ? 3 : 4)>
+__global__ __launch_bounds__(kThreads) void kernel(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+                                                   int32_t M, const uint8_t* __restrict__ wt, int32_t N, int32_t K,
+                                                   const float* __restrict__ alpha_p, uint16_t* __restrict__ out,
+                                                   int64_t ldo, float* __restrict__ partials, int32_t splits,
+                                                   int32_t nblocks) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[lds_halves<G>()];
+  const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6;
+  const int32_t id = int32_t(blockIdx.x);
+  const int32_t blk = id % nblocks, s = id / nblocks;
+  const int32_t units = K / 256;
+  const int32_t u0 = int32_t(int64_t(s) * units / splits), u1 = int32_t(int64_t(s + 1) * units / splits);
+  const int32_t nu = u1 - u0;
+  const int32_t tiles16 = (N + 15) / 16, first16 = blk * (kRows / 16);
+
+  // weight: the workgroup's rows start the descriptor; lane slot r' + 16h
+  const __amdgpu_buffer_rsrc_t rw =
+      gemm::buffer_rsrc(wt + int64_t(first16) * units * gemm::kUnitBytes);
+  Offsets o;
+  {
+    const int r = lane & 31, lp = (r & 15) + 16 * (lane >> 5);
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const int32_t t16 = min(first16 + 2 * (TW * wave + t) + (r >> 4), tiles16 - 1);
+      const uint32_t base = uint32_t(t16 - first16) * uint32_t(units) * uint32_t(gemm::kUnitBytes);
+      o.w[t] = base + 16u * uint32_t(lp);
+      o.ws[t] = base + 2048u + 4u * uint32_t(lp);
+    }
+  }
+  // Activation pieces: piece P = tid + kThreads i; each run of 64 pieces
+  // covers 8 rows x the 8 pieces of a step (whole 128-byte lines of codes),
+  // and each 8 neighbouring lanes 4 rows x 2 pieces, whose LDS rows (528
+  // bytes apart) and pieces (64 bytes) put their 16-byte writes in 8
+  // different bank groups.  (One row per lane had made every load
+  // instruction touch 64 lines: at 64 rows that staging cost as much as the
+  // MFMAs.)
+  const __amdgpu_buffer_rsrc_t rac = gemm::buffer_rsrc(ac), ras = gemm::buffer_rsrc(as);
+  AOffsets<G> ao;
+#pragma unroll
+  for (int i = 0; i < pieces_per_thread<G>(); ++i) {
+    const int P = min(tid + kThreads * i, 256 * G - 1), l = P & 63;
+    const int row = 8 * (P >> 6) + 4 * (l >> 5) + ((l >> 1) & 3), pc = 2 * ((l >> 3) & 3) + (l & 1);
+    const uint32_t arow = uint32_t(min(row, M - 1));
+    ao.c[i] = arow * uint32_t(K / 2) + 16u * uint32_t(pc);
+    ao.s[i] = arow * uint32_t(K / 16) + 4u * uint32_t(pc >> 1);
+    ao.shift[i] = 16 * (pc & 1);
+    ao.lds[i] = row * PITCH + 32 * pc;
+  }
+  _Float16* const buf0 = lds;
+  _Float16* const buf1 = lds + 32 * G * PITCH;
+
+  f32x16_t acc[TW][G];
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][g][i] = 0.f;
+
+  // Ring of D stages: step st uses weights W[st % D] (loaded D steps
+  // ahead) and activation codes A[(st + 1) % D] staged at its end (loaded
+  // D - 1 steps ahead, before the weights that follow them, since loads
+  // complete in issue order: waiting for them never waits for weights a
+  // later step needs).  Loads past the range re-read its last unit (cache
+  // hits, never used).  The prologue's loads are kept in program order
+  // (scheduling barriers), so the wait counts at the loop head, which hold
+  // for the first entry as well as for the back edge, are those of the
+  // steady state.
+  auto unit = [&](int32_t i) { return u0 + min(i, nu - 1); };
+  ARegs<G> A[D];
+  WRegs W[D];
+#pragma unroll
+  for (int d = 0; d + 1 < D; ++d) {
+    A[d] = load_a<G>(rac, ras, ao, unit(d));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    W[d] = load_w(rw, o, unit(d));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  store_a<G>(A[0], ao, buf0);
+  __syncthreads();
+  for (int32_t i = 0; i < nu; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int32_t st = i + d;
+      if (st < nu) step<G>(acc, W[d], (st & 1) ? buf1 : buf0, lane);
+      A[(d + D - 1) % D] = load_a<G>(rac, ras, ao, unit(st + D - 1));
+      W[d] = load_w(rw, o, unit(st + D));
+      store_a<G>(A[(d + 1) % D], ao, (st & 1) ? buf0 : buf1);
+      __syncthreads();
+    }
+  }
+
+  const int h = lane >> 5;
+  const int32_t n = blk * kRows + 32 * TW * wave + (lane & 31);
+  if (splits == 1) {
+    const float alpha = *alpha_p;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      if (n + 32 * t >= N) continue;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t m = 32 * g + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (m < M) out[int64_t(m) * ldo + n + 32 * t] = __builtin_bit_cast(uint16_t, (__bf16)(acc[t][g][i] * alpha));
+        }
+    }
+  } else {
+    float* part = partials + int64_t(s) * M * N;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      if (n + 32 * t >= N) continue;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t m = 32 * g + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (m < M) part[int64_t(m) * N + n + 32 * t] = acc[t][g][i];
+        }
+    }
+  }
+}
+
+}  // namespace skinny
+
 }  // namespace
 
 int w4a4_splits(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < 256) return 1;
   const int64_t units = K / 256;
   const int64_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
-  const int64_t tiles = M <= gemm::BM / 2 ? nt : nt * mt;
+  // one workgroup per 256-row column tile for a few rows (skinny::kernel)
+  const int64_t tiles = M <= skinny::kMaxM ? nt : nt * mt;
   const int64_t cus = device_cu_count();
   // only when the tiles fill at most half the CUs; at least two units per range
   if (units < 4 || 2 * tiles > cus) return 1;
@@ -249,11 +568,32 @@ hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, con
   auto* O = static_cast<uint16_t*>(out);
   const int64_t nt = (N + gemm::BN - 1) / gemm::BN, mt = (M + gemm::BM - 1) / gemm::BM;
   const int splits = partials ? w4a4_splits(M, N, K) : 1;
+  if (M <= skinny::kMaxM) {
+    // few rows: 256 weight rows per workgroup (as many workgroups as 256-row
+    // column tiles, so w4a4_splits applies unchanged)
+    static_assert(skinny::kRows == gemm::BN, "one skinny workgroup per 256-row column tile");
+    const dim3 grid(uint32_t(nt * splits)), block(skinny::kThreads);
+    float* part = splits > 1 ? partials : nullptr;
+    if (M <= 32)
+      hipLaunchKernelGGL(skinny::kernel<1>, grid, block, 0, stream, AC, AS, int32_t(M), WT, int32_t(N), int32_t(K),
+                         alpha, O, ldo, part, splits, int32_t(nt));
+    else if (M <= 64)
+      hipLaunchKernelGGL(skinny::kernel<2>, grid, block, 0, stream, AC, AS, int32_t(M), WT, int32_t(N), int32_t(K),
+                         alpha, O, ldo, part, splits, int32_t(nt));
+    else
+      hipLaunchKernelGGL(skinny::kernel<4>, grid, block, 0, stream, AC, AS, int32_t(M), WT, int32_t(N), int32_t(K),
+                         alpha, O, ldo, part, splits, int32_t(nt));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t threads = M * ((N + 3) / 4);
+    hipLaunchKernelGGL(w4a4_splitk_reduce_kernel, dim3(uint32_t((threads + 255) / 256)), dim3(256), 0, stream,
+                       partials, splits, int32_t(M), int32_t(N), alpha, O, ldo);
+    return hipGetLastError();
+  }
   if (splits > 1) {
-    const bool narrow = M <= gemm::BM / 2;
-    const int64_t tiles = narrow ? nt : nt * mt;
+    const int64_t tiles = nt * mt;
     hipLaunchKernelGGL(w4a4_splitk_kernel, dim3(uint32_t(tiles * splits)), dim3(gemm::kThreads), 0, stream, AC, AS,
-                       int32_t(M), WT, int32_t(N), int32_t(K), partials, splits, int32_t(tiles), narrow ? 1 : 0);
+                       int32_t(M), WT, int32_t(N), int32_t(K), partials, splits, int32_t(tiles));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = M * ((N + 3) / 4);
@@ -264,21 +604,14 @@ hipError_t launch_w4a4(const void* a_codes, const void* a_scales, int64_t M, con
   const int64_t total = nt * mt;
   const int64_t cus = device_cu_count();
   const int64_t rest = total % cus;
-  int64_t n_big, halves = 2;
-  if (M <= gemm::BM / 2) {
-    n_big = 0;  // one 128-row tile per column block
-    halves = 1;
-  } else {
-    // split the last round into halves when it is at most half full
-    n_big = (total > cus && rest > 0 && 2 * rest <= cus) ? total - rest : total;
-  }
+  // split the last round into halves when it is at most half full
+  const int64_t n_big = (total > cus && rest > 0 && 2 * rest <= cus) ? total - rest : total;
   const int64_t grid_big = n_big > 0 ? gemm::xcd_grid(int32_t(n_big)) : 0;
-  const int64_t grid = grid_big + halves * (total - n_big);
+  const int64_t grid = grid_big + 2 * (total - n_big);
   // whole 16-byte output pieces when the rows are 16-byte aligned
   const int vec_store = (reinterpret_cast<uintptr_t>(out) % 16 == 0 && (ldo * 2) % 16 == 0) ? 1 : 0;
   hipLaunchKernelGGL(w4a4_kernel, dim3(uint32_t(grid)), dim3(gemm::kThreads), 0, stream, AC, AS, int32_t(M), WT,
-                     int32_t(N), int32_t(K), alpha, O, ldo, vec_store, int32_t(n_big), int32_t(grid_big),
-                     int32_t(halves));
+                     int32_t(N), int32_t(K), alpha, O, ldo, vec_store, int32_t(n_big), int32_t(grid_big));
   return hipGetLastError();
 }
 

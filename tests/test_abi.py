@@ -149,14 +149,14 @@ def test_w4a4_validation(nv):
 
 
 def test_route_default_threshold():
-    # a fresh process sees the documented default M* = 64 (the measured
+    # a fresh process sees the documented default M* = 16 (the measured
     # crossover on the large fused weight)
     import sys
 
     code = "from nvfp4_block_scaled_act_amd import lib; print(lib.load().nvfp4_get_route_m_max())"
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
                          cwd=L.HERE + "/..").stdout
-    assert out.strip() == "64"
+    assert out.strip() == "16"
 
 
 def test_route_is_a_pure_threshold(nv):

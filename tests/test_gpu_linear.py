@@ -363,6 +363,35 @@ def test_w4a4_ragged(ops, orc, M, N, K):
     _w4a4_case(ops, orc, W, a, cal)
 
 
+@pytest.mark.parametrize("N,K", [(1000, 1280), (4104, 256), (600, 3072)])
+def test_w4a4_few_rows_every_group(ops, orc, N, K):
+    # batches of at most 128 rows run on 256 weight rows per workgroup with
+    # 1, 2 or 4 groups of 32 activation rows: every group count, the ragged
+    # rows of each, N not a multiple of 16 or 256, K of 5, 1 and 12 units
+    # (an odd count, a single one); with and without the split of K.  Each
+    # batch checked in full
+    import torch
+
+    M_max = 128
+    W = synth.normal_bf16(170 + N, N, K)
+    a = synth.normal_bf16(171 + N, M_max, K)
+    cal = synth.normal_bf16(172 + N, 64, K)
+    q = Quantized(ops, orc, W)
+    ga = orc.global_scale(cal)
+    gad = ops.global_scale(bf16_dev(cal))
+    ac, as_ = ops.quantize_act(bf16_dev(a), gad)
+    al = ops.alpha(q.g_dev, gad)
+    oac, oas = orc.quantize(a, ga)
+    ref, _, sabs = orc.linear_w4a4(oac, oas, q.codes, q.scales, orc.alpha(q.g, ga))
+    for M in (1, 2, 31, 32, 33, 63, 64, 65, 97, 128):
+        out = bf16_host(ops.linear_w4a4(ac[:M], as_[:M], q.w, al))
+        gemm_check(out, ref[:M], sabs[:M])
+        need = ops.linear_w4a4_workspace_bytes(M, N, K)
+        if need:
+            ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+            gemm_check(bf16_host(ops.linear_w4a4(ac[:M], as_[:M], q.w, al, workspace=ws)), ref[:M], sabs[:M])
+
+
 def test_w4a4_deterministic(ops, orc):
     W = synth.normal_bf16(70, 1024, 1024)
     q = Quantized(ops, orc, W)
@@ -490,7 +519,8 @@ def test_dispatch_routes_and_numerics(ops, orc):
     # no activation global: always W4A16
     out, route = ops.linear(ad[:8], q.w, None, a16, None)
     assert route == 0
-    # the default threshold M* = 64: W4A16 up to 64 tokens, W4A4 above
+    # the largest threshold M* = 64 (the W4A16 kernels' limit): W4A16 up to 64
+    # tokens, W4A4 above
     ops.set_route_m_max(64)
     for M in (17, 40, 64, 65, 100):
         out, route = ops.linear(ad[:M], q.w, gad, a16, a4)
