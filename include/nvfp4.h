@@ -262,14 +262,16 @@ nvfp4_status nvfp4_linear_w4a16_ex(const void* a, int64_t M, int64_t lda, const 
  *   w                  prepared weight descriptor
  *   alpha              device fp32[1]
  *   out                bf16 [M, N], ldo >= N
- * One launch over all of K, no workspace.
+ * One launch over all of K, no workspace: 256 x 256 output tiles, or for a
+ * batch of at most 128 rows, 256 weight rows per workgroup over all M rows.
+ * K above 2^24 returns UNSUPPORTED (the kernels' 32-bit weight offsets).
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_linear_w4a4(const void* a_codes, const void* a_scales, int64_t M, const nvfp4_weight* w,
                                const float* alpha, void* out, int64_t ldo, hipStream_t stream);
 
 /* nvfp4_linear_w4a4 with a workspace for a split of K across workgroups
  * (split-K).  A small batch on a weight of a few thousand rows has few
- * 256 x 256 output tiles (N = 8704 has 34 column tiles), and one workgroup per
+ * output tiles of 256 weight rows (N = 8704 has 34), and one workgroup per
  * tile leaves most CUs idle while each works through all of K.  When the
  * tiles fill at most half the CUs, K is split into S ranges of whole 256-k
  * units (S <= 16, at least two units each); tile x range workgroups store
