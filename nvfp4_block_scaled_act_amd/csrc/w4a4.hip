@@ -350,6 +350,26 @@ __device__ __forceinline__ void store_a(const ARegs<G>& a, const AOffsets<G>& o,
   }
 }
 
+// Part `part` of store_a (8 codes of piece part / 4, dword part % 4), so the
+// staging can be spread over a step's MFMA blocks.
+template <int G>
+constexpr int store_parts() {
+  return 4 * pieces_per_thread<G>();
+}
+
+template <int G>
+__device__ __forceinline__ void store_part(const ARegs<G>& a, const AOffsets<G>& o, _Float16* __restrict__ buf,
+                                           int part) {
+  const int i = part >> 2, q = part & 3;
+  if (!has_piece<G>(i)) return;
+  // groups 2 pc (dwords 0, 1) and 2 pc + 1 (dwords 2, 3) of the piece
+  const uint32_t S = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8((a.s[i] >> o.shift[i]) >> (8 * (q >> 1)), 0));
+  const uint32_t c[4] = {a.c[i].x, a.c[i].y, a.c[i].z, a.c[i].w};
+  uint32_t v[4];
+  dequant8_f16(c[q], S, v);
+  *reinterpret_cast<uint4*>(buf + o.lds[i] + 8 * q) = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // acc[t][g] += weight tile t x activation rows 32g.. over one 256-k step.
 // Register i of lane l in acc[t][g] holds activation row 32g + 8(i/4) +
 // 4(l/32) + i%4 and weight row 32t + l%32 of the wave's 64 (the activations
@@ -376,9 +396,12 @@ __device__ __forceinline__ f16x8_t weight_a(const WTileRegs& w, int j) {
   return __builtin_bit_cast(f16x8_t, make_uint4(a[0], a[1], a[2], a[3]));
 }
 
+// The next step's activation tile (codes `an`) is dequantized into nbuf in
+// parts spread over the blocks, between their MFMAs.
 template <int G>
 __device__ __forceinline__ void step(f32x16_t (&acc)[TW][G], const WRegs& w, const _Float16* __restrict__ abuf,
-                                     int lane) {
+                                     int lane, const ARegs<G>& an, const AOffsets<G>& ao,
+                                     _Float16* __restrict__ nbuf) {
   const _Float16* brow = abuf + (lane & 31) * PITCH + 16 * (lane >> 5);
   f16x8_t B[2][G], A[2][TW];
   read_b<G>(B[0], brow, 0);
@@ -397,6 +420,8 @@ __device__ __forceinline__ void step(f32x16_t (&acc)[TW][G], const WRegs& w, con
 #pragma unroll
       for (int t = 0; t < TW; ++t) A[cur ^ 1][t] = weight_a(w.t[t], j + 1);
     }
+    constexpr int every = 16 / store_parts<G>();
+    if (j % every == every - 1) store_part<G>(an, ao, nbuf, j / every);
   }
 }
 
@@ -464,20 +489,20 @@ __global__ __launch_bounds__(kThreads) void kernel(const uint8_t* __restrict__ a
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][g][i] = 0.f;
 
-  // Ring of D stages: step st uses weights W[st % D] (loaded D steps
-  // ahead) and activation codes A[(st + 1) % D] staged at its end (loaded
-  // D - 1 steps ahead, before the weights that follow them, since loads
-  // complete in issue order: waiting for them never waits for weights a
-  // later step needs).  Loads past the range re-read its last unit (cache
-  // hits, never used).  The prologue's loads are kept in program order
-  // (scheduling barriers), so the wait counts at the loop head, which hold
-  // for the first entry as well as for the back edge, are those of the
-  // steady state.
+  // Ring of D stages: step st uses weights W[st % D] and stages the
+  // activation codes A[(st + 1) % D] of the next step during its MFMAs; both
+  // are loaded D steps ahead, the activations first: loads complete in issue
+  // order, so waiting for the codes of step st + 1 waits for nothing later
+  // than the weights of step st, which are in use.  Loads past the range
+  // re-read its last unit (cache hits, never used).  The prologue's loads are
+  // kept in program order (scheduling barriers), so the wait counts at the
+  // loop head, which hold for the first entry as well as for the back edge,
+  // are those of the steady state.
   auto unit = [&](int32_t i) { return u0 + min(i, nu - 1); };
   ARegs<G> A[D];
   WRegs W[D];
 #pragma unroll
-  for (int d = 0; d + 1 < D; ++d) {
+  for (int d = 0; d < D; ++d) {
     A[d] = load_a<G>(rac, ras, ao, unit(d));
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -492,10 +517,10 @@ __global__ __launch_bounds__(kThreads) void kernel(const uint8_t* __restrict__ a
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int32_t st = i + d;
-      if (st < nu) step<G>(acc, W[d], (st & 1) ? buf1 : buf0, lane);
-      A[(d + D - 1) % D] = load_a<G>(rac, ras, ao, unit(st + D - 1));
+      if (st < nu)
+        step<G>(acc, W[d], (st & 1) ? buf1 : buf0, lane, A[(d + 1) % D], ao, (st & 1) ? buf0 : buf1);
+      A[d] = load_a<G>(rac, ras, ao, unit(st + D));
       W[d] = load_w(rw, o, unit(st + D));
-      store_a<G>(A[(d + 1) % D], ao, (st & 1) ? buf0 : buf1);
       __syncthreads();
     }
   }
