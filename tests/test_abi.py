@@ -146,6 +146,13 @@ def test_w4a4_validation(nv):
     assert f(A16, A16, 8, C.byref(wlay), A16, A16, 64, None) == UNSUP   # not a prepared weight
     wmis = _w(data=A16 + 8)
     assert f(A16, A16, 8, C.byref(wmis), A16, A16, 64, None) == ALIGN
+    # K above 2^24: the kernels' 32-bit offsets into a workgroup's weight tiles
+    wbig = _w(K=(1 << 24) + 256)
+    assert f(A16, A16, 8, C.byref(wbig), A16, A16, 64, None) == UNSUP
+    nv.nvfp4_set_route_m_max(16)
+    r = C.c_int(-1)
+    assert nv.nvfp4_linear(A16, 32, (1 << 24) + 256, C.byref(wbig), A16, A16, A16, A16, 64, A16, 1 << 30,
+                           C.byref(r), None) == UNSUP
 
 
 def test_route_default_threshold():
@@ -265,6 +272,13 @@ def test_moe_validation(nv):
     assert call(ws_bytes=need - 1) == WS
     assert call(ws=None) == WS
     assert call(x=None, T=0, ids=None, w=None, out=None, ws=None, ws_bytes=0) == OK   # empty batch
+    # an expert's gate_up past 2^32 bytes (the grouped GEMMs' 32-bit weight offsets)
+    big = 1 << 20
+    lay = L.MoeLayout()
+    assert nv.nvfp4_moe_workspace_layout(1, 1, 1, big, big, C.byref(lay)) == UNSUP
+    assert nv.nvfp4_moe_w4a4(A16, 1, big, A16, A16, 1, 1, big, C.byref(_w(N=2 * big, K=big)),
+                             C.byref(_w(N=big, K=big)), A16, A16, A16, A16, A16, big, WS0, 1 << 40, None,
+                             None) == UNSUP
 
 
 def test_stream_read_validation(nv):
@@ -359,6 +373,8 @@ def test_gated_mlp_validation(nv):
     assert f(A16, A16, M, C.byref(gu), A16, A16, A16 + 8, A16, None, None) == ALIGN   # h codes
     assert f(A16, A16, M, C.byref(gu), A16, A16, None, A16, None, None) == ARG
     assert f(None, None, 0, C.byref(gu), A16, A16, None, None, None, None) == OK        # empty batch
+    # gate_up past 2^32 bytes (the kernel's 32-bit weight offsets)
+    assert f(A16, A16, M, C.byref(_w(N=1 << 17, K=1 << 16)), A16, A16, A16, A16, None, None) == UNSUP
 
 
 def test_swizzled_scales_validation(nv):
