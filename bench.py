@@ -585,7 +585,7 @@ def bench_w4a16_cache_policy(ops, torch, reps=5):
     return rows
 
 
-def bench_moe_decode(ops, torch, Ts=(1, 4, 16), cross_Ts=(16, 64, 256, 512, 1024, 2048), reps=3):
+def bench_moe_decode(ops, torch, Ts=(1, 4, 16), cross_Ts=(16, 64, 128, 192, 256, 512, 1024, 2048), reps=3):
     """The same MoE layer at decode batch sizes through nvfp4_moe_w4a16 (bf16
     x and h, align into entries of up to 16 pairs, grouped W4A16 gate_up with
     the SiLU gate, grouped W4A16 down, route sum).  Cold banks: each call uses
@@ -1002,7 +1002,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(r4["tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(r4["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                          "traffic": load_traffic("w4a4_prefill_m8192",
-                                                 kernel_source_hash(["w4a4.hip", "gemm_w4a4.hpp", "device.hpp"]))},
+                                                 kernel_source_hash(["w4a4.hip", "gemm_w4a4.hpp", "gemm_skinny.hpp", "device.hpp"]))},
         }
         res["prepare_weight"] = {"workload": "re-tile N=8704 K=5120 (one time, not in value)",
                                  "us": round(r4["prepare_us"], 2),

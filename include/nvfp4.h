@@ -514,10 +514,11 @@ nvfp4_status nvfp4_gated_mlp_w4a4(const void* a_codes, const void* a_scales, int
  * Changes: W4A4 prefill from 4 tokens per expert on checkpoints whose experts
  * carry static input scales, W4A16 below and for decode).
  *   nvfp4_moe_route: pure; W4A4 iff has_act_globals && T*top_k > tpe * E,
- *     else W4A16.  tpe (tokens per expert) defaults to 32, the measured
- *     crossover on MI355X at E = 128, top-8, K = 2048, I = 768 (W4A16 204 us
- *     against W4A4 203 us at T = 512, 354 against 221 at T = 1024); set it
- *     with nvfp4_set_moe_route_tokens_per_expert (negative values give 0).
+ *     else W4A16.  tpe (tokens per expert) defaults to 14, the measured
+ *     crossover on MI355X at E = 128, top-8, K = 2048, I = 768 (W4A16 108 us
+ *     against W4A4 123 us at T = 192, 12 tokens per expert; 129 against 121
+ *     at T = 256, 16 per expert); set it with
+ *     nvfp4_set_moe_route_tokens_per_expert (negative values give 0).
  *   nvfp4_moe_dispatch_workspace_bytes: the workspace of the route taken.
  *   nvfp4_moe: runs the route taken, reports it in *route_taken (may be
  *     NULL).  g1 and g2 are both given (W4A4 possible) or both NULL (W4A16

@@ -16,7 +16,7 @@ namespace {
 constexpr int64_t kInt32Max = 2147483647LL;
 constexpr int64_t kW4a4MaxK = int64_t(1) << 24;  // the W4A4 kernels' 32-bit weight offsets
 std::atomic<int64_t> g_route_m_max{16};  // measured crossover, N = 62080, K = 5120 (and most weights)
-std::atomic<int64_t> g_moe_route_tpe_max{32};  // tokens per expert up to which the MoE stays W4A16
+std::atomic<int64_t> g_moe_route_tpe_max{14};  // tokens per expert up to which the MoE stays W4A16
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }

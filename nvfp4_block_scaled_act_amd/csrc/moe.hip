@@ -18,6 +18,7 @@
 // host; workgroups past the table's live entries exit at once.
 #include <algorithm>
 
+#include "gemm_skinny.hpp"
 #include "gemm_w4a4.hpp"
 #include "kernels.hpp"
 #include "quant_exact.hpp"
@@ -290,8 +291,85 @@ __device__ __forceinline__ void gate_up_tile(_Float16* __restrict__ lds, const M
   }
 }
 
+// The same gate_up for a tile of at most 32 G pairs, on skinny::mainloop:
+// waves 0..3 compute the 128 gate rows, waves 4..7 the up rows under them;
+// z goes through LDS (fp32, [gate | up][pair row][128 + 4]) so that each
+// thread then gates and quantizes whole 16-element blocks of h.
+template <int G, class RowOf>
+__device__ __forceinline__ void gate_up_tile_few(_Float16* __restrict__ lds, const MoeTile& tile, int32_t c,
+                                                 const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+                                                 int32_t K, RowOf row_of, const uint8_t* __restrict__ wt, int32_t I,
+                                                 float alpha, float g2, uint8_t* __restrict__ hc,
+                                                 uint8_t* __restrict__ hs, uint32_t* __restrict__ h_amax) {
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6), h = lane >> 5;
+  const int32_t gate_tile0 = tile.expert * (2 * I / 16) + 8 * c, up_tile0 = gate_tile0 + I / 16;
+  f32x16_t acc[skinny::TW][G];
+  skinny::mainloop<G, skinny::depth<G>()>(
+      acc, lds, xc, xs, row_of, wt, [&](int j) { return int64_t(j < 8 ? gate_tile0 + j : up_tile0 + j - 8); }, K, 0,
+      K / 256);
+  // register i of lane l: pair row 32g + 8(i/4) + 4(l/32) + i%4, weight row
+  // 32 wave + l%32 of the workgroup's 256 (the mainloop's final barrier frees
+  // the LDS)
+  constexpr int ZP = 128 + 4;
+  float* z = reinterpret_cast<float*>(lds);
+  const int col = 32 * (wave & 3) + (lane & 31);
+  float* zw = z + (wave >> 2) * (32 * G * ZP) + col;
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) zw[(32 * g + 8 * (i >> 2) + 4 * h + (i & 3)) * ZP] = acc[0][g][i];
+  __syncthreads();
+  float hmax = 0.0f;
+  for (int task = int(threadIdx.x); task < 32 * G * 8; task += skinny::kThreads) {
+    const int m = task >> 3, b = task & 7;  // pair row, 16-element block of the 128
+    if (m >= tile.rows) continue;
+    const float4* zg = reinterpret_cast<const float4*>(z + m * ZP + 16 * b);
+    const float4* zu = reinterpret_cast<const float4*>(z + (32 * G + m) * ZP + 16 * b);
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 gv = zg[q], uv = zu[q];
+      x[4 * q] = silu(alpha * gv.x) * (alpha * uv.x);
+      x[4 * q + 1] = silu(alpha * gv.y) * (alpha * uv.y);
+      x[4 * q + 2] = silu(alpha * gv.z) * (alpha * uv.z);
+      x[4 * q + 3] = silu(alpha * gv.w) * (alpha * uv.w);
+    }
+    uint32_t c0, c1;
+    const uint32_t sc = quantize16_fast(x, g2, c0, c1);
+    const int64_t slot = int64_t(tile.slot0) + m;
+    const int32_t i0 = 128 * c + 16 * b;  // first h element of the block
+    *reinterpret_cast<uint2*>(hc + slot * (I / 2) + i0 / 2) = make_uint2(c0, c1);
+    hs[slot * (I / 16) + i0 / 16] = uint8_t(sc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) hmax = __builtin_fmaxf(hmax, __builtin_fabsf(x[i]));
+  }
+  if (h_amax) {
+    uint32_t bits = __float_as_uint(hmax);
+    for (int o = 32; o > 0; o >>= 1) bits = max(bits, uint32_t(__shfl_xor(int(bits), o, 64)));
+    if (lane == 0) atomicMax(h_amax, bits);
+  }
+}
+
+// gate_up of any tile: the few-rows loop up to 128 pairs, else the 256 x 256
+// main loop.
+template <class RowOf>
+__device__ __forceinline__ void gate_up_any(_Float16* __restrict__ lds, const MoeTile& tile, int32_t c,
+                                            const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int32_t K,
+                                            RowOf row_of, const uint8_t* __restrict__ wt, int32_t I, float alpha,
+                                            float g2, uint8_t* __restrict__ hc, uint8_t* __restrict__ hs,
+                                            uint32_t* __restrict__ h_amax) {
+  if (tile.rows <= 32)
+    gate_up_tile_few<1>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
+  else if (tile.rows <= 64)
+    gate_up_tile_few<2>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
+  else if (tile.rows <= 128)
+    gate_up_tile_few<4>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
+  else
+    gate_up_tile<gemm::BM>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
+}
+
 // Workgroup -> (tile, 128-row block c of the expert's I gate rows) by
-// gemm::xcd_row_block; tiles of at most 128 pairs take the 128-row path.
+// gemm::xcd_row_block; tiles of at most 128 pairs take the few-rows loop.
 __global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int32_t K, int32_t top_k,
     const int32_t* __restrict__ sorted, const MoeTile* __restrict__ tiles, int32_t max_tiles,
@@ -305,10 +383,7 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_gate_up_kernel(
   if (tile.rows == 0) return;
   const float alpha = alpha_gu[tile.expert], g2 = *g2_p;
   auto row_of = [&](int i) { return int64_t(sorted[tile.slot0 + min(i, tile.rows - 1)] / top_k); };
-  if (tile.rows <= gemm::BM / 2)
-    gate_up_tile<gemm::BM / 2>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
-  else
-    gate_up_tile<gemm::BM>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
+  gate_up_any(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
 }
 
 // The same gate_up on a dense batch (a gated MLP's first GEMM): row tile ty
@@ -332,10 +407,7 @@ __global__ __launch_bounds__(gemm::kThreads) void gated_mlp_kernel(
   const MoeTile tile{0, m0, min(half ? gemm::BM / 2 : gemm::BM, M - m0), 0};
   const float alpha = *alpha_p, g2 = *g2_p;
   auto row_of = [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); };
-  if (tile.rows <= gemm::BM / 2)
-    gate_up_tile<gemm::BM / 2>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
-  else
-    gate_up_tile<gemm::BM>(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
+  gate_up_any(lds, tile, c, xc, xs, K, row_of, wt, I, alpha, g2, hc, hs, h_amax);
 }
 
 // down of one tile of pairs x 256 outputs (block nblk of K) of its expert,
@@ -377,8 +449,38 @@ __device__ __forceinline__ void down_tile(_Float16* __restrict__ lds, const MoeT
     }
 }
 
+// The same down for a tile of at most 32 G pairs, on skinny::mainloop:
+// register i of lane l holds pair row 32g + 8(i/4) + 4(l/32) + i%4 and output
+// 256 nblk + 32 wave + l%32, so each store writes 32 consecutive outputs.
+template <int G>
+__device__ __forceinline__ void down_tile_few(_Float16* __restrict__ lds, const MoeTile& tile, int32_t nblk,
+                                              const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs,
+                                              int32_t I, const int32_t* __restrict__ sorted,
+                                              const float* __restrict__ topk_w, const uint8_t* __restrict__ wt,
+                                              int32_t K, float alpha, float* __restrict__ ys) {
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6), h = lane >> 5;
+  const int32_t wtile0 = tile.expert * (K / 16) + nblk * 16;
+  int32_t pr = 0;  // the row's pair, loaded before the main loop
+  if (threadIdx.x < 32 * G) pr = sorted[tile.slot0 + min(int(threadIdx.x), tile.rows - 1)];
+  f32x16_t acc[skinny::TW][G];
+  skinny::mainloop<G, skinny::depth<G>()>(
+      acc, lds, hc, hs, [&](int i) { return int64_t(tile.slot0 + min(i, tile.rows - 1)); }, wt,
+      [&](int j) { return int64_t(wtile0 + j); }, I, 0, I / 256);
+  float* s_scale = reinterpret_cast<float*>(lds);
+  if (threadIdx.x < 32 * G) s_scale[threadIdx.x] = alpha * topk_w[pr];
+  __syncthreads();
+  const int32_t n = nblk * 256 + 32 * wave + (lane & 31);
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 32 * g + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (m < tile.rows) ys[(int64_t(tile.slot0) + m) * K + n] = s_scale[m] * acc[0][g][i];
+    }
+}
+
 // Workgroup -> (tile, 256-output block of K) by gemm::xcd_row_block; tiles of
-// at most 128 pairs take the 128-row path.
+// at most 128 pairs take the few-rows loop.
 __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
     const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs, int32_t I, const int32_t* __restrict__ sorted,
     const MoeTile* __restrict__ tiles, int32_t max_tiles, const float* __restrict__ topk_w, int32_t top_k,
@@ -390,8 +492,12 @@ __global__ __launch_bounds__(gemm::kThreads) void moe_down_kernel(
   const MoeTile tile = tiles[ty];
   if (tile.rows == 0) return;
   const float alpha = alpha_dn[tile.expert];
-  if (tile.rows <= gemm::BM / 2)
-    down_tile<gemm::BM / 2>(lds, tile, nblk, hc, hs, I, sorted, topk_w, top_k, wt, K, alpha, ys);
+  if (tile.rows <= 32)
+    down_tile_few<1>(lds, tile, nblk, hc, hs, I, sorted, topk_w, wt, K, alpha, ys);
+  else if (tile.rows <= 64)
+    down_tile_few<2>(lds, tile, nblk, hc, hs, I, sorted, topk_w, wt, K, alpha, ys);
+  else if (tile.rows <= 128)
+    down_tile_few<4>(lds, tile, nblk, hc, hs, I, sorted, topk_w, wt, K, alpha, ys);
   else
     down_tile<gemm::BM>(lds, tile, nblk, hc, hs, I, sorted, topk_w, top_k, wt, K, alpha, ys);
 }

@@ -334,10 +334,10 @@ def test_moe_w4a16_workspace_and_validation(nv):
 
 
 def test_moe_route_and_dispatch_validation(nv):
-    assert nv.nvfp4_get_moe_route_tokens_per_expert() == 32
+    assert nv.nvfp4_get_moe_route_tokens_per_expert() == 14
     assert nv.nvfp4_moe_route(100000, 8, 128, 0) == 0   # no static globals: W4A16 only
-    assert nv.nvfp4_moe_route(512, 8, 128, 1) == 0      # 32 tokens per expert
-    assert nv.nvfp4_moe_route(513, 8, 128, 1) == 1
+    assert nv.nvfp4_moe_route(224, 8, 128, 1) == 0      # 14 tokens per expert
+    assert nv.nvfp4_moe_route(225, 8, 128, 1) == 1
     try:
         nv.nvfp4_set_moe_route_tokens_per_expert(4)
         assert nv.nvfp4_moe_route(64, 8, 128, 1) == 0 and nv.nvfp4_moe_route(65, 8, 128, 1) == 1
@@ -345,7 +345,7 @@ def test_moe_route_and_dispatch_validation(nv):
         assert nv.nvfp4_get_moe_route_tokens_per_expert() == 0
         assert nv.nvfp4_moe_route(1, 1, 128, 1) == 1 and nv.nvfp4_moe_route(0, 8, 128, 1) == 0
     finally:
-        nv.nvfp4_set_moe_route_tokens_per_expert(32)
+        nv.nvfp4_set_moe_route_tokens_per_expert(14)
     for T, g in ((16, 1), (16, 0), (8192, 1)):
         want = (nv.nvfp4_moe_workspace_bytes if nv.nvfp4_moe_route(T, 8, 128, g) else
                 nv.nvfp4_moe_w4a16_workspace_bytes)(T, 8, 128, 2048, 768)

@@ -219,6 +219,32 @@ def test_moe_small_multi_tile(ops, orc):
     print(f"flipped tokens {len(flipped)}/{T}, code flips {ncf}, scale flips {nsf}, {stats}")
 
 
+def test_moe_few_rows_tiles(ops, orc):
+    # expert tiles of at most 128 pairs run the few-rows GEMM loop with 1, 2
+    # or 4 groups of 32 rows: 8 experts, top-2, T=160, routed so that the
+    # tiles hold 108, 85, 53, 37, 23, 12, 2 and 0 pairs (every group count,
+    # ragged); K=768 and I=512 take 3 and 2 units of 256 k
+    E, top_k, K, I, T = 8, 2, 768, 512, 160
+    bias = np.array([1.2, 0.9, 0.5, 0.2, 0.0, -0.6, -1.2, -30.0], np.float32)
+    x, ids, w, cal, cids, cw, gate_up, down = _small_case(303, T, E, top_k, K, I, bias)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    assert (counts > 64).any() and ((counts > 32) & (counts <= 64)).any() and ((counts > 0) & (counts <= 32)).any()
+    assert counts.max() <= 128
+    banks = Banks(ops, orc, gate_up, down, orc.global_scale(cal), cal=(cal, cids, cw))
+    import torch
+
+    h_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out, ws = banks.run(ops, x, ids, w, h_amax=h_amax)
+    views = ops.moe_workspace_views(ws, T, top_k, E, K, I)
+    inv = check_align(views, ids, E)
+    tokens = np.arange(T)
+    res = banks.oracle(orc, x, ids, w)
+    flipped, ncf, nsf = check_h(views, inv, res, tokens, top_k, I)
+    stats = check_out(bf16_host(out), res, tokens, flipped)
+    assert abs(h_amax.item() - res["h_amax"]) <= 1e-5 * res["h_amax"]
+    print(f"counts {counts.tolist()}: flipped tokens {len(flipped)}/{T}, code flips {ncf}, scale flips {nsf}, {stats}")
+
+
 def test_moe_skipped_ids_and_repeat(ops, orc):
     # ids outside [0, E) add nothing; a second call on the same workspace gives
     # the same h and the same output bits (the route sum has a fixed order)
@@ -454,7 +480,7 @@ def test_moe_dispatch_routes(ops, orc):
     direct16 = ops.moe_w4a16(xd, idd, wd, b4.w_gu, b4.w_dn, E, a_gu16, a_dn16)
     direct4 = ops.moe_w4a4(xd, idd, wd, b4.w_gu, b4.w_dn, E, g1, g2, b4.alpha_gu, b4.alpha_dn)
     try:
-        for tpe, want in ((32, 0), (0, 1)):   # 40*2/4 = 20 tokens per expert
+        for tpe, want in ((20, 0), (0, 1)):   # 40*2/4 = 20 tokens per expert
             ops.set_moe_route_tokens_per_expert(tpe)
             out, route = ops.moe(xd, idd, wd, b4.w_gu, b4.w_dn, E, g1, g2, b4.alpha_gu, b4.alpha_dn, a_gu16, a_dn16)
             assert route == want
@@ -463,17 +489,20 @@ def test_moe_dispatch_routes(ops, orc):
         out, route = ops.moe(xd, idd, wd, b4.w_gu, b4.w_dn, E, None, None, None, None, a_gu16, a_dn16)
         assert route == 0 and (bf16_host(out) == bf16_host(direct16)).all()
     finally:
-        ops.set_moe_route_tokens_per_expert(32)
+        ops.set_moe_route_tokens_per_expert(14)
 
 
 # ------------------------------------------------------------ gated MLP
-@pytest.mark.parametrize("M,K,I", [(300, 512, 256), (1024, 2048, 768), (4000, 512, 2304)])
+@pytest.mark.parametrize("M,K,I", [(20, 1024, 512), (100, 512, 768), (300, 512, 256), (1024, 2048, 768),
+                                   (4000, 512, 2304)])
 def test_gated_mlp_w4a4(ops, orc, M, K, I):
     # the dense gated MLP = the MoE layer with one expert, one route of weight
     # 1: h (NVFP4 under g2) against the oracle's with benign flips, then the
-    # down linear on the GPU's h against the layer's output.  (4000, 512,
-    # 2304): 16 row tiles x 18 blocks = 288 workgroup items on 256 CUs, so the
-    # last 32 run as 128-row halves, one of them on the ragged last 32 rows
+    # down linear on the GPU's h against the layer's output.  Tiles of at most
+    # 128 rows take the few-rows loop: (20, ...) one group of 32 rows, (100,
+    # ...) four, (300, ...) a 44-row tail tile (two).  (4000, 512, 2304): 16
+    # row tiles x 18 blocks = 288 workgroup items on 256 CUs, so the last 32
+    # run as 128-row halves, one of them on the ragged last 32 rows
     import torch
 
     x, _, _, cal, _, _, gate_up, down = _small_case(707 + M, M, 1, 1, K, I, calib_rows=64)
