@@ -148,9 +148,14 @@ __device__ __forceinline__ void quantize_block(const uint32_t (&d)[8], float g, 
 
 // A wave takes kRowsPerWave rows of one 64-block column range; all their
 // loads are issued before the tables are built and the first block is
-// computed (rows past the last re-read it and are not stored).
-constexpr int kRowsPerWave = 2;
+// computed (rows past the last re-read it and are not stored).  Two rows per
+// wave suit large batches; a small batch is latency-bound, and one row per
+// wave halves each wave's serial work (next to the few-rows GEMM on N =
+// 62080, K = 5120: 6.0 -> 4.1 us at M = 64, 4.2 -> 2.7 us at M = 128; at
+// M = 8192 two rows stay faster).
+constexpr int64_t kQuantizeOneRowMax = 256;  // rows up to which a wave takes one row
 
+template <int kRowsPerWave>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ a, int64_t lda,
                                                        int32_t rows, int32_t blocks_per_row,
                                                        const float* __restrict__ g_ptr,
@@ -254,10 +259,18 @@ hipError_t launch_quantize(const void* a, int64_t M, int64_t K, int64_t lda, con
   if (M == 0) return hipSuccess;
   const int32_t bpr = int32_t(K / 16);
   const int64_t rows = swz_cols > 0 ? (M + 127) / 128 * 128 : M;  // the grid covers the padding rows
-  dim3 grid((bpr + 63) / 64, uint32_t((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave)));
-  hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a), lda,
-                     int32_t(M), bpr, g, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
-                     int32_t(swz_cols), int32_t(rows));
+  const dim3 gx((bpr + 63) / 64, 1);
+  if (rows <= kQuantizeOneRowMax) {
+    const dim3 grid(gx.x, uint32_t((rows + 3) / 4));
+    hipLaunchKernelGGL(quantize_kernel<1>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a), lda,
+                       int32_t(M), bpr, g, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                       int32_t(swz_cols), int32_t(rows));
+  } else {
+    const dim3 grid(gx.x, uint32_t((rows + 7) / 8));
+    hipLaunchKernelGGL(quantize_kernel<2>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a), lda,
+                       int32_t(M), bpr, g, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                       int32_t(swz_cols), int32_t(rows));
+  }
   return hipGetLastError();
 }
 
