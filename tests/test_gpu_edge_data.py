@@ -95,7 +95,9 @@ def test_w4a16_edge_data_every_schedule(ops, orc, M, N, K):
         gemm_check(bf16_host(out), ref[:m], sabs[:m])
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 1000, 1024), (1100, 520, 2048)])
+# M = 20 and 100 run the few-rows kernel (one and four 32-row groups, N not a
+# multiple of 256); 300 and 1100 the 256 x 256 tiles
+@pytest.mark.parametrize("M,N,K", [(20, 4104, 768), (100, 1000, 1024), (300, 1000, 1024), (1100, 520, 2048)])
 def test_w4a4_edge_data(ops, orc, M, N, K):
     codes, scales = edge_weight(300 + N, N, K)
     w = ops.prepare_weight(to_dev(codes), to_dev(scales))
