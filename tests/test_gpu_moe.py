@@ -219,12 +219,14 @@ def test_moe_small_multi_tile(ops, orc):
     print(f"flipped tokens {len(flipped)}/{T}, code flips {ncf}, scale flips {nsf}, {stats}")
 
 
-def test_moe_few_rows_tiles(ops, orc):
+@pytest.mark.parametrize("K,I", [(768, 512), (256, 256)])
+def test_moe_few_rows_tiles(ops, orc, K, I):
     # expert tiles of at most 128 pairs run the few-rows GEMM loop with 1, 2
     # or 4 groups of 32 rows: 8 experts, top-2, T=160, routed so that the
     # tiles hold 108, 85, 53, 37, 23, 12, 2 and 0 pairs (every group count,
-    # ragged); K=768 and I=512 take 3 and 2 units of 256 k
-    E, top_k, K, I, T = 8, 2, 768, 512, 160
+    # ragged); K=768 and I=512 take 3 and 2 units of 256 k, K=I=256 one unit
+    # each (the prefetch ring re-reads the only unit)
+    E, top_k, T = 8, 2, 160
     bias = np.array([1.2, 0.9, 0.5, 0.2, 0.0, -0.6, -1.2, -30.0], np.float32)
     x, ids, w, cal, cids, cw, gate_up, down = _small_case(303, T, E, top_k, K, I, bias)
     counts = np.bincount(ids.reshape(-1), minlength=E)
@@ -493,14 +495,15 @@ def test_moe_dispatch_routes(ops, orc):
 
 
 # ------------------------------------------------------------ gated MLP
-@pytest.mark.parametrize("M,K,I", [(20, 1024, 512), (100, 512, 768), (300, 512, 256), (1024, 2048, 768),
-                                   (4000, 512, 2304)])
+@pytest.mark.parametrize("M,K,I", [(20, 1024, 512), (50, 256, 256), (100, 512, 768), (300, 512, 256),
+                                   (1024, 2048, 768), (4000, 512, 2304)])
 def test_gated_mlp_w4a4(ops, orc, M, K, I):
     # the dense gated MLP = the MoE layer with one expert, one route of weight
     # 1: h (NVFP4 under g2) against the oracle's with benign flips, then the
     # down linear on the GPU's h against the layer's output.  Tiles of at most
-    # 128 rows take the few-rows loop: (20, ...) one group of 32 rows, (100,
-    # ...) four, (300, ...) a 44-row tail tile (two).  (4000, 512, 2304): 16
+    # 128 rows take the few-rows loop: (20, ...) one group of 32 rows, (50,
+    # 256, 256) two, over a single 256-k unit in both GEMMs, (100, ...) four,
+    # (300, ...) a 44-row tail tile (two).  (4000, 512, 2304): 16
     # row tiles x 18 blocks = 288 workgroup items on 256 CUs, so the last 32
     # run as 128-row halves, one of them on the ragged last 32 rows
     import torch
