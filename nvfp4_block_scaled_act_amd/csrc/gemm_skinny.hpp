@@ -76,11 +76,27 @@ struct AOffsets {
   uint32_t c[pieces_per_thread<G>()], s[pieces_per_thread<G>()];
   int32_t lds[pieces_per_thread<G>()];    // fp16 offset of the piece in an LDS buffer
   int32_t shift[pieces_per_thread<G>()];  // bit offset of the piece's two scale bytes in the dword
+  int32_t first;                          // the wave's first thread (wave-uniform)
 };
 
 template <int G>
-__device__ __forceinline__ bool has_piece(int i) {
-  return 256 * G >= kThreads * (i + 1) || __builtin_amdgcn_readfirstlane(int(threadIdx.x)) + kThreads * i < 256 * G;
+__device__ __forceinline__ bool has_piece(const AOffsets<G>& o, int i) {
+  return 256 * G >= kThreads * (i + 1) || o.first + kThreads * i < 256 * G;
+}
+
+// E4M3 scale bytes 2W and 2W + 1 of a dword as an fp16 pair, in one convert
+// (exact: every E4M3 value is an fp16 value, and the convert's unit scale
+// leaves them unchanged).
+template <bool W>
+__device__ __forceinline__ f16x2_t e4m3_pair_f16(uint32_t s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, W);
+}
+
+// Half H of a pair in both halves (the packed multiply reads it by operand
+// select, so this costs no instruction).
+template <int H>
+__device__ __forceinline__ uint32_t splat_half(f16x2_t p) {
+  return __builtin_bit_cast(uint32_t, __builtin_shufflevector(p, p, H, H));
 }
 
 __device__ __forceinline__ WRegs load_w(__amdgpu_buffer_rsrc_t rsrc, const Offsets& o, int32_t unit) {
@@ -107,7 +123,7 @@ __device__ __forceinline__ ARegs<G> load_a(__amdgpu_buffer_rsrc_t rc, __amdgpu_b
   ARegs<G> a;
 #pragma unroll
   for (int i = 0; i < pieces_per_thread<G>(); ++i) {
-    if (!has_piece<G>(i)) {
+    if (!has_piece<G>(o, i)) {
       a.c[i] = make_uint4(0, 0, 0, 0);
       a.s[i] = 0;
       continue;
@@ -124,10 +140,9 @@ template <int G>
 __device__ __forceinline__ void store_a(const ARegs<G>& a, const AOffsets<G>& o, _Float16* __restrict__ buf) {
 #pragma unroll
   for (int i = 0; i < pieces_per_thread<G>(); ++i) {
-    if (!has_piece<G>(i)) continue;
-    const uint32_t sb = a.s[i] >> o.shift[i];
-    const uint32_t S0 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(sb, 0));
-    const uint32_t S1 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(sb, 1));
+    if (!has_piece<G>(o, i)) continue;
+    const f16x2_t sp = e4m3_pair_f16<false>(a.s[i] >> o.shift[i]);
+    const uint32_t S0 = splat_half<0>(sp), S1 = splat_half<1>(sp);
     uint32_t v[4][4];
     dequant8_f16(a.c[i].x, S0, v[0]);
     dequant8_f16(a.c[i].y, S0, v[1]);
@@ -146,13 +161,28 @@ constexpr int store_parts() {
   return 4 * pieces_per_thread<G>();
 }
 
+// The scale pairs of the thread's pieces (groups 2 pc, 2 pc + 1), converted
+// once per step for all its parts.
 template <int G>
-__device__ __forceinline__ void store_part(const ARegs<G>& a, const AOffsets<G>& o, _Float16* __restrict__ buf,
-                                           int part) {
+struct AScales {
+  f16x2_t p[pieces_per_thread<G>()];
+};
+
+template <int G>
+__device__ __forceinline__ AScales<G> a_scales(const ARegs<G>& a, const AOffsets<G>& o) {
+  AScales<G> s;
+#pragma unroll
+  for (int i = 0; i < pieces_per_thread<G>(); ++i) s.p[i] = e4m3_pair_f16<false>(a.s[i] >> o.shift[i]);
+  return s;
+}
+
+template <int G>
+__device__ __forceinline__ void store_part(const ARegs<G>& a, const AScales<G>& as, const AOffsets<G>& o,
+                                           _Float16* __restrict__ buf, int part) {
   const int i = part >> 2, q = part & 3;
-  if (!has_piece<G>(i)) return;
+  if (!has_piece<G>(o, i)) return;
   // groups 2 pc (dwords 0, 1) and 2 pc + 1 (dwords 2, 3) of the piece
-  const uint32_t S = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8((a.s[i] >> o.shift[i]) >> (8 * (q >> 1)), 0));
+  const uint32_t S = (q >> 1) ? splat_half<1>(as.p[i]) : splat_half<0>(as.p[i]);
   const uint32_t c[4] = {a.c[i].x, a.c[i].y, a.c[i].z, a.c[i].w};
   uint32_t v[4];
   dequant8_f16(c[q], S, v);
@@ -174,10 +204,27 @@ __device__ __forceinline__ void read_b(f16x8_t (&B)[G], const _Float16* __restri
     B[g] = *reinterpret_cast<const f16x8_t*>(brow + 32 * g * PITCH + 32 * (j >> 1) + 8 * (j & 1));
 }
 
-// Weight operand of block j = 2J + e for tile t: codes of group 2J + h, half e.
-__device__ __forceinline__ f16x8_t weight_a(const WTileRegs& w, int j) {
-  const int J = j >> 1, e = j & 1;
-  const uint32_t S2 = f32_to_f16x2_splat(__builtin_amdgcn_cvt_f32_fp8(w.sc[J & 1] >> (8 * (J >> 1)), 0));
+// A tile's scale bytes of one step as fp16 pairs: p[d][W] holds bytes 2W,
+// 2W + 1 of scale dword d.
+struct WScales {
+  f16x2_t p[2][2];
+};
+
+__device__ __forceinline__ WScales weight_scales(const WTileRegs& w) {
+  WScales s;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    s.p[d][0] = e4m3_pair_f16<false>(w.sc[d]);
+    s.p[d][1] = e4m3_pair_f16<true>(w.sc[d]);
+  }
+  return s;
+}
+
+// Weight operand of block j = 2J + e for tile t: codes of group 2J + h, half e
+// (scale byte J / 2 of dword J % 2).
+__device__ __forceinline__ f16x8_t weight_a(const WTileRegs& w, const WScales& ws, int j) {
+  const int J = j >> 1, e = j & 1, p = J >> 1;
+  const uint32_t S2 = (p & 1) ? splat_half<1>(ws.p[J & 1][p >> 1]) : splat_half<0>(ws.p[J & 1][p >> 1]);
   const uint4& q = w.q[(J & 1) * 2 + (J >> 2)];
   const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
   uint32_t a[4];
@@ -192,10 +239,14 @@ __device__ __forceinline__ void step(f32x16_t (&acc)[TW][G], const WRegs& w, con
                                      int lane, const ARegs<G>& an, const AOffsets<G>& ao,
                                      _Float16* __restrict__ nbuf) {
   const _Float16* brow = abuf + (lane & 31) * PITCH + 16 * (lane >> 5);
+  WScales ws[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) ws[t] = weight_scales(w.t[t]);
+  const AScales<G> as = a_scales<G>(an, ao);
   f16x8_t B[2][G], A[2][TW];
   read_b<G>(B[0], brow, 0);
 #pragma unroll
-  for (int t = 0; t < TW; ++t) A[0][t] = weight_a(w.t[t], 0);
+  for (int t = 0; t < TW; ++t) A[0][t] = weight_a(w.t[t], ws[t], 0);
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int cur = j & 1;
@@ -207,10 +258,10 @@ __device__ __forceinline__ void step(f32x16_t (&acc)[TW][G], const WRegs& w, con
         acc[t][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(B[cur][g], A[cur][t], acc[t][g], 0, 0, 0);
     if (j < 15) {
 #pragma unroll
-      for (int t = 0; t < TW; ++t) A[cur ^ 1][t] = weight_a(w.t[t], j + 1);
+      for (int t = 0; t < TW; ++t) A[cur ^ 1][t] = weight_a(w.t[t], ws[t], j + 1);
     }
     constexpr int every = 16 / store_parts<G>();
-    if (j % every == every - 1) store_part<G>(an, ao, nbuf, j / every);
+    if (j % every == every - 1) store_part<G>(an, as, ao, nbuf, j / every);
   }
 }
 
@@ -256,6 +307,7 @@ __device__ __forceinline__ void mainloop(f32x16_t (&acc)[TW][G], _Float16* __res
   // MFMAs.)
   const __amdgpu_buffer_rsrc_t rac = gemm::buffer_rsrc(ac), ras = gemm::buffer_rsrc(as);
   AOffsets<G> ao;
+  ao.first = __builtin_amdgcn_readfirstlane(tid & ~63);
 #pragma unroll
   for (int i = 0; i < pieces_per_thread<G>(); ++i) {
     const int P = min(tid + kThreads * i, 256 * G - 1), l = P & 63;
